@@ -1,0 +1,154 @@
+"""Seeded synthetic inputs for sink attention.
+
+This module is shared by the tests, the benchmark and the oracle checks.  It
+only draws random numbers and rounds them to bfloat16 (round to nearest
+even); it holds none of the attention arithmetic.
+
+Draw order for every workload: sequence lengths (varlen only) -> q -> k ->
+v -> sinks, from ``numpy.random.default_rng(seed)``; q/k/v are standard
+normals drawn in float32 and rounded to bf16, sinks stay float32.
+
+Workloads take the GPT-OSS attention shape (64 query heads, 8 KV heads,
+head_dim 64, scale 1/8) with the sequence lengths the pages measure decode
+at (8192 and 32768; Perplexity, "GPT-OSS on day 0", cost and performance
+section) and the 128-token window layers (NVIDIA gpt-oss announcement, model
+description).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+# Heads whose sink is forced to -inf in the ragged varlen workload: four
+# different KV groups at four different positions inside their group.
+NO_SINK_HEADS = (0, 9, 18, 27)
+
+
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round to nearest even.
+    Inputs are finite normals, so no NaN/Inf handling is needed."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    rounding = ((u >> 16) & 1) + np.uint32(0x7FFF)
+    return ((u + rounding) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float32 (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _normal_bf16(rng: np.random.Generator, shape, std: float = 1.0):
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return round_to_bf16_bits(x)
+
+
+@dataclass
+class PrefillInputs:
+    q: np.ndarray            # uint16 bf16 bits [T, Hq, D]
+    k: np.ndarray            # uint16 bf16 bits [T, Hkv, D]
+    v: np.ndarray            # uint16 bf16 bits [T, Hkv, D]
+    sinks: np.ndarray        # float32 [Hq]
+    cu_seqlens: np.ndarray   # int32 [B+1]
+    scale: float
+    lengths: list = field(default_factory=list)
+
+    @property
+    def max_seqlen(self) -> int:
+        return int(max(self.lengths)) if self.lengths else 0
+
+
+@dataclass
+class DecodeInputs:
+    q: np.ndarray            # uint16 bf16 bits [B, Hq, D]
+    k: np.ndarray            # uint16 bf16 bits [Tk, Hkv, D]
+    v: np.ndarray            # uint16 bf16 bits [Tk, Hkv, D]
+    sinks: np.ndarray        # float32 [Hq]
+    cu_seqlens_k: np.ndarray  # int32 [B+1]
+    scale: float
+    lengths: list = field(default_factory=list)
+
+    @property
+    def max_seqlen(self) -> int:
+        return int(max(self.lengths)) if self.lengths else 0
+
+
+def _cu(lengths) -> np.ndarray:
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
+    return cu
+
+
+def make_prefill(lengths, hq: int, hkv: int, d: int = 64, seed: int = 0,
+                 scale: float = 0.125, sink_std: float = 1.0,
+                 no_sink_heads=(), rng: Optional[np.random.Generator] = None):
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    lengths = [int(x) for x in lengths]
+    t = int(sum(lengths))
+    q = _normal_bf16(rng, (t, hq, d))
+    k = _normal_bf16(rng, (t, hkv, d))
+    v = _normal_bf16(rng, (t, hkv, d))
+    sinks = rng.standard_normal(size=hq, dtype=np.float32)
+    if sink_std != 1.0:
+        sinks = sinks * np.float32(sink_std)
+    for h in no_sink_heads:
+        sinks[h] = -np.inf
+    return PrefillInputs(q, k, v, sinks.astype(np.float32), _cu(lengths), scale, lengths)
+
+
+def make_decode(lengths, hq: int, hkv: int, d: int = 64, seed: int = 0,
+                scale: float = 0.125, sink_std: float = 1.0,
+                rng: Optional[np.random.Generator] = None):
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    lengths = [int(x) for x in lengths]
+    tk = int(sum(lengths))
+    q = _normal_bf16(rng, (len(lengths), hq, d))
+    k = _normal_bf16(rng, (tk, hkv, d))
+    v = _normal_bf16(rng, (tk, hkv, d))
+    sinks = rng.standard_normal(size=hq, dtype=np.float32)
+    if sink_std != 1.0:
+        sinks = sinks * np.float32(sink_std)
+    return DecodeInputs(q, k, v, sinks.astype(np.float32), _cu(lengths), scale, lengths)
+
+
+def ragged_lengths(rng: np.random.Generator, n: int = 32, lo: int = 128, hi: int = 32768):
+    """Log-uniform lengths round(exp(U[ln lo, ln hi]))."""
+    u = rng.uniform(math.log(lo), math.log(hi), size=n)
+    return [int(x) for x in np.clip(np.rint(np.exp(u)), lo, hi).astype(np.int64)]
+
+
+# ---------------------------------------------------------------------------
+# The five named workloads
+# ---------------------------------------------------------------------------
+
+def tiny_prefill(seed: int = 0) -> PrefillInputs:
+    """1 sequence of 256 tokens, 4 query heads / 1 KV head, causal."""
+    return make_prefill([256], hq=4, hkv=1, seed=seed)
+
+
+def gptoss_prefill(seed: int = 0, length: int = 8192) -> PrefillInputs:
+    """Batch 1, 8192 tokens, 64/8 heads (run causal and with a 128 window)."""
+    return make_prefill([length], hq=64, hkv=8, seed=seed)
+
+
+def gptoss_decode(seed: int = 0, batch: int = 64, ctx: int = 8192) -> DecodeInputs:
+    """64 sequences with 8192 cached tokens each, 64/8 heads, full attention."""
+    return make_decode([ctx] * batch, hq=64, hkv=8, seed=seed)
+
+
+def long_decode(seed: int = 0, batch: int = 16, ctx: int = 32768) -> DecodeInputs:
+    """16 sequences with 32768 cached tokens, sinks ~ N(0, 2) (std sqrt 2)."""
+    return make_decode([ctx] * batch, hq=64, hkv=8, seed=seed, sink_std=math.sqrt(2.0))
+
+
+def ragged_prefill(seed: int = 0, n: int = 32) -> PrefillInputs:
+    """32 sequences, lengths log-uniform in [128, 32768], 4 heads without sink."""
+    rng = np.random.default_rng(seed)
+    lengths = ragged_lengths(rng, n)
+    return make_prefill(lengths, hq=64, hkv=8, rng=rng, no_sink_heads=NO_SINK_HEADS)

@@ -1,0 +1,18 @@
+"""CPU float64 oracle for GPT-OSS-style sink attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and
+its Python binding) may import, call or link anything under this directory;
+only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` use it.  It shares no code with the GPU path.
+"""
+
+from .sink_attention import (  # noqa: F401
+    LOG2E,
+    decode_key_range,
+    decode_ref,
+    decode_split_partials_ref,
+    merge_ref,
+    prefill_mask_ref,
+    prefill_varlen_ref,
+    split_chunks_ref,
+)

@@ -1,0 +1,46 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case copies the oracle into a temporary directory, plants one mistake in
+the copy (never in the repository) and checks that the pin suite
+(tests/test_oracle_pins.py) then fails.  The mistakes: the sink multiplied by
+the softmax scale (in the max or in the denominator), the sink dropped, the
+window one key too wide, the sink in every split, the decode window one key
+too wide, the wrong GQA grouping, a base-2 lse, an unweighted merge.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTATIONS = [
+    ("big_m = np.maximum(row_max, z)", "big_m = np.maximum(row_max, z * scale)"),
+    ("den = np.exp(z - m_safe) + e.sum(axis=1)", "den = np.exp(z * scale - m_safe) + e.sum(axis=1)"),
+    ("den = np.exp(z - m_safe) + e.sum(axis=1)", "den = e.sum(axis=1)"),
+    ("valid &= jj > ii - window", "valid &= jj >= ii - window"),
+    ("zs = z[h] if s == 0 else -np.inf", "zs = z[h]"),
+    ("lo = max(0, length - window) if window > 0 else 0", "lo = max(0, length - window - 1) if window > 0 else 0"),
+    ("g = h // group", "g = h % (hq // group)"),
+    ("m_safe + np.log(np.where(has, den, 1.0))", "m_safe + np.log2(np.where(has, den, 1.0))"),
+    ("num = (w[..., None] * o_parts).sum(axis=0)", "num = o_parts.sum(axis=0)"),
+]
+
+
+@pytest.mark.parametrize("old,new", MUTATIONS, ids=[str(i) for i in range(len(MUTATIONS))])
+def test_pins_catch_planted_mistake(tmp_path, old, new):
+    for sub in ("oracle", "tests", "attention_gqa_flash_amd"):
+        shutil.copytree(os.path.join(ROOT, sub), tmp_path / sub,
+                        ignore=shutil.ignore_patterns("__pycache__", "*.so", "csrc"))
+    src = tmp_path / "oracle" / "sink_attention.py"
+    text = src.read_text()
+    assert old in text, "mutation anchor not found in the oracle"
+    src.write_text(text.replace(old, new))
+    proc = subprocess.run(
+        [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+         "tests/test_oracle_pins.py"],
+        cwd=tmp_path, capture_output=True, text=True, timeout=600)
+    assert proc.returncode != 0, "pins did not catch: %s -> %s\n%s" % (old, new, proc.stdout[-2000:])

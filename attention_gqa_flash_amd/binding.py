@@ -1,0 +1,181 @@
+"""ctypes binding of libsinkattn.so (argument marshalling only).
+
+Every step of the computation runs in the HIP library; this module checks
+tensor dtypes/devices/shapes, allocates outputs with torch, and passes raw
+device pointers and the current HIP stream across the C ABI declared in
+include/sinkattn.h.  If the library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libsinkattn.so")
+_lib = None
+
+_STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP"}
+
+
+class SinkAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("sinkattn %s: %s" % (_STATUS.get(status, str(status)), message))
+        self.status = status
+
+
+def library() -> ctypes.CDLL:
+    """Load (once) and return the HIP library; raise if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise SinkAttnError(-1, "%s is missing: build it with `python -m attention_gqa_flash_amd.build`"
+                            % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.sinkattn_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                                            vp, vp, vp]
+    lib.sinkattn_prefill_varlen.restype = ctypes.c_int
+    lib.sinkattn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.sinkattn_decode_workspace_bytes.restype = sz
+    lib.sinkattn_decode_splitkv.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, f32, i32,
+                                            vp, sz, vp, vp, vp]
+    lib.sinkattn_decode_splitkv.restype = ctypes.c_int
+    lib.sinkattn_merge_lse.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.sinkattn_merge_lse.restype = ctypes.c_int
+    lib.sinkattn_last_error.argtypes = []
+    lib.sinkattn_last_error.restype = ctypes.c_char_p
+    lib.sinkattn_version.argtypes = []
+    lib.sinkattn_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = library().sinkattn_last_error().decode()
+        raise SinkAttnError(status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dimensions (got %d)" % (name, ndim, t.dim()))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: Optional[torch.Tensor],
+                   cu_seqlens: torch.Tensor, max_seqlen: int, window: int = 0, softmax_scale: float = 0.125,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   return_lse: bool = False):
+    """Varlen prefill.  q [T, Hq, 64] bf16, k/v [T, Hkv, 64] bf16, sinks [Hq]
+    fp32 or None, cu_seqlens [B+1] int32 (device).  Returns o (and lse)."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k, "k", torch.bfloat16, 3)
+    _need(v, "v", torch.bfloat16, 3)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    t, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (t, hkv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [T, Hkv, D] matching q")
+    if sinks is not None:
+        _need(sinks, "sinks", torch.float32, 1)
+        if sinks.shape[0] != hq:
+            raise ValueError("sinks must have num_q_heads entries")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.bfloat16, 3)
+        if out.shape != q.shape:
+            raise ValueError("out must match q")
+    if return_lse and lse is None:
+        lse = torch.empty((t, hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2)
+        if lse.shape != (t, hq):
+            raise ValueError("lse must be [T, Hq]")
+    _check(library().sinkattn_prefill_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(cu_seqlens), cu_seqlens.shape[0] - 1,
+        int(max_seqlen), t, hq, hkv, d, int(window), float(softmax_scale), _ptr(out), _ptr(lse),
+        _stream(q.device)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def decode_workspace_bytes(batch: int, num_q_heads: int, head_dim: int, num_splits: int) -> int:
+    return int(library().sinkattn_decode_workspace_bytes(batch, num_q_heads, head_dim, num_splits))
+
+
+def decode_splitkv(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   cu_seqlens_k: torch.Tensor, max_seqlen_k: int, sinks: Optional[torch.Tensor],
+                   window: int = 0, softmax_scale: float = 0.125, num_splits: int = 1,
+                   workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, return_lse: bool = False):
+    """Split-KV decode.  q [B, Hq, 64] bf16, k/v cache [Tk, Hkv, 64] bf16
+    packed by cu_seqlens_k [B+1] int32.  ``workspace`` (uint8, device) is
+    allocated here when needed and not given."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 3)
+    _need(v_cache, "v_cache", torch.bfloat16, 3)
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    bsz, hq, d = q.shape
+    hkv = k_cache.shape[1]
+    if v_cache.shape != k_cache.shape or k_cache.shape[2] != d:
+        raise ValueError("k_cache and v_cache must be [Tk, Hkv, D] matching q")
+    if cu_seqlens_k.shape[0] != bsz + 1:
+        raise ValueError("cu_seqlens_k must have batch + 1 entries")
+    if sinks is not None:
+        _need(sinks, "sinks", torch.float32, 1)
+        if sinks.shape[0] != hq:
+            raise ValueError("sinks must have num_q_heads entries")
+    need = decode_workspace_bytes(bsz, hq, d, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((bsz, hq), dtype=torch.float32, device=q.device)
+    _check(library().sinkattn_decode_splitkv(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_k), bsz, int(max_seqlen_k), _ptr(sinks),
+        hq, hkv, d, int(window), float(softmax_scale), int(num_splits), _ptr(workspace), ws_bytes,
+        _ptr(out), _ptr(lse), _stream(q.device)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def merge_lse(o_parts: torch.Tensor, lse_parts: torch.Tensor, out: Optional[torch.Tensor] = None,
+              lse: Optional[torch.Tensor] = None, return_lse: bool = False):
+    """Merge partials o_parts [S, N, H, 64] fp32 with lse_parts [S, N, H]."""
+    _need(o_parts, "o_parts", torch.float32, 4)
+    _need(lse_parts, "lse_parts", torch.float32, 3)
+    s, n, h, d = o_parts.shape
+    if lse_parts.shape != (s, n, h):
+        raise ValueError("lse_parts must be [S, N, H]")
+    if out is None:
+        out = torch.empty((n, h, d), dtype=torch.bfloat16, device=o_parts.device)
+    if return_lse and lse is None:
+        lse = torch.empty((n, h), dtype=torch.float32, device=o_parts.device)
+    _check(library().sinkattn_merge_lse(_ptr(o_parts), _ptr(lse_parts), s, n, h, d, _ptr(out), _ptr(lse),
+                                        _stream(o_parts.device)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def version() -> str:
+    return library().sinkattn_version().decode()

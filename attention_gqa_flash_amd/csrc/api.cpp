@@ -1,0 +1,155 @@
+// C ABI of the sink-attention library: argument validation, workspace
+// sizing, and launches on the caller's stream.  See include/sinkattn.h for
+// the contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.hpp"
+#include "sinkattn.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sinkattn_status fail(sinkattn_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+sinkattn_status ok() {
+  g_last_error.clear();
+  return SINKATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+sinkattn_status check_heads(int32_t hq, int32_t hkv, int32_t head_dim) {
+  if (hq < 1 || hkv < 1) return fail(SINKATTN_ERR_INVALID_ARG, "head counts must be >= 1 (got %d, %d)", hq, hkv);
+  if (hq % hkv != 0)
+    return fail(SINKATTN_ERR_INVALID_ARG, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)", hq, hkv);
+  if (head_dim != 64) return fail(SINKATTN_ERR_UNSUPPORTED, "head_dim %d is not supported (only 64)", head_dim);
+  return SINKATTN_OK;
+}
+
+sinkattn_status check_scale(float scale) {
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(SINKATTN_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  return SINKATTN_OK;
+}
+
+sinkattn_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SINKATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sinkattn_last_error(void) { return g_last_error.c_str(); }
+
+const char* sinkattn_version(void) { return "sinkattn 0.1.0 (gfx950)"; }
+
+sinkattn_status sinkattn_prefill_varlen(const void* q, const void* k, const void* v, const float* sinks,
+                                        const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
+                                        int32_t total_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t window, float softmax_scale, void* o,
+                                        float* lse, void* stream) {
+  if (batch < 0 || max_seqlen < 0 || total_tokens < 0)
+    return fail(SINKATTN_ERR_INVALID_ARG, "batch, max_seqlen and total_tokens must be >= 0");
+  sinkattn_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
+  if (st != SINKATTN_OK) return st;
+  if ((st = check_scale(softmax_scale)) != SINKATTN_OK) return st;
+  if (batch == 0 || max_seqlen == 0 || total_tokens == 0) return ok();
+  if (!q || !k || !v || !o || !cu_seqlens)
+    return fail(SINKATTN_ERR_INVALID_ARG, "q, k, v, o and cu_seqlens must not be NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(SINKATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if (max_seqlen > total_tokens)
+    return fail(SINKATTN_ERR_INVALID_ARG, "max_seqlen (%d) exceeds total_tokens (%d)", max_seqlen, total_tokens);
+  const long long qtiles = (static_cast<long long>(max_seqlen) + sinkattn::prefill_qtile() - 1) / sinkattn::prefill_qtile();
+  if (qtiles > sinkattn::prefill_max_qtiles())
+    return fail(SINKATTN_ERR_UNSUPPORTED, "max_seqlen %d is too long for one launch", max_seqlen);
+  const int group = num_q_heads / num_kv_heads;
+  const long long blocks_x = static_cast<long long>(num_kv_heads) * ((group + 7) / 8) * batch;
+  if (blocks_x > 0x7fffffffLL) return fail(SINKATTN_ERR_UNSUPPORTED, "too many (batch, head) work items");
+  sinkattn::PrefillLaunch a{q, k, v, sinks, cu_seqlens, batch, max_seqlen, num_q_heads, num_kv_heads,
+                            window, softmax_scale, o, lse};
+  return hip_status(sinkattn::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
+}
+
+size_t sinkattn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t num_splits) {
+  if (batch < 0 || num_q_heads < 0 || head_dim < 0 || num_splits <= 1) return 0;
+  const size_t rows = static_cast<size_t>(num_splits) * batch * num_q_heads;
+  return round_up(rows * head_dim * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
+}
+
+sinkattn_status sinkattn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_k,
+                                        const float* sinks, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t window, float softmax_scale,
+                                        int32_t num_splits, void* workspace, size_t workspace_bytes, void* o,
+                                        float* lse, void* stream) {
+  if (batch < 0 || max_seqlen_k < 0) return fail(SINKATTN_ERR_INVALID_ARG, "batch and max_seqlen_k must be >= 0");
+  sinkattn_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
+  if (st != SINKATTN_OK) return st;
+  if ((st = check_scale(softmax_scale)) != SINKATTN_OK) return st;
+  if (num_splits < 1 || num_splits > 65536)
+    return fail(SINKATTN_ERR_INVALID_ARG, "num_splits must be in [1, 65536] (got %d)", num_splits);
+  if (num_q_heads / num_kv_heads > sinkattn::decode_max_group())
+    return fail(SINKATTN_ERR_UNSUPPORTED, "decode supports at most %d query heads per KV head",
+                sinkattn::decode_max_group());
+  if (batch == 0) return ok();
+  if (!q || !k_cache || !v_cache || !o || !cu_seqlens_k)
+    return fail(SINKATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, o and cu_seqlens_k must not be NULL");
+  if (max_seqlen_k < 1) return fail(SINKATTN_ERR_INVALID_ARG, "decode needs max_seqlen_k >= 1");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(SINKATTN_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be 16-byte aligned");
+  const long long blocks = static_cast<long long>(batch) * num_kv_heads * num_splits;
+  if (blocks > 0x7fffffffLL) return fail(SINKATTN_ERR_UNSUPPORTED, "too many (batch, head, split) work items");
+
+  sinkattn::DecodeLaunch a{q, k_cache, v_cache, sinks, cu_seqlens_k, batch, num_q_heads, num_kv_heads,
+                           window, num_splits, softmax_scale, o, lse, nullptr, nullptr};
+  if (num_splits == 1) return hip_status(sinkattn::launch_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
+
+  const size_t need = sinkattn_decode_workspace_bytes(batch, num_q_heads, head_dim, num_splits);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(SINKATTN_ERR_WORKSPACE, "workspace of %zu bytes is too small (need %zu)", workspace_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SINKATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const size_t rows = static_cast<size_t>(num_splits) * batch * num_q_heads;
+  char* ws = static_cast<char*>(workspace);
+  a.o_part = reinterpret_cast<float*>(ws);
+  a.lse_part = reinterpret_cast<float*>(ws + round_up(rows * head_dim * sizeof(float), 256));
+  hipError_t e = sinkattn::launch_decode(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_status(e, "decode launch");
+  sinkattn::MergeLaunch m{a.o_part, a.lse_part, num_splits, batch, num_q_heads, o, lse};
+  return hip_status(sinkattn::launch_merge(m, static_cast<hipStream_t>(stream)), "merge launch");
+}
+
+sinkattn_status sinkattn_merge_lse(const float* o_parts, const float* lse_parts, int32_t num_parts, int32_t n,
+                                   int32_t num_heads, int32_t head_dim, void* o, float* lse, void* stream) {
+  if (num_parts < 1 || n < 0 || num_heads < 1)
+    return fail(SINKATTN_ERR_INVALID_ARG, "need num_parts >= 1, n >= 0, num_heads >= 1");
+  if (head_dim != 64) return fail(SINKATTN_ERR_UNSUPPORTED, "head_dim %d is not supported (only 64)", head_dim);
+  if (n == 0) return ok();
+  if (!o_parts || !lse_parts || !o) return fail(SINKATTN_ERR_INVALID_ARG, "o_parts, lse_parts and o must not be NULL");
+  if (!aligned16(o_parts) || !aligned16(o)) return fail(SINKATTN_ERR_INVALID_ARG, "o_parts and o must be 16-byte aligned");
+  const long long rows = static_cast<long long>(n) * num_heads;
+  if (rows > 0x7fffffffLL) return fail(SINKATTN_ERR_UNSUPPORTED, "too many rows");
+  sinkattn::MergeLaunch m{o_parts, lse_parts, num_parts, n, num_heads, o, lse};
+  return hip_status(sinkattn::launch_merge(m, static_cast<hipStream_t>(stream)), "merge launch");
+}
+
+}  // extern "C"

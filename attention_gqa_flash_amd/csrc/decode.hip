@@ -1,0 +1,257 @@
+// Split-KV decode with per-head sinks, and the log-sum-exp merge (gfx950).
+//
+// Operation: Perplexity, "GPT-OSS on day 0", section "GPT-OSS kernels / Sink
+// attention": attention is parallelised over heads and over the KV length;
+// when the KV length is split into chunks, the sink-initialised running max
+// (and the denominator's initial 1) belongs to the first chunk only.  The
+// partial results are combined with the log-sum-exp merge that the running
+// (max, denominator) pair implies (the page does not print the formula).
+//
+// Decode kernel: one workgroup per (sequence, KV head, split).  The chunk of
+// keys is streamed once and applied to all G query heads of the KV head (the
+// G heads are the N columns of S^T = K Q^T).  Each of the 4 waves walks
+// every 4th 32-key tile of the chunk with its own online-softmax state; the
+// waves are merged through LDS at the end.  K goes straight from HBM into the
+// MFMA A-operand registers (16-byte loads); V goes through a wave-private LDS
+// tile so that it can be read transposed for O^T = V^T P^T.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace sinkattn {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kKeys = 32;  // keys per wave iteration
+
+__global__ __launch_bounds__(kThreads) void decode_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ sinks,
+    const int32_t* __restrict__ cu_seqlens_k, int batch, int hq, int hkv, int group,
+    int window, float scale_log2, int num_splits, uint16_t* __restrict__ o,
+    float* __restrict__ lse, float* __restrict__ o_part, float* __restrict__ lse_part) {
+  // Wave-private V staging tiles (first 16 KiB); the whole buffer is reused
+  // for the cross-wave merge of up to 32 heads x 64 d per wave.
+  __shared__ __attribute__((aligned(16))) float lds_buf[kWaves * 32 * kHeadDim];
+  __shared__ float red_m[kWaves][32];
+  __shared__ float red_l[kWaves][32];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 31;   // query head within the group
+  const int half = lane >> 5;
+
+  int x = blockIdx.x;
+  const int split = x % num_splits;
+  x /= num_splits;
+  const int g = x % hkv;
+  const int b = x / hkv;
+
+  const int base = cu_seqlens_k[b];
+  const int len = cu_seqlens_k[b + 1] - base;
+  const int lo = window > 0 ? max(0, len - window) : 0;
+  const int n = len - lo;
+  const int chunk = n > 0 ? (n + num_splits - 1) / num_splits : 0;
+  const int a = min(len, lo + split * chunk);
+  const int e = min(len, lo + (split + 1) * chunk);
+
+  const bool col_ok = col < group;
+  const int head = g * group + (col_ok ? col : 0);
+
+  bf16x8_t qreg[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    u32x4_t val = zero_u32x4();
+    if (col_ok) val = load16(q + (static_cast<size_t>(b) * hq + head) * kHeadDim + 16 * s + 8 * half);
+    qreg[s] = __builtin_bit_cast(bf16x8_t, val);
+  }
+
+  // The sink seeds wave 0 of split 0 only.
+  float m2 = kNegInf, lsum = 0.0f;
+  if (split == 0 && wave == 0 && sinks != nullptr && col_ok) {
+    const float z = sinks[head];
+    if (z > kNegInf) {
+      m2 = z * kLog2e;
+      lsum = half == 0 ? 1.0f : 0.0f;
+    }
+  }
+  f32x16_t acc[2] = {zero16(), zero16()};
+
+  uint16_t* vt = reinterpret_cast<uint16_t*>(lds_buf) + wave * kKeys * kHeadDim;
+  const int grp_lane = lane & 15;
+  const int dcol0 = 16 * ((lane >> 4) & 1) + 4 * (grp_lane & 3);
+
+  for (int k0 = a + kKeys * wave; k0 < e; k0 += kKeys * kWaves) {
+    // K rows as the A operand (row m <- key k0 + key_of_row(m)).
+    const int krow = k0 + key_of_row(col);
+    bf16x8_t ka[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4_t val = zero_u32x4();
+      if (krow < e) val = load16(k + (static_cast<size_t>(base + krow) * hkv + g) * kHeadDim + 16 * s + 8 * half);
+      ka[s] = __builtin_bit_cast(bf16x8_t, val);
+    }
+    // V rows into the wave's LDS tile (coalesced: 8 lanes per 128-byte row).
+    u32x4_t vv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (lane >> 3) + 8 * i;
+      const int key = k0 + r;
+      vv[i] = zero_u32x4();
+      if (key < e) vv[i] = load16(v + (static_cast<size_t>(base + key) * hkv + g) * kHeadDim + (lane & 7) * 8);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // previous tile's reads are done
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (lane >> 3) + 8 * i;
+      *reinterpret_cast<u32x4_t*>(vt + swz(r, (lane & 7) * 8)) = vv[i];
+    }
+
+    f32x16_t sacc = zero16();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sacc = mfma_32x32x16(ka[s], qreg[s], sacc);
+
+    if (k0 + kKeys > e) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (k0 + key_of_reg(r, half) >= e) sacc[r] = kNegInf;
+    }
+
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+    mx = pair_max(mx);
+    const float m_new = fmaxf(m2, mx * scale_log2);
+    const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
+    const float alpha = fast_exp2(m2 - m_use);
+    m2 = m_new;
+    float psum = 0.0f;
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const float p = fast_exp2(sacc[8 * u + tt] * scale_log2 - m_use);
+        psum += p;
+        pb[u][tt] = static_cast<__bf16>(p);
+      }
+    }
+    lsum = lsum * alpha + psum;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // V tile written
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int rbase = 16 * u + 8 * half + (grp_lane >> 2);
+        const int dcol = 32 * db + dcol0;
+        const bf16x8_t av = cat4(lds_read_tr(vt + swz(rbase, dcol)), lds_read_tr(vt + swz(rbase + 4, dcol)));
+        acc[db] = mfma_32x32x16(av, pb[u], acc[db]);
+      }
+    }
+  }
+
+  // Cross-wave merge.  Each wave publishes (m, l, unnormalised O) per head.
+  const float den = pair_sum(lsum);
+  __syncthreads();  // all waves are done with their V tiles
+  float* red_o = lds_buf;  // [wave][group][64 d]
+  if (half == 0) {
+    red_m[wave][col] = m2;
+    red_l[wave][col] = den;
+  }
+  if (col_ok) {
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = 32 * db + 8 * (r >> 2) + 4 * half + (r & 3);
+        red_o[(wave * group + col) * kHeadDim + d] = acc[db][r];
+      }
+  }
+  __syncthreads();
+
+  for (int idx = tid; idx < group * kHeadDim; idx += kThreads) {
+    const int hc = idx / kHeadDim;
+    const int d = idx % kHeadDim;
+    float big_m = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) big_m = fmaxf(big_m, red_m[w][hc]);
+    float out = 0.0f, out_lse = kNegInf;
+    if (big_m > kNegInf) {
+      float num = 0.0f, tot = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float sc = fast_exp2(red_m[w][hc] - big_m);
+        tot += sc * red_l[w][hc];
+        num += sc * red_o[(w * group + hc) * kHeadDim + d];
+      }
+      out = num / tot;
+      out_lse = (big_m + __log2f(tot)) * kLn2;
+    }
+    const int h = g * group + hc;
+    if (num_splits == 1) {
+      o[(static_cast<size_t>(b) * hq + h) * kHeadDim + d] = to_bf16_bits(out);
+      if (lse != nullptr && d == 0) lse[static_cast<size_t>(b) * hq + h] = out_lse;
+    } else {
+      const size_t prow = (static_cast<size_t>(split) * batch + b) * hq + h;
+      o_part[prow * kHeadDim + d] = out;
+      if (d == 0) lse_part[prow] = out_lse;
+    }
+  }
+}
+
+// One wave per (row, head); lane = d.
+__global__ __launch_bounds__(kThreads) void merge_kernel(
+    const float* __restrict__ o_parts, const float* __restrict__ lse_parts, int num_parts,
+    int rows, uint16_t* __restrict__ o, float* __restrict__ lse) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  float big_m = kNegInf;
+  for (int s = 0; s < num_parts; ++s) big_m = fmaxf(big_m, lse_parts[static_cast<size_t>(s) * rows + row]);
+  float out = 0.0f, out_lse = kNegInf;
+  if (big_m > kNegInf) {
+    float num = 0.0f, tot = 0.0f;
+    for (int s = 0; s < num_parts; ++s) {
+      const size_t pr = static_cast<size_t>(s) * rows + row;
+      const float w = fast_exp2((lse_parts[pr] - big_m) * kLog2e);
+      tot += w;
+      num += w * o_parts[pr * kHeadDim + lane];
+    }
+    out = num / tot;
+    out_lse = big_m + __log2f(tot) * kLn2;
+  }
+  o[static_cast<size_t>(row) * kHeadDim + lane] = to_bf16_bits(out);
+  if (lse != nullptr && lane == 0) lse[row] = out_lse;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const unsigned blocks = static_cast<unsigned>(a.batch) * a.num_kv_heads * a.num_splits;
+  hipLaunchKernelGGL(decode_kernel, dim3(blocks), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), a.sinks, a.cu_seqlens_k, a.batch,
+                     a.num_q_heads, a.num_kv_heads, group, a.window, a.softmax_scale * kLog2e,
+                     a.num_splits, static_cast<uint16_t*>(a.o), a.lse, a.o_part, a.lse_part);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream) {
+  const int rows = a.n * a.num_heads;
+  const unsigned blocks = static_cast<unsigned>((rows + kWaves - 1) / kWaves);
+  hipLaunchKernelGGL(merge_kernel, dim3(blocks), dim3(kThreads), 0, stream, a.o_parts, a.lse_parts,
+                     a.num_parts, rows, static_cast<uint16_t*>(a.o), a.lse);
+  return hipGetLastError();
+}
+
+int decode_max_group() { return 32; }
+
+}  // namespace sinkattn

@@ -1,0 +1,170 @@
+/*
+ * sinkattn -- grouped-query attention with a learned per-head sink logit,
+ * for AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The operation (Perplexity, "GPT-OSS on day 0", sections "Hopper: attention
+ * with sinks (GQA)" and "GPT-OSS kernels / Sink attention"): every query head
+ * h owns one scalar sink z_h that joins the softmax as an extra logit with no
+ * value vector.  For query row i with valid key set J(i):
+ *
+ *     s_j = softmax_scale * <q_i, k_j>,   M = max(z_h, max_j s_j)
+ *     den = exp(z_h - M) + sum_j exp(s_j - M)
+ *     o_i = sum_j exp(s_j - M) v_j / den,   lse_i = M + ln(den)
+ *
+ * The sink is in logit units: softmax_scale multiplies q.k only.  The online
+ * form starts the running max at z_h and the denominator at 1; when the key
+ * sequence is split, only the first split starts from the sink.  Layers are
+ * either causal over the full context or restricted to a sliding window of
+ * the last W keys (NVIDIA gpt-oss announcement, model description: full
+ * context and 128-token window layers alternate).  Window semantics: query i
+ * sees key j iff j <= i and (W <= 0 or j > i - W); W counts the query itself.
+ *
+ * GQA mapping: query head h reads KV head h / G with G = Hq / Hkv.
+ *
+ * Conventions shared by every entry point:
+ *  - Every pointer is a DEVICE pointer except where stated; q/k/v/o/workspace
+ *    must be 16-byte aligned.  Tensors are dense row-major with the layouts
+ *    given below (token-major, then head, then head_dim).
+ *  - bf16 is stored as raw 16-bit patterns (uint16); outputs are rounded to
+ *    nearest even from fp32 accumulators.
+ *  - The caller allocates and owns every buffer, including the workspace.
+ *    These entry points never allocate or free device memory and never
+ *    synchronise: work is enqueued on `stream` (a hipStream_t passed as
+ *    void*; NULL is the default stream) and the call returns.
+ *  - Host-checkable argument errors return a status before anything is
+ *    launched; a launch failure returns SINKATTN_ERR_HIP.  The message of the
+ *    last failure on the calling thread is sinkattn_last_error().  No C++
+ *    exception crosses this interface.
+ *  - Device-side preconditions, not checked: cu_seqlens is non-decreasing
+ *    with cu_seqlens[0] = 0 and every length <= max_seqlen; decode lengths
+ *    are >= 1; sinks are finite or -inf (-inf = that head has no sink);
+ *    inputs hold no NaN/Inf.
+ *  - Supported shapes: head_dim == 64 (other values: SINKATTN_ERR_UNSUPPORTED),
+ *    num_q_heads % num_kv_heads == 0, softmax_scale finite and > 0.
+ */
+#ifndef SINKATTN_H_
+#define SINKATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define SINKATTN_API __attribute__((visibility("default")))
+#else
+#define SINKATTN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sinkattn_status {
+  SINKATTN_OK = 0,
+  SINKATTN_ERR_INVALID_ARG = 1,
+  SINKATTN_ERR_UNSUPPORTED = 2,
+  SINKATTN_ERR_WORKSPACE = 3,
+  SINKATTN_ERR_HIP = 4
+} sinkattn_status;
+
+/*
+ * Varlen self-attention prefill with sinks (Perplexity, "GPT-OSS on day 0",
+ * Sink attention: the prefill template extended with the sink; window layers
+ * from the NVIDIA gpt-oss announcement).
+ *
+ *   q           bf16 [total_tokens, num_q_heads, head_dim]
+ *   k, v        bf16 [total_tokens, num_kv_heads, head_dim]
+ *   sinks       fp32 [num_q_heads], or NULL for "no sink" on every head
+ *   cu_seqlens  int32 [batch + 1], device; sequence b owns tokens
+ *               [cu_seqlens[b], cu_seqlens[b+1]); queries and keys of a
+ *               sequence coincide (positions local to the sequence)
+ *   max_seqlen  host int, >= every sequence length (sizes the launch)
+ *   window      <= 0: full causal; W > 0: i - W < j <= i
+ *   o           bf16 [total_tokens, num_q_heads, head_dim] (written)
+ *   lse         fp32 [total_tokens, num_q_heads], natural log, sink
+ *               included; NULL to skip.  A row with no key and no sink gets
+ *               o = 0 and lse = -inf.
+ */
+SINKATTN_API sinkattn_status sinkattn_prefill_varlen(
+    const void* q, const void* k, const void* v,
+    const float* sinks,
+    const int32_t* cu_seqlens, int32_t batch,
+    int32_t max_seqlen, int32_t total_tokens,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t window, float softmax_scale,
+    void* o, float* lse, void* stream);
+
+/*
+ * Bytes of workspace sinkattn_decode_splitkv needs for num_splits > 1:
+ * fp32 partial outputs [num_splits, batch, num_q_heads, head_dim] and fp32
+ * partial lse [num_splits, batch, num_q_heads], each 256-byte aligned.
+ * Returns 0 when num_splits <= 1 and 0 for invalid (negative) sizes.
+ */
+SINKATTN_API size_t sinkattn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                       int32_t head_dim, int32_t num_splits);
+
+/*
+ * Split-KV decode: one query token per sequence against a packed KV cache
+ * (Perplexity, "GPT-OSS on day 0", Sink attention: attention parallelised
+ * over heads and KV length; with the KV length split into chunks, the sink
+ * initialises only the first chunk).
+ *
+ *   q              bf16 [batch, num_q_heads, head_dim]; the query of
+ *                  sequence b sits at position L_b - 1
+ *   k_cache,
+ *   v_cache        bf16 [total_kv, num_kv_heads, head_dim], packed by
+ *                  cu_seqlens_k (int32 [batch + 1], device); L_b >= 1
+ *   max_seqlen_k   host int, >= every L_b
+ *   window         <= 0: keys [0, L_b); W > 0: keys [max(0, L_b - W), L_b)
+ *   num_splits     S >= 1: the key range of every sequence is cut into S
+ *                  contiguous chunks of ceil(n / S) keys (trailing chunks may
+ *                  be empty); chunk 0 holds the lowest positions and carries
+ *                  the sink.  S > 1 writes fp32 partials to the workspace and
+ *                  merges them with the log-sum-exp merge before returning.
+ *   workspace      device buffer of >= sinkattn_decode_workspace_bytes(...)
+ *                  bytes when S > 1 (SINKATTN_ERR_WORKSPACE otherwise); may
+ *                  be NULL when S == 1
+ *   o              bf16 [batch, num_q_heads, head_dim]
+ *   lse            fp32 [batch, num_q_heads] or NULL
+ *
+ * Additionally supported: G = num_q_heads / num_kv_heads <= 32 (larger
+ * groups return SINKATTN_ERR_UNSUPPORTED).
+ */
+SINKATTN_API sinkattn_status sinkattn_decode_splitkv(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_k,
+    const float* sinks,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t window, float softmax_scale, int32_t num_splits,
+    void* workspace, size_t workspace_bytes,
+    void* o, float* lse, void* stream);
+
+/*
+ * Log-sum-exp merge of num_parts partial results, each normalised by its own
+ * denominator (the combination step that the split-KV form of the
+ * Perplexity page's online softmax implies; the page does not print it):
+ *     M = max_s lse_s,  w_s = exp(lse_s - M),
+ *     o = sum_s w_s o_s / sum_s w_s,  lse = M + ln(sum_s w_s).
+ * A partial with lse = -inf is empty; if all are empty, o = 0, lse = -inf.
+ * A sink can be merged as one more partial with lse = z and o = 0.
+ *
+ *   o_parts    fp32 [num_parts, n, num_heads, head_dim]
+ *   lse_parts  fp32 [num_parts, n, num_heads]
+ *   o          bf16 [n, num_heads, head_dim]
+ *   lse        fp32 [n, num_heads] or NULL
+ */
+SINKATTN_API sinkattn_status sinkattn_merge_lse(
+    const float* o_parts, const float* lse_parts,
+    int32_t num_parts, int32_t n, int32_t num_heads, int32_t head_dim,
+    void* o, float* lse, void* stream);
+
+/* Message describing the last failed call on this thread ("" if none). */
+SINKATTN_API const char* sinkattn_last_error(void);
+
+/* Library version string. */
+SINKATTN_API const char* sinkattn_version(void);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* SINKATTN_H_ */

@@ -1,0 +1,130 @@
+"""The C-ABI library loads, exports every function include/sinkattn.h
+declares, and rejects bad arguments on the host (no GPU call is made: every
+case here fails validation before anything is launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sinkattn.h")
+LIB = os.path.join(ROOT, "attention_gqa_flash_amd", "libsinkattn.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"SINKATTN_API\s+[\w\s\*]+?\b(sinkattn_\w+)\s*\(", text)))
+
+
+def _lib():
+    from attention_gqa_flash_amd import binding
+    return binding.library()
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == sorted([
+        "sinkattn_decode_splitkv", "sinkattn_decode_workspace_bytes", "sinkattn_last_error",
+        "sinkattn_merge_lse", "sinkattn_prefill_varlen", "sinkattn_version"])
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(LIB)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_workspace_size():
+    lib = _lib()
+    assert b"sinkattn" in lib.sinkattn_version()
+    assert lib.sinkattn_decode_workspace_bytes(64, 64, 64, 1) == 0
+    rows = 16 * 64 * 64
+    expect = (rows * 64 * 4 + 255) // 256 * 256 + (rows * 4 + 255) // 256 * 256
+    assert lib.sinkattn_decode_workspace_bytes(64, 64, 64, 16) == expect
+    assert lib.sinkattn_decode_workspace_bytes(-1, 64, 64, 4) == 0
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation
+
+
+def _prefill(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, sinks=None, cu=FAKE, batch=1, max_seqlen=16, total=16, hq=8, hkv=2,
+             d=64, window=0, scale=0.125, o=FAKE, lse=None)
+    a.update(kw)
+    return lib.sinkattn_prefill_varlen(a["q"], a["k"], a["v"], a["sinks"], a["cu"], a["batch"], a["max_seqlen"],
+                                       a["total"], a["hq"], a["hkv"], a["d"], a["window"], a["scale"], a["o"],
+                                       a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=128), 2),
+    (dict(hq=6, hkv=4), 1),
+    (dict(hkv=0), 1),
+    (dict(scale=0.0), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(scale=-0.125), 1),
+    (dict(batch=-1), 1),
+    (dict(q=None), 1),
+    (dict(cu=None), 1),
+    (dict(o=ctypes.c_void_p((1 << 20) + 2)), 1),
+    (dict(max_seqlen=32, total=16), 1),
+    (dict(max_seqlen=40_000_000, total=40_000_000), 2),
+])
+def test_prefill_rejects(kw, status):
+    lib = _lib()
+    assert _prefill(lib, **kw) == status
+    assert lib.sinkattn_last_error()
+
+
+def test_prefill_empty_is_ok_without_launch():
+    lib = _lib()
+    assert _prefill(lib, batch=0) == 0
+    assert _prefill(lib, total=0, max_seqlen=0) == 0
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, batch=4, max_seqlen=100, sinks=None, hq=64, hkv=8, d=64,
+             window=0, scale=0.125, splits=1, ws=None, ws_bytes=0, o=FAKE, lse=None)
+    a.update(kw)
+    return lib.sinkattn_decode_splitkv(a["q"], a["k"], a["v"], a["cu"], a["batch"], a["max_seqlen"], a["sinks"],
+                                       a["hq"], a["hkv"], a["d"], a["window"], a["scale"], a["splits"], a["ws"],
+                                       a["ws_bytes"], a["o"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), 2),
+    (dict(hq=64, hkv=1), 2),          # group of 64 > 32
+    (dict(splits=0), 1),
+    (dict(splits=4), 3),              # no workspace
+    (dict(splits=4, ws=FAKE, ws_bytes=100), 3),
+    (dict(splits=4, ws=ctypes.c_void_p((1 << 20) + 16), ws_bytes=1 << 30), 1),  # misaligned workspace
+    (dict(max_seqlen=0), 1),
+    (dict(k=None), 1),
+    (dict(scale=float("inf")), 1),
+])
+def test_decode_rejects(kw, status):
+    lib = _lib()
+    assert _decode(lib, **kw) == status
+    assert lib.sinkattn_last_error()
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE, 0, 4, 8, 64), 1),
+    ((FAKE, FAKE, 2, 4, 8, 32), 2),
+    ((None, FAKE, 2, 4, 8, 64), 1),
+    ((FAKE, FAKE, 2, 4, 0, 64), 1),
+])
+def test_merge_rejects(args, status):
+    lib = _lib()
+    assert lib.sinkattn_merge_lse(*args, FAKE, None, None) == status
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from attention_gqa_flash_amd import binding
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(binding.SinkAttnError):
+        binding.library()

@@ -1,0 +1,165 @@
+"""GPU parity: the HIP library against the float64 CPU oracle, element by
+element, at sizes the oracle finishes in seconds (several tiles, ragged
+tails, empty and one-token sequences, every layer kind).
+
+Bar: max |err| <= 2e-2 and mean |err| <= 2e-3 on the bf16 outputs; lse
+within 1e-3 with an identical -inf pattern.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from attention_gqa_flash_amd import binding, inputs
+from oracle import decode_ref, decode_split_partials_ref, merge_ref, prefill_varlen_ref
+from tests.helpers import (assert_close_lse, assert_close_out, bf16_to_device, f32_to_device, i32_to_device,
+                           to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+def _prefill_case(p, window, with_sinks=True):
+    q, k, v = (bf16_to_device(x) for x in (p.q, p.k, p.v))
+    sinks = f32_to_device(p.sinks) if with_sinks else None
+    cu = i32_to_device(p.cu_seqlens)
+    o, lse = binding.prefill_varlen(q, k, v, sinks, cu, max(p.lengths), window, p.scale, return_lse=True)
+    torch.cuda.synchronize()
+    qf, kf, vf = (inputs.bf16_bits_to_f32(x) for x in (p.q, p.k, p.v))
+    ro, rl = prefill_varlen_ref(qf, kf, vf, p.sinks if with_sinks else None, p.cu_seqlens, window, p.scale)
+    return to_f64(o), lse.cpu().numpy(), ro, rl
+
+
+def test_tiny_prefill_config():
+    """1 sequence of 256, 4 q heads / 1 KV head, causal, seed 0."""
+    p = inputs.tiny_prefill(seed=0)
+    o, lse, ro, rl = _prefill_case(p, 0)
+    print("tiny: max|err| %.3g mean|err| %.3g" % assert_close_out(o, ro, "tiny"))
+    assert_close_lse(lse, rl, "tiny")
+
+
+@pytest.mark.parametrize("window", [0, 1, 5, 31, 32, 64, 127, 128, 129, 1000])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (16, 2), (24, 2), (64, 8)])
+def test_varlen_prefill_small(window, hq, hkv):
+    lengths = [1, 31, 32, 33, 64, 65, 127, 200, 517]
+    if hq == 64:
+        lengths = [1, 33, 130, 300]
+    p = inputs.make_prefill(lengths, hq=hq, hkv=hkv, seed=window + 100 * hq + hkv)
+    o, lse, ro, rl = _prefill_case(p, window)
+    assert_close_out(o, ro, "varlen W=%d G=%d" % (window, hq // hkv))
+    assert_close_lse(lse, rl, "varlen")
+
+
+def test_prefill_without_sinks_and_neg_inf_heads():
+    p = inputs.make_prefill([70, 129], hq=16, hkv=2, seed=3, no_sink_heads=(0, 5, 9, 15))
+    for window in (0, 128):
+        o, lse, ro, rl = _prefill_case(p, window)
+        assert_close_out(o, ro, "-inf heads")
+        assert_close_lse(lse, rl, "-inf heads")
+        o, lse, ro, rl = _prefill_case(p, window, with_sinks=False)
+        assert_close_out(o, ro, "no sinks")
+        assert_close_lse(lse, rl, "no sinks")
+
+
+def test_prefill_large_sink_gives_zero():
+    p = inputs.make_prefill([96], hq=8, hkv=1, seed=4)
+    p.sinks[:] = 40.0  # exp(40 - s) dwarfs every key for N(0,1) data at scale 1/8
+    o, lse, ro, rl = _prefill_case(p, 0)
+    assert np.abs(o).max() < 1e-10
+    assert_close_out(o, ro, "sink=+40")
+    assert_close_lse(lse, rl, "sink=+40")
+
+
+def test_prefill_empty_sequences_in_pack():
+    p = inputs.make_prefill([0, 45, 0, 0, 70, 0], hq=16, hkv=2, seed=6)
+    o, lse, ro, rl = _prefill_case(p, 0)
+    assert_close_out(o, ro, "empty seqs")
+    assert_close_lse(lse, rl, "empty seqs")
+
+
+def test_prefill_deterministic():
+    p = inputs.make_prefill([300, 77], hq=64, hkv=8, seed=7)
+    q, k, v = (bf16_to_device(x) for x in (p.q, p.k, p.v))
+    sinks, cu = f32_to_device(p.sinks), i32_to_device(p.cu_seqlens)
+    ref = binding.prefill_varlen(q, k, v, sinks, cu, 300, 0, p.scale)
+    for _ in range(10):
+        again = binding.prefill_varlen(q, k, v, sinks, cu, 300, 0, p.scale)
+        assert torch.equal(again.view(torch.int16), ref.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# Decode and merge
+# ---------------------------------------------------------------------------
+
+def _decode_case(d, window, splits):
+    q, k, v = (bf16_to_device(x) for x in (d.q, d.k, d.v))
+    o, lse = binding.decode_splitkv(q, k, v, i32_to_device(d.cu_seqlens_k), max(d.lengths),
+                                    f32_to_device(d.sinks), window, d.scale, splits, return_lse=True)
+    torch.cuda.synchronize()
+    return to_f64(o), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("window", [0, 1, 128])
+def test_decode_small_all_splits(window):
+    lengths = [1, 5, 31, 32, 33, 100, 1000, 4097]
+    d = inputs.make_decode(lengths, hq=64, hkv=8, seed=11 + window)
+    qf, kf, vf = (inputs.bf16_bits_to_f32(x) for x in (d.q, d.k, d.v))
+    ro, rl = decode_ref(qf, kf, vf, d.cu_seqlens_k, d.sinks, window, d.scale)
+    outs = []
+    for s in (1, 2, 3, 4, 16, 32, 100):
+        o, lse = _decode_case(d, window, s)
+        assert_close_out(o, ro, "decode W=%d S=%d" % (window, s))
+        assert_close_lse(lse, rl, "decode W=%d S=%d" % (window, s))
+        outs.append(o)
+    for a in outs[1:]:
+        assert_close_out(a, outs[0], "split agreement")
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 1), (8, 8), (32, 1), (12, 4)])
+def test_decode_group_shapes(hq, hkv):
+    d = inputs.make_decode([7, 64, 300], hq=hq, hkv=hkv, seed=hq * 10 + hkv)
+    qf, kf, vf = (inputs.bf16_bits_to_f32(x) for x in (d.q, d.k, d.v))
+    for window, s in ((0, 1), (0, 5), (16, 3)):
+        ro, rl = decode_ref(qf, kf, vf, d.cu_seqlens_k, d.sinks, window, d.scale)
+        o, lse = _decode_case(d, window, s)
+        assert_close_out(o, ro, "decode G=%d" % (hq // hkv))
+        assert_close_lse(lse, rl, "decode G=%d" % (hq // hkv))
+
+
+def test_decode_partials_match_oracle_partials():
+    """Run decode with S = 4 and check the merged result against the oracle's
+    own split partials merged on the CPU (sink in chunk 0 only)."""
+    d = inputs.make_decode([3, 50, 129, 513], hq=16, hkv=2, seed=12)
+    qf, kf, vf = (inputs.bf16_bits_to_f32(x) for x in (d.q, d.k, d.v))
+    op, lp = decode_split_partials_ref(qf, kf, vf, d.cu_seqlens_k, d.sinks, 0, d.scale, 4)
+    mo, ml = merge_ref(op, lp)
+    o, lse = _decode_case(d, 0, 4)
+    assert_close_out(o, mo, "partials")
+    assert_close_lse(lse, ml, "partials")
+
+
+def test_merge_kernel():
+    rng = np.random.default_rng(13)
+    s, n, h, dim = 5, 37, 6, 64
+    o_parts = rng.standard_normal((s, n, h, dim)).astype(np.float32)
+    lse_parts = (3.0 * rng.standard_normal((s, n, h))).astype(np.float32)
+    lse_parts[1, :5] = -np.inf          # some empty partials
+    lse_parts[:, 7, 2] = -np.inf        # one row entirely empty
+    o_parts[1, :5] = 0.0
+    o_parts[:, 7, 2] = 0.0
+    o, lse = binding.merge_lse(f32_to_device(o_parts), f32_to_device(lse_parts), return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = merge_ref(o_parts.astype(np.float64), lse_parts.astype(np.float64))
+    assert_close_out(to_f64(o), ro, "merge")
+    assert_close_lse(lse.cpu().numpy(), rl, "merge")
+    assert np.all(to_f64(o)[7, 2] == 0.0)
+
+
+def test_decode_deterministic():
+    d = inputs.make_decode([4000, 17], hq=64, hkv=8, seed=14)
+    q, k, v = (bf16_to_device(x) for x in (d.q, d.k, d.v))
+    cu, sinks = i32_to_device(d.cu_seqlens_k), f32_to_device(d.sinks)
+    for s in (1, 8):
+        ref = binding.decode_splitkv(q, k, v, cu, 4000, sinks, 0, d.scale, s)
+        for _ in range(5):
+            again = binding.decode_splitkv(q, k, v, cu, 4000, sinks, 0, d.scale, s)
+            assert torch.equal(again.view(torch.int16), ref.view(torch.int16))

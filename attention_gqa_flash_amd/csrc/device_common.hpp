@@ -53,6 +53,19 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// acc + p.x + p.y for a packed bf16 pair (v_dot2c_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float add_pair(bf16x2_t p, float acc) {
+  const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  return __builtin_amdgcn_fdot2_f32_bf16(p, ones, acc, false);
+}
+
+// True if the predicate holds on any lane of the wave.
+__device__ __forceinline__ bool wave_any(bool pred) {
+  return __builtin_amdgcn_ballot_w64(pred) != 0;
+}
+
 // fp32 -> bf16 bits, round to nearest even (inputs are finite or +-0).
 __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));

@@ -28,18 +28,57 @@ namespace sinkattn {
 namespace {
 
 constexpr int kQTile = 32;     // query tokens per workgroup
-constexpr int kKTile = 64;     // keys per LDS tile
+constexpr int kKTile = 64;     // keys per LDS tile (two 32-key halves)
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kHeadsPerBlock = 8;
+// Lazy rescaling: the reference max of a row only moves when a new logit
+// exceeds it by more than 2^8 (log2 units), so P <= 256 and the running
+// output is rescaled rarely.  o = acc / l is unchanged in exact arithmetic.
+constexpr float kRescaleLog2 = 8.0f;
 
-__global__ __launch_bounds__(kThreads) void prefill_kernel(
+struct TileRegs {
+  u32x4_t k[2];
+  u32x4_t v[2];
+};
+
+// Global -> registers for one 64-key tile: thread -> (row, 16-byte chunk).
+__device__ __forceinline__ void load_tile(TileRegs& r, const uint16_t* __restrict__ k,
+                                          const uint16_t* __restrict__ v, int seq0, int len, int hkv,
+                                          int g, int key0, int tid) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = (tid >> 3) + 32 * i;
+    const int key = key0 + row;
+    r.k[i] = zero_u32x4();
+    r.v[i] = zero_u32x4();
+    if (key < len) {
+      const size_t off = (static_cast<size_t>(seq0 + key) * hkv + g) * kHeadDim + (tid & 7) * 8;
+      r.k[i] = load16(k + off);
+      r.v[i] = load16(v + off);
+    }
+  }
+}
+
+__device__ __forceinline__ void store_tile(const TileRegs& r, uint16_t* k_lds, uint16_t* v_lds, int tid) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = (tid >> 3) + 32 * i;
+    const int dst = swz(row, (tid & 7) * 8);
+    *reinterpret_cast<u32x4_t*>(k_lds + dst) = r.k[i];
+    *reinterpret_cast<u32x4_t*>(v_lds + dst) = r.v[i];
+  }
+}
+
+template <bool kWindow>
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ sinks,
     const int32_t* __restrict__ cu_seqlens, int hq, int hkv, int group, int n_hchunk,
     int n_qtiles, int window, float scale_log2, uint16_t* __restrict__ o,
     float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kKTile * kHeadDim];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kKTile * kHeadDim];
+  // Two LDS buffers per operand: tile t+1 is written while tile t is read.
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kKTile * kHeadDim];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kKTile * kHeadDim];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -58,6 +97,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   const int len = cu_seqlens[b + 1] - seq0;
   const int q0 = qt * kQTile;
   if (q0 >= len) return;  // uniform over the workgroup
+
+  const int last_q = min(len - 1, q0 + kQTile - 1);
+  const int first_key = kWindow ? max(0, q0 - window + 1) : 0;
+  const int t_begin = first_key / kKTile;
+  const int t_end = last_q / kKTile;
+
+  // Start the first K/V tile on its way before anything else.
+  TileRegs regs;
+  load_tile(regs, k, v, seq0, len, hkv, g, t_begin * kKTile, tid);
 
   // Query heads of this wave (two column blocks of 32).
   int head[2];
@@ -87,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     }
   }
 
-  // Online-softmax state per column block.  The running max m is kept in
+  // Online-softmax state per column block.  The reference max m is kept in
   // log2 units (scaled logits); the sink seeds it, and its "1" is counted once
   // (in the lower lane of the pair).
   float m2[2], lsum[2];
@@ -106,122 +154,103 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     acc[c][1] = zero16();
   }
 
-  const int last_q = min(len - 1, q0 + kQTile - 1);
-  const int first_key = window > 0 ? max(0, q0 - window + 1) : 0;
-  const int t_begin = first_key / kKTile;
-  const int t_end = last_q / kKTile;
+  store_tile(regs, k_lds[0], v_lds[0], tid);
+  __syncthreads();
+
+  const int grp_lane = lane & 15;
+  const int dcol0 = 16 * ((lane >> 4) & 1) + 4 * (grp_lane & 3);
 
   for (int t = t_begin; t <= t_end; ++t) {
-    const int key0 = t * kKTile;
-    __syncthreads();
-    // Stage K and V tiles: 64 rows x 128 B each; thread -> (row, 16-B chunk).
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      const int ch = tid & 7;
-      const int key = key0 + r;
-      u32x4_t kv = zero_u32x4(), vv = zero_u32x4();
-      if (key < len) {
-        const size_t off = (static_cast<size_t>(seq0 + key) * hkv + g) * kHeadDim + ch * 8;
-        kv = load16(k + off);
-        vv = load16(v + off);
-      }
-      const int dst = swz(r, ch * 8);
-      *reinterpret_cast<u32x4_t*>(k_lds + dst) = kv;
-      *reinterpret_cast<u32x4_t*>(v_lds + dst) = vv;
-    }
-    __syncthreads();
-    if (!wave_active) continue;
+    const int buf = (t - t_begin) & 1;
+    const bool more = t < t_end;
+    if (more) load_tile(regs, k, v, seq0, len, hkv, g, (t + 1) * kKTile, tid);
 
-    // S^T = K Q^T for two 32-key blocks and two column blocks.
-    f32x16_t sacc[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb][0] = zero16();
-      sacc[kb][1] = zero16();
-      const int row = kb * 32 + key_of_row(col);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(k_lds + swz(row, 16 * s + 8 * half));
-        sacc[kb][0] = mfma_32x32x16(a, qreg[0][s], sacc[kb][0]);
-        sacc[kb][1] = mfma_32x32x16(a, qreg[1][s], sacc[kb][1]);
-      }
-    }
-
-    // Mask only tiles that reach past the first query (diagonal) or behind
-    // the window of the last query.
-    const bool need_mask = (key0 + kKTile - 1 > q0) || (window > 0 && key0 <= last_q - window);
-    if (need_mask) {
+    if (wave_active) {
+      const uint16_t* kt = k_lds[buf];
+      const uint16_t* vt = v_lds[buf];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        const int kbase = t * kKTile + kb * 32;
+        // Halves no query of the tile can see are skipped.
+        const bool dead = (kbase > last_q) || (kWindow && kbase + 31 <= q0 - window);
+        if (dead) continue;
+
+        // S^T = K Q^T for 32 keys and two column blocks.
+        f32x16_t sacc[2] = {zero16(), zero16()};
+        const int row = kb * 32 + key_of_row(col);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb * 32 + key_of_reg(r, half);
-          const bool ok = key <= qtok && (window <= 0 || key > qtok - window);
-          if (!ok) {
-            sacc[kb][0][r] = kNegInf;
-            sacc[kb][1][r] = kNegInf;
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + swz(row, 16 * s + 8 * half));
+          sacc[0] = mfma_32x32x16(a, qreg[0][s], sacc[0]);
+          sacc[1] = mfma_32x32x16(a, qreg[1][s], sacc[1]);
+        }
+
+        const bool need_mask = (kbase + 31 > q0) || (kWindow && kbase <= last_q - window);
+        if (need_mask) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kbase + key_of_reg(r, half);
+            const bool ok = key <= qtok && (!kWindow || key > qtok - window);
+            if (!ok) {
+              sacc[0][r] = kNegInf;
+              sacc[1][r] = kNegInf;
+            }
+          }
+        }
+
+        // Online softmax (log2 domain), P in bf16 as the B operand of O^T.
+        bf16x8_t pb[2][2];  // [c][u]
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          float mx = sacc[c][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[c][r]);
+          mx = pair_max(mx) * scale_log2;
+          const bool need = mx > m2[c] + kRescaleLog2;
+          if (wave_any(need)) {
+            const float m_new = need ? mx : m2[c];
+            const float alpha = fast_exp2(m2[c] - m_new);
+            m2[c] = m_new;
+            lsum[c] *= alpha;
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) acc[c][db][r] *= alpha;
+          }
+          const float m_use = (m2[c] == kNegInf) ? 0.0f : m2[c];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            bf16x8_t pv;
+#pragma unroll
+            for (int tt = 0; tt < 8; ++tt)
+              pv[tt] = static_cast<__bf16>(fast_exp2(fmaf(sacc[c][8 * u + tt], scale_log2, -m_use)));
+#pragma unroll
+            for (int tt = 0; tt < 8; tt += 2) {
+              bf16x2_t pr = {pv[tt], pv[tt + 1]};
+              lsum[c] = add_pair(pr, lsum[c]);
+            }
+            pb[c][u] = pv;
+          }
+        }
+
+        // O^T += V^T P^T: lane (d = l % 32 of block db, half) reads V rows
+        // kb*32 + 16u + 8 half + 0..7 at its column (two transposing reads).
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int rbase = kb * 32 + 16 * u + 8 * half + (grp_lane >> 2);
+            const int dcol = 32 * db + dcol0;
+            const bf16x8_t a = cat4(lds_read_tr(vt + swz(rbase, dcol)), lds_read_tr(vt + swz(rbase + 4, dcol)));
+            acc[0][db] = mfma_32x32x16(a, pb[0][u], acc[0][db]);
+            acc[1][db] = mfma_32x32x16(a, pb[1][u], acc[1][db]);
           }
         }
       }
     }
 
-    // Online softmax (log2 domain) and P in bf16 as the B operand of O^T.
-    bf16x8_t pb[2][2][2];  // [c][kb][u]
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][c][r]);
-      mx = pair_max(mx);
-      const float m_new = fmaxf(m2[c], mx * scale_log2);
-      const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-      const float alpha = fast_exp2(m2[c] - m_use);
-      m2[c] = m_new;
-      float psum = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          bf16x8_t pv;
-#pragma unroll
-          for (int tt = 0; tt < 8; ++tt) {
-            const float p = fast_exp2(sacc[kb][c][8 * u + tt] * scale_log2 - m_use);
-            psum += p;
-            pv[tt] = static_cast<__bf16>(p);
-          }
-          pb[c][kb][u] = pv;
-        }
-      }
-      lsum[c] = lsum[c] * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[c][db][r] *= alpha;
-    }
-
-    // O^T += V^T P^T.  Lane (d = l % 32 of block db, half) needs V rows
-    // kb*32 + 16u + 8 half + 0..7 at its column: two transposing reads.
-    const int grp_lane = lane & 15;
-    const int dcol0 = 16 * ((lane >> 4) & 1) + 4 * (grp_lane & 3);
-#pragma unroll
-    for (int db = 0; db < 2; ++db) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int rbase = kb * 32 + 16 * u + 8 * half + (grp_lane >> 2);
-          const int dcol = 32 * db + dcol0;
-          const bf16x4_t lo = lds_read_tr(v_lds + swz(rbase, dcol));
-          const bf16x4_t hi = lds_read_tr(v_lds + swz(rbase + 4, dcol));
-          const bf16x8_t a = cat4(lo, hi);
-          acc[0][db] = mfma_32x32x16(a, pb[0][kb][u], acc[0][db]);
-          acc[1][db] = mfma_32x32x16(a, pb[1][kb][u], acc[1][db]);
-        }
-      }
-    }
+    if (more) store_tile(regs, k_lds[buf ^ 1], v_lds[buf ^ 1], tid);
+    __syncthreads();
   }
 
   if (!wave_active) return;
@@ -258,7 +287,9 @@ hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream) {
   const int n_hchunk = (group + kHeadsPerBlock - 1) / kHeadsPerBlock;
   const int n_qtiles = (a.max_seqlen + kQTile - 1) / kQTile;
   dim3 grid(static_cast<unsigned>(a.num_kv_heads) * n_hchunk * a.batch, n_qtiles, 1);
-  hipLaunchKernelGGL(prefill_kernel, grid, dim3(kThreads), 0, stream,
+  const bool windowed = a.window > 0 && a.window < a.max_seqlen;
+  auto kernel = windowed ? prefill_kernel<true> : prefill_kernel<false>;
+  hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.sinks, a.cu_seqlens, a.num_q_heads,
                      a.num_kv_heads, group, n_hchunk, n_qtiles, a.window,

@@ -5,7 +5,12 @@ import numpy as np
 # Tolerances on bf16 outputs against the float64 oracle (fp32 accumulation).
 MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
-LSE_ABS = 1e-3
+# lse is fp32, but the prefill kernel sums the bf16-rounded probabilities it
+# also feeds to P.V (so the output weights stay consistent with their
+# normaliser).  Each weight carries a relative rounding error of at most
+# 2^-9 (bf16 round-to-nearest-even), so ln(den) may move by up to
+# 2^-9 = 1.95e-3; twice that covers the fp32 exp2/log2 approximations.
+LSE_ABS = 4e-3
 
 
 def bf16_to_device(bits, device="cuda"):

@@ -11,9 +11,12 @@
 // keys is streamed once and applied to all G query heads of the KV head (the
 // G heads are the N columns of S^T = K Q^T).  Each of the 4 waves walks
 // every 4th 32-key tile of the chunk with its own online-softmax state; the
-// waves are merged through LDS at the end.  K goes straight from HBM into the
-// MFMA A-operand registers (16-byte loads); V goes through a wave-private LDS
-// tile so that it can be read transposed for O^T = V^T P^T.
+// waves are merged through LDS at the end.  K and V rows are read with fully
+// coalesced 16-byte loads (8 lanes per 128-byte row; a key row of one head is
+// 128 contiguous bytes, rows are Hkv * 128 bytes apart), the next tile of a
+// wave is in flight while the current one is computed, and each tile passes
+// through a wave-private LDS tile: K is read back in MFMA A-operand order, V
+// with the transposing read that O^T = V^T P^T needs.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -25,14 +28,38 @@ constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kKeys = 32;  // keys per wave iteration
 
+// One 32-key tile of one wave, in registers, K and V rows in coalesced
+// order: lane l holds the 16-byte chunk l % 8 of rows l / 8 + 8 i.  Keys at or
+// beyond `end` read as zero.
+struct TileRegs {
+  u32x4_t k[4];
+  u32x4_t v[4];
+};
+
+__device__ __forceinline__ void load_tile(TileRegs& t, const uint16_t* __restrict__ k,
+                                          const uint16_t* __restrict__ v, int base, int hkv, int g,
+                                          int k0, int end, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = k0 + (lane >> 3) + 8 * i;
+    t.k[i] = zero_u32x4();
+    t.v[i] = zero_u32x4();
+    if (key < end) {
+      const size_t off = (static_cast<size_t>(base + key) * hkv + g) * kHeadDim + (lane & 7) * 8;
+      t.k[i] = load16(k + off);
+      t.v[i] = load16(v + off);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ sinks,
     const int32_t* __restrict__ cu_seqlens_k, int batch, int hq, int hkv, int group,
     int window, float scale_log2, int num_splits, uint16_t* __restrict__ o,
     float* __restrict__ lse, float* __restrict__ o_part, float* __restrict__ lse_part) {
-  // Wave-private V staging tiles (first 16 KiB); the whole buffer is reused
-  // for the cross-wave merge of up to 32 heads x 64 d per wave.
+  // Wave-private K and V staging tiles (2 x 4 KiB per wave); the whole
+  // buffer is reused for the cross-wave merge of up to 32 heads x 64 d.
   __shared__ __attribute__((aligned(16))) float lds_buf[kWaves * 32 * kHeadDim];
   __shared__ float red_m[kWaves][32];
   __shared__ float red_l[kWaves][32];
@@ -79,39 +106,39 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   }
   f32x16_t acc[2] = {zero16(), zero16()};
 
-  uint16_t* vt = reinterpret_cast<uint16_t*>(lds_buf) + wave * kKeys * kHeadDim;
+  uint16_t* kt = reinterpret_cast<uint16_t*>(lds_buf) + wave * 2 * kKeys * kHeadDim;
+  uint16_t* vt = kt + kKeys * kHeadDim;
   const int grp_lane = lane & 15;
   const int dcol0 = 16 * ((lane >> 4) & 1) + 4 * (grp_lane & 3);
+  const int krow = key_of_row(col);
 
-  for (int k0 = a + kKeys * wave; k0 < e; k0 += kKeys * kWaves) {
-    // K rows as the A operand (row m <- key k0 + key_of_row(m)).
-    const int krow = k0 + key_of_row(col);
-    bf16x8_t ka[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4_t val = zero_u32x4();
-      if (krow < e) val = load16(k + (static_cast<size_t>(base + krow) * hkv + g) * kHeadDim + 16 * s + 8 * half);
-      ka[s] = __builtin_bit_cast(bf16x8_t, val);
-    }
-    // V rows into the wave's LDS tile (coalesced: 8 lanes per 128-byte row).
-    u32x4_t vv[4];
+  // Register double buffering: the loads of the next tile of this wave are in
+  // flight while the current one is computed.
+  TileRegs cur, nxt;
+  int k0 = a + kKeys * wave;
+  if (k0 < e) load_tile(cur, k, v, base, hkv, g, k0, e, lane);
+
+  for (; k0 < e; k0 += kKeys * kWaves) {
+    const int k1 = k0 + kKeys * kWaves;
+    if (k1 < e) load_tile(nxt, k, v, base, hkv, g, k1, e, lane);
+
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // previous tile's LDS reads are done
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = (lane >> 3) + 8 * i;
-      const int key = k0 + r;
-      vv[i] = zero_u32x4();
-      if (key < e) vv[i] = load16(v + (static_cast<size_t>(base + key) * hkv + g) * kHeadDim + (lane & 7) * 8);
+      const int dst = swz(r, (lane & 7) * 8);
+      *reinterpret_cast<u32x4_t*>(kt + dst) = cur.k[i];
+      *reinterpret_cast<u32x4_t*>(vt + dst) = cur.v[i];
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // previous tile's reads are done
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (lane >> 3) + 8 * i;
-      *reinterpret_cast<u32x4_t*>(vt + swz(r, (lane & 7) * 8)) = vv[i];
-    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // K and V tiles written
 
+    // S^T = K Q^T: MFMA row m reads key row key_of_row(m) of the tile.
     f32x16_t sacc = zero16();
 #pragma unroll
-    for (int s = 0; s < 4; ++s) sacc = mfma_32x32x16(ka[s], qreg[s], sacc);
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + swz(krow, 16 * s + 8 * half));
+      sacc = mfma_32x32x16(a, qreg[s], sacc);
+    }
 
     if (k0 + kKeys > e) {
 #pragma unroll
@@ -119,11 +146,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
         if (k0 + key_of_reg(r, half) >= e) sacc[r] = kNegInf;
     }
 
-    float mx = kNegInf;
+    float mx = sacc[0];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-    mx = pair_max(mx);
-    const float m_new = fmaxf(m2, mx * scale_log2);
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+    mx = pair_max(mx) * scale_log2;
+    const float m_new = fmaxf(m2, mx);
     const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
     const float alpha = fast_exp2(m2 - m_use);
     m2 = m_new;
@@ -133,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
-        const float p = fast_exp2(sacc[8 * u + tt] * scale_log2 - m_use);
+        const float p = fast_exp2(fmaf(sacc[8 * u + tt], scale_log2, -m_use));
         psum += p;
         pb[u][tt] = static_cast<__bf16>(p);
       }
@@ -144,7 +171,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
 
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // V tile written
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
 #pragma unroll
@@ -155,6 +181,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
         acc[db] = mfma_32x32x16(av, pb[u], acc[db]);
       }
     }
+    cur = nxt;
   }
 
   // Cross-wave merge.  Each wave publishes (m, l, unnormalised O) per head.

@@ -32,7 +32,7 @@ def hipcc() -> str:
 
 def common_flags() -> list[str]:
     return [
-        "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
+        "-O3", "-std=c++17", "-fno-honor-nans", "-fPIC", "--offload-arch=" + ARCH,
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
         # keep the compiler from forming packed-fp32 VALU ops
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -95,6 +95,17 @@ __device__ __forceinline__ bf16x8_t cat4(const bf16x4_t& a, const bf16x4_t& b) {
   return r;
 }
 
+// 16-byte global -> LDS copy that bypasses registers (global_load_lds_dwordx4):
+// lane L of the wave writes the 16 bytes it loads from `src` to
+// lds_base + 16 L.  lds_base must be the same for every lane of the wave.
+// Completion is tracked by vmcnt.
+__device__ __forceinline__ void load16_to_lds(const uint16_t* src, uint16_t* lds_base) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void*)(lds_base), 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ u32x4_t load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }

@@ -31,10 +31,14 @@ constexpr int kQTile = 32;     // query tokens per workgroup
 constexpr int kKTile = 64;     // keys per LDS tile (two 32-key halves)
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kHeadsPerBlock = 8;
-// Lazy rescaling: the reference max of a row only moves when a new logit
-// exceeds it by more than 2^8 (log2 units), so P <= 256 and the running
-// output is rescaled rarely.  o = acc / l is unchanged in exact arithmetic.
-constexpr float kRescaleLog2 = 8.0f;
+// Lazy reference max.  Probabilities are taken against a per-row reference
+// m (log2 units) that only moves when the new keys push a row's partial
+// denominator past 2^32 (or when the row has no reference yet); the running
+// output and denominator are then rescaled.  Values below the reference by
+// more than 126 underflow to 0, which is exact to fp32 precision relative to
+// the reference's own weight (>= 1) already counted.  o = acc / l is
+// unchanged in exact arithmetic.
+constexpr float kRescaleSum = 4294967296.0f;  // 2^32
 
 struct TileRegs {
   u32x4_t k[2];
@@ -157,8 +161,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
   store_tile(regs, k_lds[0], v_lds[0], tid);
   __syncthreads();
 
+  // LDS read offsets (elements, within a 32-row half of a tile).  K^T rows
+  // as the A operand: row key_of_row(col), d = 16 s + 8 half.  V^T operand:
+  // lane (d = l % 32 of block db, half) needs rows 16 u + 8 half + 0..7 at
+  // its column, as two transposing reads of 4 rows (i = 0, 1); under the
+  // chunk swizzle read (db, u, i) sits at vbase + 1024 u + 256 i + 32 (db ^ i).
+  int koff[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) koff[s] = swz(key_of_row(col), 16 * s + 8 * half);
   const int grp_lane = lane & 15;
   const int dcol0 = 16 * ((lane >> 4) & 1) + 4 * (grp_lane & 3);
+  const int vbase = (8 * half + (grp_lane >> 2)) * kHeadDim + ((((dcol0 >> 3) ^ (grp_lane >> 2)) & 3) << 3) +
+                    (dcol0 & 7);
 
   for (int t = t_begin; t <= t_end; ++t) {
     const int buf = (t - t_begin) & 1;
@@ -177,10 +191,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
 
         // S^T = K Q^T for 32 keys and two column blocks.
         f32x16_t sacc[2] = {zero16(), zero16()};
-        const int row = kb * 32 + key_of_row(col);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + swz(row, 16 * s + 8 * half));
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + kb * 32 * kHeadDim + koff[s]);
           sacc[0] = mfma_32x32x16(a, qreg[0][s], sacc[0]);
           sacc[1] = mfma_32x32x16(a, qreg[1][s], sacc[1]);
         }
@@ -199,25 +212,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
         }
 
         // Online softmax (log2 domain), P in bf16 as the B operand of O^T.
+        // Fast path: P against the current reference m, no row max.
         bf16x8_t pb[2][2];  // [c][u]
+        float tsum[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          float mx = sacc[c][0];
-#pragma unroll
-          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[c][r]);
-          mx = pair_max(mx) * scale_log2;
-          const bool need = mx > m2[c] + kRescaleLog2;
-          if (wave_any(need)) {
-            const float m_new = need ? mx : m2[c];
-            const float alpha = fast_exp2(m2[c] - m_new);
-            m2[c] = m_new;
-            lsum[c] *= alpha;
-#pragma unroll
-            for (int db = 0; db < 2; ++db)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) acc[c][db][r] *= alpha;
-          }
-          const float m_use = (m2[c] == kNegInf) ? 0.0f : m2[c];
+          const float m_use = m2[c] == kNegInf ? 0.0f : m2[c];
+          float l = 0.0f;
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             bf16x8_t pv;
@@ -227,11 +228,55 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
 #pragma unroll
             for (int tt = 0; tt < 8; tt += 2) {
               bf16x2_t pr = {pv[tt], pv[tt + 1]};
-              lsum[c] = add_pair(pr, lsum[c]);
+              l = add_pair(pr, l);
             }
             pb[c][u] = pv;
           }
+          tsum[c] = l;
         }
+        // Slow path (rare): a row without reference yet, or keys far above
+        // it.  Move the reference to the row max, redo P, rescale the state.
+        const bool slow0 = m2[0] == kNegInf || !(tsum[0] <= kRescaleSum);
+        const bool slow1 = m2[1] == kNegInf || !(tsum[1] <= kRescaleSum);
+        if (wave_any(slow0 || slow1)) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            float mx = sacc[c][0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[c][r]);
+            mx = pair_max(mx) * scale_log2;
+            const bool slow = c == 0 ? slow0 : slow1;
+            // the pair agrees on `slow` (same reference, and the pair's
+            // sums are compared lane by lane, so make it pair-uniform)
+            const bool move = pair_max(slow ? 1.0f : 0.0f) > 0.0f && mx > m2[c];
+            const float m_new = move ? mx : m2[c];
+            const float alpha = move ? fast_exp2(m2[c] - m_new) : 1.0f;
+            m2[c] = m_new;
+            lsum[c] *= alpha;
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) acc[c][db][r] *= alpha;
+            const float m_use = m_new == kNegInf ? 0.0f : m_new;
+            float l = 0.0f;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              bf16x8_t pv;
+#pragma unroll
+              for (int tt = 0; tt < 8; ++tt)
+                pv[tt] = static_cast<__bf16>(fast_exp2(fmaf(sacc[c][8 * u + tt], scale_log2, -m_use)));
+#pragma unroll
+              for (int tt = 0; tt < 8; tt += 2) {
+                bf16x2_t pr = {pv[tt], pv[tt + 1]};
+                l = add_pair(pr, l);
+              }
+              pb[c][u] = pv;
+            }
+            tsum[c] = l;
+          }
+        }
+        lsum[0] += tsum[0];
+        lsum[1] += tsum[1];
 
         // O^T += V^T P^T: lane (d = l % 32 of block db, half) reads V rows
         // kb*32 + 16u + 8 half + 0..7 at its column (two transposing reads).
@@ -239,9 +284,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
         for (int db = 0; db < 2; ++db) {
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            const int rbase = kb * 32 + 16 * u + 8 * half + (grp_lane >> 2);
-            const int dcol = 32 * db + dcol0;
-            const bf16x8_t a = cat4(lds_read_tr(vt + swz(rbase, dcol)), lds_read_tr(vt + swz(rbase + 4, dcol)));
+            const uint16_t* vp = vt + vbase + kb * 32 * kHeadDim + 1024 * u;
+            const bf16x8_t a = cat4(lds_read_tr(vp + 32 * db), lds_read_tr(vp + 256 + 32 * (db ^ 1)));
             acc[0][db] = mfma_32x32x16(a, pb[0][u], acc[0][db]);
             acc[1][db] = mfma_32x32x16(a, pb[1][u], acc[1][db]);
           }

@@ -276,6 +276,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="also run one plain device-to-device copy of this many MiB (a reference "
+                         "for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -285,6 +288,14 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline()   # before the GPU is touched
+    if args.calibration_copy_mib > 0:
+        import torch
+        n = args.calibration_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     g = gpu_bench(args.steps, args.warmup)
     out = {
         "metric": METRIC, "value": g["value"],

@@ -27,10 +27,21 @@ namespace sinkattn {
 
 namespace {
 
-constexpr int kQTile = 32;     // query tokens per workgroup
-constexpr int kKTile = 64;     // keys per LDS tile (two 32-key halves)
-constexpr int kThreads = 256;  // 4 waves
+constexpr int kQTile = 32;  // query tokens per workgroup
+#ifndef SINKATTN_PREFILL_KTILE
+#define SINKATTN_PREFILL_KTILE 128
+#endif
+constexpr int kKTile = SINKATTN_PREFILL_KTILE;  // keys per LDS tile (32-key halves)
+constexpr int kHalves = kKTile / 32;
 constexpr int kHeadsPerBlock = 8;
+// kCols query heads ("column blocks" of 32 columns) per wave; the workgroup
+// has 8 / kCols waves.
+template <int kCols>
+constexpr int threads_for() { return 64 * (kHeadsPerBlock / kCols); }
+#ifndef SINKATTN_PREFILL_COLS
+#define SINKATTN_PREFILL_COLS 2
+#endif
+constexpr int kColsPerWave = SINKATTN_PREFILL_COLS;
 // Lazy reference max.  Probabilities are taken against a per-row reference
 // m (log2 units) that only moves when the new keys push a row's partial
 // denominator past 2^32 (or when the row has no reference yet); the running
@@ -40,41 +51,51 @@ constexpr int kHeadsPerBlock = 8;
 // unchanged in exact arithmetic.
 constexpr float kRescaleSum = 4294967296.0f;  // 2^32
 
-struct TileRegs {
-  u32x4_t k[2];
-  u32x4_t v[2];
-};
-
-// Global -> registers for one 64-key tile: thread -> (row, 16-byte chunk).
-__device__ __forceinline__ void load_tile(TileRegs& r, const uint16_t* __restrict__ k,
-                                          const uint16_t* __restrict__ v, int seq0, int len, int hkv,
-                                          int g, int key0, int tid) {
+// Issue the copy of one K/V tile (kKTile rows x 8 16-byte chunks of each)
+// HBM -> LDS without passing through registers (global_load_lds).  Slot n
+// = 64 (kPer wave + i) + lane of the tile holds row n / 8, chunk position
+// n % 8, which under the chunk swizzle is global chunk (n % 8) ^ swz_f(row).  Rows past the sequence end are clamped to its
+// last key: they only ever meet masked logits.
+template <int kThreads>
+__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                           uint16_t* k_dst, uint16_t* v_dst, int seq0, int len, int hkv,
+                                           int g, int key0, int wave, int lane) {
+  constexpr int kPer = kKTile * 8 / kThreads;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = (tid >> 3) + 32 * i;
-    const int key = key0 + row;
-    r.k[i] = zero_u32x4();
-    r.v[i] = zero_u32x4();
-    if (key < len) {
-      const size_t off = (static_cast<size_t>(seq0 + key) * hkv + g) * kHeadDim + (tid & 7) * 8;
-      r.k[i] = load16(k + off);
-      r.v[i] = load16(v + off);
+  for (int i = 0; i < kPer; ++i) {
+    const int slot0 = 64 * (kPer * wave + i);
+    const int row = (slot0 >> 3) + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz_f(row);
+    const int key = min(key0 + row, len - 1);
+    const size_t off = (static_cast<size_t>(seq0 + key) * hkv + g) * kHeadDim + chunk * 8;
+    load16_to_lds(k + off, k_dst + slot0 * 8);
+    load16_to_lds(v + off, v_dst + slot0 * 8);
+  }
+}
+
+// P (bf16, the B operand of O^T) for one 32-key half of one column block
+// against the reference max m_use (log2 units); returns this lane's partial
+// sum of the bf16-rounded probabilities.
+__device__ __forceinline__ float probs(const f32x16_t& sacc, bf16x8_t (&pb)[2], float m_use, float scale_log2) {
+  float l = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    bf16x8_t pv;
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+      pv[tt] = static_cast<__bf16>(fast_exp2(fmaf(sacc[8 * u + tt], scale_log2, -m_use)));
+#pragma unroll
+    for (int tt = 0; tt < 8; tt += 2) {
+      bf16x2_t pr = {pv[tt], pv[tt + 1]};
+      l = add_pair(pr, l);
     }
+    pb[u] = pv;
   }
+  return l;
 }
 
-__device__ __forceinline__ void store_tile(const TileRegs& r, uint16_t* k_lds, uint16_t* v_lds, int tid) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = (tid >> 3) + 32 * i;
-    const int dst = swz(row, (tid & 7) * 8);
-    *reinterpret_cast<u32x4_t*>(k_lds + dst) = r.k[i];
-    *reinterpret_cast<u32x4_t*>(v_lds + dst) = r.v[i];
-  }
-}
-
-template <bool kWindow>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
+template <bool kWindow, int kCols>
+__global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_per_eu(4 / kCols, 4 / kCols))) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ sinks,
     const int32_t* __restrict__ cu_seqlens, int hq, int hkv, int group, int n_hchunk,
@@ -84,6 +105,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kKTile * kHeadDim];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kKTile * kHeadDim];
 
+  constexpr int kThreads = threads_for<kCols>();
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -108,15 +130,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
   const int t_end = last_q / kKTile;
 
   // Start the first K/V tile on its way before anything else.
-  TileRegs regs;
-  load_tile(regs, k, v, seq0, len, hkv, g, t_begin * kKTile, tid);
+  auto issue = [&](int tt) {
+    issue_tile<kThreads>(k, v, k_lds[(tt - t_begin) & 1], v_lds[(tt - t_begin) & 1], seq0, len, hkv, g,
+                         tt * kKTile, wave, lane);
+  };
+  issue(t_begin);
 
-  // Query heads of this wave (two column blocks of 32).
-  int head[2];
-  bool head_ok[2];
+  // Query heads of this wave (kCols column blocks of 32).
+  int head[kCols];
+  bool head_ok[kCols];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int slot = hchunk * kHeadsPerBlock + wave * 2 + c;
+  for (int c = 0; c < kCols; ++c) {
+    const int slot = hchunk * kHeadsPerBlock + wave * kCols + c;
     head_ok[c] = slot < group;
     head[c] = g * group + (head_ok[c] ? slot : 0);
   }
@@ -125,9 +150,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
   const bool row_ok = qtok < len;
 
   // Q^T as the B operand: lane holds query column `col`, d = 16 s + 8 half + t.
-  bf16x8_t qreg[2][4];
+  bf16x8_t qreg[kCols][4];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < kCols; ++c) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u32x4_t val = zero_u32x4();
@@ -142,10 +167,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
   // Online-softmax state per column block.  The reference max m is kept in
   // log2 units (scaled logits); the sink seeds it, and its "1" is counted once
   // (in the lower lane of the pair).
-  float m2[2], lsum[2];
-  f32x16_t acc[2][2];
+  float m2[kCols], lsum[kCols];
+  f32x16_t acc[kCols][2];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < kCols; ++c) {
     const float z = (sinks != nullptr && head_ok[c]) ? sinks[head[c]] : kNegInf;
     if (z > kNegInf) {
       m2[c] = z * kLog2e;
@@ -158,150 +183,151 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
     acc[c][1] = zero16();
   }
 
-  store_tile(regs, k_lds[0], v_lds[0], tid);
+  wait_vmem();
   __syncthreads();
 
-  // LDS read offsets (elements, within a 32-row half of a tile).  K^T rows
-  // as the A operand: row key_of_row(col), d = 16 s + 8 half.  V^T operand:
+  // LDS read offsets (elements, within a 32-row half of a tile).  K rows as
+  // the A operand: row key_of_row(col), d = 16 s + 8 half.  V^T operand:
   // lane (d = l % 32 of block db, half) needs rows 16 u + 8 half + 0..7 at
-  // its column, as two transposing reads of 4 rows (i = 0, 1); under the
-  // chunk swizzle read (db, u, i) sits at vbase + 1024 u + 256 i + 32 (db ^ i).
+  // its column, as two transposing reads of 4 rows (i = 0, 1); the swizzle
+  // depends on the row's low four bits only, so read (db, u, i) sits at
+  // voff[db][i] + 1024 u.
   int koff[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) koff[s] = swz(key_of_row(col), 16 * s + 8 * half);
   const int grp_lane = lane & 15;
   const int dcol0 = 16 * ((lane >> 4) & 1) + 4 * (grp_lane & 3);
-  const int vbase = (8 * half + (grp_lane >> 2)) * kHeadDim + ((((dcol0 >> 3) ^ (grp_lane >> 2)) & 3) << 3) +
-                    (dcol0 & 7);
+  int voff[2][2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) voff[db][i] = swz(8 * half + (grp_lane >> 2) + 4 * i, 32 * db + dcol0);
 
-  for (int t = t_begin; t <= t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
-    const bool more = t < t_end;
-    if (more) load_tile(regs, k, v, seq0, len, hkv, g, (t + 1) * kKTile, tid);
+  // Keys are walked in 32-key halves h_begin..h_end (every half holds a key
+  // some query of the tile sees); tiles of kKTile keys are what is staged.
+  const int h_begin = first_key >> 5;
+  const int h_end = last_q >> 5;
+  const uint16_t* k_base = &k_lds[0][0];
+  const uint16_t* v_base = &v_lds[0][0];
+  auto half_off = [&](int hh) {
+    const int t = hh / kHalves;
+    return ((t - t_begin) & 1) * (kKTile * kHeadDim) + (hh - t * kHalves) * (32 * kHeadDim);
+  };
 
+  // Operands are read from LDS one step ahead of the MFMAs that use them:
+  // K of the next half during the current half, V of a half before its
+  // softmax, so the LDS latency overlaps other work.
+  bf16x8_t kop[4];
+  bf16x8_t vop[2][2];
+  auto read_k = [&](int hh) {
+    const uint16_t* kt = k_base + half_off(hh);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kop[s] = *reinterpret_cast<const bf16x8_t*>(kt + koff[s]);
+  };
+  auto read_v = [&](int hh) {
+    const uint16_t* vt = v_base + half_off(hh);
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        vop[db][u] = cat4(lds_read_tr(vt + voff[db][0] + 1024 * u), lds_read_tr(vt + voff[db][1] + 1024 * u));
+  };
+
+  int t = t_begin;
+  if (t < t_end) issue(t + 1);
+  if (wave_active) read_k(h_begin);
+
+  for (int hh = h_begin; hh <= h_end; ++hh) {
+    const bool tile_last = (hh == h_end) || ((hh + 1) % kHalves == 0);
     if (wave_active) {
-      const uint16_t* kt = k_lds[buf];
-      const uint16_t* vt = v_lds[buf];
+      const int kbase = hh * 32;
+      // S^T = K Q^T for 32 keys and the wave's column blocks.
+      f32x16_t sacc[kCols];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int kbase = t * kKTile + kb * 32;
-        // Halves no query of the tile can see are skipped.
-        const bool dead = (kbase > last_q) || (kWindow && kbase + 31 <= q0 - window);
-        if (dead) continue;
+      for (int c = 0; c < kCols; ++c) sacc[c] = zero16();
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int c = 0; c < kCols; ++c) sacc[c] = mfma_32x32x16(kop[s], qreg[c][s], sacc[c]);
+      read_v(hh);
+      if (!tile_last) read_k(hh + 1);
 
-        // S^T = K Q^T for 32 keys and two column blocks.
-        f32x16_t sacc[2] = {zero16(), zero16()};
+      const bool need_mask = (kbase + 31 > q0) || (kWindow && kbase <= last_q - window);
+      if (need_mask) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + kb * 32 * kHeadDim + koff[s]);
-          sacc[0] = mfma_32x32x16(a, qreg[0][s], sacc[0]);
-          sacc[1] = mfma_32x32x16(a, qreg[1][s], sacc[1]);
-        }
-
-        const bool need_mask = (kbase + 31 > q0) || (kWindow && kbase <= last_q - window);
-        if (need_mask) {
+        for (int r = 0; r < 16; ++r) {
+          const int key = kbase + key_of_reg(r, half);
+          const bool ok = key <= qtok && (!kWindow || key > qtok - window);
+          if (!ok) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kbase + key_of_reg(r, half);
-            const bool ok = key <= qtok && (!kWindow || key > qtok - window);
-            if (!ok) {
-              sacc[0][r] = kNegInf;
-              sacc[1][r] = kNegInf;
-            }
-          }
-        }
-
-        // Online softmax (log2 domain), P in bf16 as the B operand of O^T.
-        // Fast path: P against the current reference m, no row max.
-        bf16x8_t pb[2][2];  // [c][u]
-        float tsum[2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const float m_use = m2[c] == kNegInf ? 0.0f : m2[c];
-          float l = 0.0f;
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            bf16x8_t pv;
-#pragma unroll
-            for (int tt = 0; tt < 8; ++tt)
-              pv[tt] = static_cast<__bf16>(fast_exp2(fmaf(sacc[c][8 * u + tt], scale_log2, -m_use)));
-#pragma unroll
-            for (int tt = 0; tt < 8; tt += 2) {
-              bf16x2_t pr = {pv[tt], pv[tt + 1]};
-              l = add_pair(pr, l);
-            }
-            pb[c][u] = pv;
-          }
-          tsum[c] = l;
-        }
-        // Slow path (rare): a row without reference yet, or keys far above
-        // it.  Move the reference to the row max, redo P, rescale the state.
-        const bool slow0 = m2[0] == kNegInf || !(tsum[0] <= kRescaleSum);
-        const bool slow1 = m2[1] == kNegInf || !(tsum[1] <= kRescaleSum);
-        if (wave_any(slow0 || slow1)) {
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            float mx = sacc[c][0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[c][r]);
-            mx = pair_max(mx) * scale_log2;
-            const bool slow = c == 0 ? slow0 : slow1;
-            // the pair agrees on `slow` (same reference, and the pair's
-            // sums are compared lane by lane, so make it pair-uniform)
-            const bool move = pair_max(slow ? 1.0f : 0.0f) > 0.0f && mx > m2[c];
-            const float m_new = move ? mx : m2[c];
-            const float alpha = move ? fast_exp2(m2[c] - m_new) : 1.0f;
-            m2[c] = m_new;
-            lsum[c] *= alpha;
-#pragma unroll
-            for (int db = 0; db < 2; ++db)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) acc[c][db][r] *= alpha;
-            const float m_use = m_new == kNegInf ? 0.0f : m_new;
-            float l = 0.0f;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              bf16x8_t pv;
-#pragma unroll
-              for (int tt = 0; tt < 8; ++tt)
-                pv[tt] = static_cast<__bf16>(fast_exp2(fmaf(sacc[c][8 * u + tt], scale_log2, -m_use)));
-#pragma unroll
-              for (int tt = 0; tt < 8; tt += 2) {
-                bf16x2_t pr = {pv[tt], pv[tt + 1]};
-                l = add_pair(pr, l);
-              }
-              pb[c][u] = pv;
-            }
-            tsum[c] = l;
-          }
-        }
-        lsum[0] += tsum[0];
-        lsum[1] += tsum[1];
-
-        // O^T += V^T P^T: lane (d = l % 32 of block db, half) reads V rows
-        // kb*32 + 16u + 8 half + 0..7 at its column (two transposing reads).
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const uint16_t* vp = vt + vbase + kb * 32 * kHeadDim + 1024 * u;
-            const bf16x8_t a = cat4(lds_read_tr(vp + 32 * db), lds_read_tr(vp + 256 + 32 * (db ^ 1)));
-            acc[0][db] = mfma_32x32x16(a, pb[0][u], acc[0][db]);
-            acc[1][db] = mfma_32x32x16(a, pb[1][u], acc[1][db]);
+            for (int c = 0; c < kCols; ++c) sacc[c][r] = kNegInf;
           }
         }
       }
+
+      // Online softmax (log2 domain), P in bf16 as the B operand of O^T.
+      // Fast path: P against the current reference m, no row max.
+      bf16x8_t pb[kCols][2];  // [c][u]
+      float tsum[kCols];
+      bool slow[kCols];
+      bool any_slow = false;
+#pragma unroll
+      for (int c = 0; c < kCols; ++c) {
+        tsum[c] = probs(sacc[c], pb[c], m2[c] == kNegInf ? 0.0f : m2[c], scale_log2);
+        slow[c] = m2[c] == kNegInf || !(tsum[c] <= kRescaleSum);
+        any_slow |= slow[c];
+      }
+      // Slow path (rare): a row without reference yet, or keys far above
+      // it.  Move the reference to the row max (uniformly over the lane
+      // pair), rescale the state, redo P.
+      if (wave_any(any_slow)) {
+#pragma unroll
+        for (int c = 0; c < kCols; ++c) {
+          float mx = sacc[c][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[c][r]);
+          mx = pair_max(mx) * scale_log2;
+          const bool move = pair_max(slow[c] ? 1.0f : 0.0f) > 0.0f && mx > m2[c];
+          const float m_new = move ? mx : m2[c];
+          const float alpha = move ? fast_exp2(m2[c] - m_new) : 1.0f;
+          m2[c] = m_new;
+          lsum[c] *= alpha;
+#pragma unroll
+          for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[c][db][r] *= alpha;
+          tsum[c] = probs(sacc[c], pb[c], m_new == kNegInf ? 0.0f : m_new, scale_log2);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < kCols; ++c) lsum[c] += tsum[c];
+
+      // O^T += V^T P^T.
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int c = 0; c < kCols; ++c) acc[c][db] = mfma_32x32x16(vop[db][u], pb[c][u], acc[c][db]);
     }
 
-    if (more) store_tile(regs, k_lds[buf ^ 1], v_lds[buf ^ 1], tid);
-    __syncthreads();
+    // Tile boundary: wait for the next tile (issued one tile ago) and
+    // publish it; the barrier also retires every read of the current
+    // buffer, which then receives the tile after next.
+    if (tile_last && hh < h_end) {
+      ++t;
+      wait_vmem();
+      __syncthreads();
+      if (t < t_end) issue(t + 1);
+      if (wave_active) read_k(hh + 1);
+    }
   }
 
   if (!wave_active) return;
 
   // Epilogue: full denominator over the lane pair, normalise, store bf16.
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < kCols; ++c) {
     const float den = pair_sum(lsum[c]);
     if (!head_ok[c] || !row_ok) continue;
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
@@ -332,8 +358,8 @@ hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream) {
   const int n_qtiles = (a.max_seqlen + kQTile - 1) / kQTile;
   dim3 grid(static_cast<unsigned>(a.num_kv_heads) * n_hchunk * a.batch, n_qtiles, 1);
   const bool windowed = a.window > 0 && a.window < a.max_seqlen;
-  auto kernel = windowed ? prefill_kernel<true> : prefill_kernel<false>;
-  hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream,
+  auto kernel = windowed ? prefill_kernel<true, kColsPerWave> : prefill_kernel<false, kColsPerWave>;
+  hipLaunchKernelGGL(kernel, grid, dim3(threads_for<kColsPerWave>()), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.sinks, a.cu_seqlens, a.num_q_heads,
                      a.num_kv_heads, group, n_hchunk, n_qtiles, a.window,

@@ -245,10 +245,14 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
       f32x16_t sacc[kCols];
 #pragma unroll
       for (int c = 0; c < kCols; ++c) sacc[c] = zero16();
+      // Raised wave priority while MFMAs are issued: with two waves per SIMD
+      // this favours the wave that can keep the matrix core busy.
+      __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int c = 0; c < kCols; ++c) sacc[c] = mfma_32x32x16(kop[s], qreg[c][s], sacc[c]);
+      __builtin_amdgcn_s_setprio(0);
       read_v(hh);
       if (!tile_last) read_k(hh + 1);
 
@@ -303,12 +307,14 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
       for (int c = 0; c < kCols; ++c) lsum[c] += tsum[c];
 
       // O^T += V^T P^T.
+      __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int c = 0; c < kCols; ++c) acc[c][db] = mfma_32x32x16(vop[db][u], pb[c][u], acc[c][db]);
+      __builtin_amdgcn_s_setprio(0);
     }
 
     // Tile boundary: wait for the next tile (issued one tile ago) and

@@ -46,8 +46,8 @@ __device__ __forceinline__ void load_tile(TileRegs& t, const uint16_t* __restric
     t.v[i] = zero_u32x4();
     if (key < end) {
       const size_t off = (static_cast<size_t>(base + key) * hkv + g) * kHeadDim + (lane & 7) * 8;
-      t.k[i] = load16(k + off);
-      t.v[i] = load16(v + off);
+      t.k[i] = load16_stream(k + off);
+      t.v[i] = load16_stream(v + off);
     }
   }
 }
@@ -233,24 +233,45 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   }
 }
 
-// One wave per (row, head); lane = d.
+// Log-sum-exp merge: one wave per (row, head), lane = d.  The partials of a
+// row are read in batches of kMergeBatch independent loads so that their
+// latencies overlap; the running (max, weight sum, weighted sum) is updated
+// per batch with the same rescaling as the online softmax.
+constexpr int kMergeBatch = 8;
+
 __global__ __launch_bounds__(kThreads) void merge_kernel(
     const float* __restrict__ o_parts, const float* __restrict__ lse_parts, int num_parts,
     int rows, uint16_t* __restrict__ o, float* __restrict__ lse) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (row >= rows) return;
-  float big_m = kNegInf;
-  for (int s = 0; s < num_parts; ++s) big_m = fmaxf(big_m, lse_parts[static_cast<size_t>(s) * rows + row]);
+  float big_m = kNegInf, tot = 0.0f, num = 0.0f;
+  for (int s0 = 0; s0 < num_parts; s0 += kMergeBatch) {
+    float l[kMergeBatch], ov[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int sp = s0 + j;
+      const size_t pr = static_cast<size_t>(sp < num_parts ? sp : s0) * rows + row;
+      l[j] = sp < num_parts ? lse_parts[pr] : kNegInf;
+      ov[j] = o_parts[pr * kHeadDim + lane];
+    }
+    float bm = big_m;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) bm = fmaxf(bm, l[j]);
+    if (bm == kNegInf) continue;  // nothing but empty partials so far
+    const float rescale = fast_exp2((big_m - bm) * kLog2e);  // 0 when big_m = -inf
+    tot *= rescale;
+    num *= rescale;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const float w = fast_exp2((l[j] - bm) * kLog2e);
+      tot += w;
+      num += w * ov[j];
+    }
+    big_m = bm;
+  }
   float out = 0.0f, out_lse = kNegInf;
   if (big_m > kNegInf) {
-    float num = 0.0f, tot = 0.0f;
-    for (int s = 0; s < num_parts; ++s) {
-      const size_t pr = static_cast<size_t>(s) * rows + row;
-      const float w = fast_exp2((lse_parts[pr] - big_m) * kLog2e);
-      tot += w;
-      num += w * o_parts[pr * kHeadDim + lane];
-    }
     out = num / tot;
     out_lse = big_m + __log2f(tot) * kLn2;
   }

@@ -119,7 +119,7 @@ sinkattn_status sinkattn_decode_splitkv(const void* q, const void* k_cache, cons
   const long long blocks = static_cast<long long>(batch) * num_kv_heads * num_splits;
   if (blocks > 0x7fffffffLL) return fail(SINKATTN_ERR_UNSUPPORTED, "too many (batch, head, split) work items");
 
-  sinkattn::DecodeLaunch a{q, k_cache, v_cache, sinks, cu_seqlens_k, batch, num_q_heads, num_kv_heads,
+  sinkattn::DecodeLaunch a{q, k_cache, v_cache, sinks, cu_seqlens_k, batch, max_seqlen_k, num_q_heads, num_kv_heads,
                            window, num_splits, softmax_scale, o, lse, nullptr, nullptr};
   if (num_splits == 1) return hip_status(sinkattn::launch_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
 

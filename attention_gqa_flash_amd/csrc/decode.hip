@@ -24,9 +24,13 @@ namespace sinkattn {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // merge kernel: 4 waves, one row each
 constexpr int kWaves = 4;
 constexpr int kKeys = 32;  // keys per wave iteration
+// The decode workgroup has kDecWaves waves: 4 for long key chunks, 2 when a
+// chunk holds at most kShortChunk keys (fewer waves to merge per workgroup,
+// twice the workgroups resident per CU).
+constexpr int kShortChunk = 1024;
 
 // One 32-key tile of one wave, in registers, K and V rows in coalesced
 // order: lane l holds the 16-byte chunk l % 8 of rows l / 8 + 8 i.  Keys at or
@@ -52,7 +56,8 @@ __device__ __forceinline__ void load_tile(TileRegs& t, const uint16_t* __restric
   }
 }
 
-__global__ __launch_bounds__(kThreads) void decode_kernel(
+template <int kDecWaves>
+__global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ sinks,
     const int32_t* __restrict__ cu_seqlens_k, int batch, int hq, int hkv, int group,
@@ -60,9 +65,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     float* __restrict__ lse, float* __restrict__ o_part, float* __restrict__ lse_part) {
   // Wave-private K and V staging tiles (2 x 4 KiB per wave); the whole
   // buffer is reused for the cross-wave merge of up to 32 heads x 64 d.
-  __shared__ __attribute__((aligned(16))) float lds_buf[kWaves * 32 * kHeadDim];
-  __shared__ float red_m[kWaves][32];
-  __shared__ float red_l[kWaves][32];
+  __shared__ __attribute__((aligned(16))) float lds_buf[(kDecWaves < 4 ? 4 : kDecWaves) * 32 * kHeadDim];
+  __shared__ float red_m[kDecWaves][32];
+  __shared__ float red_l[kDecWaves][32];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -118,8 +123,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   int k0 = a + kKeys * wave;
   if (k0 < e) load_tile(cur, k, v, base, hkv, g, k0, e, lane);
 
-  for (; k0 < e; k0 += kKeys * kWaves) {
-    const int k1 = k0 + kKeys * kWaves;
+  for (; k0 < e; k0 += kKeys * kDecWaves) {
+    const int k1 = k0 + kKeys * kDecWaves;
     if (k1 < e) load_tile(nxt, k, v, base, hkv, g, k1, e, lane);
 
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // previous tile's LDS reads are done
@@ -203,17 +208,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   }
   __syncthreads();
 
-  for (int idx = tid; idx < group * kHeadDim; idx += kThreads) {
+  for (int idx = tid; idx < group * kHeadDim; idx += 64 * kDecWaves) {
     const int hc = idx / kHeadDim;
     const int d = idx % kHeadDim;
     float big_m = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) big_m = fmaxf(big_m, red_m[w][hc]);
+    for (int w = 0; w < kDecWaves; ++w) big_m = fmaxf(big_m, red_m[w][hc]);
     float out = 0.0f, out_lse = kNegInf;
     if (big_m > kNegInf) {
       float num = 0.0f, tot = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < kDecWaves; ++w) {
         const float sc = fast_exp2(red_m[w][hc] - big_m);
         tot += sc * red_l[w][hc];
         num += sc * red_o[(w * group + hc) * kHeadDim + d];
@@ -284,7 +289,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
   const unsigned blocks = static_cast<unsigned>(a.batch) * a.num_kv_heads * a.num_splits;
-  hipLaunchKernelGGL(decode_kernel, dim3(blocks), dim3(kThreads), 0, stream,
+  const long long keys_per_split = (static_cast<long long>(a.max_seqlen_k) + a.num_splits - 1) / a.num_splits;
+  const bool short_chunks = keys_per_split <= kShortChunk;
+  auto kernel = short_chunks ? decode_kernel<2> : decode_kernel<4>;
+  hipLaunchKernelGGL(kernel, dim3(blocks), dim3(short_chunks ? 128 : 256), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.sinks, a.cu_seqlens_k, a.batch,
                      a.num_q_heads, a.num_kv_heads, group, a.window, a.softmax_scale * kLog2e,

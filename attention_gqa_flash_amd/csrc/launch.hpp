@@ -25,7 +25,7 @@ struct DecodeLaunch {
   const void* v;
   const float* sinks;
   const int32_t* cu_seqlens_k;
-  int batch, num_q_heads, num_kv_heads, window, num_splits;
+  int batch, max_seqlen_k, num_q_heads, num_kv_heads, window, num_splits;
   float softmax_scale;
   void* o;          // bf16 output when num_splits == 1
   float* lse;       // optional, num_splits == 1

@@ -5,7 +5,7 @@ Where the oracle cannot finish the whole output in seconds (long prefill),
 it computes a sample of rows one by one: every row of the first tiles, rows
 around tile and window boundaries, the last rows of every sequence and
 seeded random rows, each for all 64 heads.  Decode outputs are compared in
-full.  Bar: max |err| <= 2e-2, mean |err| <= 2e-3, lse within 1e-3.
+full.  Bar: max |err| <= 2e-2, mean |err| <= 2e-3, lse within 4e-3.
 """
 
 import numpy as np

@@ -101,9 +101,13 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
     const int32_t* __restrict__ cu_seqlens, int hq, int hkv, int group, int n_hchunk,
     int n_qtiles, int window, float scale_log2, uint16_t* __restrict__ o,
     float* __restrict__ lse) {
-  // Two LDS buffers per operand: tile t+1 is written while tile t is read.
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kKTile * kHeadDim];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kKTile * kHeadDim];
+  // Two LDS tile buffers (K rows then V rows): tile t+1 is written while
+  // tile t is read.  They are separate arrays, and every access names one of
+  // them statically (tiles are processed in pairs), so the compiler can tell
+  // that the asynchronous copy into one buffer does not touch the other and
+  // does not make reads of the current tile wait for the next one.
+  __shared__ __attribute__((aligned(16))) uint16_t kv_lds0[2 * kKTile * kHeadDim];
+  __shared__ __attribute__((aligned(16))) uint16_t kv_lds1[2 * kKTile * kHeadDim];
 
   constexpr int kThreads = threads_for<kCols>();
   const int tid = threadIdx.x;
@@ -130,11 +134,8 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
   const int t_end = last_q / kKTile;
 
   // Start the first K/V tile on its way before anything else.
-  auto issue = [&](int tt) {
-    issue_tile<kThreads>(k, v, k_lds[(tt - t_begin) & 1], v_lds[(tt - t_begin) & 1], seq0, len, hkv, g,
-                         tt * kKTile, wave, lane);
-  };
-  issue(t_begin);
+  issue_tile<kThreads>(k, v, kv_lds0, kv_lds0 + kKTile * kHeadDim, seq0, len, hkv, g, t_begin * kKTile,
+                       wave, lane);
 
   // Query heads of this wave (kCols column blocks of 32).
   int head[kCols];
@@ -207,25 +208,17 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
   // some query of the tile sees); tiles of kKTile keys are what is staged.
   const int h_begin = first_key >> 5;
   const int h_end = last_q >> 5;
-  const uint16_t* k_base = &k_lds[0][0];
-  const uint16_t* v_base = &v_lds[0][0];
-  auto half_off = [&](int hh) {
-    const int t = hh / kHalves;
-    return ((t - t_begin) & 1) * (kKTile * kHeadDim) + (hh - t * kHalves) * (32 * kHeadDim);
-  };
 
   // Operands are read from LDS one step ahead of the MFMAs that use them:
   // K of the next half during the current half, V of a half before its
   // softmax, so the LDS latency overlaps other work.
   bf16x8_t kop[4];
   bf16x8_t vop[2][2];
-  auto read_k = [&](int hh) {
-    const uint16_t* kt = k_base + half_off(hh);
+  auto read_k = [&](const uint16_t* kt) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) kop[s] = *reinterpret_cast<const bf16x8_t*>(kt + koff[s]);
   };
-  auto read_v = [&](int hh) {
-    const uint16_t* vt = v_base + half_off(hh);
+  auto read_v = [&](const uint16_t* vt) {
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -233,100 +226,116 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
         vop[db][u] = cat4(lds_read_tr(vt + voff[db][0] + 1024 * u), lds_read_tr(vt + voff[db][1] + 1024 * u));
   };
 
-  int t = t_begin;
-  if (t < t_end) issue(t + 1);
-  if (wave_active) read_k(h_begin);
+  // One 32-key half: kt / vt point at its K and V rows in LDS, kt_next at
+  // the K rows of the next half (nullptr at a tile end).
+  auto step = [&](int hh, const uint16_t* vt, const uint16_t* kt_next) {
+    const int kbase = hh * 32;
+    // S^T = K Q^T for 32 keys and the wave's column blocks.
+    f32x16_t sacc[kCols];
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) sacc[c] = zero16();
+    // Raised wave priority while MFMAs are issued: with two waves per SIMD
+    // this favours the wave that can keep the matrix core busy.
+    __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int c = 0; c < kCols; ++c) sacc[c] = mfma_32x32x16(kop[s], qreg[c][s], sacc[c]);
+    __builtin_amdgcn_s_setprio(0);
+    read_v(vt);
+    if (kt_next != nullptr) read_k(kt_next);
 
-  for (int hh = h_begin; hh <= h_end; ++hh) {
-    const bool tile_last = (hh == h_end) || ((hh + 1) % kHalves == 0);
-    if (wave_active) {
-      const int kbase = hh * 32;
-      // S^T = K Q^T for 32 keys and the wave's column blocks.
-      f32x16_t sacc[kCols];
+    const bool need_mask = (kbase + 31 > q0) || (kWindow && kbase <= last_q - window);
+    if (need_mask) {
 #pragma unroll
-      for (int c = 0; c < kCols; ++c) sacc[c] = zero16();
-      // Raised wave priority while MFMAs are issued: with two waves per SIMD
-      // this favours the wave that can keep the matrix core busy.
-      __builtin_amdgcn_s_setprio(2);
+      for (int r = 0; r < 16; ++r) {
+        const int key = kbase + key_of_reg(r, half);
+        const bool ok = key <= qtok && (!kWindow || key > qtok - window);
+        if (!ok) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int c = 0; c < kCols; ++c) sacc[c] = mfma_32x32x16(kop[s], qreg[c][s], sacc[c]);
-      __builtin_amdgcn_s_setprio(0);
-      read_v(hh);
-      if (!tile_last) read_k(hh + 1);
-
-      const bool need_mask = (kbase + 31 > q0) || (kWindow && kbase <= last_q - window);
-      if (need_mask) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kbase + key_of_reg(r, half);
-          const bool ok = key <= qtok && (!kWindow || key > qtok - window);
-          if (!ok) {
-#pragma unroll
-            for (int c = 0; c < kCols; ++c) sacc[c][r] = kNegInf;
-          }
+          for (int c = 0; c < kCols; ++c) sacc[c][r] = kNegInf;
         }
       }
+    }
 
-      // Online softmax (log2 domain), P in bf16 as the B operand of O^T.
-      // Fast path: P against the current reference m, no row max.
-      bf16x8_t pb[kCols][2];  // [c][u]
-      float tsum[kCols];
-      bool slow[kCols];
-      bool any_slow = false;
+    // Online softmax (log2 domain), P in bf16 as the B operand of O^T.
+    // Fast path: P against the current reference m, no row max.
+    bf16x8_t pb[kCols][2];  // [c][u]
+    float tsum[kCols];
+    bool slow[kCols];
+    bool any_slow = false;
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) {
+      tsum[c] = probs(sacc[c], pb[c], m2[c] == kNegInf ? 0.0f : m2[c], scale_log2);
+      slow[c] = m2[c] == kNegInf || !(tsum[c] <= kRescaleSum);
+      any_slow |= slow[c];
+    }
+    // Slow path (rare): a row without reference yet, or keys far above
+    // it.  Move the reference to the row max (uniformly over the lane
+    // pair), rescale the state, redo P.
+    if (wave_any(any_slow)) {
 #pragma unroll
       for (int c = 0; c < kCols; ++c) {
-        tsum[c] = probs(sacc[c], pb[c], m2[c] == kNegInf ? 0.0f : m2[c], scale_log2);
-        slow[c] = m2[c] == kNegInf || !(tsum[c] <= kRescaleSum);
-        any_slow |= slow[c];
+        float mx = sacc[c][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[c][r]);
+        mx = pair_max(mx) * scale_log2;
+        const bool move = pair_max(slow[c] ? 1.0f : 0.0f) > 0.0f && mx > m2[c];
+        const float m_new = move ? mx : m2[c];
+        const float alpha = move ? fast_exp2(m2[c] - m_new) : 1.0f;
+        m2[c] = m_new;
+        lsum[c] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[c][db][r] *= alpha;
+        tsum[c] = probs(sacc[c], pb[c], m_new == kNegInf ? 0.0f : m_new, scale_log2);
       }
-      // Slow path (rare): a row without reference yet, or keys far above
-      // it.  Move the reference to the row max (uniformly over the lane
-      // pair), rescale the state, redo P.
-      if (wave_any(any_slow)) {
-#pragma unroll
-        for (int c = 0; c < kCols; ++c) {
-          float mx = sacc[c][0];
-#pragma unroll
-          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[c][r]);
-          mx = pair_max(mx) * scale_log2;
-          const bool move = pair_max(slow[c] ? 1.0f : 0.0f) > 0.0f && mx > m2[c];
-          const float m_new = move ? mx : m2[c];
-          const float alpha = move ? fast_exp2(m2[c] - m_new) : 1.0f;
-          m2[c] = m_new;
-          lsum[c] *= alpha;
-#pragma unroll
-          for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[c][db][r] *= alpha;
-          tsum[c] = probs(sacc[c], pb[c], m_new == kNegInf ? 0.0f : m_new, scale_log2);
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < kCols; ++c) lsum[c] += tsum[c];
-
-      // O^T += V^T P^T.
-      __builtin_amdgcn_s_setprio(2);
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int c = 0; c < kCols; ++c) acc[c][db] = mfma_32x32x16(vop[db][u], pb[c][u], acc[c][db]);
-      __builtin_amdgcn_s_setprio(0);
     }
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) lsum[c] += tsum[c];
 
-    // Tile boundary: wait for the next tile (issued one tile ago) and
-    // publish it; the barrier also retires every read of the current
-    // buffer, which then receives the tile after next.
-    if (tile_last && hh < h_end) {
-      ++t;
+    // O^T += V^T P^T.
+    __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int c = 0; c < kCols; ++c) acc[c][db] = mfma_32x32x16(vop[db][u], pb[c][u], acc[c][db]);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // All halves of tile t, which sits in buffer `cur`; at the tile boundary
+  // the next tile (buffer `nxt`, issued one tile ago) is waited for and
+  // published, and the tile after it is issued into `cur`, whose reads the
+  // barrier has retired.
+  auto run_tile = [&](int t, uint16_t* cur, uint16_t* nxt) {
+    const int hb = max(h_begin, t * kHalves);
+    const int he = min(h_end, t * kHalves + kHalves - 1);
+    if (wave_active) {
+      for (int hh = hb; hh <= he; ++hh) {
+        const int i = hh - t * kHalves;
+        step(hh, cur + kKTile * kHeadDim + i * 32 * kHeadDim, hh < he ? cur + (i + 1) * 32 * kHeadDim : nullptr);
+      }
+    }
+    if (t < t_end) {
       wait_vmem();
       __syncthreads();
-      if (t < t_end) issue(t + 1);
-      if (wave_active) read_k(hh + 1);
+      if (t + 2 <= t_end)
+        issue_tile<kThreads>(k, v, cur, cur + kKTile * kHeadDim, seq0, len, hkv, g, (t + 2) * kKTile, wave,
+                             lane);
+      if (wave_active) read_k(nxt);
     }
+  };
+
+  if (t_begin < t_end)
+    issue_tile<kThreads>(k, v, kv_lds1, kv_lds1 + kKTile * kHeadDim, seq0, len, hkv, g, (t_begin + 1) * kKTile,
+                         wave, lane);
+  if (wave_active) read_k(kv_lds0 + (h_begin - t_begin * kHalves) * 32 * kHeadDim);
+  for (int t = t_begin; t <= t_end; t += 2) {
+    run_tile(t, kv_lds0, kv_lds1);
+    if (t + 1 <= t_end) run_tile(t + 1, kv_lds1, kv_lds0);
   }
 
   if (!wave_active) return;

@@ -116,6 +116,20 @@ __device__ __forceinline__ void load16_to_lds(const uint16_t* src, uint16_t* lds
   __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void*)(lds_base), 16, 0, 0);
 }
 
+// The same copy issued from inline assembly, invisible to the compiler's
+// memory-counter tracking: the compiler then adds no vmcnt waits of its own
+// before LDS reads, so reads of one buffer do not wait for a copy into
+// another.  The caller orders every read of the destination after the copy
+// with wait_vmem() and a barrier.  The LDS base goes through M0, which no
+// other code of the kernels using this sets or reads.
+__device__ __forceinline__ void load16_to_lds_untracked(const uint16_t* src, uint16_t* lds_base) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(lds_base)));
+  a = __builtin_amdgcn_readfirstlane(a);
+  asm volatile("" : "+s"(a));
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void*)(uintptr_t)(a), 16, 0, 0);
+}
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ u32x4_t load16(const uint16_t* p) {

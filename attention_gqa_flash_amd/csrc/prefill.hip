@@ -68,16 +68,17 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ k, const
     const int chunk = (lane & 7) ^ swz_f(row);
     const int key = min(key0 + row, len - 1);
     const size_t off = (static_cast<size_t>(seq0 + key) * hkv + g) * kHeadDim + chunk * 8;
-    load16_to_lds(k + off, k_dst + slot0 * 8);
-    load16_to_lds(v + off, v_dst + slot0 * 8);
+    load16_to_lds_untracked(k + off, k_dst + slot0 * 8);
+    load16_to_lds_untracked(v + off, v_dst + slot0 * 8);
   }
 }
 
 // P (bf16, the B operand of O^T) for one 32-key half of one column block
 // against the reference max m_use (log2 units); returns this lane's partial
-// sum of the bf16-rounded probabilities.
+// sum of the bf16-rounded probabilities (two independent chains, one per
+// 16-key step, to keep the dependency chain short).
 __device__ __forceinline__ float probs(const f32x16_t& sacc, bf16x8_t (&pb)[2], float m_use, float scale_log2) {
-  float l = 0.0f;
+  float l[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     bf16x8_t pv;
@@ -87,11 +88,11 @@ __device__ __forceinline__ float probs(const f32x16_t& sacc, bf16x8_t (&pb)[2], 
 #pragma unroll
     for (int tt = 0; tt < 8; tt += 2) {
       bf16x2_t pr = {pv[tt], pv[tt + 1]};
-      l = add_pair(pr, l);
+      l[u] = add_pair(pr, l[u]);
     }
     pb[u] = pv;
   }
-  return l;
+  return l[0] + l[1];
 }
 
 template <bool kWindow, int kCols>
@@ -226,84 +227,85 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
         vop[db][u] = cat4(lds_read_tr(vt + voff[db][0] + 1024 * u), lds_read_tr(vt + voff[db][1] + 1024 * u));
   };
 
-  // One 32-key half: kt / vt point at its K and V rows in LDS, kt_next at
-  // the K rows of the next half (nullptr at a tile end).
+  // Softmax of column block c for one unmasked half: P against the current
+  // reference, and in the rare slow case (a row without reference yet, or
+  // keys far above it) the reference moves to the row max (uniformly over
+  // the lane pair), the state is rescaled and P is redone.
+  auto softmax_block = [&](int c, const f32x16_t& s_c, bf16x8_t (&pb_c)[2]) {
+    float tsum = probs(s_c, pb_c, m2[c] == kNegInf ? 0.0f : m2[c], scale_log2);
+    const bool slow = m2[c] == kNegInf || !(tsum <= kRescaleSum);
+    if (wave_any(slow)) {
+      float mx = s_c[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_c[r]);
+      mx = pair_max(mx) * scale_log2;
+      const bool move = pair_max(slow ? 1.0f : 0.0f) > 0.0f && mx > m2[c];
+      const float m_new = move ? mx : m2[c];
+      const float alpha = move ? fast_exp2(m2[c] - m_new) : 1.0f;
+      m2[c] = m_new;
+      lsum[c] *= alpha;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[c][db][r] *= alpha;
+      tsum = probs(s_c, pb_c, m_new == kNegInf ? 0.0f : m_new, scale_log2);
+    }
+    lsum[c] += tsum;
+  };
+
+  // Causal / window mask of column block c (a half crossing the diagonal or
+  // the window's lower edge).
+  auto mask_block = [&](int kbase, f32x16_t& s_c) {
+    // Register r of this lane holds key kbase + key_of_reg(r, half); compare
+    // the compile-time part key_of_reg(r, 0) against the query's distance.
+    const int lim = qtok - kbase - 8 * half;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int off = key_of_reg(r, 0);
+      const bool ok = off <= lim && (!kWindow || off > lim - window);
+      if (!ok) s_c[r] = kNegInf;
+    }
+  };
+
+  // One 32-key half.  vt points at its V rows in LDS, kt_next at the K rows
+  // of the next half (read unconditionally, which keeps the half free of
+  // extra branches).  The column blocks are staggered so
+  // that the softmax (VALU) of block c overlaps the MFMAs of S for block
+  // c + 1 and of O^T for block c - 1:
+  //   S_0 | S_1 + softmax_0 | PV_0 + softmax_1 | PV_1.
+  // The K rows of the next half are read once the last S MFMA has taken its
+  // operands, so they can reuse the same registers.  The (rare) mask of block
+  // c sits just before the block that holds softmax_c.
   auto step = [&](int hh, const uint16_t* vt, const uint16_t* kt_next) {
     const int kbase = hh * 32;
-    // S^T = K Q^T for 32 keys and the wave's column blocks.
-    f32x16_t sacc[kCols];
-#pragma unroll
-    for (int c = 0; c < kCols; ++c) sacc[c] = zero16();
-    // Raised wave priority while MFMAs are issued: with two waves per SIMD
-    // this favours the wave that can keep the matrix core busy.
-    __builtin_amdgcn_s_setprio(2);
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int c = 0; c < kCols; ++c) sacc[c] = mfma_32x32x16(kop[s], qreg[c][s], sacc[c]);
-    __builtin_amdgcn_s_setprio(0);
-    read_v(vt);
-    if (kt_next != nullptr) read_k(kt_next);
-
     const bool need_mask = (kbase + 31 > q0) || (kWindow && kbase <= last_q - window);
-    if (need_mask) {
+    f32x16_t sacc[kCols];
+    bf16x8_t pb[kCols][2];
+    auto s_chain = [&](int c) {
+      sacc[c] = zero16();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kbase + key_of_reg(r, half);
-        const bool ok = key <= qtok && (!kWindow || key > qtok - window);
-        if (!ok) {
+      for (int s = 0; s < 4; ++s) sacc[c] = mfma_32x32x16(kop[s], qreg[c][s], sacc[c]);
+    };
+    auto pv_chain = [&](int c) {
 #pragma unroll
-          for (int c = 0; c < kCols; ++c) sacc[c][r] = kNegInf;
-        }
-      }
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) acc[c][db] = mfma_32x32x16(vop[db][u], pb[c][u], acc[c][db]);
+    };
+    s_chain(0);
+    read_v(vt);
+    if (need_mask) mask_block(kbase, sacc[0]);
+#pragma unroll
+    for (int c = 1; c < kCols; ++c) s_chain(c);
+    softmax_block(0, sacc[0], pb[0]);
+    read_k(kt_next);
+#pragma unroll
+    for (int c = 1; c < kCols; ++c) {
+      if (need_mask) mask_block(kbase, sacc[c]);
+      pv_chain(c - 1);
+      softmax_block(c, sacc[c], pb[c]);
     }
-
-    // Online softmax (log2 domain), P in bf16 as the B operand of O^T.
-    // Fast path: P against the current reference m, no row max.
-    bf16x8_t pb[kCols][2];  // [c][u]
-    float tsum[kCols];
-    bool slow[kCols];
-    bool any_slow = false;
-#pragma unroll
-    for (int c = 0; c < kCols; ++c) {
-      tsum[c] = probs(sacc[c], pb[c], m2[c] == kNegInf ? 0.0f : m2[c], scale_log2);
-      slow[c] = m2[c] == kNegInf || !(tsum[c] <= kRescaleSum);
-      any_slow |= slow[c];
-    }
-    // Slow path (rare): a row without reference yet, or keys far above
-    // it.  Move the reference to the row max (uniformly over the lane
-    // pair), rescale the state, redo P.
-    if (wave_any(any_slow)) {
-#pragma unroll
-      for (int c = 0; c < kCols; ++c) {
-        float mx = sacc[c][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[c][r]);
-        mx = pair_max(mx) * scale_log2;
-        const bool move = pair_max(slow[c] ? 1.0f : 0.0f) > 0.0f && mx > m2[c];
-        const float m_new = move ? mx : m2[c];
-        const float alpha = move ? fast_exp2(m2[c] - m_new) : 1.0f;
-        m2[c] = m_new;
-        lsum[c] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[c][db][r] *= alpha;
-        tsum[c] = probs(sacc[c], pb[c], m_new == kNegInf ? 0.0f : m_new, scale_log2);
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < kCols; ++c) lsum[c] += tsum[c];
-
-    // O^T += V^T P^T.
-    __builtin_amdgcn_s_setprio(2);
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int c = 0; c < kCols; ++c) acc[c][db] = mfma_32x32x16(vop[db][u], pb[c][u], acc[c][db]);
-    __builtin_amdgcn_s_setprio(0);
+    pv_chain(kCols - 1);
   };
 
   // All halves of tile t, which sits in buffer `cur`; at the tile boundary
@@ -311,12 +313,18 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
   // published, and the tile after it is issued into `cur`, whose reads the
   // barrier has retired.
   auto run_tile = [&](int t, uint16_t* cur, uint16_t* nxt) {
-    const int hb = max(h_begin, t * kHalves);
-    const int he = min(h_end, t * kHalves + kHalves - 1);
+    // The halves of a tile are unrolled so that every LDS address is a
+    // per-lane base plus an immediate offset.  The K rows read after the
+    // last half of the range come from a fixed slot of the current tile;
+    // they are either overwritten after the barrier or never used.
+    const int ib = max(h_begin - t * kHalves, 0);
+    const int ie = min(h_end - t * kHalves, kHalves - 1);
     if (wave_active) {
-      for (int hh = hb; hh <= he; ++hh) {
-        const int i = hh - t * kHalves;
-        step(hh, cur + kKTile * kHeadDim + i * 32 * kHeadDim, hh < he ? cur + (i + 1) * 32 * kHeadDim : nullptr);
+#pragma unroll
+      for (int i = 0; i < kHalves; ++i) {
+        if (i >= ib && i <= ie)
+          step(t * kHalves + i, cur + kKTile * kHeadDim + i * 32 * kHeadDim,
+               cur + ((i + 1) % kHalves) * 32 * kHeadDim);
       }
     }
     if (t < t_end) {

@@ -84,6 +84,9 @@ sinkattn_status sinkattn_prefill_varlen(const void* q, const void* k, const void
   const int group = num_q_heads / num_kv_heads;
   const long long blocks_x = static_cast<long long>(num_kv_heads) * ((group + 7) / 8) * batch;
   if (blocks_x > 0x7fffffffLL) return fail(SINKATTN_ERR_UNSUPPORTED, "too many (batch, head) work items");
+  // K/V rows of one sequence are addressed with 32-bit byte offsets.
+  if (static_cast<long long>(max_seqlen) * num_kv_heads * head_dim * 2 >= (1LL << 31))
+    return fail(SINKATTN_ERR_UNSUPPORTED, "max_seqlen * num_kv_heads * head_dim * 2 must stay below 2^31");
   sinkattn::PrefillLaunch a{q, k, v, sinks, cu_seqlens, batch, max_seqlen, num_q_heads, num_kv_heads,
                             window, softmax_scale, o, lse};
   return hip_status(sinkattn::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");

@@ -116,18 +116,25 @@ __device__ __forceinline__ void load16_to_lds(const uint16_t* src, uint16_t* lds
   __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void*)(lds_base), 16, 0, 0);
 }
 
-// The same copy issued from inline assembly, invisible to the compiler's
-// memory-counter tracking: the compiler then adds no vmcnt waits of its own
-// before LDS reads, so reads of one buffer do not wait for a copy into
-// another.  The caller orders every read of the destination after the copy
-// with wait_vmem() and a barrier.  The LDS base goes through M0, which no
-// other code of the kernels using this sets or reads.
-__device__ __forceinline__ void load16_to_lds_untracked(const uint16_t* src, uint16_t* lds_base) {
-  typedef __attribute__((address_space(3))) void lds_void;
-  uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(lds_base)));
-  a = __builtin_amdgcn_readfirstlane(a);
-  asm volatile("" : "+s"(a));
-  __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void*)(uintptr_t)(a), 16, 0, 0);
+// The same copy issued from inline assembly, so the compiler does not know
+// about it: it adds no vmcnt waits of its own before LDS reads (it would
+// otherwise make every transposing read wait for every copy in flight).  The
+// caller orders each read of the destination after the copy with a vmcnt
+// wait and a barrier.  The LDS address goes through M0, which the kernels
+// using this do not otherwise use (checked on their assembly when the
+// library is built).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load16_to_lds_untracked(const uint16_t* src, uint32_t lds_addr) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS address (byte offset in the workgroup's LDS) of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  typedef __attribute__((address_space(3))) const void lds_cvoid;
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cvoid*)(p)));
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

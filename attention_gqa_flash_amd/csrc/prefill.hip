@@ -14,12 +14,17 @@
 // block index so that the blocks of one KV head land on the same XCD (blocks
 // are dealt to the 8 XCDs round-robin) and share its L2.
 //
-// Per key tile of 64 keys and per wave (64 query columns):
-//   S^T = K Q^T          16 MFMA 32x32x16 (K from LDS, Q held in registers)
-//   mask                 only on tiles that cross the diagonal / window edge
-//   online softmax       running max in log2 units, exp2, per-lane partial
-//                        denominators (the lane pair shares the max)
-//   O^T += V^T P^T       16 MFMA (V read transposed from LDS)
+// Per 32-key step h and per wave (two column blocks of 32 query columns):
+//   S^T = K Q^T          8 MFMA 32x32x16 (K from LDS, Q held in registers)
+//   mask                 only on steps that cross the diagonal / window edge
+//   online softmax       reference max in log2 units, exp2, per-lane partial
+//                        denominators (the lane pair shares the reference)
+//   O^T += V^T P^T       8 MFMA (V read transposed from LDS)
+// The steps are software-pipelined: while the VALU normalises step h, the
+// matrix core computes S for step h + 1 and O^T for step h - 1, all from one
+// basic block, so each wave keeps both units busy on its own.  K/V tiles of
+// 64 keys rotate through four LDS buffers, copied HBM -> LDS three tiles
+// ahead of use.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -28,11 +33,8 @@ namespace sinkattn {
 namespace {
 
 constexpr int kQTile = 32;  // query tokens per workgroup
-#ifndef SINKATTN_PREFILL_KTILE
-#define SINKATTN_PREFILL_KTILE 128
-#endif
-constexpr int kKTile = SINKATTN_PREFILL_KTILE;  // keys per LDS tile (32-key halves)
-constexpr int kHalves = kKTile / 32;
+constexpr int kKTile = 64;  // keys per LDS tile (two 32-key steps)
+constexpr int kBufs = 4;    // LDS tile buffers in the ring
 constexpr int kHeadsPerBlock = 8;
 // kCols query heads ("column blocks" of 32 columns) per wave; the workgroup
 // has 8 / kCols waves.
@@ -54,12 +56,13 @@ constexpr float kRescaleSum = 4294967296.0f;  // 2^32
 // Issue the copy of one K/V tile (kKTile rows x 8 16-byte chunks of each)
 // HBM -> LDS without passing through registers (global_load_lds).  Slot n
 // = 64 (kPer wave + i) + lane of the tile holds row n / 8, chunk position
-// n % 8, which under the chunk swizzle is global chunk (n % 8) ^ swz_f(row).  Rows past the sequence end are clamped to its
-// last key: they only ever meet masked logits.
+// n % 8, which under the chunk swizzle is global chunk (n % 8) ^ swz_f(row).
+// Rows past the sequence end are clamped to its last key: they only ever
+// meet masked logits.  Each thread issues 2 kPer copies per tile.
 template <int kThreads>
-__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                                           uint16_t* k_dst, uint16_t* v_dst, int seq0, int len, int hkv,
-                                           int g, int key0, int wave, int lane) {
+__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ k_seq, const uint16_t* __restrict__ v_seq,
+                                           uint32_t k_dst, uint32_t v_dst, int len, int row_stride, int key0,
+                                           int wave, int lane) {
   constexpr int kPer = kKTile * 8 / kThreads;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
@@ -67,9 +70,16 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ k, const
     const int row = (slot0 >> 3) + (lane >> 3);
     const int chunk = (lane & 7) ^ swz_f(row);
     const int key = min(key0 + row, len - 1);
-    const size_t off = (static_cast<size_t>(seq0 + key) * hkv + g) * kHeadDim + chunk * 8;
-    load16_to_lds_untracked(k + off, k_dst + slot0 * 8);
-    load16_to_lds_untracked(v + off, v_dst + slot0 * 8);
+    // 32-bit byte offset from the sequence's first row of this KV head (the
+    // host bounds max_seqlen * row_stride * 2 below 2^31).  Kept opaque so
+    // the compiler recomputes it here (uniform base + 32-bit lane offset)
+    // instead of carrying one 64-bit pointer per copy through the loop.
+    uint32_t off = static_cast<uint32_t>(key * row_stride + chunk * 8) * 2u;
+    asm volatile("" : "+v"(off));
+    load16_to_lds_untracked(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(k_seq) + off),
+                            k_dst + slot0 * 16);
+    load16_to_lds_untracked(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(v_seq) + off),
+                            v_dst + slot0 * 16);
   }
 }
 
@@ -95,6 +105,26 @@ __device__ __forceinline__ float probs(const f32x16_t& sacc, bf16x8_t (&pb)[2], 
   return l[0] + l[1];
 }
 
+template <int N>
+struct Parity {
+  static constexpr int value = N;
+};
+
+template <int kThreads>
+constexpr int copies_per_tile() { return 2 * (kKTile * 8 / kThreads); }
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_keep() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that also retires this wave's LDS reads first (so a tile
+// copy issued after it cannot overwrite data still being read) and that the
+// compiler does not move memory operations across.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <bool kWindow, int kCols>
 __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_per_eu(4 / kCols, 4 / kCols))) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -102,15 +132,13 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
     const int32_t* __restrict__ cu_seqlens, int hq, int hkv, int group, int n_hchunk,
     int n_qtiles, int window, float scale_log2, uint16_t* __restrict__ o,
     float* __restrict__ lse) {
-  // Two LDS tile buffers (K rows then V rows): tile t+1 is written while
-  // tile t is read.  They are separate arrays, and every access names one of
-  // them statically (tiles are processed in pairs), so the compiler can tell
-  // that the asynchronous copy into one buffer does not touch the other and
-  // does not make reads of the current tile wait for the next one.
-  __shared__ __attribute__((aligned(16))) uint16_t kv_lds0[2 * kKTile * kHeadDim];
-  __shared__ __attribute__((aligned(16))) uint16_t kv_lds1[2 * kKTile * kHeadDim];
+  // Ring of LDS tile buffers, each K rows then V rows.  Tile t lives in
+  // buffer (t - t_begin) % kBufs; the loop below is unrolled over the ring so
+  // every LDS address is a per-lane base plus an immediate offset.
+  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[kBufs][2 * kKTile * kHeadDim];
 
   constexpr int kThreads = threads_for<kCols>();
+  constexpr int kCopies = copies_per_tile<kThreads>();
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -133,10 +161,28 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
   const int first_key = kWindow ? max(0, q0 - window + 1) : 0;
   const int t_begin = first_key / kKTile;
   const int t_end = last_q / kKTile;
+  // 32-key steps h_begin..h_end: every one holds a key some query of the
+  // tile sees.
+  const int h_begin = first_key >> 5;
+  const int h_end = last_q >> 5;
 
-  // Start the first K/V tile on its way before anything else.
-  issue_tile<kThreads>(k, v, kv_lds0, kv_lds0 + kKTile * kHeadDim, seq0, len, hkv, g, t_begin * kKTile,
-                       wave, lane);
+  // K / V rows of this sequence and KV head; a key's row is hkv * 64
+  // elements further on.
+  const size_t kv0 = (static_cast<size_t>(seq0) * hkv + g) * kHeadDim;
+  const uint16_t* k_seq = k + kv0;
+  const uint16_t* v_seq = v + kv0;
+  // LDS byte address of the ring and the wave index, both uniform.
+  const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_address(&kv_lds[0][0]));
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto issue = [&](int tt, int buf) {
+    const uint32_t dst = ring + static_cast<uint32_t>(buf) * (2 * kKTile * kHeadDim * 2);
+    issue_tile<kThreads>(k_seq, v_seq, dst, dst + kKTile * kHeadDim * 2, len, hkv * kHeadDim, tt * kKTile,
+                         wave_u, lane);
+  };
+  // The first kBufs tiles go out before anything else.
+#pragma unroll
+  for (int i = 0; i < kBufs; ++i)
+    if (t_begin + i <= t_end) issue(t_begin + i, i);
 
   // Query heads of this wave (kCols column blocks of 32).
   int head[kCols];
@@ -185,10 +231,7 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
     acc[c][1] = zero16();
   }
 
-  wait_vmem();
-  __syncthreads();
-
-  // LDS read offsets (elements, within a 32-row half of a tile).  K rows as
+  // LDS read offsets (elements, within a 32-row step of a tile).  K rows as
   // the A operand: row key_of_row(col), d = 16 s + 8 half.  V^T operand:
   // lane (d = l % 32 of block db, half) needs rows 16 u + 8 half + 0..7 at
   // its column, as two transposing reads of 4 rows (i = 0, 1); the swizzle
@@ -205,14 +248,12 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
 #pragma unroll
     for (int i = 0; i < 2; ++i) voff[db][i] = swz(8 * half + (grp_lane >> 2) + 4 * i, 32 * db + dcol0);
 
-  // Keys are walked in 32-key halves h_begin..h_end (every half holds a key
-  // some query of the tile sees); tiles of kKTile keys are what is staged.
-  const int h_begin = first_key >> 5;
-  const int h_end = last_q >> 5;
-
-  // Operands are read from LDS one step ahead of the MFMAs that use them:
-  // K of the next half during the current half, V of a half before its
-  // softmax, so the LDS latency overlaps other work.
+  // Pipeline registers.  S is double-buffered by step parity (static in the
+  // unrolled loop, so no register copies): S of step h in s_buf[h & 1].  P
+  // has one buffer: the O^T MFMAs of step h - 1 read it before the softmax
+  // of step h overwrites it.  V^T of the previous step, K of the next.
+  f32x16_t s_buf[2][kCols];
+  bf16x8_t p_buf[kCols][2];
   bf16x8_t kop[4];
   bf16x8_t vop[2][2];
   auto read_k = [&](const uint16_t* kt) {
@@ -226,39 +267,35 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
       for (int u = 0; u < 2; ++u)
         vop[db][u] = cat4(lds_read_tr(vt + voff[db][0] + 1024 * u), lds_read_tr(vt + voff[db][1] + 1024 * u));
   };
-
-  // Softmax of column block c for one unmasked half: P against the current
-  // reference, and in the rare slow case (a row without reference yet, or
-  // keys far above it) the reference moves to the row max (uniformly over
-  // the lane pair), the state is rescaled and P is redone.
-  auto softmax_block = [&](int c, const f32x16_t& s_c, bf16x8_t (&pb_c)[2]) {
-    float tsum = probs(s_c, pb_c, m2[c] == kNegInf ? 0.0f : m2[c], scale_log2);
-    const bool slow = m2[c] == kNegInf || !(tsum <= kRescaleSum);
-    if (wave_any(slow)) {
-      float mx = s_c[0];
+  // K rows / V rows of step hh, which sits in buffer `buf`.
+  auto k_rows = [&](int buf, int hh) { return kv_lds[buf] + (hh & 1) * 32 * kHeadDim; };
+  auto v_rows = [&](int buf, int hh) { return kv_lds[buf] + kKTile * kHeadDim + (hh & 1) * 32 * kHeadDim; };
+  auto s_chains = [&](f32x16_t (&s_out)[kCols]) {
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_c[r]);
-      mx = pair_max(mx) * scale_log2;
-      const bool move = pair_max(slow ? 1.0f : 0.0f) > 0.0f && mx > m2[c];
-      const float m_new = move ? mx : m2[c];
-      const float alpha = move ? fast_exp2(m2[c] - m_new) : 1.0f;
-      m2[c] = m_new;
-      lsum[c] *= alpha;
+    for (int c = 0; c < kCols; ++c) s_out[c] = zero16();
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[c][db][r] *= alpha;
-      tsum = probs(s_c, pb_c, m_new == kNegInf ? 0.0f : m_new, scale_log2);
-    }
-    lsum[c] += tsum;
+      for (int c = 0; c < kCols; ++c) s_out[c] = mfma_32x32x16(kop[s], qreg[c][s], s_out[c]);
+  };
+  auto pv_chains = [&](const bf16x8_t (&p)[kCols][2]) {
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int c = 0; c < kCols; ++c) acc[c][db] = mfma_32x32x16(vop[db][u], p[c][u], acc[c][db]);
   };
 
-  // Causal / window mask of column block c (a half crossing the diagonal or
-  // the window's lower edge).
-  auto mask_block = [&](int kbase, f32x16_t& s_c) {
-    // Register r of this lane holds key kbase + key_of_reg(r, half); compare
-    // the compile-time part key_of_reg(r, 0) against the query's distance.
-    const int lim = qtok - kbase - 8 * half;
+  // Causal / window mask of step hh (a step crossing the diagonal or the
+  // window's lower edge).  Register r of this lane holds key
+  // 32 hh + key_of_reg(r, half).
+  auto need_mask = [&](int hh) {
+    const int kbase = hh * 32;
+    return (kbase + 31 > q0) || (kWindow && kbase <= last_q - window);
+  };
+  auto mask = [&](int hh, f32x16_t& s_c) {
+    const int lim = qtok - hh * 32 - 8 * half;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int off = key_of_reg(r, 0);
@@ -267,88 +304,132 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
     }
   };
 
-  // One 32-key half.  vt points at its V rows in LDS, kt_next at the K rows
-  // of the next half (read unconditionally, which keeps the half free of
-  // extra branches).  The column blocks are staggered so
-  // that the softmax (VALU) of block c overlaps the MFMAs of S for block
-  // c + 1 and of O^T for block c - 1:
-  //   S_0 | S_1 + softmax_0 | PV_0 + softmax_1 | PV_1.
-  // The K rows of the next half are read once the last S MFMA has taken its
-  // operands, so they can reuse the same registers.  The (rare) mask of block
-  // c sits just before the block that holds softmax_c.
-  auto step = [&](int hh, const uint16_t* vt, const uint16_t* kt_next) {
-    const int kbase = hh * 32;
-    const bool need_mask = (kbase + 31 > q0) || (kWindow && kbase <= last_q - window);
-    f32x16_t sacc[kCols];
-    bf16x8_t pb[kCols][2];
-    auto s_chain = [&](int c) {
-      sacc[c] = zero16();
-#pragma unroll
-      for (int s = 0; s < 4; ++s) sacc[c] = mfma_32x32x16(kop[s], qreg[c][s], sacc[c]);
-    };
-    auto pv_chain = [&](int c) {
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) acc[c][db] = mfma_32x32x16(vop[db][u], pb[c][u], acc[c][db]);
-    };
-    s_chain(0);
-    read_v(vt);
-    if (need_mask) mask_block(kbase, sacc[0]);
-#pragma unroll
-    for (int c = 1; c < kCols; ++c) s_chain(c);
-    softmax_block(0, sacc[0], pb[0]);
-    read_k(kt_next);
-#pragma unroll
-    for (int c = 1; c < kCols; ++c) {
-      if (need_mask) mask_block(kbase, sacc[c]);
-      pv_chain(c - 1);
-      softmax_block(c, sacc[c], pb[c]);
-    }
-    pv_chain(kCols - 1);
+  // Reference max as used by the fast path: -m (0 for a row without
+  // reference yet) and the partial-sum limit above which the slow path runs
+  // (-1, i.e. always, for a row without reference).  Updated only when m
+  // moves.
+  float m_neg[kCols], sum_lim[kCols];
+  auto set_ref = [&](int c) {
+    const bool none = m2[c] == kNegInf;
+    m_neg[c] = none ? 0.0f : -m2[c];
+    sum_lim[c] = none ? -1.0f : kRescaleSum;
   };
-
-  // All halves of tile t, which sits in buffer `cur`; at the tile boundary
-  // the next tile (buffer `nxt`, issued one tile ago) is waited for and
-  // published, and the tile after it is issued into `cur`, whose reads the
-  // barrier has retired.
-  auto run_tile = [&](int t, uint16_t* cur, uint16_t* nxt) {
-    // The halves of a tile are unrolled so that every LDS address is a
-    // per-lane base plus an immediate offset.  The K rows read after the
-    // last half of the range come from a fixed slot of the current tile;
-    // they are either overwritten after the barrier or never used.
-    const int ib = max(h_begin - t * kHalves, 0);
-    const int ie = min(h_end - t * kHalves, kHalves - 1);
-    if (wave_active) {
 #pragma unroll
-      for (int i = 0; i < kHalves; ++i) {
-        if (i >= ib && i <= ie)
-          step(t * kHalves + i, cur + kKTile * kHeadDim + i * 32 * kHeadDim,
-               cur + ((i + 1) % kHalves) * 32 * kHeadDim);
+  for (int c = 0; c < kCols; ++c) set_ref(c);
+
+  // One pipelined step hh with parity `par` (= hh & 1); its tile sits in
+  // buffer `buf`, the next tile in `buf_next`.
+  auto step = [&](int hh, auto par_c, int buf, int buf_next) {
+    constexpr int par = decltype(par_c)::value;
+    f32x16_t (&s_cur)[kCols] = s_buf[par];
+    f32x16_t (&s_next)[kCols] = s_buf[par ^ 1];
+    bf16x8_t (&p_cur)[kCols][2] = p_buf;
+    if (need_mask(hh)) {
+#pragma unroll
+      for (int c = 0; c < kCols; ++c) mask(hh, s_cur[c]);
+    }
+    // Matrix core: S of step hh + 1 and O^T of step hh - 1.
+    s_chains(s_next);
+    pv_chains(p_buf);
+    // VALU: P of step hh against the current reference (fast path).
+    float tsum[kCols];
+    bool slow[kCols];
+    bool any_slow = false;
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) {
+      tsum[c] = probs(s_cur[c], p_cur[c], -m_neg[c], scale_log2);
+      slow[c] = !(tsum[c] <= sum_lim[c]);
+      any_slow |= slow[c];
+    }
+    // Slow path (rare): a row without reference yet, or keys far above it.
+    // Move the reference to the row max (uniformly over the lane pair),
+    // rescale the state (O^T of step hh - 1 included), redo P.
+    if (wave_any(any_slow)) {
+#pragma unroll
+      for (int c = 0; c < kCols; ++c) {
+        float mx = s_cur[c][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_cur[c][r]);
+        mx = pair_max(mx) * scale_log2;
+        const bool move = pair_max(slow[c] ? 1.0f : 0.0f) > 0.0f && mx > m2[c];
+        const float m_new = move ? mx : m2[c];
+        const float alpha = move ? fast_exp2(m2[c] - m_new) : 1.0f;
+        m2[c] = m_new;
+        set_ref(c);
+        lsum[c] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[c][db][r] *= alpha;
+        tsum[c] = probs(s_cur[c], p_cur[c], -m_neg[c], scale_log2);
       }
     }
-    if (t < t_end) {
-      wait_vmem();
-      __syncthreads();
-      if (t + 2 <= t_end)
-        issue_tile<kThreads>(k, v, cur, cur + kKTile * kHeadDim, seq0, len, hkv, g, (t + 2) * kKTile, wave,
-                             lane);
-      if (wave_active) read_k(nxt);
-    }
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) lsum[c] += tsum[c];
+    // Operands for the next step: V^T of this step, K of step hh + 2 (same
+    // half of the next tile).  Past the last step these reads return unused
+    // data from resident buffers.  They stay behind this step's MFMAs (no
+    // second set of operand registers); their latency is covered by the next
+    // step's softmax.
+    __builtin_amdgcn_sched_barrier(0);
+    read_v(v_rows(buf, hh));
+    read_k(k_rows(buf_next, hh));
   };
 
-  if (t_begin < t_end)
-    issue_tile<kThreads>(k, v, kv_lds1, kv_lds1 + kKTile * kHeadDim, seq0, len, hkv, g, (t_begin + 1) * kKTile,
-                         wave, lane);
-  if (wave_active) read_k(kv_lds0 + (h_begin - t_begin * kHalves) * 32 * kHeadDim);
-  for (int t = t_begin; t <= t_end; t += 2) {
-    run_tile(t, kv_lds0, kv_lds1);
-    if (t + 1 <= t_end) run_tile(t + 1, kv_lds1, kv_lds0);
+  // Wait for the first tiles (all copies issued so far), publish them.
+  wait_vmem_keep<0>();
+  lds_barrier();
+
+  if (wave_active) {
+    // Prologue: S of step h_begin, K of step h_begin + 1, empty P of step
+    // h_begin - 1 and zero V^T (the first step's O^T update adds nothing).
+    read_k(kv_lds[0] + (h_begin & 1) * 32 * kHeadDim);
+    const bool odd = h_begin & 1;
+    if (odd) s_chains(s_buf[1]); else s_chains(s_buf[0]);
+    const int h1 = h_begin + 1;
+    read_k(kv_lds[((h1 >> 1) - t_begin) & (kBufs - 1)] + (h1 & 1) * 32 * kHeadDim);
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) p_buf[c][u] = __builtin_bit_cast(bf16x8_t, zero_u32x4());
+    }
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      vop[db][0] = __builtin_bit_cast(bf16x8_t, zero_u32x4());
+      vop[db][1] = __builtin_bit_cast(bf16x8_t, zero_u32x4());
+    }
+  }
+
+  for (int t0 = t_begin; t0 <= t_end; t0 += kBufs) {
+#pragma unroll
+    for (int j = 0; j < 2 * kBufs; ++j) {
+      const int bi = j >> 1;  // buffer of tile t (static after unrolling)
+      const int t = t0 + bi;
+      const int hh = 2 * t + (j & 1);
+      // Tile boundary: tile t + 1 (read from step 2t on) must have landed
+      // for every wave; tile t - 1's buffer is then free for tile t + 3.
+      if ((j & 1) == 0 && t > t_begin && t <= t_end) {
+        if (t + 2 >= t_begin + kBufs && t + 2 <= t_end)
+          wait_vmem_keep<kCopies>();  // tile t + 2 may still be in flight
+        else
+          wait_vmem_keep<0>();
+        lds_barrier();
+        if (t + 3 <= t_end) issue(t + 3, (bi + 3) & (kBufs - 1));
+      }
+      if (wave_active && hh >= h_begin && hh <= h_end) {
+        if ((j & 1) == 0)
+          step(hh, Parity<0>{}, bi, (bi + 1) & (kBufs - 1));
+        else
+          step(hh, Parity<1>{}, bi, (bi + 1) & (kBufs - 1));
+      }
+    }
   }
 
   if (!wave_active) return;
+  // Epilogue: O^T of the last step.
+  pv_chains(p_buf);
 
-  // Epilogue: full denominator over the lane pair, normalise, store bf16.
+  // Full denominator over the lane pair, normalise, store bf16.
 #pragma unroll
   for (int c = 0; c < kCols; ++c) {
     const float den = pair_sum(lsum[c]);

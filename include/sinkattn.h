@@ -83,6 +83,10 @@ typedef enum sinkattn_status {
  *   lse         fp32 [total_tokens, num_q_heads], natural log, sink
  *               included; NULL to skip.  A row with no key and no sink gets
  *               o = 0 and lse = -inf.
+ *
+ * Additionally required: max_seqlen * num_kv_heads * head_dim * 2 < 2^31
+ * (one sequence's K/V rows are addressed with 32-bit byte offsets; larger
+ * return SINKATTN_ERR_UNSUPPORTED).
  */
 SINKATTN_API sinkattn_status sinkattn_prefill_varlen(
     const void* q, const void* k, const void* v,

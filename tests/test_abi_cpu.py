@@ -72,6 +72,8 @@ def _prefill(lib, **kw):
     (dict(o=ctypes.c_void_p((1 << 20) + 2)), 1),
     (dict(max_seqlen=32, total=16), 1),
     (dict(max_seqlen=40_000_000, total=40_000_000), 2),
+    # one sequence's K/V rows past 2^31 bytes (32-bit row offsets)
+    (dict(max_seqlen=1 << 20, total=1 << 20, hq=128, hkv=128), 2),
 ])
 def test_prefill_rejects(kw, status):
     lib = _lib()

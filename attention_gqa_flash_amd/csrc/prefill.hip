@@ -429,13 +429,17 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
   // Epilogue: O^T of the last step.
   pv_chains(p_buf);
 
-  // Full denominator over the lane pair, normalise, store bf16.
+  // Full denominator over the lane pair, normalise, store bf16.  The token
+  // index is recomputed here (opaque to common-subexpression elimination) so
+  // the Q addresses are not kept alive across the loop.
+  int tok = seq0 + qtok;
+  asm volatile("" : "+v"(tok));
 #pragma unroll
   for (int c = 0; c < kCols; ++c) {
     const float den = pair_sum(lsum[c]);
     if (!head_ok[c] || !row_ok) continue;
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    const size_t orow = (static_cast<size_t>(seq0 + qtok) * hq + head[c]) * kHeadDim;
+    const size_t orow = (static_cast<size_t>(tok) * hq + head[c]) * kHeadDim;
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
 #pragma unroll
@@ -449,7 +453,7 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
     }
     if (lse != nullptr && half == 0) {
       const float l = den > 0.0f ? (m2[c] + __log2f(den)) * kLn2 : kNegInf;
-      lse[static_cast<size_t>(seq0 + qtok) * hq + head[c]] = l;
+      lse[static_cast<size_t>(tok) * hq + head[c]] = l;
     }
   }
 }

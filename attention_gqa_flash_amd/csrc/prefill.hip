@@ -105,6 +105,7 @@ __device__ __forceinline__ float probs(const f32x16_t& sacc, bf16x8_t (&pb)[2], 
   return l[0] + l[1];
 }
 
+// Compile-time integer (step parity, buffer index) passed to generic lambdas.
 template <int N>
 struct Parity {
   static constexpr int value = N;
@@ -319,8 +320,10 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
 
   // One pipelined step hh with parity `par` (= hh & 1); its tile sits in
   // buffer `buf`, the next tile in `buf_next`.
-  auto step = [&](int hh, auto par_c, int buf, int buf_next) {
+  auto step = [&](int hh, auto par_c, auto buf_c) __attribute__((always_inline)) {
     constexpr int par = decltype(par_c)::value;
+    constexpr int buf = decltype(buf_c)::value;
+    constexpr int buf_next = (buf + 1) & (kBufs - 1);
     f32x16_t (&s_cur)[kCols] = s_buf[par];
     f32x16_t (&s_next)[kCols] = s_buf[par ^ 1];
     bf16x8_t (&p_cur)[kCols][2] = p_buf;
@@ -400,29 +403,31 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
     }
   }
 
-  for (int t0 = t_begin; t0 <= t_end; t0 += kBufs) {
-#pragma unroll
-    for (int j = 0; j < 2 * kBufs; ++j) {
-      const int bi = j >> 1;  // buffer of tile t (static after unrolling)
-      const int t = t0 + bi;
-      const int hh = 2 * t + (j & 1);
-      // Tile boundary: tile t + 1 (read from step 2t on) must have landed
-      // for every wave; tile t - 1's buffer is then free for tile t + 3.
-      if ((j & 1) == 0 && t > t_begin && t <= t_end) {
-        if (t + 2 >= t_begin + kBufs && t + 2 <= t_end)
-          wait_vmem_keep<kCopies>();  // tile t + 2 may still be in flight
-        else
-          wait_vmem_keep<0>();
-        lds_barrier();
-        if (t + 3 <= t_end) issue(t + 3, (bi + 3) & (kBufs - 1));
-      }
-      if (wave_active && hh >= h_begin && hh <= h_end) {
-        if ((j & 1) == 0)
-          step(hh, Parity<0>{}, bi, (bi + 1) & (kBufs - 1));
-        else
-          step(hh, Parity<1>{}, bi, (bi + 1) & (kBufs - 1));
-      }
+  // Tile t (buffer bi, a compile-time constant) and its two steps.
+  auto tile = [&](int t0, auto bi_c) __attribute__((always_inline)) {
+    constexpr int bi = decltype(bi_c)::value;
+    const int t = t0 + bi;
+    if (t > t_end) return;
+    // Tile boundary: tile t + 1 (read from step 2t on) must have landed for
+    // every wave; tile t - 1's buffer is then free for tile t + 3.
+    if (t > t_begin) {
+      if (t + 2 >= t_begin + kBufs && t + 2 <= t_end)
+        wait_vmem_keep<kCopies>();  // tile t + 2 may still be in flight
+      else
+        wait_vmem_keep<0>();
+      lds_barrier();
+      if (t + 3 <= t_end) issue(t + 3, (bi + 3) & (kBufs - 1));
     }
+    if (!wave_active) return;
+    if (2 * t >= h_begin && 2 * t <= h_end) step(2 * t, Parity<0>{}, Parity<bi>{});
+    if (2 * t + 1 >= h_begin && 2 * t + 1 <= h_end) step(2 * t + 1, Parity<1>{}, Parity<bi>{});
+  };
+
+  for (int t0 = t_begin; t0 <= t_end; t0 += kBufs) {
+    tile(t0, Parity<0>{});
+    tile(t0, Parity<1>{});
+    tile(t0, Parity<2>{});
+    tile(t0, Parity<3>{});
   }
 
   if (!wave_active) return;
@@ -430,10 +435,10 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
   pv_chains(p_buf);
 
   // Full denominator over the lane pair, normalise, store bf16.  The token
-  // index is recomputed here (opaque to common-subexpression elimination) so
-  // the Q addresses are not kept alive across the loop.
-  int tok = seq0 + qtok;
-  asm volatile("" : "+v"(tok));
+  // index is recomputed here from the lane id (mbcnt) so that no address or
+  // index from the prologue stays alive across the loop.
+  const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int tok = seq0 + q0 + (lane_e & 31);
 #pragma unroll
   for (int c = 0; c < kCols; ++c) {
     const float den = pair_sum(lsum[c]);

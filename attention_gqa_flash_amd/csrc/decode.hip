@@ -57,15 +57,16 @@ __device__ __forceinline__ void load_tile(TileRegs& t, const uint16_t* __restric
 }
 
 template <int kDecWaves>
-__global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(
+__device__ __forceinline__ void decode_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ sinks,
     const int32_t* __restrict__ cu_seqlens_k, int batch, int hq, int hkv, int group,
     int window, float scale_log2, int num_splits, uint16_t* __restrict__ o,
     float* __restrict__ lse, float* __restrict__ o_part, float* __restrict__ lse_part) {
   // Wave-private K and V staging tiles (2 x 4 KiB per wave); the whole
-  // buffer is reused for the cross-wave merge of up to 32 heads x 64 d.
-  __shared__ __attribute__((aligned(16))) float lds_buf[(kDecWaves < 4 ? 4 : kDecWaves) * 32 * kHeadDim];
+  // buffer is reused for the cross-wave merge of up to 32 heads x 64 d per
+  // wave (index (wave * group + head) * 64 + d).
+  __shared__ __attribute__((aligned(16))) float lds_buf[kDecWaves * 32 * kHeadDim];
   __shared__ float red_m[kDecWaves][32];
   __shared__ float red_l[kDecWaves][32];
 
@@ -244,6 +245,29 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(
 // per batch with the same rescaling as the online softmax.
 constexpr int kMergeBatch = 8;
 
+// Short splits (at most kShortChunk keys): two-wave workgroups at three
+// waves per SIMD, i.e. more workgroups and so more loads in flight.
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3, 3))) void decode_kernel_w2(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ sinks, const int32_t* __restrict__ cu_seqlens_k, int batch, int hq, int hkv,
+    int group, int window, float scale_log2, int num_splits, uint16_t* __restrict__ o, float* __restrict__ lse,
+    float* __restrict__ o_part, float* __restrict__ lse_part) {
+  decode_body<2>(q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, group, window, scale_log2, num_splits, o, lse,
+                 o_part, lse_part);
+}
+
+// Long splits: four-wave workgroups at the compiler's own register budget
+// (two waves per SIMD; at three, S = 4 on 64 x 8192 would end on a
+// two-thirds-full round of workgroups).
+__global__ __launch_bounds__(256) void decode_kernel_w4(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ sinks, const int32_t* __restrict__ cu_seqlens_k, int batch, int hq, int hkv,
+    int group, int window, float scale_log2, int num_splits, uint16_t* __restrict__ o, float* __restrict__ lse,
+    float* __restrict__ o_part, float* __restrict__ lse_part) {
+  decode_body<4>(q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, group, window, scale_log2, num_splits, o, lse,
+                 o_part, lse_part);
+}
+
 __global__ __launch_bounds__(kThreads) void merge_kernel(
     const float* __restrict__ o_parts, const float* __restrict__ lse_parts, int num_parts,
     int rows, uint16_t* __restrict__ o, float* __restrict__ lse) {
@@ -291,7 +315,7 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   const unsigned blocks = static_cast<unsigned>(a.batch) * a.num_kv_heads * a.num_splits;
   const long long keys_per_split = (static_cast<long long>(a.max_seqlen_k) + a.num_splits - 1) / a.num_splits;
   const bool short_chunks = keys_per_split <= kShortChunk;
-  auto kernel = short_chunks ? decode_kernel<2> : decode_kernel<4>;
+  auto kernel = short_chunks ? decode_kernel_w2 : decode_kernel_w4;
   hipLaunchKernelGGL(kernel, dim3(blocks), dim3(short_chunks ? 128 : 256), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.sinks, a.cu_seqlens_k, a.batch,

@@ -337,17 +337,17 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
     // VALU: P of step hh against the current reference (fast path).
     float tsum[kCols];
     bool slow[kCols];
-    bool any_slow = false;
+    uint64_t slow_lanes = 0;  // ballot of each compare: no boolean materialised
 #pragma unroll
     for (int c = 0; c < kCols; ++c) {
       tsum[c] = probs(s_cur[c], p_cur[c], -m_neg[c], scale_log2);
       slow[c] = !(tsum[c] <= sum_lim[c]);
-      any_slow |= slow[c];
+      slow_lanes |= __builtin_amdgcn_ballot_w64(slow[c]);
     }
     // Slow path (rare): a row without reference yet, or keys far above it.
     // Move the reference to the row max (uniformly over the lane pair),
     // rescale the state (O^T of step hh - 1 included), redo P.
-    if (wave_any(any_slow)) {
+    if (slow_lanes != 0) {
 #pragma unroll
       for (int c = 0; c < kCols; ++c) {
         float mx = s_cur[c][0];

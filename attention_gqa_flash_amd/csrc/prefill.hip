@@ -331,9 +331,15 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
 #pragma unroll
       for (int c = 0; c < kCols; ++c) mask(hh, s_cur[c]);
     }
-    // Matrix core: S of step hh + 1 and O^T of step hh - 1.
+    // Matrix core: S of step hh + 1 and O^T of step hh - 1.  The operands of
+    // the next step are read as soon as these MFMAs have taken the current
+    // ones (same registers): K of step hh + 2 (same half of the next tile)
+    // and V^T of this step.  Past the last step these reads return unused
+    // data from resident buffers.  The softmax below covers their latency.
     s_chains(s_next);
+    read_k(k_rows(buf_next, hh));
     pv_chains(p_buf);
+    read_v(v_rows(buf, hh));
     // VALU: P of step hh against the current reference (fast path).
     float tsum[kCols];
     bool slow[kCols];
@@ -369,14 +375,6 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
     }
 #pragma unroll
     for (int c = 0; c < kCols; ++c) lsum[c] += tsum[c];
-    // Operands for the next step: V^T of this step, K of step hh + 2 (same
-    // half of the next tile).  Past the last step these reads return unused
-    // data from resident buffers.  They stay behind this step's MFMAs (no
-    // second set of operand registers); their latency is covered by the next
-    // step's softmax.
-    __builtin_amdgcn_sched_barrier(0);
-    read_v(v_rows(buf, hh));
-    read_k(k_rows(buf_next, hh));
   };
 
   // Wait for the first tiles (all copies issued so far), publish them.

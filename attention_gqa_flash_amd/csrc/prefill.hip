@@ -140,9 +140,10 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
 
   constexpr int kThreads = threads_for<kCols>();
   constexpr int kCopies = copies_per_tile<kThreads>();
+  constexpr int kRowsPerWave = kQTile / (kThreads / 64);  // Q / O block rows moved per wave
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: head maths in SGPRs
   const int col = lane & 31;   // query token within the tile
   const int half = lane >> 5;  // which k-half / row-half of the MFMA layouts
 
@@ -172,18 +173,32 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
   const size_t kv0 = (static_cast<size_t>(seq0) * hkv + g) * kHeadDim;
   const uint16_t* k_seq = k + kv0;
   const uint16_t* v_seq = v + kv0;
-  // LDS byte address of the ring and the wave index, both uniform.
+  // LDS byte address of the ring (uniform).
   const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_address(&kv_lds[0][0]));
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   auto issue = [&](int tt, int buf) {
     const uint32_t dst = ring + static_cast<uint32_t>(buf) * (2 * kKTile * kHeadDim * 2);
     issue_tile<kThreads>(k_seq, v_seq, dst, dst + kKTile * kHeadDim * 2, len, hkv * kHeadDim, tt * kKTile,
-                         wave_u, lane);
+                         wave, lane);
   };
-  // The first kBufs tiles go out before anything else.
+  // The first two tiles go out before anything else, then the workgroup's
+  // Q block (32 tokens x 8 head slots x 128 B, 1 KB contiguous per token)
+  // into buffers 2 and 3, which receive their tiles once Q is in registers.
+  if (t_begin <= t_end) issue(t_begin, 0);
+  if (t_begin + 1 <= t_end) issue(t_begin + 1, 1);
+  uint16_t* const q_lds = &kv_lds[2][0];
+  {
+    const uint32_t q_dst = ring + 2 * (2 * kKTile * kHeadDim * 2);
+    const int slot = lane >> 3;
+    const int head_q = g * group + min(hchunk * kHeadsPerBlock + slot, group - 1);
 #pragma unroll
-  for (int i = 0; i < kBufs; ++i)
-    if (t_begin + i <= t_end) issue(t_begin + i, i);
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int r = kRowsPerWave * wave + i;  // token row of the block
+      const int chunk = (lane & 7) ^ (r & 7);
+      const int tok = min(q0 + r, len - 1);
+      const uint16_t* src = q + (static_cast<size_t>(seq0 + tok) * hq + head_q) * kHeadDim + chunk * 8;
+      load16_to_lds_untracked(src, q_dst + static_cast<uint32_t>(r) * (kHeadsPerBlock * kHeadDim * 2));
+    }
+  }
 
   // Query heads of this wave (kCols column blocks of 32).
   int head[kCols];
@@ -196,22 +211,10 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
   }
   const bool wave_active = head_ok[0];
   const int qtok = q0 + col;
-  const bool row_ok = qtok < len;
 
-  // Q^T as the B operand: lane holds query column `col`, d = 16 s + 8 half + t.
+  // Q^T as the B operand (lane holds query column `col`, d = 16 s + 8 half
+  // + t), read from the Q block in LDS once it has landed.
   bf16x8_t qreg[kCols][4];
-#pragma unroll
-  for (int c = 0; c < kCols; ++c) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4_t val = zero_u32x4();
-      if (head_ok[c] && row_ok) {
-        const size_t off = (static_cast<size_t>(seq0 + qtok) * hq + head[c]) * kHeadDim + 16 * s + 8 * half;
-        val = load16(q + off);
-      }
-      qreg[c][s] = __builtin_bit_cast(bf16x8_t, val);
-    }
-  }
 
   // Online-softmax state per column block.  The reference max m is kept in
   // log2 units (scaled logits); the sink seeds it, and its "1" is counted once
@@ -377,9 +380,22 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
     for (int c = 0; c < kCols; ++c) lsum[c] += tsum[c];
   };
 
-  // Wait for the first tiles (all copies issued so far), publish them.
+  // Wait for the first tiles and the Q block (all copies issued so far),
+  // publish them, take Q into registers, then hand buffers 2 and 3 to their
+  // tiles.
   wait_vmem_keep<0>();
   lds_barrier();
+#pragma unroll
+  for (int c = 0; c < kCols; ++c) {
+    const int slot = wave * kCols + c;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      qreg[c][s] = *reinterpret_cast<const bf16x8_t*>(q_lds + col * (kHeadsPerBlock * kHeadDim) + slot * kHeadDim +
+                                                     (((2 * s + half) ^ (col & 7)) << 3));
+  }
+  lds_barrier();
+  if (t_begin + 2 <= t_end) issue(t_begin + 2, 2);
+  if (t_begin + 3 <= t_end) issue(t_begin + 3, 3);
 
   if (wave_active) {
     // Prologue: S of step h_begin, K of step h_begin + 1, empty P of step
@@ -428,35 +444,60 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
     tile(t0, Parity<3>{});
   }
 
-  if (!wave_active) return;
-  // Epilogue: O^T of the last step.
-  pv_chains(p_buf);
-
-  // Full denominator over the lane pair, normalise, store bf16.  The token
-  // index is recomputed here from the lane id (mbcnt) so that no address or
-  // index from the prologue stays alive across the loop.
-  const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-  const int tok = seq0 + q0 + (lane_e & 31);
+  // Epilogue.  Every K/V read is done once all waves pass this barrier;
+  // buffers 0 and 1 then stage the O block (same layout as the Q block) so
+  // that it is stored as whole 1 KB token rows.
+  lds_barrier();
+  uint16_t* const o_lds = &kv_lds[0][0];
+  if (wave_active) {
+    pv_chains(p_buf);  // O^T of the last step
+    const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int colr = lane_e & 31;  // recomputed: nothing from the prologue stays alive
 #pragma unroll
-  for (int c = 0; c < kCols; ++c) {
-    const float den = pair_sum(lsum[c]);
-    if (!head_ok[c] || !row_ok) continue;
-    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    const size_t orow = (static_cast<size_t>(tok) * hq + head[c]) * kHeadDim;
+    for (int c = 0; c < kCols; ++c) {
+      // Full denominator over the lane pair, normalise, bf16 into LDS.
+      const float den = pair_sum(lsum[c]);
+      const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+      const int slot = wave * kCols + c;
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
+      for (int db = 0; db < 2; ++db) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u16x4_t w;
+        for (int j = 0; j < 4; ++j) {
+          u16x4_t w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = to_bf16_bits(acc[c][db][4 * j + i] * inv);
-        const int d = 32 * db + 8 * j + 4 * half;
-        *reinterpret_cast<u16x4_t*>(o + orow + d) = w;
+          for (int i = 0; i < 4; ++i) w[i] = to_bf16_bits(acc[c][db][4 * j + i] * inv);
+          // d = 32 db + 8 j + 4 half: chunk 4 db + j, bytes 8 half of it.
+          *reinterpret_cast<u16x4_t*>(o_lds + colr * (kHeadsPerBlock * kHeadDim) + slot * kHeadDim +
+                                      (((4 * db + j) ^ (colr & 7)) << 3) + 4 * half) = w;
+        }
+      }
+      if (lse != nullptr && half == 0 && head_ok[c] && q0 + colr < len) {
+        const float l = den > 0.0f ? (m2[c] + __log2f(den)) * kLn2 : kNegInf;
+        lse[static_cast<size_t>(seq0 + q0 + colr) * hq + head[c]] = l;
       }
     }
-    if (lse != nullptr && half == 0) {
-      const float l = den > 0.0f ? (m2[c] + __log2f(den)) * kLn2 : kNegInf;
-      lse[static_cast<size_t>(tok) * hq + head[c]] = l;
+  }
+  lds_barrier();
+  // Whole rows: wave w stores tokens 8 w .. 8 w + 7, lane L the 16 B chunk
+  // (L & 7) of head slot L >> 3 (un-swizzled on the way out).
+  {
+    // Lane id recomputed here so no address of this loop is built before the
+    // main loop and carried across it.
+    const int lane_s = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int slot = lane_s >> 3;
+    const bool slot_ok = hchunk * kHeadsPerBlock + slot < group;
+    const int head_o = g * group + hchunk * kHeadsPerBlock + slot;
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int r = kRowsPerWave * wave + i;
+      const int pos = lane_s & 7;
+      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(o_lds + r * (kHeadsPerBlock * kHeadDim) +
+                                                           slot * kHeadDim + pos * 8);
+      if (slot_ok && q0 + r < len) {
+        const int chunk = pos ^ (r & 7);
+        *reinterpret_cast<u32x4_t*>(o + (static_cast<size_t>(seq0 + q0 + r) * hq + head_o) * kHeadDim +
+                                    chunk * 8) = val;
+      }
     }
   }
 }

@@ -38,7 +38,7 @@ def test_tiny_prefill_config():
 
 
 @pytest.mark.parametrize("window", [0, 1, 5, 31, 32, 64, 127, 128, 129, 1000])
-@pytest.mark.parametrize("hq,hkv", [(8, 2), (16, 2), (24, 2), (64, 8)])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (16, 2), (24, 2), (64, 8), (8, 8), (32, 1)])
 def test_varlen_prefill_small(window, hq, hkv):
     lengths = [1, 31, 32, 33, 64, 65, 127, 200, 517]
     if hq == 64:

@@ -31,6 +31,11 @@ constexpr int kKeys = 32;  // keys per wave iteration
 // chunk holds at most kShortChunk keys (fewer waves to merge per workgroup,
 // twice the workgroups resident per CU).
 constexpr int kShortChunk = 1024;
+// With at least kSplitPerWaveMin splits of more than kShortChunk keys, each
+// wave of a four-wave workgroup owns a split (64 x 8192 at S = 4: 6.0 TB/s
+// against 5.5 with the waves interleaved; at S = 16, 512-key splits, the
+// two-wave interleaved kernel is 12% faster).
+constexpr int kSplitPerWaveMin = 4;
 
 // One 32-key tile of one wave, in registers, K and V rows in coalesced
 // order: lane l holds the 16-byte chunk l % 8 of rows l / 8 + 8 i.  Keys at or
@@ -56,7 +61,10 @@ __device__ __forceinline__ void load_tile(TileRegs& t, const uint16_t* __restric
   }
 }
 
-template <int kDecWaves>
+// kSplitPerWave: each wave owns one whole split (split = 4 * group of
+// splits + wave) and writes that split's partial itself; otherwise the waves
+// of the workgroup interleave over one split and merge through LDS.
+template <int kDecWaves, bool kSplitPerWave>
 __device__ __forceinline__ void decode_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ sinks,
@@ -77,8 +85,15 @@ __device__ __forceinline__ void decode_body(
   const int half = lane >> 5;
 
   int x = blockIdx.x;
-  const int split = x % num_splits;
-  x /= num_splits;
+  int split;
+  if (kSplitPerWave) {
+    const int n_sgroups = (num_splits + kDecWaves - 1) / kDecWaves;
+    split = (x % n_sgroups) * kDecWaves + wave;
+    x /= n_sgroups;
+  } else {
+    split = x % num_splits;
+    x /= num_splits;
+  }
   const int g = x % hkv;
   const int b = x / hkv;
 
@@ -87,8 +102,9 @@ __device__ __forceinline__ void decode_body(
   const int lo = window > 0 ? max(0, len - window) : 0;
   const int n = len - lo;
   const int chunk = n > 0 ? (n + num_splits - 1) / num_splits : 0;
-  const int a = min(len, lo + split * chunk);
-  const int e = min(len, lo + (split + 1) * chunk);
+  // (a wave past the last split gets an empty range and writes nothing)
+  const int a = split < num_splits ? min(len, lo + split * chunk) : len;
+  const int e = split < num_splits ? min(len, lo + (split + 1) * chunk) : len;
 
   const bool col_ok = col < group;
   const int head = g * group + (col_ok ? col : 0);
@@ -101,9 +117,9 @@ __device__ __forceinline__ void decode_body(
     qreg[s] = __builtin_bit_cast(bf16x8_t, val);
   }
 
-  // The sink seeds wave 0 of split 0 only.
+  // The sink seeds split 0 only (its wave 0 when the waves share a split).
   float m2 = kNegInf, lsum = 0.0f;
-  if (split == 0 && wave == 0 && sinks != nullptr && col_ok) {
+  if (split == 0 && (kSplitPerWave || wave == 0) && sinks != nullptr && col_ok) {
     const float z = sinks[head];
     if (z > kNegInf) {
       m2 = z * kLog2e;
@@ -121,11 +137,12 @@ __device__ __forceinline__ void decode_body(
   // Register double buffering: the loads of the next tile of this wave are in
   // flight while the current one is computed.
   TileRegs cur, nxt;
-  int k0 = a + kKeys * wave;
+  constexpr int kStride = kSplitPerWave ? kKeys : kKeys * kDecWaves;
+  int k0 = kSplitPerWave ? a : a + kKeys * wave;
   if (k0 < e) load_tile(cur, k, v, base, hkv, g, k0, e, lane);
 
-  for (; k0 < e; k0 += kKeys * kDecWaves) {
-    const int k1 = k0 + kKeys * kDecWaves;
+  for (; k0 < e; k0 += kStride) {
+    const int k1 = k0 + kStride;
     if (k1 < e) load_tile(nxt, k, v, base, hkv, g, k1, e, lane);
 
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // previous tile's LDS reads are done
@@ -190,8 +207,24 @@ __device__ __forceinline__ void decode_body(
     cur = nxt;
   }
 
-  // Cross-wave merge.  Each wave publishes (m, l, unnormalised O) per head.
   const float den = pair_sum(lsum);
+  if (kSplitPerWave) {
+    // This wave's split alone: normalise and write its partial.
+    if (split >= num_splits || !col_ok) return;
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    const size_t prow = (static_cast<size_t>(split) * batch + b) * hq + head;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = 32 * db + 8 * (r >> 2) + 4 * half + (r & 3);
+        o_part[prow * kHeadDim + d] = acc[db][r] * inv;
+      }
+    if (half == 0) lse_part[prow] = den > 0.0f ? (m2 + __log2f(den)) * kLn2 : kNegInf;
+    return;
+  }
+
+  // Cross-wave merge.  Each wave publishes (m, l, unnormalised O) per head.
   __syncthreads();  // all waves are done with their V tiles
   float* red_o = lds_buf;  // [wave][group][64 d]
   if (half == 0) {
@@ -252,8 +285,19 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const float* __restrict__ sinks, const int32_t* __restrict__ cu_seqlens_k, int batch, int hq, int hkv,
     int group, int window, float scale_log2, int num_splits, uint16_t* __restrict__ o, float* __restrict__ lse,
     float* __restrict__ o_part, float* __restrict__ lse_part) {
-  decode_body<2>(q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, group, window, scale_log2, num_splits, o, lse,
+  decode_body<2, false>(q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, group, window, scale_log2, num_splits, o, lse,
                  o_part, lse_part);
+}
+
+// Four or more long splits: four-wave workgroups, one split per wave (each
+// wave writes its split's partial; no cross-wave merge).
+__global__ __launch_bounds__(256) void decode_kernel_ps(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ sinks, const int32_t* __restrict__ cu_seqlens_k, int batch, int hq, int hkv,
+    int group, int window, float scale_log2, int num_splits, uint16_t* __restrict__ o, float* __restrict__ lse,
+    float* __restrict__ o_part, float* __restrict__ lse_part) {
+  decode_body<4, true>(q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, group, window, scale_log2, num_splits, o,
+                       lse, o_part, lse_part);
 }
 
 // Long splits: four-wave workgroups at the compiler's own register budget
@@ -264,7 +308,7 @@ __global__ __launch_bounds__(256) void decode_kernel_w4(
     const float* __restrict__ sinks, const int32_t* __restrict__ cu_seqlens_k, int batch, int hq, int hkv,
     int group, int window, float scale_log2, int num_splits, uint16_t* __restrict__ o, float* __restrict__ lse,
     float* __restrict__ o_part, float* __restrict__ lse_part) {
-  decode_body<4>(q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, group, window, scale_log2, num_splits, o, lse,
+  decode_body<4, false>(q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, group, window, scale_log2, num_splits, o, lse,
                  o_part, lse_part);
 }
 
@@ -315,8 +359,11 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   const unsigned blocks = static_cast<unsigned>(a.batch) * a.num_kv_heads * a.num_splits;
   const long long keys_per_split = (static_cast<long long>(a.max_seqlen_k) + a.num_splits - 1) / a.num_splits;
   const bool short_chunks = keys_per_split <= kShortChunk;
-  auto kernel = short_chunks ? decode_kernel_w2 : decode_kernel_w4;
-  hipLaunchKernelGGL(kernel, dim3(blocks), dim3(short_chunks ? 128 : 256), 0, stream,
+  const bool per_wave = a.num_splits >= kSplitPerWaveMin && !short_chunks;
+  auto kernel = per_wave ? decode_kernel_ps : short_chunks ? decode_kernel_w2 : decode_kernel_w4;
+  const unsigned grid = per_wave ? static_cast<unsigned>(a.batch) * a.num_kv_heads * ((a.num_splits + 3) / 4)
+                                 : blocks;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(per_wave || !short_chunks ? 256 : 128), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.sinks, a.cu_seqlens_k, a.batch,
                      a.num_q_heads, a.num_kv_heads, group, a.window, a.softmax_scale * kLog2e,

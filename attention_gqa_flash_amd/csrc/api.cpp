@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 
 #include "launch.hpp"
@@ -53,6 +54,50 @@ sinkattn_status hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// Debug mode: SINKATTN_DEBUG_CHECKS=1 in the environment (read on every
+// call) runs the device-side precondition checks before a launch.
+bool debug_checks() {
+  const char* v = std::getenv("SINKATTN_DEBUG_CHECKS");
+  return v != nullptr && v[0] == '1' && v[1] == '\0';
+}
+
+sinkattn_status check_failed(unsigned flags) {
+  static const struct {
+    unsigned bit;
+    const char* what;
+  } kNames[] = {
+      {sinkattn::kCheckOffsetsStart, "cu_seqlens[0] != 0"},
+      {sinkattn::kCheckOffsetsOrder, "cu_seqlens is not non-decreasing"},
+      {sinkattn::kCheckLengthMax, "a sequence is longer than the declared maximum"},
+      {sinkattn::kCheckLengthMin, "a decode sequence is empty (needs L_b >= 1)"},
+      {sinkattn::kCheckOffsetsTotal, "cu_seqlens[batch] exceeds total_tokens"},
+      {sinkattn::kCheckSinks, "a sink is NaN or +inf"},
+      {sinkattn::kCheckQ, "q holds NaN or Inf"},
+      {sinkattn::kCheckK, "k holds NaN or Inf"},
+      {sinkattn::kCheckV, "v holds NaN or Inf"},
+      {sinkattn::kCheckParts, "o_parts holds NaN or Inf, or lse_parts NaN or +inf"},
+  };
+  std::string msg = "debug checks failed:";
+  for (const auto& n : kNames)
+    if (flags & n.bit) (msg += " ") += n.what, msg += ";";
+  g_last_error = msg;
+  return SINKATTN_ERR_INVALID_ARG;
+}
+
+// Runs the queued checks and turns their flags into a status.
+sinkattn_status check_result(hipStream_t stream, int* total) {
+  unsigned flags = 0;
+  int t = 0;
+  const hipError_t e = sinkattn::check_read(&flags, &t, stream);
+  if (e != hipSuccess) return fail(SINKATTN_ERR_HIP, "debug checks: %s", hipGetErrorString(e));
+  if (total != nullptr) *total = t;
+  return flags != 0u ? check_failed(flags) : SINKATTN_OK;
+}
+
+sinkattn_status hip_queue(hipError_t e) {
+  return e == hipSuccess ? SINKATTN_OK : fail(SINKATTN_ERR_HIP, "debug checks: %s", hipGetErrorString(e));
+}
+
 }  // namespace
 
 extern "C" {
@@ -87,6 +132,19 @@ sinkattn_status sinkattn_prefill_varlen(const void* q, const void* k, const void
   // K/V rows of one sequence are addressed with 32-bit byte offsets.
   if (static_cast<long long>(max_seqlen) * num_kv_heads * head_dim * 2 >= (1LL << 31))
     return fail(SINKATTN_ERR_UNSUPPORTED, "max_seqlen * num_kv_heads * head_dim * 2 must stay below 2^31");
+  if (debug_checks()) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t qn = static_cast<size_t>(total_tokens) * num_q_heads * head_dim;
+    const size_t kvn = static_cast<size_t>(total_tokens) * num_kv_heads * head_dim;
+    if ((st = hip_queue(sinkattn::check_clear(s))) != SINKATTN_OK) return st;
+    if ((st = hip_queue(sinkattn::check_offsets(cu_seqlens, batch, max_seqlen, 0, total_tokens, s))) != SINKATTN_OK)
+      return st;
+    if ((st = hip_queue(sinkattn::check_sinks(sinks, num_q_heads, s))) != SINKATTN_OK) return st;
+    if ((st = hip_queue(sinkattn::check_bf16(q, qn, sinkattn::kCheckQ, s))) != SINKATTN_OK) return st;
+    if ((st = hip_queue(sinkattn::check_bf16(k, kvn, sinkattn::kCheckK, s))) != SINKATTN_OK) return st;
+    if ((st = hip_queue(sinkattn::check_bf16(v, kvn, sinkattn::kCheckV, s))) != SINKATTN_OK) return st;
+    if ((st = check_result(s, nullptr)) != SINKATTN_OK) return st;
+  }
   sinkattn::PrefillLaunch a{q, k, v, sinks, cu_seqlens, batch, max_seqlen, num_q_heads, num_kv_heads,
                             window, softmax_scale, o, lse};
   return hip_status(sinkattn::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
@@ -122,6 +180,22 @@ sinkattn_status sinkattn_decode_splitkv(const void* q, const void* k_cache, cons
   const long long blocks = static_cast<long long>(batch) * num_kv_heads * num_splits;
   if (blocks > 0x7fffffffLL) return fail(SINKATTN_ERR_UNSUPPORTED, "too many (batch, head, split) work items");
 
+  if (debug_checks()) {
+    // Offsets first: they size the K/V scan.
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = hip_queue(sinkattn::check_clear(s))) != SINKATTN_OK) return st;
+    if ((st = hip_queue(sinkattn::check_offsets(cu_seqlens_k, batch, max_seqlen_k, 1, -1, s))) != SINKATTN_OK)
+      return st;
+    if ((st = hip_queue(sinkattn::check_sinks(sinks, num_q_heads, s))) != SINKATTN_OK) return st;
+    const size_t qn = static_cast<size_t>(batch) * num_q_heads * head_dim;
+    if ((st = hip_queue(sinkattn::check_bf16(q, qn, sinkattn::kCheckQ, s))) != SINKATTN_OK) return st;
+    int total_kv = 0;
+    if ((st = check_result(s, &total_kv)) != SINKATTN_OK) return st;
+    const size_t kvn = static_cast<size_t>(total_kv) * num_kv_heads * head_dim;
+    if ((st = hip_queue(sinkattn::check_bf16(k_cache, kvn, sinkattn::kCheckK, s))) != SINKATTN_OK) return st;
+    if ((st = hip_queue(sinkattn::check_bf16(v_cache, kvn, sinkattn::kCheckV, s))) != SINKATTN_OK) return st;
+    if ((st = check_result(s, nullptr)) != SINKATTN_OK) return st;
+  }
   sinkattn::DecodeLaunch a{q, k_cache, v_cache, sinks, cu_seqlens_k, batch, max_seqlen_k, num_q_heads, num_kv_heads,
                            window, num_splits, softmax_scale, o, lse, nullptr, nullptr};
   if (num_splits == 1) return hip_status(sinkattn::launch_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
@@ -151,6 +225,18 @@ sinkattn_status sinkattn_merge_lse(const float* o_parts, const float* lse_parts,
   if (!aligned16(o_parts) || !aligned16(o)) return fail(SINKATTN_ERR_INVALID_ARG, "o_parts and o must be 16-byte aligned");
   const long long rows = static_cast<long long>(n) * num_heads;
   if (rows > 0x7fffffffLL) return fail(SINKATTN_ERR_UNSUPPORTED, "too many rows");
+  if (debug_checks()) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t prow = static_cast<size_t>(num_parts) * rows;
+    sinkattn_status st;
+    if ((st = hip_queue(sinkattn::check_clear(s))) != SINKATTN_OK) return st;
+    if ((st = hip_queue(sinkattn::check_f32(o_parts, prow * head_dim, sinkattn::kCheckParts, false, s))) !=
+        SINKATTN_OK)
+      return st;
+    if ((st = hip_queue(sinkattn::check_f32(lse_parts, prow, sinkattn::kCheckParts, true, s))) != SINKATTN_OK)
+      return st;
+    if ((st = check_result(s, nullptr)) != SINKATTN_OK) return st;
+  }
   sinkattn::MergeLaunch m{o_parts, lse_parts, num_parts, n, num_heads, o, lse};
   return hip_status(sinkattn::launch_merge(m, static_cast<hipStream_t>(stream)), "merge launch");
 }

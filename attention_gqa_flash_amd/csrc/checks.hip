@@ -1,0 +1,126 @@
+// Device-side precondition checks, run by the C ABI before a launch when
+// SINKATTN_DEBUG_CHECKS=1 is set in the environment.  They cover what the
+// host cannot see without reading device memory: sequence offsets (monotone,
+// starting at 0, lengths within the declared maximum, decode lengths >= 1),
+// sinks (finite or -inf; NaN and +inf are undefined), and NaN / Inf in the
+// bf16 inputs and in merge partials.
+//
+// Each check kernel ORs a bit into g_check_flags; the host clears the word
+// before and reads it back after (hipMemcpyFromSymbol), synchronising the
+// stream.  Debug mode is for diagnosis: calls that overlap on one device
+// share the flag word.
+#include "launch.hpp"
+
+namespace sinkattn {
+
+namespace {
+
+__device__ unsigned g_check_flags;
+__device__ int g_check_total;  // cu_seqlens[batch] of the last offsets check
+
+__global__ void clear_flags_kernel() {
+  g_check_flags = 0u;
+  g_check_total = 0;
+}
+
+__global__ void check_offsets_kernel(const int32_t* __restrict__ cu, int batch, int max_len, int min_len,
+                                     int total_limit) {
+  unsigned bits = 0;
+  for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < batch; b += gridDim.x * blockDim.x) {
+    const int lo = cu[b], hi = cu[b + 1];
+    if (b == 0 && lo != 0) bits |= kCheckOffsetsStart;
+    if (hi < lo) bits |= kCheckOffsetsOrder;
+    else if (hi - lo > max_len) bits |= kCheckLengthMax;
+    else if (hi - lo < min_len) bits |= kCheckLengthMin;
+    if (b == batch - 1) {
+      if (total_limit >= 0 && hi > total_limit) bits |= kCheckOffsetsTotal;
+      g_check_total = hi;
+    }
+  }
+  if (bits != 0u) atomicOr(&g_check_flags, bits);
+}
+
+// Floating-point classes are tested on the bit patterns: the library is
+// built without NaN semantics (-fno-honor-nans), so x != x would fold away.
+__device__ __forceinline__ bool is_nan_bits(uint32_t u) { return (u & 0x7fffffffu) > 0x7f800000u; }
+constexpr uint32_t kPosInfBits = 0x7f800000u;
+constexpr uint32_t kNegInfBits = 0xff800000u;
+
+__global__ void check_sinks_kernel(const float* __restrict__ sinks, int n) {
+  unsigned bits = 0;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const uint32_t u = __float_as_uint(sinks[i]);
+    if (is_nan_bits(u) || u == kPosInfBits) bits |= kCheckSinks;
+  }
+  if (bits != 0u) atomicOr(&g_check_flags, bits);
+}
+
+// bf16 NaN or Inf: exponent bits all ones.
+__global__ void check_bf16_kernel(const uint16_t* __restrict__ x, size_t n, unsigned bit) {
+  unsigned bad = 0;
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    bad |= (x[i] & 0x7f80u) == 0x7f80u;
+  if (bad != 0u) atomicOr(&g_check_flags, bit);
+}
+
+// fp32 values must not be NaN or +inf, nor -inf unless allow_neg_inf.
+__global__ void check_f32_kernel(const float* __restrict__ x, size_t n, unsigned bit, int allow_neg_inf) {
+  unsigned bad = 0;
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const uint32_t u = __float_as_uint(x[i]);
+    bad |= is_nan_bits(u) || u == kPosInfBits || (!allow_neg_inf && u == kNegInfBits);
+  }
+  if (bad != 0u) atomicOr(&g_check_flags, bit);
+}
+
+unsigned grid_for(size_t n) {
+  const size_t blocks = (n + 255) / 256;
+  return static_cast<unsigned>(blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks));
+}
+
+}  // namespace
+
+hipError_t check_clear(hipStream_t stream) {
+  hipLaunchKernelGGL(clear_flags_kernel, dim3(1), dim3(1), 0, stream);
+  return hipGetLastError();
+}
+
+hipError_t check_offsets(const int32_t* cu, int batch, int max_len, int min_len, int total_limit,
+                         hipStream_t stream) {
+  if (batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(check_offsets_kernel, dim3(grid_for(batch)), dim3(256), 0, stream, cu, batch, max_len,
+                     min_len, total_limit);
+  return hipGetLastError();
+}
+
+hipError_t check_sinks(const float* sinks, int n, hipStream_t stream) {
+  if (sinks == nullptr || n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(check_sinks_kernel, dim3(grid_for(n)), dim3(256), 0, stream, sinks, n);
+  return hipGetLastError();
+}
+
+hipError_t check_bf16(const void* x, size_t n, unsigned bit, hipStream_t stream) {
+  if (x == nullptr || n == 0) return hipSuccess;
+  hipLaunchKernelGGL(check_bf16_kernel, dim3(grid_for(n)), dim3(256), 0, stream, static_cast<const uint16_t*>(x),
+                     n, bit);
+  return hipGetLastError();
+}
+
+hipError_t check_f32(const float* x, size_t n, unsigned bit, bool allow_neg_inf, hipStream_t stream) {
+  if (x == nullptr || n == 0) return hipSuccess;
+  hipLaunchKernelGGL(check_f32_kernel, dim3(grid_for(n)), dim3(256), 0, stream, x, n, bit, allow_neg_inf ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t check_read(unsigned* flags, int* total, hipStream_t stream) {
+  hipError_t e = hipMemcpyFromSymbolAsync(flags, HIP_SYMBOL(g_check_flags), sizeof(unsigned), 0,
+                                          hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyFromSymbolAsync(total, HIP_SYMBOL(g_check_total), sizeof(int), 0, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  return e;
+}
+
+}  // namespace sinkattn

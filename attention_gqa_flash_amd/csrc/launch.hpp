@@ -45,6 +45,30 @@ hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream);
 
+// Device-side precondition checks (debug mode).  Bits of the flag word:
+enum CheckBits : unsigned {
+  kCheckOffsetsStart = 1u << 0,  // cu_seqlens[0] != 0
+  kCheckOffsetsOrder = 1u << 1,  // cu_seqlens decreasing somewhere
+  kCheckLengthMax = 1u << 2,     // a length above the declared maximum
+  kCheckLengthMin = 1u << 3,     // a length below the minimum (decode: 1)
+  kCheckOffsetsTotal = 1u << 4,  // cu_seqlens[batch] above the declared total
+  kCheckSinks = 1u << 5,         // a sink is NaN or +inf
+  kCheckQ = 1u << 6,             // NaN / Inf in q
+  kCheckK = 1u << 7,             // NaN / Inf in k
+  kCheckV = 1u << 8,             // NaN / Inf in v
+  kCheckParts = 1u << 9,         // NaN / Inf in o_parts, NaN / +inf in lse_parts
+  kCheckAll = (1u << 10) - 1u,
+};
+hipError_t check_clear(hipStream_t stream);
+hipError_t check_offsets(const int32_t* cu, int batch, int max_len, int min_len, int total_limit,
+                         hipStream_t stream);
+hipError_t check_sinks(const float* sinks, int n, hipStream_t stream);
+hipError_t check_bf16(const void* x, size_t n, unsigned bit, hipStream_t stream);
+hipError_t check_f32(const float* x, size_t n, unsigned bit, bool allow_neg_inf, hipStream_t stream);
+// Reads the flag word and cu_seqlens[batch] of the last offsets check;
+// synchronises the stream.
+hipError_t check_read(unsigned* flags, int* total, hipStream_t stream);
+
 int prefill_max_qtiles();
 int prefill_qtile();
 int decode_max_group();

@@ -28,17 +28,24 @@
  *  - bf16 is stored as raw 16-bit patterns (uint16); outputs are rounded to
  *    nearest even from fp32 accumulators.
  *  - The caller allocates and owns every buffer, including the workspace.
- *    These entry points never allocate or free device memory and never
- *    synchronise: work is enqueued on `stream` (a hipStream_t passed as
- *    void*; NULL is the default stream) and the call returns.
+ *    These entry points never allocate or free device memory and (outside
+ *    the debug mode below) never synchronise: work is enqueued on `stream`
+ *    (a hipStream_t passed as void*; NULL is the default stream) and the
+ *    call returns.
  *  - Host-checkable argument errors return a status before anything is
  *    launched; a launch failure returns SINKATTN_ERR_HIP.  The message of the
  *    last failure on the calling thread is sinkattn_last_error().  No C++
  *    exception crosses this interface.
- *  - Device-side preconditions, not checked: cu_seqlens is non-decreasing
- *    with cu_seqlens[0] = 0 and every length <= max_seqlen; decode lengths
- *    are >= 1; sinks are finite or -inf (-inf = that head has no sink);
- *    inputs hold no NaN/Inf.
+ *  - Device-side preconditions: cu_seqlens is non-decreasing with
+ *    cu_seqlens[0] = 0 and every length <= max_seqlen (prefill:
+ *    cu_seqlens[batch] <= total_tokens); decode lengths are >= 1; sinks are
+ *    finite or -inf (-inf = that head has no sink); q/k/v hold no NaN/Inf;
+ *    merge partials hold no NaN/Inf (lse_parts may be -inf = empty part).
+ *    They are not checked by default.  With SINKATTN_DEBUG_CHECKS=1 in the
+ *    environment (read on every call) each entry point first checks them on
+ *    the device, synchronising `stream`, and returns SINKATTN_ERR_INVALID_ARG
+ *    naming the failed conditions without launching the attention kernels.
+ *    Debug checks of calls that overlap on one device share one flag word.
  *  - Supported shapes: head_dim == 64 (other values: SINKATTN_ERR_UNSUPPORTED),
  *    num_q_heads % num_kv_heads == 0, softmax_scale finite and > 0.
  */

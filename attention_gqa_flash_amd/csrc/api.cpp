@@ -123,12 +123,9 @@ sinkattn_status sinkattn_prefill_varlen(const void* q, const void* k, const void
     return fail(SINKATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
   if (max_seqlen > total_tokens)
     return fail(SINKATTN_ERR_INVALID_ARG, "max_seqlen (%d) exceeds total_tokens (%d)", max_seqlen, total_tokens);
-  const long long qtiles = (static_cast<long long>(max_seqlen) + sinkattn::prefill_qtile() - 1) / sinkattn::prefill_qtile();
-  if (qtiles > sinkattn::prefill_max_qtiles())
-    return fail(SINKATTN_ERR_UNSUPPORTED, "max_seqlen %d is too long for one launch", max_seqlen);
   const int group = num_q_heads / num_kv_heads;
-  const long long blocks_x = static_cast<long long>(num_kv_heads) * ((group + 7) / 8) * batch;
-  if (blocks_x > 0x7fffffffLL) return fail(SINKATTN_ERR_UNSUPPORTED, "too many (batch, head) work items");
+  if (sinkattn::prefill_blocks(batch, total_tokens, num_kv_heads, group) > sinkattn::prefill_max_blocks())
+    return fail(SINKATTN_ERR_UNSUPPORTED, "too many (query tile, head) work items for one launch");
   // K/V rows of one sequence are addressed with 32-bit byte offsets.
   if (static_cast<long long>(max_seqlen) * num_kv_heads * head_dim * 2 >= (1LL << 31))
     return fail(SINKATTN_ERR_UNSUPPORTED, "max_seqlen * num_kv_heads * head_dim * 2 must stay below 2^31");
@@ -145,8 +142,8 @@ sinkattn_status sinkattn_prefill_varlen(const void* q, const void* k, const void
     if ((st = hip_queue(sinkattn::check_bf16(v, kvn, sinkattn::kCheckV, s))) != SINKATTN_OK) return st;
     if ((st = check_result(s, nullptr)) != SINKATTN_OK) return st;
   }
-  sinkattn::PrefillLaunch a{q, k, v, sinks, cu_seqlens, batch, max_seqlen, num_q_heads, num_kv_heads,
-                            window, softmax_scale, o, lse};
+  sinkattn::PrefillLaunch a{q, k, v, sinks, cu_seqlens, batch, max_seqlen, total_tokens, num_q_heads,
+                            num_kv_heads, window, softmax_scale, o, lse};
   return hip_status(sinkattn::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
 }
 

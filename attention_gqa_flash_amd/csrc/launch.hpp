@@ -13,7 +13,7 @@ struct PrefillLaunch {
   const void* v;
   const float* sinks;
   const int32_t* cu_seqlens;
-  int batch, max_seqlen, num_q_heads, num_kv_heads, window;
+  int batch, max_seqlen, total_tokens, num_q_heads, num_kv_heads, window;
   float softmax_scale;
   void* o;
   float* lse;
@@ -69,8 +69,9 @@ hipError_t check_f32(const float* x, size_t n, unsigned bit, bool allow_neg_inf,
 // synchronises the stream.
 hipError_t check_read(unsigned* flags, int* total, hipStream_t stream);
 
-int prefill_max_qtiles();
-int prefill_qtile();
+// Workgroups of one prefill launch, and the most one launch can take.
+long long prefill_blocks(int batch, int total_tokens, int num_kv_heads, int group);
+long long prefill_max_blocks();
 int decode_max_group();
 
 }  // namespace sinkattn

@@ -126,12 +126,38 @@ __device__ __forceinline__ void wait_vmem_keep() {
 // compiler does not move memory operations across.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// First work item of sequence b: floor((cu[b] + 31 b) / 32).  Consecutive
+// starts differ by at least ceil(len_b / 32) and by at most one more, so the
+// items of a batch number floor((T + 31 B) / 32) at most, with T the tokens.
+__device__ __forceinline__ int item_start(int cu_b, int b) {
+  return static_cast<int>((static_cast<long long>(cu_b) + static_cast<long long>(kQTile - 1) * b) / kQTile);
+}
+
+// The sequence that owns work item w: the largest b < batch with
+// item_start(cu[b], b) <= w (starts are non-decreasing for valid offsets),
+// or -1.  A 64-way search: each round probes one offset per lane, so up to
+// 64 sequences take one round of loads and 4096 take two.
+__device__ __forceinline__ int find_sequence(const int32_t* __restrict__ cu, int batch, int w, int lane) {
+  int lo = 0, n = batch;  // the answer lies in [lo, lo + n)
+  while (true) {
+    const int stride = (n + 63) / 64;
+    const int probe = lo + lane * stride;
+    bool le = false;
+    if (probe < lo + n) le = item_start(cu[probe], probe) <= w;
+    const int cnt = __popcll(__builtin_amdgcn_ballot_w64(le));
+    if (cnt == 0) return -1;
+    lo += (cnt - 1) * stride;
+    if (stride == 1) return lo;
+    n = min(stride, n - (cnt - 1) * stride);
+  }
+}
+
 template <bool kWindow, int kCols>
 __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_per_eu(4 / kCols, 4 / kCols))) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ sinks,
     const int32_t* __restrict__ cu_seqlens, int hq, int hkv, int group, int n_hchunk,
-    int n_qtiles, int window, float scale_log2, uint16_t* __restrict__ o,
+    int batch, int max_seqlen, int window, float scale_log2, uint16_t* __restrict__ o,
     float* __restrict__ lse) {
   // Ring of LDS tile buffers, each K rows then V rows.  Tile t lives in
   // buffer (t - t_begin) % kBufs; the loop below is unrolled over the ring so
@@ -147,17 +173,30 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
   const int col = lane & 31;   // query token within the tile
   const int half = lane >> 5;  // which k-half / row-half of the MFMA layouts
 
+  // blockIdx.x = (w * n_hchunk + hchunk) * hkv + g: consecutive workgroups
+  // take consecutive KV heads, so with 8 KV heads each XCD (they receive
+  // workgroups round-robin) serves one head.  Work item w names a query tile
+  // in batch order (item_start), the top tile of a sequence first: the
+  // workgroups in flight on an XCD belong to one or two sequences and share
+  // their K/V through its L2, and within a sequence the longest tiles start
+  // first.
   int x = blockIdx.x;
   const int g = x % hkv;
   x /= hkv;
   const int hchunk = x % n_hchunk;
-  const int b = x / n_hchunk;
-  const int qt = n_qtiles - 1 - static_cast<int>(blockIdx.y);
+  const int w = x / n_hchunk;
+  const int b = find_sequence(cu_seqlens, batch, w, lane);
+  if (b < 0) return;  // uniform over the workgroup
 
   const int seq0 = cu_seqlens[b];
-  const int len = cu_seqlens[b + 1] - seq0;
+  // Lengths above max_seqlen break a precondition; clamping keeps every
+  // access inside the bounds the host checked.
+  const int len = min(cu_seqlens[b + 1] - seq0, max_seqlen);
+  const int n_tiles = len > 0 ? (len + kQTile - 1) / kQTile : 0;
+  const int j = w - item_start(seq0, b);
+  if (j >= n_tiles) return;  // a spare item between two sequences
+  const int qt = n_tiles - 1 - j;
   const int q0 = qt * kQTile;
-  if (q0 >= len) return;  // uniform over the workgroup
 
   const int last_q = min(len - 1, q0 + kQTile - 1);
   const int first_key = kWindow ? max(0, q0 - window + 1) : 0;
@@ -507,19 +546,25 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
   const int n_hchunk = (group + kHeadsPerBlock - 1) / kHeadsPerBlock;
-  const int n_qtiles = (a.max_seqlen + kQTile - 1) / kQTile;
-  dim3 grid(static_cast<unsigned>(a.num_kv_heads) * n_hchunk * a.batch, n_qtiles, 1);
+  const long long blocks = prefill_blocks(a.batch, a.total_tokens, a.num_kv_heads, group);
+  if (blocks <= 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>(blocks), 1, 1);
   const bool windowed = a.window > 0 && a.window < a.max_seqlen;
   auto kernel = windowed ? prefill_kernel<true, kColsPerWave> : prefill_kernel<false, kColsPerWave>;
   hipLaunchKernelGGL(kernel, grid, dim3(threads_for<kColsPerWave>()), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.sinks, a.cu_seqlens, a.num_q_heads,
-                     a.num_kv_heads, group, n_hchunk, n_qtiles, a.window,
+                     a.num_kv_heads, group, n_hchunk, a.batch, a.max_seqlen, a.window,
                      a.softmax_scale * kLog2e, static_cast<uint16_t*>(a.o), a.lse);
   return hipGetLastError();
 }
 
-int prefill_max_qtiles() { return 65535; }
-int prefill_qtile() { return kQTile; }
+long long prefill_blocks(int batch, int total_tokens, int num_kv_heads, int group) {
+  const long long items = (static_cast<long long>(total_tokens) + static_cast<long long>(kQTile - 1) * batch) / kQTile;
+  return items * num_kv_heads * ((group + kHeadsPerBlock - 1) / kHeadsPerBlock);
+}
+
+// hipLaunchKernelGGL takes at most 2^32 - 1 work-items along x.
+long long prefill_max_blocks() { return 0xffffffffLL / threads_for<kColsPerWave>(); }
 
 }  // namespace sinkattn

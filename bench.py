@@ -15,9 +15,18 @@ counts are algorithmic (unmasked query-key pairs; Q + O + the K/V rows
 attended + sinks), measured with HIP events on the stream the kernels run
 on.  Inputs are resident in HBM before timing; the prefill leg rotates three
 input sets so that its 151 MB working set does not stay in the 256 MB
-Infinity Cache between steps.
+Infinity Cache between steps.  Each leg reports mean, median and min.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Also reported (not part of the step or of `value`): decode at 1, 4 and 16
+splits; the tiny 256-token prefill; the long-context decode pair (16 x 32768
+cached tokens, 32 splits, full then 128-window); the ragged 32-sequence
+varlen prefill (causal and 128-window); a streaming-read and a copy
+bandwidth reference; the engine clock (sysfs pp_dpm_sclk) sampled during the step.
+Small working sets are timed after a 512 MiB cache scrub.  The long-decode
+and ragged inputs are drawn on the device from a seeded generator (same
+distributions as the host-generated parity inputs) to keep start-up short.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
 """
 
 from __future__ import annotations
@@ -54,25 +63,25 @@ def visible_pairs(length: int, window: int) -> int:
     return window * length - window * (window - 1) // 2
 
 
-def prefill_flops(lengths, window) -> float:
-    return 4.0 * D * HQ * sum(visible_pairs(n, window) for n in lengths)
+def prefill_flops(lengths, window, hq=HQ) -> float:
+    return 4.0 * D * hq * sum(visible_pairs(n, window) for n in lengths)
 
 
-def prefill_bytes(lengths, window) -> float:
+def prefill_bytes(lengths, window, hq=HQ, hkv=HKV) -> float:
     t = sum(lengths)
-    qo = 2 * t * HQ * D * 2
-    kv = 2 * t * HKV * D * 2          # every key is attended by some query
-    return float(qo + kv + HQ * 4 + (len(lengths) + 1) * 4)
+    qo = 2 * t * hq * D * 2
+    kv = 2 * t * hkv * D * 2          # every key is attended by some query
+    return float(qo + kv + hq * 4 + (len(lengths) + 1) * 4)
 
 
-def decode_bytes(lengths, window) -> float:
+def decode_bytes(lengths, window, hq=HQ, hkv=HKV) -> float:
     keys = sum(min(n, window) if window > 0 else n for n in lengths)
-    return float(2 * len(lengths) * HQ * D * 2 + 2 * keys * HKV * D * 2 + HQ * 4 + (len(lengths) + 1) * 4)
+    return float(2 * len(lengths) * hq * D * 2 + 2 * keys * hkv * D * 2 + hq * 4 + (len(lengths) + 1) * 4)
 
 
-def decode_flops(lengths, window) -> float:
+def decode_flops(lengths, window, hq=HQ) -> float:
     keys = sum(min(n, window) if window > 0 else n for n in lengths)
-    return 4.0 * D * HQ * keys
+    return 4.0 * D * hq * keys
 
 
 # ---------------------------------------------------------------------------
@@ -159,13 +168,92 @@ def _traffic(kernel: str):
     return ent.get("bytes_per_launch")
 
 
-def gpu_bench(steps: int, warmup: int) -> dict:
+class _ClockSampler:
+    """Samples the engine clock of the GPU under test on a host thread while
+    kernels run: the current level of sysfs pp_dpm_sclk (the line marked
+    '*'), plus the hwmon power reading where present.  Best effort: None
+    where the files are missing or unreadable."""
+
+    def __init__(self, pci_bus: str):
+        import glob
+        cards = []
+        for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+            if os.path.exists(os.path.join(dev, "pp_dpm_sclk")):
+                cards.append(dev)
+        match = [d for d in cards if os.path.realpath(d).lower().endswith(pci_bus.lower())]
+        dev = match[0] if match else (cards[0] if len(cards) == 1 else None)
+        self.sclk = os.path.join(dev, "pp_dpm_sclk") if dev else None
+        power = sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*", "power1_input"))) if dev else []
+        self.power = power[0] if power else None
+        self.mhz, self.watts = [], []
+        self._stop = None
+        self._thread = None
+
+    @staticmethod
+    def _read(path):
+        try:
+            with open(path) as f:
+                return f.read()
+        except OSError:
+            return None
+
+    def _sample(self):
+        text = self._read(self.sclk)
+        if text:
+            for line in text.splitlines():
+                if line.rstrip().endswith("*"):
+                    digits = "".join(ch for ch in line.split(":", 1)[-1] if ch.isdigit())
+                    if digits:
+                        self.mhz.append(int(digits))
+        if self.power:
+            text = self._read(self.power)
+            if text and text.strip().isdigit():
+                self.watts.append(int(text.strip()) / 1e6)
+
+    def __enter__(self):
+        import threading
+        if self.sclk is None:
+            return self
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                self._sample()
+                self._stop.wait(0.005)
+
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        def med(xs):
+            return sorted(xs)[len(xs) // 2] if xs else None
+        return {"source": self.sclk, "mhz_median": med(self.mhz), "mhz_min": min(self.mhz) if self.mhz else None,
+                "mhz_max": max(self.mhz) if self.mhz else None, "samples": len(self.mhz),
+                "power_w_median": med(self.watts)}
+
+
+def _stats(ms_list):
+    import numpy as np
+    a = np.asarray(ms_list, dtype=np.float64)
+    return {"median_ms": float(np.median(a)), "min_ms": float(a.min()), "mean_ms": float(a.mean()),
+            "reps": int(a.size)}
+
+
+def gpu_bench(steps: int, warmup: int, extras: bool = True) -> dict:
     import numpy as np
     import torch
 
     from attention_gqa_flash_amd import binding, inputs
 
     dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    pci_bus = "%04x:%02x:%02x.0" % (props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
 
     def bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -209,30 +297,68 @@ def gpu_bench(steps: int, warmup: int) -> dict:
     for i in range(warmup):
         step(i, False)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(i, True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    clock = _ClockSampler(pci_bus)
+    with clock:
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i, True)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
 
-    def mean_ms(name):
-        return float(np.mean([a.elapsed_time(b) for a, b in ev[name]]))
+    leg = {name: _stats([a.elapsed_time(b) for a, b in ev[name]]) for name in ev}
+    t_causal, t_window, t_decode = (leg[n]["mean_ms"] for n in ("causal", "window", "decode"))
 
-    t_causal, t_window, t_decode = mean_ms("causal"), mean_ms("window"), mean_ms("decode")
+    # Infinity-Cache scrub for legs whose working set would otherwise stay
+    # cached between repetitions: a 512 MiB write outside the timed region.
+    scrub_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
-    # decode at the other split counts (reported; not part of the step)
+    def scrub():
+        scrub_buf.fill_(1)
+
+    def timed(fn, reps=20, warm=5, scrub_each=False):
+        for _ in range(warm):
+            fn()
+        pairs = []
+        for _ in range(reps):
+            if scrub_each:
+                scrub()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            pairs.append((a, b))
+        torch.cuda.synchronize()
+        return _stats([a.elapsed_time(b) for a, b in pairs])
+
+    def hbm_entry(st, nbytes, flops=None):
+        gbs = nbytes / (st["median_ms"] * 1e-3) / 1e9
+        e = dict(st, algorithmic_bytes=nbytes, gbs_median=gbs,
+                 gbs_best=nbytes / (st["min_ms"] * 1e-3) / 1e9, pct_hbm_peak=100 * gbs / PEAK_HBM_GBS)
+        if flops is not None:
+            e["algorithmic_flop"] = flops
+            e["tflops_median"] = flops / (st["median_ms"] * 1e-3) / 1e12
+            e["pct_mfma_peak"] = 100 * e["tflops_median"] / PEAK_BF16_TFLOPS
+        return e
+
+    def mfma_entry(st, flops, nbytes):
+        tf = flops / (st["median_ms"] * 1e-3) / 1e12
+        return dict(st, algorithmic_flop=flops, algorithmic_bytes=nbytes, tflops_median=tf,
+                    tflops_best=flops / (st["min_ms"] * 1e-3) / 1e12, pct_mfma_peak=100 * tf / PEAK_BF16_TFLOPS,
+                    pct_hbm_peak=100 * nbytes / (st["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS)
+
+    # decode at every split count of the 64 x 8192 workload (the step uses 16)
     per_split = {}
     for s_count in (1, 4, 16):
-        for _ in range(3):
-            binding.decode_splitkv(dq, dk, dv, dcu, DEC_CTX, dsinks, 0, scale, s_count, workspace=ws, out=do)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(10):
-            binding.decode_splitkv(dq, dk, dv, dcu, DEC_CTX, dsinks, 0, scale, s_count, workspace=ws, out=do)
-        b.record()
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / 10
-        per_split[str(s_count)] = {"ms": ms, "GB/s": decode_bytes([DEC_CTX] * DEC_BATCH, 0) / (ms * 1e-3) / 1e9}
+        st = timed(lambda: binding.decode_splitkv(dq, dk, dv, dcu, DEC_CTX, dsinks, 0, scale, s_count,
+                                                  workspace=ws, out=do))
+        e = hbm_entry(st, decode_bytes([DEC_CTX] * DEC_BATCH, 0))
+        e["GB/s"] = e["gbs_median"]
+        per_split[str(s_count)] = e
+
+    other = {}
+    if extras:
+        sets.clear()
+        other = _other_configs(torch, np, binding, inputs, dev, bf16, timed, hbm_entry, mfma_entry)
 
     f_causal = prefill_flops([PREFILL_LEN], 0)
     f_window = prefill_flops([PREFILL_LEN], WINDOW)
@@ -257,25 +383,126 @@ def gpu_bench(steps: int, warmup: int) -> dict:
                    "achieved": decode_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                    "frac": decode_gbs / PEAK_HBM_GBS, "traffic": _traffic("decode_s16"),
                    "ms": t_decode, "algorithmic_bytes": b_decode}
-    props = torch.cuda.get_device_properties(dev)
     return {
         "value": value, "ms_per_step": wall * 1e3 / steps,
         "prefill": {"tflops": prefill_tflops, "pct_mfma_peak": 100 * prefill_tflops / PEAK_BF16_TFLOPS,
                     "causal_ms": t_causal, "window_ms": t_window, "causal_tflops": causal_tflops,
-                    "window_tflops": window_tflops, "window_gbs": window_gbs},
+                    "window_tflops": window_tflops, "window_gbs": window_gbs,
+                    "causal_timing": leg["causal"], "window_timing": leg["window"]},
         "decode": {"gbs": decode_gbs, "pct_hbm_peak": 100 * decode_gbs / PEAK_HBM_GBS, "ms": t_decode,
-                   "splits": DEC_SPLITS, "by_splits": per_split},
+                   "splits": DEC_SPLITS, "timing": leg["decode"], "by_splits": per_split},
         "roofline": roof_causal, "rooflines": [roof_causal, roof_window, roof_decode],
-        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "other_configs": other.get("configs"), "bandwidth_reference": other.get("bandwidth"),
+        "engine_clock": clock.summary(),
+        "device": {"name": props.name, "cus": props.multi_processor_count, "arch": props.gcnArchName,
+                   "pci_bus": pci_bus},
     }
+
+
+def _device_normal_bf16(torch, shape, gen, dev, std=1.0):
+    """N(0, std^2) drawn in fp32 on the device from a seeded generator and
+    rounded to bf16 (round to nearest even): timing-only inputs with the
+    distribution of the host-generated parity inputs."""
+    x = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.to(torch.bfloat16)
+
+
+def _other_configs(torch, np, binding, inputs, dev, bf16, timed, hbm_entry, mfma_entry) -> dict:
+    """The workloads besides the step: the tiny prefill, the long-context
+    decode pair (full then 128-window, 32 splits) and the ragged 32-sequence
+    varlen prefill (causal and 128-window), plus an achievable-bandwidth
+    reference.  Each is timed alone with HIP events around the one call:
+    5 warm-ups, 20 repetitions, median and min."""
+    out = {}
+    scale = 0.125
+
+    # tiny: 1 x 256 tokens, 4 q heads / 1 KV head, causal (host inputs, seed 0)
+    p = inputs.tiny_prefill(seed=0)
+    tq, tk, tv = bf16(p.q), bf16(p.k), bf16(p.v)
+    ts, tcu = torch.from_numpy(p.sinks).to(dev), torch.from_numpy(p.cu_seqlens).to(dev)
+    to = torch.empty_like(tq)
+    st = timed(lambda: binding.prefill_varlen(tq, tk, tv, ts, tcu, 256, 0, scale, out=to), scrub_each=True)
+    out["tiny_prefill_causal"] = dict(mfma_entry(st, prefill_flops([256], 0, hq=4), prefill_bytes([256], 0, 4, 1)),
+                                      bound="launch latency", shape="B=1, L=256, 4/1 heads")
+
+    gen = torch.Generator(device=dev)
+
+    # long decode: 16 x 32768 cached tokens, sinks std sqrt(2), 32 splits
+    gen.manual_seed(1)
+    nb, ctx, splits = 16, 32768, 32
+    lq = _device_normal_bf16(torch, (nb, HQ, D), gen, dev)
+    lk = _device_normal_bf16(torch, (nb * ctx, HKV, D), gen, dev)
+    lv = _device_normal_bf16(torch, (nb * ctx, HKV, D), gen, dev)
+    lsinks = torch.randn(HQ, generator=gen, device=dev, dtype=torch.float32) * math.sqrt(2.0)
+    lcu = torch.arange(0, (nb + 1) * ctx, ctx, dtype=torch.int32, device=dev)
+    lo = torch.empty_like(lq)
+    lws = torch.empty(binding.decode_workspace_bytes(nb, HQ, D, splits), dtype=torch.uint8, device=dev)
+    pair = []
+    for window in (0, WINDOW):
+        st = timed(lambda: binding.decode_splitkv(lq, lk, lv, lcu, ctx, lsinks, window, scale, splits,
+                                                  workspace=lws, out=lo), scrub_each=(window > 0))
+        e = hbm_entry(st, decode_bytes([ctx] * nb, window), decode_flops([ctx] * nb, window))
+        e["shape"] = "B=16, ctx 32768, 64/8 heads, S=32, window %d" % window
+        out["long_decode_%s" % ("full" if window == 0 else "w128")] = e
+        pair.append(e)
+    pb = sum(e["algorithmic_bytes"] for e in pair)
+    pms = sum(e["median_ms"] for e in pair)
+    out["long_decode_pair"] = {"median_ms": pms, "algorithmic_bytes": pb,
+                               "gbs_median": pb / (pms * 1e-3) / 1e9,
+                               "pct_hbm_peak": 100 * pb / (pms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    del lq, lk, lv, lo, lws
+
+    # ragged varlen prefill: 32 sequences with the log-uniform lengths of
+    # seed 0, heads 0, 9, 18, 27 without sink
+    lengths = inputs.ragged_lengths(np.random.default_rng(0), 32)
+    total, lmax = int(sum(lengths)), int(max(lengths))
+    gen.manual_seed(2)
+    rq = _device_normal_bf16(torch, (total, HQ, D), gen, dev)
+    rk = _device_normal_bf16(torch, (total, HKV, D), gen, dev)
+    rv = _device_normal_bf16(torch, (total, HKV, D), gen, dev)
+    rs = torch.randn(HQ, generator=gen, device=dev, dtype=torch.float32)
+    rs[list(inputs.NO_SINK_HEADS)] = -math.inf
+    rcu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32), device=dev)
+    ro = torch.empty_like(rq)
+    for window in (0, WINDOW):
+        st = timed(lambda: binding.prefill_varlen(rq, rk, rv, rs, rcu, lmax, window, scale, out=ro),
+                   reps=20 if window else 10)
+        f, b = prefill_flops(lengths, window), prefill_bytes(lengths, window)
+        e = mfma_entry(st, f, b) if window == 0 else hbm_entry(st, b, f)
+        e["shape"] = "32 sequences, T=%d, max L=%d, 64/8 heads, window %d" % (total, lmax, window)
+        e["bound"] = "mfma" if window == 0 else "hbm"
+        out["ragged_prefill_%s" % ("causal" if window == 0 else "w128")] = e
+    del rq, rk, rv, ro
+    torch.cuda.synchronize()
+
+    # achievable bandwidth: a 2 GiB streaming read (torch sum over fp32) and a
+    # 2 GiB device-to-device copy (4 GiB moved)
+    n = (2 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    acc = torch.empty((), dtype=torch.float32, device=dev)
+    st_read = timed(lambda: torch.sum(a, dim=0, out=acc), reps=10, warm=3)
+    st_copy = timed(lambda: b.copy_(a), reps=10, warm=3)
+    bw = {"read_2GiB": dict(st_read, gbs_median=(n * 4) / (st_read["median_ms"] * 1e-3) / 1e9,
+                            gbs_best=(n * 4) / (st_read["min_ms"] * 1e-3) / 1e9, kernel="torch.sum fp32"),
+          "copy_2GiB": dict(st_copy, gbs_median=(2 * n * 4) / (st_copy["median_ms"] * 1e-3) / 1e9,
+                            gbs_best=(2 * n * 4) / (st_copy["min_ms"] * 1e-3) / 1e9,
+                            kernel="torch copy_ (read + write counted)")}
+    del a, b
+    torch.cuda.synchronize()
+    return {"configs": out, "bandwidth": bw}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the other workloads and the bandwidth reference (the step only)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (a reference "
                          "for HBM byte counters)")
@@ -296,7 +523,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    g = gpu_bench(args.steps, args.warmup)
+    g = gpu_bench(args.steps, args.warmup, extras=not args.no_extras)
     out = {
         "metric": METRIC, "value": g["value"],
         "unit": "% of MI355X peak (mean of prefill bf16-MFMA and decode HBM fractions)",
@@ -309,7 +536,8 @@ def main():
                    "prefill": {"batch": 1, "seq_len": PREFILL_LEN, "windows": [0, WINDOW]},
                    "decode": {"batch": DEC_BATCH, "context": DEC_CTX, "splits": DEC_SPLITS}},
         "prefill": g["prefill"], "decode": g["decode"], "roofline": g["roofline"], "rooflines": g["rooflines"],
-        "cpu_baseline": cpu, "device": g["device"],
+        "cpu_baseline": cpu, "other_configs": g["other_configs"],
+        "bandwidth_reference": g["bandwidth_reference"], "engine_clock": g["engine_clock"], "device": g["device"],
     }
     print(json.dumps(out))
 

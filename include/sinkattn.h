@@ -84,7 +84,7 @@ typedef enum sinkattn_status {
  *   cu_seqlens  int32 [batch + 1], device; sequence b owns tokens
  *               [cu_seqlens[b], cu_seqlens[b+1]); queries and keys of a
  *               sequence coincide (positions local to the sequence)
- *   max_seqlen  host int, >= every sequence length (sizes the launch)
+ *   max_seqlen  host int, >= every sequence length
  *   window      <= 0: full causal; W > 0: i - W < j <= i
  *   o           bf16 [total_tokens, num_q_heads, head_dim] (written)
  *   lse         fp32 [total_tokens, num_q_heads], natural log, sink
@@ -92,8 +92,10 @@ typedef enum sinkattn_status {
  *               o = 0 and lse = -inf.
  *
  * Additionally required: max_seqlen * num_kv_heads * head_dim * 2 < 2^31
- * (one sequence's K/V rows are addressed with 32-bit byte offsets; larger
- * return SINKATTN_ERR_UNSUPPORTED).
+ * (one sequence's K/V rows are addressed with 32-bit byte offsets), and
+ * num_kv_heads * ceil(group / 8) * floor((total_tokens + 31 * batch) / 32)
+ * below 2^24 (workgroups of one launch, one per 32-query tile of each KV
+ * head and group of 8 query heads); otherwise SINKATTN_ERR_UNSUPPORTED.
  */
 SINKATTN_API sinkattn_status sinkattn_prefill_varlen(
     const void* q, const void* k, const void* v,

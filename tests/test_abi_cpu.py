@@ -74,6 +74,8 @@ def _prefill(lib, **kw):
     (dict(max_seqlen=40_000_000, total=40_000_000), 2),
     # one sequence's K/V rows past 2^31 bytes (32-bit row offsets)
     (dict(max_seqlen=1 << 20, total=1 << 20, hq=128, hkv=128), 2),
+    # 64 KV heads x 2^25 query tiles: more than 2^24 - 1 workgroups
+    (dict(max_seqlen=1000, total=1 << 30, hq=64, hkv=64), 2),
 ])
 def test_prefill_rejects(kw, status):
     lib = _lib()

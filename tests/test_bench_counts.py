@@ -1,0 +1,65 @@
+"""The algorithmic work counts behind the benchmark's roofline fractions.
+
+FLOP = 4 * head_dim * q_heads * (number of unmasked query-key pairs); bytes
+= Q + O + the K/V rows some query attends + sinks + offsets.  The pair count
+is checked by enumeration of the mask (causal, optional window of W keys
+including the query itself: the 128-token sliding-window layers of NVIDIA's
+gpt-oss Blackwell announcement, model-description paragraph), the totals
+against the figures these formulas give at the benchmark shapes.
+"""
+
+import importlib.util
+import os
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+@pytest.mark.parametrize("length", [1, 2, 5, 127, 128, 129, 300])
+@pytest.mark.parametrize("window", [0, 1, 2, 127, 128, 129, 400])
+def test_visible_pairs_enumeration(length, window):
+    b = _bench()
+    brute = sum(1 for i in range(length) for j in range(i + 1) if window <= 0 or j > i - window)
+    assert b.visible_pairs(length, window) == brute
+
+
+def test_step_counts():
+    b = _bench()
+    # causal 8192: 8192 * 8193 / 2 pairs x 4 x 64 x 64
+    assert b.prefill_flops([8192], 0) == 4 * 64 * 64 * (8192 * 8193 // 2)
+    assert abs(b.prefill_flops([8192], 0) - 5.498e11) / 5.498e11 < 1e-3
+    # window 128: 128 pairs for every query from 127 on, i + 1 before
+    assert b.prefill_flops([8192], 128) == 4 * 64 * 64 * (128 * 8192 - 128 * 127 // 2)
+    # Q + O: 2 x 8192 x 64 x 64 x 2 B; K + V: 2 x 8192 x 8 x 64 x 2 B
+    assert b.prefill_bytes([8192], 0) == 2 * 8192 * 64 * 64 * 2 + 2 * 8192 * 8 * 64 * 2 + 64 * 4 + 2 * 4
+    # decode 64 x 8192: the whole KV cache (1 GiB) plus Q and O
+    kv = 2 * 64 * 8192 * 8 * 64 * 2
+    assert kv == 1 << 30
+    assert b.decode_bytes([8192] * 64, 0) == kv + 2 * 64 * 64 * 64 * 2 + 64 * 4 + 65 * 4
+    # decode with a 128 window reads only the last 128 keys of each sequence
+    assert b.decode_bytes([32768] * 16, 128) == 2 * 16 * 128 * 8 * 64 * 2 + 2 * 16 * 64 * 64 * 2 + 64 * 4 + 17 * 4
+    assert b.decode_flops([32768] * 16, 128) == 4 * 64 * 64 * 16 * 128
+    # short sequences under a window read all their keys
+    assert b.decode_bytes([100], 128) == b.decode_bytes([100], 0)
+
+
+def test_tiny_counts():
+    b = _bench()
+    assert b.prefill_flops([256], 0, hq=4) == 4 * 64 * 4 * (256 * 257 // 2)
+    assert b.prefill_bytes([256], 0, 4, 1) == 2 * 256 * 4 * 64 * 2 + 2 * 256 * 64 * 2 + 4 * 4 + 2 * 4
+
+
+def test_gpus_above_one_exits():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr

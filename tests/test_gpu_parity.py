@@ -76,6 +76,34 @@ def test_prefill_empty_sequences_in_pack():
     assert_close_lse(lse, rl, "empty seqs")
 
 
+@pytest.mark.parametrize("n_seqs,max_len", [(150, 90), (4100, 3)])
+def test_prefill_many_sequences(n_seqs, max_len):
+    """Batches past 64 sequences: the work-item search takes two and three
+    rounds (up to 64 sequences take one)."""
+    rng = np.random.default_rng(n_seqs)
+    lengths = [int(x) for x in rng.integers(0, max_len + 1, size=n_seqs)]
+    p = inputs.make_prefill(lengths, hq=8, hkv=2, seed=n_seqs)
+    for window in (0, 2):
+        o, lse, ro, rl = _prefill_case(p, window)
+        assert_close_out(o, ro, "%d seqs W=%d" % (n_seqs, window))
+        assert_close_lse(lse, rl, "%d seqs" % n_seqs)
+
+
+def test_prefill_rows_past_the_last_sequence_untouched():
+    """Buffers longer than cu_seqlens[batch]: rows past it are not written."""
+    p = inputs.make_prefill([40, 0, 97], hq=16, hkv=2, seed=8)
+    pad = 75
+    q, k, v = (bf16_to_device(np.concatenate([x, np.zeros((pad,) + x.shape[1:], x.dtype)])) for x in (p.q, p.k, p.v))
+    out = torch.full(q.shape, 3.0, dtype=torch.bfloat16, device=q.device)
+    binding.prefill_varlen(q, k, v, f32_to_device(p.sinks), i32_to_device(p.cu_seqlens), 97, 0, p.scale, out=out)
+    torch.cuda.synchronize()
+    t = int(p.cu_seqlens[-1])
+    assert bool((out[t:] == 3.0).all())
+    qf, kf, vf = (inputs.bf16_bits_to_f32(x) for x in (p.q, p.k, p.v))
+    ro, _ = prefill_varlen_ref(qf, kf, vf, p.sinks, p.cu_seqlens, 0, p.scale)
+    assert_close_out(to_f64(out[:t]), ro, "padded buffers")
+
+
 def test_prefill_deterministic():
     p = inputs.make_prefill([300, 77], hq=64, hkv=8, seed=7)
     q, k, v = (bf16_to_device(x) for x in (p.q, p.k, p.v))

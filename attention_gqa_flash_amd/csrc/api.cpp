@@ -208,6 +208,7 @@ sinkattn_status sinkattn_decode_splitkv(const void* q, const void* k_cache, cons
   a.lse_part = reinterpret_cast<float*>(ws + round_up(rows * head_dim * sizeof(float), 256));
   hipError_t e = sinkattn::launch_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_status(e, "decode launch");
+  if (sinkattn::decode_merges_in_kernel(a)) return ok();
   sinkattn::MergeLaunch m{a.o_part, a.lse_part, num_splits, batch, num_q_heads, o, lse};
   return hip_status(sinkattn::launch_merge(m, static_cast<hipStream_t>(stream)), "merge launch");
 }

@@ -36,6 +36,13 @@ constexpr int kShortChunk = 1024;
 // against 5.5 with the waves interleaved; at S = 16, 512-key splits, the
 // two-wave interleaved kernel is 12% faster).
 constexpr int kSplitPerWaveMin = 4;
+// Splits of at most kKeys keys over a range of at most kDirectMaxKeys keys
+// (window layers cut into many splits) are not formed: the merge of
+// normalised split partials is exact, so it equals attention over the whole
+// range, which one workgroup per (sequence, KV head) evaluates in a third of
+// the time the partials and their merge take (16 x 32768 cached tokens,
+// 128-key window, 32 splits: 4.9 against 13.5 us back to back).
+constexpr int kDirectMaxKeys = 1024;
 
 // One 32-key tile of one wave, in registers, K and V rows in coalesced
 // order: lane l holds the 16-byte chunk l % 8 of rows l / 8 + 8 i.  Keys at or
@@ -273,10 +280,23 @@ __device__ __forceinline__ void decode_body(
 }
 
 // Log-sum-exp merge: one wave per (row, head), lane = d.  The partials of a
-// row are read in batches of kMergeBatch independent loads so that their
-// latencies overlap; the running (max, weight sum, weighted sum) is updated
-// per batch with the same rescaling as the online softmax.
-constexpr int kMergeBatch = 8;
+// row are read in batches of kMergeBatch (every load of a batch in flight at
+// once: one memory latency for up to 32 splits); the running (max, weight
+// sum, weighted sum) is updated per batch with the same rescaling as the
+// online softmax.
+constexpr int kMergeBatch = 32;
+
+// Max / sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
 
 // Short splits (at most kShortChunk keys): two-wave workgroups at three
 // waves per SIMD, i.e. more workgroups and so more loads in flight.
@@ -320,27 +340,27 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
   if (row >= rows) return;
   float big_m = kNegInf, tot = 0.0f, num = 0.0f;
   for (int s0 = 0; s0 < num_parts; s0 += kMergeBatch) {
-    float l[kMergeBatch], ov[kMergeBatch];
+    const int cnt = min(kMergeBatch, num_parts - s0);
+    // The batch's lse values (lane j holds part s0 + j) and O values (register
+    // j holds part s0 + j at d = lane) are all requested before any is used.
+    // Registers past the batch re-read its last part; their weight is 0.
+    const float l = lane < cnt ? lse_parts[static_cast<size_t>(s0 + lane) * rows + row] : kNegInf;
+    float ov[kMergeBatch];
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
-      const int sp = s0 + j;
-      const size_t pr = static_cast<size_t>(sp < num_parts ? sp : s0) * rows + row;
-      l[j] = sp < num_parts ? lse_parts[pr] : kNegInf;
+      const size_t pr = static_cast<size_t>(s0 + min(j, cnt - 1)) * rows + row;
       ov[j] = o_parts[pr * kHeadDim + lane];
     }
-    float bm = big_m;
-#pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) bm = fmaxf(bm, l[j]);
-    if (bm == kNegInf) continue;  // nothing but empty partials so far
-    const float rescale = fast_exp2((big_m - bm) * kLog2e);  // 0 when big_m = -inf
-    tot *= rescale;
+    const float bm = fmaxf(big_m, wave_max(l));
+    // (no branch on bm: the O loads above stay ahead of the reduction)
+    const float ref = bm > kNegInf ? bm : 0.0f;
+    const float rescale = fast_exp2((big_m - ref) * kLog2e);  // 0 while big_m = -inf
+    const float w = fast_exp2((l - ref) * kLog2e);             // 0 for empty parts and idle lanes
+    tot = tot * rescale + wave_sum(w);
     num *= rescale;
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      const float w = fast_exp2((l[j] - bm) * kLog2e);
-      tot += w;
-      num += w * ov[j];
-    }
+    for (int j = 0; j < kMergeBatch; ++j)
+      num += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j)) * ov[j];
     big_m = bm;
   }
   float out = 0.0f, out_lse = kNegInf;
@@ -354,20 +374,32 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
 
 }  // namespace
 
+// Keys of the longest range a decode query attends.
+static long long max_range(const DecodeLaunch& a) {
+  return a.window > 0 ? std::min<long long>(a.max_seqlen_k, a.window) : a.max_seqlen_k;
+}
+
+bool decode_merges_in_kernel(const DecodeLaunch& a) {
+  const long long keys_per_split = (max_range(a) + a.num_splits - 1) / a.num_splits;
+  return a.num_splits > 1 && keys_per_split <= kKeys && max_range(a) <= kDirectMaxKeys;
+}
+
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
-  const unsigned blocks = static_cast<unsigned>(a.batch) * a.num_kv_heads * a.num_splits;
-  const long long keys_per_split = (static_cast<long long>(a.max_seqlen_k) + a.num_splits - 1) / a.num_splits;
+  // Splits of at most 32 keys: the whole range in one workgroup per
+  // (sequence, KV head), o written directly.
+  const int splits = decode_merges_in_kernel(a) ? 1 : a.num_splits;
+  const unsigned blocks = static_cast<unsigned>(a.batch) * a.num_kv_heads * splits;
+  const long long keys_per_split = (max_range(a) + splits - 1) / splits;
   const bool short_chunks = keys_per_split <= kShortChunk;
-  const bool per_wave = a.num_splits >= kSplitPerWaveMin && !short_chunks;
+  const bool per_wave = splits >= kSplitPerWaveMin && !short_chunks;
   auto kernel = per_wave ? decode_kernel_ps : short_chunks ? decode_kernel_w2 : decode_kernel_w4;
-  const unsigned grid = per_wave ? static_cast<unsigned>(a.batch) * a.num_kv_heads * ((a.num_splits + 3) / 4)
-                                 : blocks;
+  const unsigned grid = per_wave ? static_cast<unsigned>(a.batch) * a.num_kv_heads * ((splits + 3) / 4) : blocks;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(per_wave || !short_chunks ? 256 : 128), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.sinks, a.cu_seqlens_k, a.batch,
                      a.num_q_heads, a.num_kv_heads, group, a.window, a.softmax_scale * kLog2e,
-                     a.num_splits, static_cast<uint16_t*>(a.o), a.lse, a.o_part, a.lse_part);
+                     splits, static_cast<uint16_t*>(a.o), a.lse, a.o_part, a.lse_part);
   return hipGetLastError();
 }
 

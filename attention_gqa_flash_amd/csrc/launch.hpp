@@ -27,8 +27,8 @@ struct DecodeLaunch {
   const int32_t* cu_seqlens_k;
   int batch, max_seqlen_k, num_q_heads, num_kv_heads, window, num_splits;
   float softmax_scale;
-  void* o;          // bf16 output when num_splits == 1
-  float* lse;       // optional, num_splits == 1
+  void* o;          // bf16 output when num_splits == 1 or merged in the kernel
+  float* lse;       // optional, likewise
   float* o_part;    // fp32 partials when num_splits > 1
   float* lse_part;
 };
@@ -43,6 +43,9 @@ struct MergeLaunch {
 
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
+// True when launch_decode writes o (and lse) itself although num_splits > 1
+// (splits of at most 32 keys are evaluated as one range): no merge follows.
+bool decode_merges_in_kernel(const DecodeLaunch& a);
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream);
 
 // Device-side precondition checks (debug mode).  Bits of the flag word:

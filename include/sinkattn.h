@@ -131,8 +131,15 @@ SINKATTN_API size_t sinkattn_decode_workspace_bytes(int32_t batch, int32_t num_q
  *   num_splits     S >= 1: the key range of every sequence is cut into S
  *                  contiguous chunks of ceil(n / S) keys (trailing chunks may
  *                  be empty); chunk 0 holds the lowest positions and carries
- *                  the sink.  S > 1 writes fp32 partials to the workspace and
- *                  merges them with the log-sum-exp merge before returning.
+ *                  the sink.  With S > 1 each chunk's partial is normalised
+ *                  on its own, written to the workspace in fp32, and the
+ *                  partials are combined with the log-sum-exp merge
+ *                  (sinkattn_merge_lse) before returning.  The merge is
+ *                  exact, so every S gives the same result up to fp32
+ *                  rounding; when the chunks would hold at most 32 keys of a
+ *                  range of at most 1024 (window layers with many splits),
+ *                  the range is evaluated whole (as S = 1) and the workspace
+ *                  is not touched.
  *   workspace      device buffer of >= sinkattn_decode_workspace_bytes(...)
  *                  bytes when S > 1 (SINKATTN_ERR_WORKSPACE otherwise); may
  *                  be NULL when S == 1

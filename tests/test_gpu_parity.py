@@ -153,6 +153,31 @@ def test_decode_group_shapes(hq, hkv):
         assert_close_lse(lse, rl, "decode G=%d" % (hq // hkv))
 
 
+@pytest.mark.parametrize("hq,hkv", [(64, 8), (32, 1), (8, 8)])
+@pytest.mark.parametrize("window,splits", [(0, 4), (0, 64), (128, 32), (128, 200), (7, 3), (1, 2)])
+def test_decode_short_splits(hq, hkv, window, splits):
+    """Splits of at most 32 keys, which the library evaluates as one range
+    (the merge is exact): short caches, window layers, more splits than
+    keys, sinks of -inf on some heads and no sink tensor."""
+    lengths = [1, 2, 17, 32, 33, 64, 127, 128, 129, 500]
+    if window == 0:
+        lengths = [x for x in lengths if x <= 128]
+    nos = tuple(h for h in (0, 5, hq - 1) if h < hq)
+    d = inputs.make_decode(lengths, hq=hq, hkv=hkv, seed=window * 7 + splits + hq)
+    d.sinks[list(nos)] = -np.inf
+    qf, kf, vf = (inputs.bf16_bits_to_f32(x) for x in (d.q, d.k, d.v))
+    ro, rl = decode_ref(qf, kf, vf, d.cu_seqlens_k, d.sinks, window, d.scale)
+    o, lse = _decode_case(d, window, splits)
+    assert_close_out(o, ro, "short splits W=%d S=%d" % (window, splits))
+    assert_close_lse(lse, rl, "short splits")
+    q, k, v = (bf16_to_device(x) for x in (d.q, d.k, d.v))
+    o2 = binding.decode_splitkv(q, k, v, i32_to_device(d.cu_seqlens_k), max(d.lengths), None, window, d.scale,
+                                splits)
+    torch.cuda.synchronize()
+    ro2, _ = decode_ref(qf, kf, vf, d.cu_seqlens_k, None, window, d.scale)
+    assert_close_out(to_f64(o2), ro2, "short splits, no sinks")
+
+
 def test_decode_partials_match_oracle_partials():
     """Run decode with S = 4 and check the merged result against the oracle's
     own split partials merged on the CPU (sink in chunk 0 only)."""

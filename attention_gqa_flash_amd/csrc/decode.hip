@@ -45,8 +45,9 @@ constexpr int kSplitPerWaveMin = 4;
 constexpr int kDirectMaxKeys = 1024;
 
 // One 32-key tile of one wave, in registers, K and V rows in coalesced
-// order: lane l holds the 16-byte chunk l % 8 of rows l / 8 + 8 i.  Keys at or
-// beyond `end` read as zero.
+// order: lane l holds the 16-byte chunk l % 8 of rows l / 8 + 8 i.  Rows at or
+// beyond `end` (> k0) repeat row end - 1: their logits are masked to -inf, so
+// their weights are 0 and the (finite) V values drop out.
 struct TileRegs {
   u32x4_t k[4];
   u32x4_t v[4];
@@ -57,14 +58,10 @@ __device__ __forceinline__ void load_tile(TileRegs& t, const uint16_t* __restric
                                           int k0, int end, int lane) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int key = k0 + (lane >> 3) + 8 * i;
-    t.k[i] = zero_u32x4();
-    t.v[i] = zero_u32x4();
-    if (key < end) {
-      const size_t off = (static_cast<size_t>(base + key) * hkv + g) * kHeadDim + (lane & 7) * 8;
-      t.k[i] = load16_stream(k + off);
-      t.v[i] = load16_stream(v + off);
-    }
+    const int key = min(k0 + (lane >> 3) + 8 * i, end - 1);
+    const size_t off = (static_cast<size_t>(base + key) * hkv + g) * kHeadDim + (lane & 7) * 8;
+    t.k[i] = load16_stream(k + off);
+    t.v[i] = load16_stream(v + off);
   }
 }
 
@@ -116,25 +113,6 @@ __device__ __forceinline__ void decode_body(
   const bool col_ok = col < group;
   const int head = g * group + (col_ok ? col : 0);
 
-  bf16x8_t qreg[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    u32x4_t val = zero_u32x4();
-    if (col_ok) val = load16(q + (static_cast<size_t>(b) * hq + head) * kHeadDim + 16 * s + 8 * half);
-    qreg[s] = __builtin_bit_cast(bf16x8_t, val);
-  }
-
-  // The sink seeds split 0 only (its wave 0 when the waves share a split).
-  float m2 = kNegInf, lsum = 0.0f;
-  if (split == 0 && (kSplitPerWave || wave == 0) && sinks != nullptr && col_ok) {
-    const float z = sinks[head];
-    if (z > kNegInf) {
-      m2 = z * kLog2e;
-      lsum = half == 0 ? 1.0f : 0.0f;
-    }
-  }
-  f32x16_t acc[2] = {zero16(), zero16()};
-
   uint16_t* kt = reinterpret_cast<uint16_t*>(lds_buf) + wave * 2 * kKeys * kHeadDim;
   uint16_t* vt = kt + kKeys * kHeadDim;
   const int grp_lane = lane & 15;
@@ -142,11 +120,28 @@ __device__ __forceinline__ void decode_body(
   const int krow = key_of_row(col);
 
   // Register double buffering: the loads of the next tile of this wave are in
-  // flight while the current one is computed.
+  // flight while the current one is computed.  The first tile is requested
+  // before Q and the sink, so the three latencies overlap.
   TileRegs cur, nxt;
   constexpr int kStride = kSplitPerWave ? kKeys : kKeys * kDecWaves;
   int k0 = kSplitPerWave ? a : a + kKeys * wave;
   if (k0 < e) load_tile(cur, k, v, base, hkv, g, k0, e, lane);
+
+  bf16x8_t qreg[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    // (every lane loads; columns past the group repeat the group's first
+    // head: S columns are independent, and theirs are never written)
+    const u32x4_t val = load16(q + (static_cast<size_t>(b) * hq + head) * kHeadDim + 16 * s + 8 * half);
+    qreg[s] = __builtin_bit_cast(bf16x8_t, val);
+  }
+  // The sink belongs to split 0 only (its wave 0 when the waves share a
+  // split).  It is folded into the state after the keys (the order of the
+  // logits does not matter), so nothing waits for it before the loop.
+  float z = kNegInf;
+  if (split == 0 && (kSplitPerWave || wave == 0) && sinks != nullptr && col_ok) z = sinks[head];
+  float m2 = kNegInf, lsum = 0.0f;
+  f32x16_t acc[2] = {zero16(), zero16()};
 
   for (; k0 < e; k0 += kStride) {
     const int k1 = k0 + kStride;
@@ -212,6 +207,19 @@ __device__ __forceinline__ void decode_body(
       }
     }
     cur = nxt;
+  }
+
+  // The sink: one more logit z (already in natural-log units) with no value.
+  if (z > kNegInf) {
+    const float z2 = z * kLog2e;
+    const float m_new = fmaxf(m2, z2);
+    const float alpha = fast_exp2(m2 - m_new);  // 0 when no key was seen
+    lsum = lsum * alpha + (half == 0 ? fast_exp2(z2 - m_new) : 0.0f);
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    m2 = m_new;
   }
 
   const float den = pair_sum(lsum);

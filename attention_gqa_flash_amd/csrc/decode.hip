@@ -7,11 +7,15 @@
 // partial results are combined with the log-sum-exp merge that the running
 // (max, denominator) pair implies (the page does not print the formula).
 //
-// Decode kernel: one workgroup per (sequence, KV head, split).  The chunk of
-// keys is streamed once and applied to all G query heads of the KV head (the
-// G heads are the N columns of S^T = K Q^T).  Each of the 4 waves walks
-// every 4th 32-key tile of the chunk with its own online-softmax state; the
-// waves are merged through LDS at the end.  K and V rows are read with fully
+// Decode kernels: a wave streams keys of one KV head once and applies them to
+// all G query heads of that KV head (the G heads are the N columns of
+// S^T = K Q^T).  Workgroups: one per (sequence, KV head, split) whose 2 or 4
+// waves walk interleaved 32-key tiles of the chunk with their own online-
+// softmax states, merged through LDS at the end (decode_kernel_w2/_w4); one
+// per (sequence, KV head, 4 splits) with a split per wave (decode_kernel_ps);
+// or, with four or more splits, one per (sequence, split) with a wave per KV
+// head (decode_kernel_hw), so that a workgroup reads whole token rows of the
+// cache.  K and V rows are read with fully
 // coalesced 16-byte loads (8 lanes per 128-byte row; a key row of one head is
 // 128 contiguous bytes, rows are Hkv * 128 bytes apart), the next tile of a
 // wave is in flight while the current one is computed, and each tile passes
@@ -36,6 +40,13 @@ constexpr int kShortChunk = 1024;
 // against 5.5 with the waves interleaved; at S = 16, 512-key splits, the
 // two-wave interleaved kernel is 12% faster).
 constexpr int kSplitPerWaveMin = 4;
+// With at least kHeadPerWaveMinSplits splits of at least kHeadPerWaveMinKeys
+// keys over 4 to 8 KV heads, a workgroup is one (sequence, split) and its
+// waves are the KV heads (decode_kernel_hw): 64 x 8192 at S = 4 from 182 to
+// 167 us, 16 x 32768 at S = 32 from 180 to 171 us.  (Forcing four waves per
+// SIMD spills and runs 20-40% slower.)
+constexpr int kHeadPerWaveMinSplits = 4;
+constexpr int kHeadPerWaveMinKeys = 128;
 // Splits of at most kKeys keys over a range of at most kDirectMaxKeys keys
 // (window layers cut into many splits) are not formed: the merge of
 // normalised split partials is exact, so it equals attention over the whole
@@ -66,9 +77,14 @@ __device__ __forceinline__ void load_tile(TileRegs& t, const uint16_t* __restric
 }
 
 // kSplitPerWave: each wave owns one whole split (split = 4 * group of
-// splits + wave) and writes that split's partial itself; otherwise the waves
-// of the workgroup interleave over one split and merge through LDS.
-template <int kDecWaves, bool kSplitPerWave>
+// splits + wave) and writes that split's partial itself; kHeadPerWave: the
+// workgroup is one (sequence, split) and wave w takes KV head w of it, so the
+// waves together read whole 1 KB token rows (all KV heads) at about the same
+// time, which streams faster than 128-byte pieces 1 KB apart read by
+// separate workgroups (6.9 against 6.2 TB/s, measured with plain loads);
+// otherwise the waves of the workgroup interleave over one split and merge
+// through LDS.
+template <int kDecWaves, bool kSplitPerWave, bool kHeadPerWave = false>
 __device__ __forceinline__ void decode_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ sinks,
@@ -88,9 +104,13 @@ __device__ __forceinline__ void decode_body(
   const int col = lane & 31;   // query head within the group
   const int half = lane >> 5;
 
+  constexpr bool kOwnSplit = kSplitPerWave || kHeadPerWave;  // the wave streams its range alone
   int x = blockIdx.x;
   int split;
-  if (kSplitPerWave) {
+  if (kHeadPerWave) {
+    split = x % num_splits;
+    x = (x / num_splits) * hkv + wave;  // (sequence, KV head = wave)
+  } else if (kSplitPerWave) {
     const int n_sgroups = (num_splits + kDecWaves - 1) / kDecWaves;
     split = (x % n_sgroups) * kDecWaves + wave;
     x /= n_sgroups;
@@ -123,8 +143,8 @@ __device__ __forceinline__ void decode_body(
   // flight while the current one is computed.  The first tile is requested
   // before Q and the sink, so the three latencies overlap.
   TileRegs cur, nxt;
-  constexpr int kStride = kSplitPerWave ? kKeys : kKeys * kDecWaves;
-  int k0 = kSplitPerWave ? a : a + kKeys * wave;
+  constexpr int kStride = kOwnSplit ? kKeys : kKeys * kDecWaves;
+  int k0 = kOwnSplit ? a : a + kKeys * wave;
   if (k0 < e) load_tile(cur, k, v, base, hkv, g, k0, e, lane);
 
   bf16x8_t qreg[4];
@@ -139,7 +159,7 @@ __device__ __forceinline__ void decode_body(
   // split).  It is folded into the state after the keys (the order of the
   // logits does not matter), so nothing waits for it before the loop.
   float z = kNegInf;
-  if (split == 0 && (kSplitPerWave || wave == 0) && sinks != nullptr && col_ok) z = sinks[head];
+  if (split == 0 && (kOwnSplit || wave == 0) && sinks != nullptr && col_ok) z = sinks[head];
   float m2 = kNegInf, lsum = 0.0f;
   f32x16_t acc[2] = {zero16(), zero16()};
 
@@ -223,7 +243,7 @@ __device__ __forceinline__ void decode_body(
   }
 
   const float den = pair_sum(lsum);
-  if (kSplitPerWave) {
+  if (kOwnSplit) {
     // This wave's split alone: normalise and write its partial.
     if (split >= num_splits || !col_ok) return;
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
@@ -328,6 +348,17 @@ __global__ __launch_bounds__(256) void decode_kernel_ps(
                        lse, o_part, lse_part);
 }
 
+// Four or more splits over 4 to 8 KV heads: one workgroup per (sequence,
+// split), one wave per KV head.
+__global__ __launch_bounds__(512) void decode_kernel_hw(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ sinks, const int32_t* __restrict__ cu_seqlens_k, int batch, int hq, int hkv,
+    int group, int window, float scale_log2, int num_splits, uint16_t* __restrict__ o, float* __restrict__ lse,
+    float* __restrict__ o_part, float* __restrict__ lse_part) {
+  decode_body<8, false, true>(q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, group, window, scale_log2, num_splits, o,
+                              lse, o_part, lse_part);
+}
+
 // Long splits: four-wave workgroups at the compiler's own register budget
 // (two waves per SIMD; at three, S = 4 on 64 x 8192 would end on a
 // two-thirds-full round of workgroups).
@@ -400,6 +431,15 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   const unsigned blocks = static_cast<unsigned>(a.batch) * a.num_kv_heads * splits;
   const long long keys_per_split = (max_range(a) + splits - 1) / splits;
   const bool short_chunks = keys_per_split <= kShortChunk;
+  if (splits >= kHeadPerWaveMinSplits && a.num_kv_heads >= 4 && a.num_kv_heads <= 8 &&
+      keys_per_split >= kHeadPerWaveMinKeys) {
+    hipLaunchKernelGGL(decode_kernel_hw, dim3(static_cast<unsigned>(a.batch) * splits), dim3(64 * a.num_kv_heads), 0,
+                       stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), a.sinks, a.cu_seqlens_k, a.batch, a.num_q_heads,
+                       a.num_kv_heads, group, a.window, a.softmax_scale * kLog2e, splits,
+                       static_cast<uint16_t*>(a.o), a.lse, a.o_part, a.lse_part);
+    return hipGetLastError();
+  }
   const bool per_wave = splits >= kSplitPerWaveMin && !short_chunks;
   auto kernel = per_wave ? decode_kernel_ps : short_chunks ? decode_kernel_w2 : decode_kernel_w4;
   const unsigned grid = per_wave ? static_cast<unsigned>(a.batch) * a.num_kv_heads * ((splits + 3) / 4) : blocks;

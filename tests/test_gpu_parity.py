@@ -178,6 +178,21 @@ def test_decode_short_splits(hq, hkv, window, splits):
     assert_close_out(to_f64(o2), ro2, "short splits, no sinks")
 
 
+@pytest.mark.parametrize("hq,hkv", [(16, 4), (20, 5), (48, 6), (56, 7), (64, 8)])
+@pytest.mark.parametrize("splits", [4, 6, 13])
+def test_decode_one_wave_per_kv_head(hq, hkv, splits):
+    """Four or more splits of at least 128 keys over 4 to 8 KV heads: one
+    workgroup per (sequence, split), one wave per KV head; ragged lengths so
+    some splits are short or empty, and a -inf sink."""
+    d = inputs.make_decode([1, 200, 1500, 2600], hq=hq, hkv=hkv, seed=hq + splits)
+    d.sinks[1] = -np.inf
+    qf, kf, vf = (inputs.bf16_bits_to_f32(x) for x in (d.q, d.k, d.v))
+    ro, rl = decode_ref(qf, kf, vf, d.cu_seqlens_k, d.sinks, 0, d.scale)
+    o, lse = _decode_case(d, 0, splits)
+    assert_close_out(o, ro, "wave per head G=%d S=%d" % (hq // hkv, splits))
+    assert_close_lse(lse, rl, "wave per head")
+
+
 def test_decode_partials_match_oracle_partials():
     """Run decode with S = 4 and check the merged result against the oracle's
     own split partials merged on the CPU (sink in chunk 0 only)."""

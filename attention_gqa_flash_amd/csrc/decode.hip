@@ -47,6 +47,10 @@ constexpr int kSplitPerWaveMin = 4;
 // SIMD spills and runs 20-40% slower.)
 constexpr int kHeadPerWaveMinSplits = 4;
 constexpr int kHeadPerWaveMinKeys = 128;
+// Consecutive splits of a sequence share a decode_kernel_hw workgroup when
+// the launch would otherwise exceed about kHeadPerWaveTarget workgroups (two
+// per CU): 64 x 8192 at S = 16, 184 to 180 us.
+constexpr long long kHeadPerWaveTarget = 512;
 // Splits of at most kKeys keys over a range of at most kDirectMaxKeys keys
 // (window layers cut into many splits) are not formed: the merge of
 // normalised split partials is exact, so it equals attention over the whole
@@ -90,7 +94,7 @@ __device__ __forceinline__ void decode_body(
     const uint16_t* __restrict__ v, const float* __restrict__ sinks,
     const int32_t* __restrict__ cu_seqlens_k, int batch, int hq, int hkv, int group,
     int window, float scale_log2, int num_splits, uint16_t* __restrict__ o,
-    float* __restrict__ lse, float* __restrict__ o_part, float* __restrict__ lse_part) {
+    float* __restrict__ lse, float* __restrict__ o_part, float* __restrict__ lse_part, int splits_per_wg = 1) {
   // Wave-private K and V staging tiles (2 x 4 KiB per wave); the whole
   // buffer is reused for the cross-wave merge of up to 32 heads x 64 d per
   // wave (index (wave * group + head) * 64 + d).
@@ -107,9 +111,12 @@ __device__ __forceinline__ void decode_body(
   constexpr bool kOwnSplit = kSplitPerWave || kHeadPerWave;  // the wave streams its range alone
   int x = blockIdx.x;
   int split;
+  int split_stop = 0;  // kHeadPerWave: the workgroup's splits are [split, split_stop)
   if (kHeadPerWave) {
-    split = x % num_splits;
-    x = (x / num_splits) * hkv + wave;  // (sequence, KV head = wave)
+    const int n_sgroups = (num_splits + splits_per_wg - 1) / splits_per_wg;
+    split = (x % n_sgroups) * splits_per_wg;
+    split_stop = min(num_splits, split + splits_per_wg);
+    x = (x / n_sgroups) * hkv + wave;  // (sequence, KV head = wave)
   } else if (kSplitPerWave) {
     const int n_sgroups = (num_splits + kDecWaves - 1) / kDecWaves;
     split = (x % n_sgroups) * kDecWaves + wave;
@@ -126,9 +133,10 @@ __device__ __forceinline__ void decode_body(
   const int lo = window > 0 ? max(0, len - window) : 0;
   const int n = len - lo;
   const int chunk = n > 0 ? (n + num_splits - 1) / num_splits : 0;
+  auto split_end = [&](int sp) { return sp < num_splits ? min(len, lo + (sp + 1) * chunk) : len; };
   // (a wave past the last split gets an empty range and writes nothing)
   const int a = split < num_splits ? min(len, lo + split * chunk) : len;
-  const int e = split < num_splits ? min(len, lo + (split + 1) * chunk) : len;
+  int e = split_end(split);
 
   const bool col_ok = col < group;
   const int head = g * group + (col_ok ? col : 0);
@@ -163,10 +171,37 @@ __device__ __forceinline__ void decode_body(
   float m2 = kNegInf, lsum = 0.0f;
   f32x16_t acc[2] = {zero16(), zero16()};
 
-  for (; k0 < e; k0 += kStride) {
-    const int k1 = k0 + kStride;
-    if (k1 < e) load_tile(nxt, k, v, base, hkv, g, k1, e, lane);
-
+  // The sink: one more logit z (already in natural-log units) with no value.
+  auto fold_sink = [&]() {
+    if (z > kNegInf) {
+      const float z2 = z * kLog2e;
+      const float m_new = fmaxf(m2, z2);
+      const float alpha = fast_exp2(m2 - m_new);  // 0 when no key was seen
+      lsum = lsum * alpha + (half == 0 ? fast_exp2(z2 - m_new) : 0.0f);
+  #pragma unroll
+      for (int db = 0; db < 2; ++db)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      m2 = m_new;
+    }
+  };
+  // This wave's split sp alone: normalise and write its partial.
+  auto write_partial = [&](int sp, float den) {
+    if (sp >= num_splits || !col_ok) return;
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    const size_t prow = (static_cast<size_t>(sp) * batch + b) * hq + head;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = 32 * db + 8 * (r >> 2) + 4 * half + (r & 3);
+        o_part[prow * kHeadDim + d] = acc[db][r] * inv;
+      }
+    if (half == 0) lse_part[prow] = den > 0.0f ? (m2 + __log2f(den)) * kLn2 : kNegInf;
+  };
+  // One 32-key tile (keys k0 .. k0 + 31; those at or past `end` masked) into
+  // the wave's online-softmax state.
+  auto tile_step = [&](const TileRegs& cur, int k0, int end) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // previous tile's LDS reads are done
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -185,10 +220,10 @@ __device__ __forceinline__ void decode_body(
       sacc = mfma_32x32x16(a, qreg[s], sacc);
     }
 
-    if (k0 + kKeys > e) {
+    if (k0 + kKeys > end) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (k0 + key_of_reg(r, half) >= e) sacc[r] = kNegInf;
+        if (k0 + key_of_reg(r, half) >= end) sacc[r] = kNegInf;
     }
 
     float mx = sacc[0];
@@ -226,36 +261,47 @@ __device__ __forceinline__ void decode_body(
         acc[db] = mfma_32x32x16(av, pb[u], acc[db]);
       }
     }
+  };
+
+  if constexpr (kHeadPerWave) {
+    // The workgroup's splits one after another: the next split's first tile
+    // (it starts where this one ends) is loaded during this split's last, and
+    // each split's partial is written when it ends.
+    int sp = split;
+    while (true) {
+      for (; k0 < e; k0 += kKeys) {
+        const int k1 = k0 + kKeys;
+        if (k1 < e)
+          load_tile(nxt, k, v, base, hkv, g, k1, e, lane);
+        else if (sp + 1 < split_stop && e < split_end(sp + 1))
+          load_tile(nxt, k, v, base, hkv, g, e, split_end(sp + 1), lane);
+        tile_step(cur, k0, e);
+        cur = nxt;
+      }
+      fold_sink();
+      write_partial(sp, pair_sum(lsum));
+      if (++sp >= split_stop) return;
+      z = kNegInf;  // the sink belongs to split 0 only
+      m2 = kNegInf;
+      lsum = 0.0f;
+      acc[0] = zero16();
+      acc[1] = zero16();
+      k0 = e;
+      e = split_end(sp);
+    }
+  }
+
+  for (; k0 < e; k0 += kStride) {
+    const int k1 = k0 + kStride;
+    if (k1 < e) load_tile(nxt, k, v, base, hkv, g, k1, e, lane);
+    tile_step(cur, k0, e);
     cur = nxt;
   }
 
-  // The sink: one more logit z (already in natural-log units) with no value.
-  if (z > kNegInf) {
-    const float z2 = z * kLog2e;
-    const float m_new = fmaxf(m2, z2);
-    const float alpha = fast_exp2(m2 - m_new);  // 0 when no key was seen
-    lsum = lsum * alpha + (half == 0 ? fast_exp2(z2 - m_new) : 0.0f);
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-    m2 = m_new;
-  }
-
+  fold_sink();
   const float den = pair_sum(lsum);
-  if (kOwnSplit) {
-    // This wave's split alone: normalise and write its partial.
-    if (split >= num_splits || !col_ok) return;
-    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    const size_t prow = (static_cast<size_t>(split) * batch + b) * hq + head;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int d = 32 * db + 8 * (r >> 2) + 4 * half + (r & 3);
-        o_part[prow * kHeadDim + d] = acc[db][r] * inv;
-      }
-    if (half == 0) lse_part[prow] = den > 0.0f ? (m2 + __log2f(den)) * kLn2 : kNegInf;
+  if constexpr (kOwnSplit) {
+    write_partial(split, den);
     return;
   }
 
@@ -354,9 +400,9 @@ __global__ __launch_bounds__(512) void decode_kernel_hw(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ sinks, const int32_t* __restrict__ cu_seqlens_k, int batch, int hq, int hkv,
     int group, int window, float scale_log2, int num_splits, uint16_t* __restrict__ o, float* __restrict__ lse,
-    float* __restrict__ o_part, float* __restrict__ lse_part) {
+    float* __restrict__ o_part, float* __restrict__ lse_part, int splits_per_wg) {
   decode_body<8, false, true>(q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, group, window, scale_log2, num_splits, o,
-                              lse, o_part, lse_part);
+                              lse, o_part, lse_part, splits_per_wg);
 }
 
 // Long splits: four-wave workgroups at the compiler's own register budget
@@ -433,11 +479,14 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
   const bool short_chunks = keys_per_split <= kShortChunk;
   if (splits >= kHeadPerWaveMinSplits && a.num_kv_heads >= 4 && a.num_kv_heads <= 8 &&
       keys_per_split >= kHeadPerWaveMinKeys) {
-    hipLaunchKernelGGL(decode_kernel_hw, dim3(static_cast<unsigned>(a.batch) * splits), dim3(64 * a.num_kv_heads), 0,
-                       stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+    const long long units = static_cast<long long>(a.batch) * splits;
+    const int per_wg = static_cast<int>(std::max<long long>(1, std::min<long long>(splits, units / kHeadPerWaveTarget)));
+    const long long groups = static_cast<long long>(a.batch) * ((splits + per_wg - 1) / per_wg);
+    hipLaunchKernelGGL(decode_kernel_hw, dim3(static_cast<unsigned>(groups)), dim3(64 * a.num_kv_heads), 0, stream,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), a.sinks, a.cu_seqlens_k, a.batch, a.num_q_heads,
                        a.num_kv_heads, group, a.window, a.softmax_scale * kLog2e, splits,
-                       static_cast<uint16_t*>(a.o), a.lse, a.o_part, a.lse_part);
+                       static_cast<uint16_t*>(a.o), a.lse, a.o_part, a.lse_part, per_wg);
     return hipGetLastError();
   }
   const bool per_wave = splits >= kSplitPerWaveMin && !short_chunks;

@@ -193,6 +193,21 @@ def test_decode_one_wave_per_kv_head(hq, hkv, splits):
     assert_close_lse(lse, rl, "wave per head")
 
 
+def test_decode_one_wave_per_kv_head_several_splits_per_workgroup():
+    """Enough (sequence, split) pairs that consecutive splits share a
+    workgroup (40 x 32 here): partials of every split, empty ones included,
+    merged."""
+    rng = np.random.default_rng(41)
+    lengths = [4200 if i % 3 == 0 else int(rng.integers(1, 5000)) for i in range(40)]
+    d = inputs.make_decode(lengths, hq=16, hkv=4, seed=41)
+    qf, kf, vf = (inputs.bf16_bits_to_f32(x) for x in (d.q, d.k, d.v))
+    ro, rl = decode_ref(qf, kf, vf, d.cu_seqlens_k, d.sinks, 0, d.scale)
+    for splits in (32, 27):
+        o, lse = _decode_case(d, 0, splits)
+        assert_close_out(o, ro, "several splits per workgroup S=%d" % splits)
+        assert_close_lse(lse, rl, "several splits per workgroup")
+
+
 def test_decode_partials_match_oracle_partials():
     """Run decode with S = 4 and check the merged result against the oracle's
     own split partials merged on the CPU (sink in chunk 0 only)."""

@@ -187,10 +187,11 @@ def test_decode_one_wave_per_kv_head(hq, hkv, splits):
     d = inputs.make_decode([1, 200, 1500, 2600], hq=hq, hkv=hkv, seed=hq + splits)
     d.sinks[1] = -np.inf
     qf, kf, vf = (inputs.bf16_bits_to_f32(x) for x in (d.q, d.k, d.v))
-    ro, rl = decode_ref(qf, kf, vf, d.cu_seqlens_k, d.sinks, 0, d.scale)
-    o, lse = _decode_case(d, 0, splits)
-    assert_close_out(o, ro, "wave per head G=%d S=%d" % (hq // hkv, splits))
-    assert_close_lse(lse, rl, "wave per head")
+    for window in (0, 1200):  # 1200 keys: >= 128 per split at S = 4 and 6, not at 13
+        ro, rl = decode_ref(qf, kf, vf, d.cu_seqlens_k, d.sinks, window, d.scale)
+        o, lse = _decode_case(d, window, splits)
+        assert_close_out(o, ro, "wave per head G=%d S=%d W=%d" % (hq // hkv, splits, window))
+        assert_close_lse(lse, rl, "wave per head")
 
 
 def test_decode_one_wave_per_kv_head_several_splits_per_workgroup():

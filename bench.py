@@ -130,6 +130,7 @@ def cpu_baseline() -> dict:
         t_dec = time.perf_counter() - t0
     dec_gbs = decode_bytes([DEC_CTX] * DEC_BATCH, 0) / t_dec / 1e9
     value = 100.0 * 0.5 * (pre_tflops / PEAK_BF16_TFLOPS + dec_gbs / PEAK_HBM_GBS)
+    others = _cpu_other_configs(cores)
     return {
         "value": value, "unit": "% of MI355X peak (same formula as value)", "cores": cores, "kind": "oracle",
         "sample": "one whole step: prefill 1 x 8192 tokens (causal + 128-window layers) and decode 64 x 8192 "
@@ -137,7 +138,64 @@ def cpu_baseline() -> dict:
                   "for prefill, excluded for decode)" % cores,
         "prefill_tflops_f64": pre_tflops, "prefill_seconds": t_pre,
         "decode_gbs_f64": dec_gbs, "decode_seconds": t_dec,
+        "other_configs": others,
     }
+
+
+def _cpu_other_configs(cores: int) -> dict:
+    """The oracle on the other workloads, each on a bounded sample: the whole
+    tiny prefill; 2 of the 16 long-decode sequences (both layers); for the
+    ragged prefill, 3 of its sequences (the longest, a middle and a short
+    one; all rows of the two shorter, 256 evenly spaced rows of the
+    longest), both layers.  Rates are float64 GFLOP/s (or GB/s of the
+    algorithmic bytes); `seconds_full` extrapolates to the whole workload."""
+    import numpy as np
+
+    from attention_gqa_flash_amd import inputs
+    from oracle import decode_ref, prefill_varlen_ref
+
+    out = {}
+    p = inputs.tiny_prefill(seed=0)
+    qf, kf, vf = (inputs.bf16_bits_to_f32(x) for x in (p.q, p.k, p.v))
+    t0 = time.perf_counter()
+    prefill_varlen_ref(qf, kf, vf, p.sinks, p.cu_seqlens, 0, p.scale)
+    t = time.perf_counter() - t0
+    f = prefill_flops([256], 0, hq=4)
+    out["tiny_prefill_causal"] = {"seconds": t, "gflops_f64": f / t / 1e9, "sample": "whole workload, 1 process"}
+
+    d = inputs.make_decode([32768] * 2, HQ, HKV, D, seed=0, sink_std=math.sqrt(2.0))
+    qf, kf, vf = (inputs.bf16_bits_to_f32(x) for x in (d.q, d.k, d.v))
+    for window in (0, WINDOW):
+        t0 = time.perf_counter()
+        decode_ref(qf, kf, vf, d.cu_seqlens_k, d.sinks, window, d.scale)
+        t = time.perf_counter() - t0
+        b = decode_bytes([32768] * 2, window)
+        out["long_decode_%s" % ("full" if window == 0 else "w128")] = {
+            "seconds": t, "gbs_f64": b / t / 1e9, "seconds_full": t * 8,
+            "sample": "2 of 16 sequences x 32768 keys, 1 process"}
+
+    lengths = sorted(inputs.ragged_lengths(np.random.default_rng(0), 32))
+    pick = [lengths[-1], lengths[len(lengths) // 2], lengths[4]]
+    p = inputs.make_prefill(pick, HQ, HKV, D, seed=0)
+    qf, kf, vf = (inputs.bf16_bits_to_f32(x) for x in (p.q, p.k, p.v))
+    rows = list(np.linspace(0, pick[0] - 1, 256).astype(np.int64)) + list(range(pick[0], sum(pick)))
+    total_causal = prefill_flops(lengths, 0)
+    total_window = prefill_flops(lengths, WINDOW)
+    for window, total in ((0, total_causal), (WINDOW, total_window)):
+        # flop of exactly the sampled rows
+        fl = 0.0
+        for r in rows:
+            seq = 0 if r < pick[0] else (1 if r < pick[0] + pick[1] else 2)
+            i = r - sum(pick[:seq])
+            fl += 4.0 * D * HQ * (min(i + 1, window) if window > 0 else i + 1)
+        t0 = time.perf_counter()
+        prefill_varlen_ref(qf, kf, vf, p.sinks, p.cu_seqlens, window, p.scale, rows=rows, workers=cores)
+        t = time.perf_counter() - t0
+        out["ragged_prefill_%s" % ("causal" if window == 0 else "w128")] = {
+            "seconds": t, "gflops_f64": fl / t / 1e9, "seconds_full": total / (fl / t),
+            "sample": "%d rows of sequences of %s tokens, %d processes (pool start-up included)"
+                      % (len(rows), pick, cores)}
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -32,6 +32,7 @@ distributions as the host-generated parity inputs) to keep start-up short.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import math
@@ -277,7 +278,7 @@ class _ClockSampler:
         def run():
             while not self._stop.is_set():
                 self._sample()
-                self._stop.wait(0.005)
+                self._stop.wait(0.02)
 
         self._thread = threading.Thread(target=run, daemon=True)
         self._thread.start()
@@ -300,7 +301,7 @@ def _stats(ms_list):
     import numpy as np
     a = np.asarray(ms_list, dtype=np.float64)
     return {"median_ms": float(np.median(a)), "min_ms": float(a.min()), "mean_ms": float(a.mean()),
-            "reps": int(a.size)}
+            "max_ms": float(a.max()), "reps": int(a.size)}
 
 
 def gpu_bench(steps: int, warmup: int, extras: bool = True) -> dict:
@@ -333,9 +334,12 @@ def gpu_bench(steps: int, warmup: int, extras: bool = True) -> dict:
 
     ev = {name: [] for name in ("causal", "window", "decode")}
 
+    # events for every timed step exist before the timed loop starts
+    all_marks = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+
     def step(i, record):
         s = sets[i % 3]
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        marks = all_marks[i] if record else None
         if record:
             marks[0].record()
         binding.prefill_varlen(s["q"], s["k"], s["v"], s["sinks"], s["cu"], PREFILL_LEN, 0, scale, out=s["o"])
@@ -355,13 +359,20 @@ def gpu_bench(steps: int, warmup: int, extras: bool = True) -> dict:
     for i in range(warmup):
         step(i, False)
     torch.cuda.synchronize()
+    # No garbage-collector pass inside the timed loop: a full collection can
+    # hold the host thread long enough for the GPU to run out of queued work.
+    gc.collect()
+    gc.disable()
     clock = _ClockSampler(pci_bus)
-    with clock:
-        t0 = time.perf_counter()
-        for i in range(steps):
-            step(i, True)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+    try:
+        with clock:
+            t0 = time.perf_counter()
+            for i in range(steps):
+                step(i, True)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+    finally:
+        gc.enable()
 
     leg = {name: _stats([a.elapsed_time(b) for a, b in ev[name]]) for name in ev}
     t_causal, t_window, t_decode = (leg[n]["mean_ms"] for n in ("causal", "window", "decode"))
@@ -557,7 +568,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the other workloads and the bandwidth reference (the step only)")

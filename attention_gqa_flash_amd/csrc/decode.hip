@@ -13,9 +13,11 @@
 // waves walk interleaved 32-key tiles of the chunk with their own online-
 // softmax states, merged through LDS at the end (decode_kernel_w2/_w4); one
 // per (sequence, KV head, 4 splits) with a split per wave (decode_kernel_ps);
-// or, with four or more splits, one per (sequence, split) with a wave per KV
-// head (decode_kernel_hw), so that a workgroup reads whole token rows of the
-// cache.  K and V rows are read with fully
+// one per (sequence, pair of KV heads, split) with four interleaved waves
+// per head (decode_kernel_w8p, one long split); or, with four or more
+// splits, one per (sequence, split) with a wave per KV head
+// (decode_kernel_hw).  The last two read adjacent pieces of the same token
+// rows of the cache from one workgroup, which streams faster.  K and V rows are read with fully
 // coalesced 16-byte loads (8 lanes per 128-byte row; a key row of one head is
 // 128 contiguous bytes, rows are Hkv * 128 bytes apart), the next tile of a
 // wave is in flight while the current one is computed, and each tile passes
@@ -88,7 +90,7 @@ __device__ __forceinline__ void load_tile(TileRegs& t, const uint16_t* __restric
 // separate workgroups (6.9 against 6.2 TB/s, measured with plain loads);
 // otherwise the waves of the workgroup interleave over one split and merge
 // through LDS.
-template <int kDecWaves, bool kSplitPerWave, bool kHeadPerWave = false>
+template <int kDecWaves, bool kSplitPerWave, bool kHeadPerWave = false, int kHeadsPerWG = 1>
 __device__ __forceinline__ void decode_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ sinks,
@@ -109,6 +111,12 @@ __device__ __forceinline__ void decode_body(
   const int half = lane >> 5;
 
   constexpr bool kOwnSplit = kSplitPerWave || kHeadPerWave;  // the wave streams its range alone
+  // kHeadsPerWG > 1 (interleaved mode): the workgroup serves kHeadsPerWG
+  // adjacent KV heads; wave w takes head w % kHeadsPerWG and is the
+  // (w / kHeadsPerWG)-th of the kIl waves interleaving over that head's keys.
+  constexpr int kIl = kDecWaves / kHeadsPerWG;
+  const int hsub = wave % kHeadsPerWG;
+  const int wl = wave / kHeadsPerWG;
   int x = blockIdx.x;
   int split;
   int split_stop = 0;  // kHeadPerWave: the workgroup's splits are [split, split_stop)
@@ -124,6 +132,10 @@ __device__ __forceinline__ void decode_body(
   } else {
     split = x % num_splits;
     x /= num_splits;
+    if (kHeadsPerWG > 1) {
+      const int pairs = hkv / kHeadsPerWG;
+      x = (x / pairs) * hkv + (x % pairs) * kHeadsPerWG + hsub;
+    }
   }
   const int g = x % hkv;
   const int b = x / hkv;
@@ -151,8 +163,8 @@ __device__ __forceinline__ void decode_body(
   // flight while the current one is computed.  The first tile is requested
   // before Q and the sink, so the three latencies overlap.
   TileRegs cur, nxt;
-  constexpr int kStride = kOwnSplit ? kKeys : kKeys * kDecWaves;
-  int k0 = kOwnSplit ? a : a + kKeys * wave;
+  constexpr int kStride = kOwnSplit ? kKeys : kKeys * kIl;
+  int k0 = kOwnSplit ? a : a + kKeys * wl;
   if (k0 < e) load_tile(cur, k, v, base, hkv, g, k0, e, lane);
 
   bf16x8_t qreg[4];
@@ -167,7 +179,7 @@ __device__ __forceinline__ void decode_body(
   // split).  It is folded into the state after the keys (the order of the
   // logits does not matter), so nothing waits for it before the loop.
   float z = kNegInf;
-  if (split == 0 && (kOwnSplit || wave == 0) && sinks != nullptr && col_ok) z = sinks[head];
+  if (split == 0 && (kOwnSplit || wl == 0) && sinks != nullptr && col_ok) z = sinks[head];
   float m2 = kNegInf, lsum = 0.0f;
   f32x16_t acc[2] = {zero16(), zero16()};
 
@@ -323,17 +335,19 @@ __device__ __forceinline__ void decode_body(
   }
   __syncthreads();
 
-  for (int idx = tid; idx < group * kHeadDim; idx += 64 * kDecWaves) {
-    const int hc = idx / kHeadDim;
+  for (int idx = tid; idx < kHeadsPerWG * group * kHeadDim; idx += 64 * kDecWaves) {
+    const int hs = idx / (group * kHeadDim);  // KV head within the workgroup
+    const int hc = (idx / kHeadDim) % group;
     const int d = idx % kHeadDim;
     float big_m = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) big_m = fmaxf(big_m, red_m[w][hc]);
+    for (int i = 0; i < kIl; ++i) big_m = fmaxf(big_m, red_m[hs + kHeadsPerWG * i][hc]);
     float out = 0.0f, out_lse = kNegInf;
     if (big_m > kNegInf) {
       float num = 0.0f, tot = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) {
+      for (int i = 0; i < kIl; ++i) {
+        const int w = hs + kHeadsPerWG * i;
         const float sc = fast_exp2(red_m[w][hc] - big_m);
         tot += sc * red_l[w][hc];
         num += sc * red_o[(w * group + hc) * kHeadDim + d];
@@ -341,7 +355,7 @@ __device__ __forceinline__ void decode_body(
       out = num / tot;
       out_lse = (big_m + __log2f(tot)) * kLn2;
     }
-    const int h = g * group + hc;
+    const int h = (g - hsub + hs) * group + hc;
     if (num_splits == 1) {
       o[(static_cast<size_t>(b) * hq + h) * kHeadDim + d] = to_bf16_bits(out);
       if (lse != nullptr && d == 0) lse[static_cast<size_t>(b) * hq + h] = out_lse;
@@ -403,6 +417,20 @@ __global__ __launch_bounds__(512) void decode_kernel_hw(
     float* __restrict__ o_part, float* __restrict__ lse_part, int splits_per_wg) {
   decode_body<8, false, true>(q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, group, window, scale_log2, num_splits, o,
                               lse, o_part, lse_part, splits_per_wg);
+}
+
+// One split of more than kShortChunk keys over an even number of KV heads:
+// eight-wave workgroups serving two adjacent KV heads with four interleaved
+// waves each, so that a workgroup reads 256 contiguous bytes of every token
+// row it touches (a plain-load probe: 6.4-6.6 TB/s against 6.0-6.2 for one
+// head per workgroup; 64 x 8192 at S = 1 from 180 to 165 us).
+__global__ __launch_bounds__(512) void decode_kernel_w8p(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ sinks, const int32_t* __restrict__ cu_seqlens_k, int batch, int hq, int hkv,
+    int group, int window, float scale_log2, int num_splits, uint16_t* __restrict__ o, float* __restrict__ lse,
+    float* __restrict__ o_part, float* __restrict__ lse_part) {
+  decode_body<8, false, false, 2>(q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, group, window, scale_log2,
+                                  num_splits, o, lse, o_part, lse_part);
 }
 
 // Long splits: four-wave workgroups at the compiler's own register budget
@@ -487,6 +515,14 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
                        static_cast<const uint16_t*>(a.v), a.sinks, a.cu_seqlens_k, a.batch, a.num_q_heads,
                        a.num_kv_heads, group, a.window, a.softmax_scale * kLog2e, splits,
                        static_cast<uint16_t*>(a.o), a.lse, a.o_part, a.lse_part, per_wg);
+    return hipGetLastError();
+  }
+  if (splits == 1 && !short_chunks && a.num_kv_heads % 2 == 0) {
+    hipLaunchKernelGGL(decode_kernel_w8p, dim3(static_cast<unsigned>(a.batch) * (a.num_kv_heads / 2)), dim3(512), 0,
+                       stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), a.sinks, a.cu_seqlens_k, a.batch, a.num_q_heads,
+                       a.num_kv_heads, group, a.window, a.softmax_scale * kLog2e, splits,
+                       static_cast<uint16_t*>(a.o), a.lse, a.o_part, a.lse_part);
     return hipGetLastError();
   }
   const bool per_wave = splits >= kSplitPerWaveMin && !short_chunks;

@@ -209,6 +209,21 @@ def test_decode_one_wave_per_kv_head_several_splits_per_workgroup():
         assert_close_lse(lse, rl, "several splits per workgroup")
 
 
+@pytest.mark.parametrize("hq,hkv", [(16, 2), (24, 6), (64, 8), (40, 10)])
+def test_decode_single_split_kv_head_pairs(hq, hkv):
+    """One split of more than 1024 keys over an even number of KV heads:
+    eight-wave workgroups serving two KV heads each (four interleaved waves
+    per head, merged through LDS); full and 2000-key window layers."""
+    d = inputs.make_decode([1, 1100, 3000, 5000], hq=hq, hkv=hkv, seed=hq * 3 + hkv)
+    d.sinks[hq - 1] = -np.inf
+    qf, kf, vf = (inputs.bf16_bits_to_f32(x) for x in (d.q, d.k, d.v))
+    for window in (0, 2000):
+        ro, rl = decode_ref(qf, kf, vf, d.cu_seqlens_k, d.sinks, window, d.scale)
+        o, lse = _decode_case(d, window, 1)
+        assert_close_out(o, ro, "head pairs G=%d W=%d" % (hq // hkv, window))
+        assert_close_lse(lse, rl, "head pairs")
+
+
 def test_decode_partials_match_oracle_partials():
     """Run decode with S = 4 and check the merged result against the oracle's
     own split partials merged on the CPU (sink in chunk 0 only)."""

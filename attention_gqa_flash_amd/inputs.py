@@ -117,6 +117,53 @@ def make_decode(lengths, hq: int, hkv: int, d: int = 64, seed: int = 0,
     return DecodeInputs(q, k, v, sinks.astype(np.float32), _cu(lengths), scale, lengths)
 
 
+@dataclass
+class DecodeFp8Inputs:
+    q: np.ndarray            # uint16 bf16 bits [B, Hq, D]
+    k: np.ndarray            # uint8 E4M3 codes [Tk, Hkv, D]
+    v: np.ndarray            # uint8 E4M3 codes [Tk, Hkv, D]
+    k_scale: float           # K = k_scale * e4m3(k)
+    v_scale: float
+    sinks: np.ndarray        # float32 [Hq]
+    cu_seqlens_k: np.ndarray  # int32 [B+1]
+    scale: float
+    lengths: list = field(default_factory=list)
+
+    @property
+    def max_seqlen(self) -> int:
+        return int(max(self.lengths)) if self.lengths else 0
+
+
+def to_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """float32 -> E4M3 codes (uint8), round to nearest even, clamped to the
+    largest finite magnitude (448) first.  Encoding is done by torch's
+    float8_e4m3fn cast (input generation only)."""
+    import torch
+    x = np.clip(np.asarray(x, dtype=np.float32), -448.0, 448.0)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def make_decode_fp8(lengths, hq: int, hkv: int, d: int = 64, seed: int = 0,
+                    scale: float = 0.125, sink_std: float = 1.0,
+                    k_scale: float = 1.0 / 16, v_scale: float = 1.0 / 16,
+                    rng: Optional[np.random.Generator] = None) -> DecodeFp8Inputs:
+    """Decode inputs with an E4M3 KV cache: K and V are N(0,1) values divided
+    by their per-tensor scale and rounded to E4M3 (the cache then holds
+    k_scale * e4m3(code) ~ N(0,1) to within the format's precision).  Draw
+    order as make_decode: q, k, v, sinks."""
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    lengths = [int(x) for x in lengths]
+    tk = int(sum(lengths))
+    q = _normal_bf16(rng, (len(lengths), hq, d))
+    k = to_e4m3_codes(rng.standard_normal(size=(tk, hkv, d), dtype=np.float32) / np.float32(k_scale))
+    v = to_e4m3_codes(rng.standard_normal(size=(tk, hkv, d), dtype=np.float32) / np.float32(v_scale))
+    sinks = rng.standard_normal(size=hq, dtype=np.float32)
+    if sink_std != 1.0:
+        sinks = sinks * np.float32(sink_std)
+    return DecodeFp8Inputs(q, k, v, float(k_scale), float(v_scale), sinks.astype(np.float32), _cu(lengths), scale,
+                           lengths)
+
+
 def ragged_lengths(rng: np.random.Generator, n: int = 32, lo: int = 128, hi: int = 32768):
     """Log-uniform lengths round(exp(U[ln lo, ln hi]))."""
     u = rng.uniform(math.log(lo), math.log(hi), size=n)

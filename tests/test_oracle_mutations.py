@@ -5,7 +5,9 @@ the copy (never in the repository) and checks that the pin suite
 (tests/test_oracle_pins.py) then fails.  The mistakes: the sink multiplied by
 the softmax scale (in the max or in the denominator), the sink dropped, the
 window one key too wide, the sink in every split, the decode window one key
-too wide, the wrong GQA grouping, a base-2 lse, an unweighted merge.
+too wide, the wrong GQA grouping, a base-2 lse, an unweighted merge; and
+for the FP8 oracle (checked by tests/test_oracle_fp8.py): exponent bias 8
+instead of 7, subnormals scaled like normals, the two scales swapped.
 """
 
 import os
@@ -30,17 +32,32 @@ MUTATIONS = [
 ]
 
 
-@pytest.mark.parametrize("old,new", MUTATIONS, ids=[str(i) for i in range(len(MUTATIONS))])
-def test_pins_catch_planted_mistake(tmp_path, old, new):
+FP8_MUTATIONS = [
+    ("np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64))", "np.ldexp(1.0 + m / 8.0, (e - 8).astype(np.int64))"),
+    ("subnormal = np.ldexp(m / 8.0, -6)", "subnormal = np.ldexp(1.0 + m / 8.0, -7)"),
+    ("k = float(k_scale) * e4m3_to_float64(k_codes)", "k = float(v_scale) * e4m3_to_float64(k_codes)"),
+]
+
+
+def _run_pins(tmp_path, module, old, new, pin_file):
     for sub in ("oracle", "tests", "attention_gqa_flash_amd"):
         shutil.copytree(os.path.join(ROOT, sub), tmp_path / sub,
                         ignore=shutil.ignore_patterns("__pycache__", "*.so", "csrc"))
-    src = tmp_path / "oracle" / "sink_attention.py"
+    src = tmp_path / "oracle" / module
     text = src.read_text()
     assert old in text, "mutation anchor not found in the oracle"
     src.write_text(text.replace(old, new))
     proc = subprocess.run(
-        [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-         "tests/test_oracle_pins.py"],
+        [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", pin_file],
         cwd=tmp_path, capture_output=True, text=True, timeout=600)
     assert proc.returncode != 0, "pins did not catch: %s -> %s\n%s" % (old, new, proc.stdout[-2000:])
+
+
+@pytest.mark.parametrize("old,new", MUTATIONS, ids=[str(i) for i in range(len(MUTATIONS))])
+def test_pins_catch_planted_mistake(tmp_path, old, new):
+    _run_pins(tmp_path, "sink_attention.py", old, new, "tests/test_oracle_pins.py")
+
+
+@pytest.mark.parametrize("old,new", FP8_MUTATIONS, ids=["fp8_%d" % i for i in range(len(FP8_MUTATIONS))])
+def test_fp8_pins_catch_planted_mistake(tmp_path, old, new):
+    _run_pins(tmp_path, "fp8.py", old, new, "tests/test_oracle_fp8.py")

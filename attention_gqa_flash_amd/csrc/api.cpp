@@ -153,16 +153,20 @@ size_t sinkattn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32
   return round_up(rows * head_dim * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
 }
 
-sinkattn_status sinkattn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
-                                        const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_k,
-                                        const float* sinks, int32_t num_q_heads, int32_t num_kv_heads,
-                                        int32_t head_dim, int32_t window, float softmax_scale,
-                                        int32_t num_splits, void* workspace, size_t workspace_bytes, void* o,
-                                        float* lse, void* stream) {
+// Decode over a bf16 cache, or (fp8) an E4M3 cache with per-tensor scales.
+static sinkattn_status decode_common(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_k,
+                                     const float* sinks, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t window, float softmax_scale, int32_t num_splits, void* workspace,
+                                     size_t workspace_bytes, void* o, float* lse, void* stream, bool fp8,
+                                     float k_scale, float v_scale) {
   if (batch < 0 || max_seqlen_k < 0) return fail(SINKATTN_ERR_INVALID_ARG, "batch and max_seqlen_k must be >= 0");
   sinkattn_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
   if (st != SINKATTN_OK) return st;
   if ((st = check_scale(softmax_scale)) != SINKATTN_OK) return st;
+  if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) && v_scale > 0.0f))
+    return fail(SINKATTN_ERR_INVALID_ARG, "k_scale and v_scale must be finite and > 0 (got %g, %g)", k_scale,
+                v_scale);
   if (num_splits < 1 || num_splits > 65536)
     return fail(SINKATTN_ERR_INVALID_ARG, "num_splits must be in [1, 65536] (got %d)", num_splits);
   if (num_q_heads / num_kv_heads > sinkattn::decode_max_group())
@@ -189,12 +193,18 @@ sinkattn_status sinkattn_decode_splitkv(const void* q, const void* k_cache, cons
     int total_kv = 0;
     if ((st = check_result(s, &total_kv)) != SINKATTN_OK) return st;
     const size_t kvn = static_cast<size_t>(total_kv) * num_kv_heads * head_dim;
-    if ((st = hip_queue(sinkattn::check_bf16(k_cache, kvn, sinkattn::kCheckK, s))) != SINKATTN_OK) return st;
-    if ((st = hip_queue(sinkattn::check_bf16(v_cache, kvn, sinkattn::kCheckV, s))) != SINKATTN_OK) return st;
+    if (fp8) {
+      if ((st = hip_queue(sinkattn::check_e4m3(k_cache, kvn, sinkattn::kCheckK, s))) != SINKATTN_OK) return st;
+      if ((st = hip_queue(sinkattn::check_e4m3(v_cache, kvn, sinkattn::kCheckV, s))) != SINKATTN_OK) return st;
+    } else {
+      if ((st = hip_queue(sinkattn::check_bf16(k_cache, kvn, sinkattn::kCheckK, s))) != SINKATTN_OK) return st;
+      if ((st = hip_queue(sinkattn::check_bf16(v_cache, kvn, sinkattn::kCheckV, s))) != SINKATTN_OK) return st;
+    }
     if ((st = check_result(s, nullptr)) != SINKATTN_OK) return st;
   }
   sinkattn::DecodeLaunch a{q, k_cache, v_cache, sinks, cu_seqlens_k, batch, max_seqlen_k, num_q_heads, num_kv_heads,
-                           window, num_splits, softmax_scale, o, lse, nullptr, nullptr};
+                           window, num_splits, softmax_scale, o, lse, nullptr, nullptr, fp8,
+                           fp8 ? k_scale : 1.0f, fp8 ? v_scale : 1.0f};
   if (num_splits == 1) return hip_status(sinkattn::launch_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
 
   const size_t need = sinkattn_decode_workspace_bytes(batch, num_q_heads, head_dim, num_splits);
@@ -211,6 +221,28 @@ sinkattn_status sinkattn_decode_splitkv(const void* q, const void* k_cache, cons
   if (sinkattn::decode_merges_in_kernel(a)) return ok();
   sinkattn::MergeLaunch m{a.o_part, a.lse_part, num_splits, batch, num_q_heads, o, lse};
   return hip_status(sinkattn::launch_merge(m, static_cast<hipStream_t>(stream)), "merge launch");
+}
+
+sinkattn_status sinkattn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_k,
+                                        const float* sinks, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t window, float softmax_scale,
+                                        int32_t num_splits, void* workspace, size_t workspace_bytes, void* o,
+                                        float* lse, void* stream) {
+  return decode_common(q, k_cache, v_cache, cu_seqlens_k, batch, max_seqlen_k, sinks, num_q_heads, num_kv_heads,
+                       head_dim, window, softmax_scale, num_splits, workspace, workspace_bytes, o, lse, stream, false,
+                       1.0f, 1.0f);
+}
+
+sinkattn_status sinkattn_decode_splitkv_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale,
+                                            float v_scale, const int32_t* cu_seqlens_k, int32_t batch,
+                                            int32_t max_seqlen_k, const float* sinks, int32_t num_q_heads,
+                                            int32_t num_kv_heads, int32_t head_dim, int32_t window,
+                                            float softmax_scale, int32_t num_splits, void* workspace,
+                                            size_t workspace_bytes, void* o, float* lse, void* stream) {
+  return decode_common(q, k_cache, v_cache, cu_seqlens_k, batch, max_seqlen_k, sinks, num_q_heads, num_kv_heads,
+                       head_dim, window, softmax_scale, num_splits, workspace, workspace_bytes, o, lse, stream, true,
+                       k_scale, v_scale);
 }
 
 sinkattn_status sinkattn_merge_lse(const float* o_parts, const float* lse_parts, int32_t num_parts, int32_t n,

@@ -3,7 +3,7 @@
 // host cannot see without reading device memory: sequence offsets (monotone,
 // starting at 0, lengths within the declared maximum, decode lengths >= 1),
 // sinks (finite or -inf; NaN and +inf are undefined), and NaN / Inf in the
-// bf16 inputs and in merge partials.
+// bf16 inputs (NaN codes in E4M3 caches) and in merge partials.
 //
 // Each check kernel ORs a bit into g_check_flags; the host clears the word
 // before and reads it back after (hipMemcpyFromSymbol), synchronising the
@@ -64,6 +64,15 @@ __global__ void check_bf16_kernel(const uint16_t* __restrict__ x, size_t n, unsi
   if (bad != 0u) atomicOr(&g_check_flags, bit);
 }
 
+// E4M3 NaN: the codes 0x7f and 0xff (the format has no infinities).
+__global__ void check_e4m3_kernel(const uint8_t* __restrict__ x, size_t n, unsigned bit) {
+  unsigned bad = 0;
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    bad |= (x[i] & 0x7fu) == 0x7fu;
+  if (bad != 0u) atomicOr(&g_check_flags, bit);
+}
+
 // fp32 values must not be NaN or +inf, nor -inf unless allow_neg_inf.
 __global__ void check_f32_kernel(const float* __restrict__ x, size_t n, unsigned bit, int allow_neg_inf) {
   unsigned bad = 0;
@@ -105,6 +114,13 @@ hipError_t check_bf16(const void* x, size_t n, unsigned bit, hipStream_t stream)
   if (x == nullptr || n == 0) return hipSuccess;
   hipLaunchKernelGGL(check_bf16_kernel, dim3(grid_for(n)), dim3(256), 0, stream, static_cast<const uint16_t*>(x),
                      n, bit);
+  return hipGetLastError();
+}
+
+hipError_t check_e4m3(const void* x, size_t n, unsigned bit, hipStream_t stream) {
+  if (x == nullptr || n == 0) return hipSuccess;
+  hipLaunchKernelGGL(check_e4m3_kernel, dim3(grid_for(n)), dim3(256), 0, stream, static_cast<const uint8_t*>(x), n,
+                     bit);
   return hipGetLastError();
 }
 

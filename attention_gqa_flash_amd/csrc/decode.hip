@@ -62,23 +62,82 @@ constexpr long long kHeadPerWaveTarget = 512;
 constexpr int kDirectMaxKeys = 1024;
 
 // One 32-key tile of one wave, in registers, K and V rows in coalesced
-// order: lane l holds the 16-byte chunk l % 8 of rows l / 8 + 8 i.  Rows at or
-// beyond `end` (> k0) repeat row end - 1: their logits are masked to -inf, so
-// their weights are 0 and the (finite) V values drop out.
+// order.  bf16 cache: lane l holds the 16-byte chunk l % 8 of rows
+// l / 8 + 8 i (a head's row is 128 bytes).  FP8 (E4M3) cache: lane l holds the
+// 16-byte chunk l % 4 (16 codes) of rows l / 4 + 16 i (a head's row is 64
+// bytes).  Rows at or beyond `end` (> k0) repeat row end - 1: their logits
+// are masked to -inf, so their weights are 0 and the (finite) V values drop
+// out.
+template <bool kFp8>
 struct TileRegs {
-  u32x4_t k[4];
-  u32x4_t v[4];
+  u32x4_t k[kFp8 ? 2 : 4];
+  u32x4_t v[kFp8 ? 2 : 4];
 };
 
-__device__ __forceinline__ void load_tile(TileRegs& t, const uint16_t* __restrict__ k,
-                                          const uint16_t* __restrict__ v, int base, int hkv, int g,
+template <bool kFp8>
+__device__ __forceinline__ void load_tile(TileRegs<kFp8>& t, const void* __restrict__ k,
+                                          const void* __restrict__ v, int base, int hkv, int g,
                                           int k0, int end, int lane) {
+  if constexpr (kFp8) {
+    const uint8_t* kb = static_cast<const uint8_t*>(k);
+    const uint8_t* vb = static_cast<const uint8_t*>(v);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = min(k0 + (lane >> 3) + 8 * i, end - 1);
-    const size_t off = (static_cast<size_t>(base + key) * hkv + g) * kHeadDim + (lane & 7) * 8;
-    t.k[i] = load16_stream(k + off);
-    t.v[i] = load16_stream(v + off);
+    for (int i = 0; i < 2; ++i) {
+      const int key = min(k0 + (lane >> 2) + 16 * i, end - 1);
+      const size_t off = (static_cast<size_t>(base + key) * hkv + g) * kHeadDim + (lane & 3) * 16;  // bytes
+      t.k[i] = load16_stream(reinterpret_cast<const uint16_t*>(kb + off));
+      t.v[i] = load16_stream(reinterpret_cast<const uint16_t*>(vb + off));
+    }
+  } else {
+    const uint16_t* kh = static_cast<const uint16_t*>(k);
+    const uint16_t* vh = static_cast<const uint16_t*>(v);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = min(k0 + (lane >> 3) + 8 * i, end - 1);
+      const size_t off = (static_cast<size_t>(base + key) * hkv + g) * kHeadDim + (lane & 7) * 8;
+      t.k[i] = load16_stream(kh + off);
+      t.v[i] = load16_stream(vh + off);
+    }
+  }
+}
+
+// 16 E4M3 codes (one 16-byte chunk) -> 16 bf16 in two 16-byte halves.  E4M3
+// values are exactly representable in bf16; the conversion runs with scale 1.
+__device__ __forceinline__ void e4m3x16_to_bf16(u32x4_t c, u32x4_t& lo, u32x4_t& hi) {
+  uint32_t w[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    w[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j], 1.0f, false));
+    w[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j], 1.0f, true));
+  }
+  lo = u32x4_t{w[0], w[1], w[2], w[3]};
+  hi = u32x4_t{w[4], w[5], w[6], w[7]};
+}
+
+// The tile into the wave's LDS staging (bf16, swizzled rows of 64 values).
+template <bool kFp8>
+__device__ __forceinline__ void stage_tile(const TileRegs<kFp8>& cur, uint16_t* kt, uint16_t* vt, int lane) {
+  if constexpr (kFp8) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = (lane >> 2) + 16 * i;
+      const int c0 = (lane & 3) * 16;
+      u32x4_t lo, hi;
+      e4m3x16_to_bf16(cur.k[i], lo, hi);
+      *reinterpret_cast<u32x4_t*>(kt + swz(r, c0)) = lo;
+      *reinterpret_cast<u32x4_t*>(kt + swz(r, c0 + 8)) = hi;
+      e4m3x16_to_bf16(cur.v[i], lo, hi);
+      *reinterpret_cast<u32x4_t*>(vt + swz(r, c0)) = lo;
+      *reinterpret_cast<u32x4_t*>(vt + swz(r, c0 + 8)) = hi;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (lane >> 3) + 8 * i;
+      const int dst = swz(r, (lane & 7) * 8);
+      *reinterpret_cast<u32x4_t*>(kt + dst) = cur.k[i];
+      *reinterpret_cast<u32x4_t*>(vt + dst) = cur.v[i];
+    }
   }
 }
 
@@ -90,13 +149,14 @@ __device__ __forceinline__ void load_tile(TileRegs& t, const uint16_t* __restric
 // separate workgroups (6.9 against 6.2 TB/s, measured with plain loads);
 // otherwise the waves of the workgroup interleave over one split and merge
 // through LDS.
-template <int kDecWaves, bool kSplitPerWave, bool kHeadPerWave = false, int kHeadsPerWG = 1>
+template <int kDecWaves, bool kSplitPerWave, bool kHeadPerWave = false, int kHeadsPerWG = 1, bool kFp8 = false>
 __device__ __forceinline__ void decode_body(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const float* __restrict__ sinks,
+    const uint16_t* __restrict__ q, const void* __restrict__ k,
+    const void* __restrict__ v, const float* __restrict__ sinks,
     const int32_t* __restrict__ cu_seqlens_k, int batch, int hq, int hkv, int group,
     int window, float scale_log2, int num_splits, uint16_t* __restrict__ o,
-    float* __restrict__ lse, float* __restrict__ o_part, float* __restrict__ lse_part, int splits_per_wg = 1) {
+    float* __restrict__ lse, float* __restrict__ o_part, float* __restrict__ lse_part, int splits_per_wg = 1,
+    float v_scale = 1.0f) {
   // Wave-private K and V staging tiles (2 x 4 KiB per wave); the whole
   // buffer is reused for the cross-wave merge of up to 32 heads x 64 d per
   // wave (index (wave * group + head) * 64 + d).
@@ -162,7 +222,7 @@ __device__ __forceinline__ void decode_body(
   // Register double buffering: the loads of the next tile of this wave are in
   // flight while the current one is computed.  The first tile is requested
   // before Q and the sink, so the three latencies overlap.
-  TileRegs cur, nxt;
+  TileRegs<kFp8> cur, nxt;
   constexpr int kStride = kOwnSplit ? kKeys : kKeys * kIl;
   int k0 = kOwnSplit ? a : a + kKeys * wl;
   if (k0 < e) load_tile(cur, k, v, base, hkv, g, k0, e, lane);
@@ -200,7 +260,8 @@ __device__ __forceinline__ void decode_body(
   // This wave's split sp alone: normalise and write its partial.
   auto write_partial = [&](int sp, float den) {
     if (sp >= num_splits || !col_ok) return;
-    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    if constexpr (kFp8) inv *= v_scale;  // V = v_scale * e4m3(code)
     const size_t prow = (static_cast<size_t>(sp) * batch + b) * hq + head;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
@@ -213,15 +274,9 @@ __device__ __forceinline__ void decode_body(
   };
   // One 32-key tile (keys k0 .. k0 + 31; those at or past `end` masked) into
   // the wave's online-softmax state.
-  auto tile_step = [&](const TileRegs& cur, int k0, int end) {
+  auto tile_step = [&](const TileRegs<kFp8>& cur, int k0, int end) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // previous tile's LDS reads are done
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (lane >> 3) + 8 * i;
-      const int dst = swz(r, (lane & 7) * 8);
-      *reinterpret_cast<u32x4_t*>(kt + dst) = cur.k[i];
-      *reinterpret_cast<u32x4_t*>(vt + dst) = cur.v[i];
-    }
+    stage_tile<kFp8>(cur, kt, vt, lane);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // K and V tiles written
 
     // S^T = K Q^T: MFMA row m reads key row key_of_row(m) of the tile.
@@ -353,6 +408,7 @@ __device__ __forceinline__ void decode_body(
         num += sc * red_o[(w * group + hc) * kHeadDim + d];
       }
       out = num / tot;
+      if constexpr (kFp8) out *= v_scale;  // V = v_scale * e4m3(code)
       out_lse = (big_m + __log2f(tot)) * kLn2;
     }
     const int h = (g - hsub + hs) * group + hc;
@@ -386,37 +442,38 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// All decode kernels take the same arguments; k and v point at bf16 or, with
+// kFp8, E4M3 caches (scale_log2 then includes the K scale; v_scale is applied
+// to the outputs).
+#define SINKATTN_DECODE_PARAMS                                                                             \
+  const uint16_t *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,                  \
+      const float *__restrict__ sinks, const int32_t *__restrict__ cu_seqlens_k, int batch, int hq, int hkv, \
+      int group, int window, float scale_log2, int num_splits, uint16_t *__restrict__ o, float *__restrict__ lse, \
+      float *__restrict__ o_part, float *__restrict__ lse_part, int splits_per_wg, float v_scale
+#define SINKATTN_DECODE_ARGS                                                                                  \
+  q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, group, window, scale_log2, num_splits, o, lse, o_part, lse_part, \
+      splits_per_wg, v_scale
+
 // Short splits (at most kShortChunk keys): two-wave workgroups at three
 // waves per SIMD, i.e. more workgroups and so more loads in flight.
+template <bool kFp8>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3, 3))) void decode_kernel_w2(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ sinks, const int32_t* __restrict__ cu_seqlens_k, int batch, int hq, int hkv,
-    int group, int window, float scale_log2, int num_splits, uint16_t* __restrict__ o, float* __restrict__ lse,
-    float* __restrict__ o_part, float* __restrict__ lse_part) {
-  decode_body<2, false>(q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, group, window, scale_log2, num_splits, o, lse,
-                 o_part, lse_part);
+    SINKATTN_DECODE_PARAMS) {
+  decode_body<2, false, false, 1, kFp8>(SINKATTN_DECODE_ARGS);
 }
 
 // Four or more long splits: four-wave workgroups, one split per wave (each
 // wave writes its split's partial; no cross-wave merge).
-__global__ __launch_bounds__(256) void decode_kernel_ps(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ sinks, const int32_t* __restrict__ cu_seqlens_k, int batch, int hq, int hkv,
-    int group, int window, float scale_log2, int num_splits, uint16_t* __restrict__ o, float* __restrict__ lse,
-    float* __restrict__ o_part, float* __restrict__ lse_part) {
-  decode_body<4, true>(q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, group, window, scale_log2, num_splits, o,
-                       lse, o_part, lse_part);
+template <bool kFp8>
+__global__ __launch_bounds__(256) void decode_kernel_ps(SINKATTN_DECODE_PARAMS) {
+  decode_body<4, true, false, 1, kFp8>(SINKATTN_DECODE_ARGS);
 }
 
 // Four or more splits over 4 to 8 KV heads: one workgroup per (sequence,
 // split), one wave per KV head.
-__global__ __launch_bounds__(512) void decode_kernel_hw(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ sinks, const int32_t* __restrict__ cu_seqlens_k, int batch, int hq, int hkv,
-    int group, int window, float scale_log2, int num_splits, uint16_t* __restrict__ o, float* __restrict__ lse,
-    float* __restrict__ o_part, float* __restrict__ lse_part, int splits_per_wg) {
-  decode_body<8, false, true>(q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, group, window, scale_log2, num_splits, o,
-                              lse, o_part, lse_part, splits_per_wg);
+template <bool kFp8>
+__global__ __launch_bounds__(512) void decode_kernel_hw(SINKATTN_DECODE_PARAMS) {
+  decode_body<8, false, true, 1, kFp8>(SINKATTN_DECODE_ARGS);
 }
 
 // One split of more than kShortChunk keys over an even number of KV heads:
@@ -424,26 +481,21 @@ __global__ __launch_bounds__(512) void decode_kernel_hw(
 // waves each, so that a workgroup reads 256 contiguous bytes of every token
 // row it touches (a plain-load probe: 6.4-6.6 TB/s against 6.0-6.2 for one
 // head per workgroup; 64 x 8192 at S = 1 from 180 to 165 us).
-__global__ __launch_bounds__(512) void decode_kernel_w8p(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ sinks, const int32_t* __restrict__ cu_seqlens_k, int batch, int hq, int hkv,
-    int group, int window, float scale_log2, int num_splits, uint16_t* __restrict__ o, float* __restrict__ lse,
-    float* __restrict__ o_part, float* __restrict__ lse_part) {
-  decode_body<8, false, false, 2>(q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, group, window, scale_log2,
-                                  num_splits, o, lse, o_part, lse_part);
+template <bool kFp8>
+__global__ __launch_bounds__(512) void decode_kernel_w8p(SINKATTN_DECODE_PARAMS) {
+  decode_body<8, false, false, 2, kFp8>(SINKATTN_DECODE_ARGS);
 }
 
 // Long splits: four-wave workgroups at the compiler's own register budget
 // (two waves per SIMD; at three, S = 4 on 64 x 8192 would end on a
 // two-thirds-full round of workgroups).
-__global__ __launch_bounds__(256) void decode_kernel_w4(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ sinks, const int32_t* __restrict__ cu_seqlens_k, int batch, int hq, int hkv,
-    int group, int window, float scale_log2, int num_splits, uint16_t* __restrict__ o, float* __restrict__ lse,
-    float* __restrict__ o_part, float* __restrict__ lse_part) {
-  decode_body<4, false>(q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, group, window, scale_log2, num_splits, o, lse,
-                 o_part, lse_part);
+template <bool kFp8>
+__global__ __launch_bounds__(256) void decode_kernel_w4(SINKATTN_DECODE_PARAMS) {
+  decode_body<4, false, false, 1, kFp8>(SINKATTN_DECODE_ARGS);
 }
+
+#undef SINKATTN_DECODE_PARAMS
+#undef SINKATTN_DECODE_ARGS
 
 __global__ __launch_bounds__(kThreads) void merge_kernel(
     const float* __restrict__ o_parts, const float* __restrict__ lse_parts, int num_parts,
@@ -497,43 +549,46 @@ bool decode_merges_in_kernel(const DecodeLaunch& a) {
   return a.num_splits > 1 && keys_per_split <= kKeys && max_range(a) <= kDirectMaxKeys;
 }
 
-hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
+template <bool kFp8>
+static hipError_t launch_decode_t(const DecodeLaunch& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
   // Splits of at most 32 keys: the whole range in one workgroup per
   // (sequence, KV head), o written directly.
   const int splits = decode_merges_in_kernel(a) ? 1 : a.num_splits;
-  const unsigned blocks = static_cast<unsigned>(a.batch) * a.num_kv_heads * splits;
   const long long keys_per_split = (max_range(a) + splits - 1) / splits;
   const bool short_chunks = keys_per_split <= kShortChunk;
+  const float scale_log2 = a.softmax_scale * a.k_scale * kLog2e;
+  unsigned grid = static_cast<unsigned>(a.batch) * a.num_kv_heads * splits;
+  unsigned threads = 128;
+  int per_wg = 1;
+  decltype(&decode_kernel_w4<kFp8>) kernel = decode_kernel_w2<kFp8>;
   if (splits >= kHeadPerWaveMinSplits && a.num_kv_heads >= 4 && a.num_kv_heads <= 8 &&
       keys_per_split >= kHeadPerWaveMinKeys) {
     const long long units = static_cast<long long>(a.batch) * splits;
-    const int per_wg = static_cast<int>(std::max<long long>(1, std::min<long long>(splits, units / kHeadPerWaveTarget)));
-    const long long groups = static_cast<long long>(a.batch) * ((splits + per_wg - 1) / per_wg);
-    hipLaunchKernelGGL(decode_kernel_hw, dim3(static_cast<unsigned>(groups)), dim3(64 * a.num_kv_heads), 0, stream,
-                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), a.sinks, a.cu_seqlens_k, a.batch, a.num_q_heads,
-                       a.num_kv_heads, group, a.window, a.softmax_scale * kLog2e, splits,
-                       static_cast<uint16_t*>(a.o), a.lse, a.o_part, a.lse_part, per_wg);
-    return hipGetLastError();
+    per_wg = static_cast<int>(std::max<long long>(1, std::min<long long>(splits, units / kHeadPerWaveTarget)));
+    grid = static_cast<unsigned>(static_cast<long long>(a.batch) * ((splits + per_wg - 1) / per_wg));
+    threads = 64 * a.num_kv_heads;
+    kernel = decode_kernel_hw<kFp8>;
+  } else if (splits == 1 && !short_chunks && a.num_kv_heads % 2 == 0) {
+    grid = static_cast<unsigned>(a.batch) * (a.num_kv_heads / 2);
+    threads = 512;
+    kernel = decode_kernel_w8p<kFp8>;
+  } else if (splits >= kSplitPerWaveMin && !short_chunks) {
+    grid = static_cast<unsigned>(a.batch) * a.num_kv_heads * ((splits + 3) / 4);
+    threads = 256;
+    kernel = decode_kernel_ps<kFp8>;
+  } else if (!short_chunks) {
+    threads = 256;
+    kernel = decode_kernel_w4<kFp8>;
   }
-  if (splits == 1 && !short_chunks && a.num_kv_heads % 2 == 0) {
-    hipLaunchKernelGGL(decode_kernel_w8p, dim3(static_cast<unsigned>(a.batch) * (a.num_kv_heads / 2)), dim3(512), 0,
-                       stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), a.sinks, a.cu_seqlens_k, a.batch, a.num_q_heads,
-                       a.num_kv_heads, group, a.window, a.softmax_scale * kLog2e, splits,
-                       static_cast<uint16_t*>(a.o), a.lse, a.o_part, a.lse_part);
-    return hipGetLastError();
-  }
-  const bool per_wave = splits >= kSplitPerWaveMin && !short_chunks;
-  auto kernel = per_wave ? decode_kernel_ps : short_chunks ? decode_kernel_w2 : decode_kernel_w4;
-  const unsigned grid = per_wave ? static_cast<unsigned>(a.batch) * a.num_kv_heads * ((splits + 3) / 4) : blocks;
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(per_wave || !short_chunks ? 256 : 128), 0, stream,
-                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), a.sinks, a.cu_seqlens_k, a.batch,
-                     a.num_q_heads, a.num_kv_heads, group, a.window, a.softmax_scale * kLog2e,
-                     splits, static_cast<uint16_t*>(a.o), a.lse, a.o_part, a.lse_part);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, stream, static_cast<const uint16_t*>(a.q), a.k, a.v,
+                     a.sinks, a.cu_seqlens_k, a.batch, a.num_q_heads, a.num_kv_heads, group, a.window, scale_log2,
+                     splits, static_cast<uint16_t*>(a.o), a.lse, a.o_part, a.lse_part, per_wg, a.v_scale);
   return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
+  return a.fp8 ? launch_decode_t<true>(a, stream) : launch_decode_t<false>(a, stream);
 }
 
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream) {

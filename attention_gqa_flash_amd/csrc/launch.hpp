@@ -21,7 +21,7 @@ struct PrefillLaunch {
 
 struct DecodeLaunch {
   const void* q;
-  const void* k;
+  const void* k;    // bf16, or E4M3 codes when fp8
   const void* v;
   const float* sinks;
   const int32_t* cu_seqlens_k;
@@ -31,6 +31,9 @@ struct DecodeLaunch {
   float* lse;       // optional, likewise
   float* o_part;    // fp32 partials when num_splits > 1
   float* lse_part;
+  bool fp8 = false;       // K/V caches hold E4M3 codes
+  float k_scale = 1.0f;   // K = k_scale * e4m3(code)
+  float v_scale = 1.0f;   // V = v_scale * e4m3(code)
 };
 
 struct MergeLaunch {
@@ -67,6 +70,8 @@ hipError_t check_offsets(const int32_t* cu, int batch, int max_len, int min_len,
                          hipStream_t stream);
 hipError_t check_sinks(const float* sinks, int n, hipStream_t stream);
 hipError_t check_bf16(const void* x, size_t n, unsigned bit, hipStream_t stream);
+// E4M3 codes: NaN (all exponent and mantissa bits set).
+hipError_t check_e4m3(const void* x, size_t n, unsigned bit, hipStream_t stream);
 hipError_t check_f32(const float* x, size_t n, unsigned bit, bool allow_neg_inf, hipStream_t stream);
 // Reads the flag word and cu_seqlens[batch] of the last offsets check;
 // synchronises the stream.

@@ -159,6 +159,39 @@ SINKATTN_API sinkattn_status sinkattn_decode_splitkv(
     void* o, float* lse, void* stream);
 
 /*
+ * Split-KV decode against an FP8 KV cache (vLLM, "GPT-OSS performance
+ * optimizations on NVIDIA Blackwell", FlashInfer integration: the KV cache
+ * is stored in FP8).  The page names neither the 8-bit format nor the
+ * scaling; this entry point takes OCP E4M3 codes (1 sign, 4 exponent and 3
+ * mantissa bits, bias 7, no infinities; 0x7f and 0xff are NaN) with one fp32
+ * scale per tensor:
+ *     K[t, g, d] = k_scale * e4m3(k_cache[t, g, d]),
+ *     V[t, g, d] = v_scale * e4m3(v_cache[t, g, d]),
+ * and otherwise computes exactly what sinkattn_decode_splitkv computes on
+ * those K and V (same arguments, splits, sink rule, workspace and errors).
+ *
+ *   k_cache,
+ *   v_cache        uint8 E4M3 codes [total_kv, num_kv_heads, head_dim],
+ *                  16-byte aligned; NaN codes are a precondition violation
+ *                  (reported under SINKATTN_DEBUG_CHECKS=1)
+ *   k_scale,
+ *   v_scale        host floats, finite and > 0 (SINKATTN_ERR_INVALID_ARG
+ *                  otherwise)
+ *
+ * Workspace: sinkattn_decode_workspace_bytes(batch, num_q_heads, head_dim,
+ * num_splits), as for the bf16 cache.
+ */
+SINKATTN_API sinkattn_status sinkattn_decode_splitkv_fp8(
+    const void* q, const void* k_cache, const void* v_cache,
+    float k_scale, float v_scale,
+    const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_k,
+    const float* sinks,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t window, float softmax_scale, int32_t num_splits,
+    void* workspace, size_t workspace_bytes,
+    void* o, float* lse, void* stream);
+
+/*
  * Log-sum-exp merge of num_parts partial results, each normalised by its own
  * denominator (the combination step that the split-KV form of the
  * Perplexity page's online softmax implies; the page does not print it):

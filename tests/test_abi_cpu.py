@@ -27,8 +27,8 @@ def _lib():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted([
-        "sinkattn_decode_splitkv", "sinkattn_decode_workspace_bytes", "sinkattn_last_error",
-        "sinkattn_merge_lse", "sinkattn_prefill_varlen", "sinkattn_version"])
+        "sinkattn_decode_splitkv", "sinkattn_decode_splitkv_fp8", "sinkattn_decode_workspace_bytes",
+        "sinkattn_last_error", "sinkattn_merge_lse", "sinkattn_prefill_varlen", "sinkattn_version"])
 
 
 def test_every_declared_symbol_is_exported():
@@ -113,6 +113,35 @@ def test_decode_rejects(kw, status):
     lib = _lib()
     assert _decode(lib, **kw) == status
     assert lib.sinkattn_last_error()
+
+
+def _decode_fp8(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=0.0625, vs=0.0625, cu=FAKE, batch=4, max_seqlen=100, sinks=None, hq=64,
+             hkv=8, d=64, window=0, scale=0.125, splits=1, ws=None, ws_bytes=0, o=FAKE, lse=None)
+    a.update(kw)
+    return lib.sinkattn_decode_splitkv_fp8(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["cu"], a["batch"],
+                                           a["max_seqlen"], a["sinks"], a["hq"], a["hkv"], a["d"], a["window"],
+                                           a["scale"], a["splits"], a["ws"], a["ws_bytes"], a["o"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=0.0), 1),
+    (dict(vs=-1.0), 1),
+    (dict(ks=float("nan")), 1),
+    (dict(vs=float("inf")), 1),
+    (dict(d=128), 2),
+    (dict(splits=4), 3),              # no workspace
+    (dict(v=None), 1),
+    (dict(k=ctypes.c_void_p((1 << 20) + 8)), 1),  # misaligned cache
+])
+def test_decode_fp8_rejects(kw, status):
+    lib = _lib()
+    assert _decode_fp8(lib, **kw) == status
+    assert lib.sinkattn_last_error()
+
+
+def test_decode_fp8_empty_batch_is_ok_without_launch():
+    assert _decode_fp8(_lib(), batch=0) == 0
 
 
 @pytest.mark.parametrize("args,status", [

@@ -38,7 +38,7 @@ def test_tiny_prefill_config():
 
 
 @pytest.mark.parametrize("window", [0, 1, 5, 31, 32, 64, 127, 128, 129, 1000])
-@pytest.mark.parametrize("hq,hkv", [(8, 2), (16, 2), (24, 2), (64, 8), (8, 8), (32, 1)])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (16, 2), (24, 2), (64, 8), (8, 8), (32, 1), (32, 16)])
 def test_varlen_prefill_small(window, hq, hkv):
     lengths = [1, 31, 32, 33, 64, 65, 127, 200, 517]
     if hq == 64:
@@ -178,7 +178,7 @@ def test_decode_short_splits(hq, hkv, window, splits):
     assert_close_out(to_f64(o2), ro2, "short splits, no sinks")
 
 
-@pytest.mark.parametrize("hq,hkv", [(16, 4), (20, 5), (48, 6), (56, 7), (64, 8)])
+@pytest.mark.parametrize("hq,hkv", [(16, 4), (20, 5), (48, 6), (56, 7), (64, 8), (128, 4)])
 @pytest.mark.parametrize("splits", [4, 6, 13])
 def test_decode_one_wave_per_kv_head(hq, hkv, splits):
     """Four or more splits of at least 128 keys over 4 to 8 KV heads: one

@@ -18,7 +18,7 @@ input sets so that its 151 MB working set does not stay in the 256 MB
 Infinity Cache between steps.  Each leg reports mean, median and min.
 
 Also reported (not part of the step or of `value`): decode at 1, 4 and 16
-splits; the tiny 256-token prefill; the long-context decode pair (16 x 32768
+splits, also against an FP8 (E4M3) cache with per-tensor scales; the tiny 256-token prefill; the long-context decode pair (16 x 32768
 cached tokens, 32 splits, full then 128-window); the ragged 32-sequence
 varlen prefill (causal and 128-window); a streaming-read and a copy
 bandwidth reference; the engine clock (sysfs pp_dpm_sclk) sampled during the step.
@@ -75,9 +75,12 @@ def prefill_bytes(lengths, window, hq=HQ, hkv=HKV) -> float:
     return float(qo + kv + hq * 4 + (len(lengths) + 1) * 4)
 
 
-def decode_bytes(lengths, window, hq=HQ, hkv=HKV) -> float:
+def decode_bytes(lengths, window, hq=HQ, hkv=HKV, kv_elem_bytes=2) -> float:
+    """Q + O (bf16) + the K/V rows attended (kv_elem_bytes per element: 2 for
+    bf16, 1 for an E4M3 cache) + sinks + offsets."""
     keys = sum(min(n, window) if window > 0 else n for n in lengths)
-    return float(2 * len(lengths) * hq * D * 2 + 2 * keys * hkv * D * 2 + hq * 4 + (len(lengths) + 1) * 4)
+    return float(2 * len(lengths) * hq * D * 2 + 2 * keys * hkv * D * kv_elem_bytes + hq * 4
+                 + (len(lengths) + 1) * 4)
 
 
 def decode_flops(lengths, window, hq=HQ) -> float:
@@ -424,6 +427,9 @@ def gpu_bench(steps: int, warmup: int, extras: bool = True) -> dict:
         e["GB/s"] = e["gbs_median"]
         per_split[str(s_count)] = e
 
+    # the same workload against an FP8 (E4M3) cache with per-tensor scales
+    fp8 = _fp8_decode(torch, binding, dev, dq, dsinks, dcu, ws, do, timed, hbm_entry)
+
     other = {}
     if extras:
         sets.clear()
@@ -459,13 +465,43 @@ def gpu_bench(steps: int, warmup: int, extras: bool = True) -> dict:
                     "window_tflops": window_tflops, "window_gbs": window_gbs,
                     "causal_timing": leg["causal"], "window_timing": leg["window"]},
         "decode": {"gbs": decode_gbs, "pct_hbm_peak": 100 * decode_gbs / PEAK_HBM_GBS, "ms": t_decode,
-                   "splits": DEC_SPLITS, "timing": leg["decode"], "by_splits": per_split},
+                   "splits": DEC_SPLITS, "timing": leg["decode"], "by_splits": per_split,
+                   "fp8_kv_by_splits": fp8},
         "roofline": roof_causal, "rooflines": [roof_causal, roof_window, roof_decode],
         "other_configs": other.get("configs"), "bandwidth_reference": other.get("bandwidth"),
         "engine_clock": clock.summary(),
         "device": {"name": props.name, "cus": props.multi_processor_count, "arch": props.gcnArchName,
                    "pci_bus": pci_bus},
     }
+
+
+def _fp8_decode(torch, binding, dev, dq, dsinks, dcu, ws, do, timed, hbm_entry) -> dict:
+    """64 x 8192 decode against an E4M3 cache (K = k_scale * e4m3(code), V
+    likewise), S = 1, 4, 16: the codes are N(0,1) / scale rounded to E4M3 on
+    the device from a seeded generator (timing-only inputs; parity runs on
+    host-generated codes).  Bytes count one byte per cached element."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3)
+    k_scale, v_scale = 1.0 / 16, 1.0 / 16
+    shape = (DEC_BATCH * DEC_CTX, HKV, D)
+
+    def codes(s):
+        x = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).mul_(1.0 / s)
+        c = x.to(torch.float8_e4m3fn).view(torch.uint8)
+        del x
+        return c
+
+    fk, fv = codes(k_scale), codes(v_scale)
+    out = {}
+    for s_count in (1, 4, 16):
+        st = timed(lambda: binding.decode_splitkv_fp8(dq, fk, fv, k_scale, v_scale, dcu, DEC_CTX, dsinks, 0, 0.125,
+                                                      s_count, workspace=ws, out=do))
+        e = hbm_entry(st, decode_bytes([DEC_CTX] * DEC_BATCH, 0, kv_elem_bytes=1))
+        e["shape"] = "B=64, ctx 8192, 64/8 heads, E4M3 K/V, S=%d" % s_count
+        out[str(s_count)] = e
+    del fk, fv
+    torch.cuda.synchronize()
+    return out
 
 
 def _device_normal_bf16(torch, shape, gen, dev, std=1.0):

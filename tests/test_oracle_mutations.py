@@ -7,7 +7,9 @@ the softmax scale (in the max or in the denominator), the sink dropped, the
 window one key too wide, the sink in every split, the decode window one key
 too wide, the wrong GQA grouping, a base-2 lse, an unweighted merge; and
 for the FP8 oracle (checked by tests/test_oracle_fp8.py): exponent bias 8
-instead of 7, subnormals scaled like normals, the two scales swapped.
+instead of 7, subnormals scaled like normals, the two scales swapped; and
+for the append oracle (tests/test_oracle_append.py): top-left causal
+alignment, the window one key too wide, queries one position late.
 """
 
 import os
@@ -39,6 +41,13 @@ FP8_MUTATIONS = [
 ]
 
 
+APPEND_MUTATIONS = [
+    ("off = lk - lq", "off = 0"),                                   # top-left causal alignment
+    ("valid &= jj > pos[:, None] - window", "valid &= jj >= pos[:, None] - window"),
+    ("pos = off + blk ", "pos = off + blk + 1 "),                   # query one position late
+]
+
+
 def _run_pins(tmp_path, module, old, new, pin_file):
     for sub in ("oracle", "tests", "attention_gqa_flash_amd"):
         shutil.copytree(os.path.join(ROOT, sub), tmp_path / sub,
@@ -61,3 +70,8 @@ def test_pins_catch_planted_mistake(tmp_path, old, new):
 @pytest.mark.parametrize("old,new", FP8_MUTATIONS, ids=["fp8_%d" % i for i in range(len(FP8_MUTATIONS))])
 def test_fp8_pins_catch_planted_mistake(tmp_path, old, new):
     _run_pins(tmp_path, "fp8.py", old, new, "tests/test_oracle_fp8.py")
+
+
+@pytest.mark.parametrize("old,new", APPEND_MUTATIONS, ids=["append_%d" % i for i in range(len(APPEND_MUTATIONS))])
+def test_append_pins_catch_planted_mistake(tmp_path, old, new):
+    _run_pins(tmp_path, "append.py", old, new, "tests/test_oracle_append.py")

@@ -40,6 +40,9 @@ def library() -> ctypes.CDLL:
     lib.sinkattn_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
                                             vp, vp, vp]
     lib.sinkattn_prefill_varlen.restype = ctypes.c_int
+    lib.sinkattn_prefill_append.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                            f32, vp, vp, vp]
+    lib.sinkattn_prefill_append.restype = ctypes.c_int
     lib.sinkattn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.sinkattn_decode_workspace_bytes.restype = sz
     lib.sinkattn_decode_splitkv.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, f32, i32,
@@ -119,6 +122,48 @@ def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: Opt
         _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(cu_seqlens), cu_seqlens.shape[0] - 1,
         int(max_seqlen), t, hq, hkv, d, int(window), float(softmax_scale), _ptr(out), _ptr(lse),
         _stream(q.device)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def prefill_append(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: Optional[torch.Tensor],
+                   cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                   window: int = 0, softmax_scale: float = 0.125, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, return_lse: bool = False):
+    """Append prefill / multi-token-query decode: q [Tq, Hq, 64] bf16 packed
+    by cu_seqlens_q, k/v [Tk, Hkv, 64] bf16 packed by cu_seqlens_k (both
+    [B+1] int32, device); each sequence's queries are its last tokens
+    (bottom-right causal).  Returns o (and lse)."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k, "k", torch.bfloat16, 3)
+    _need(v, "v", torch.bfloat16, 3)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    tq, hq, d = q.shape
+    tk, hkv = k.shape[0], k.shape[1]
+    if k.shape[2] != d or v.shape != k.shape:
+        raise ValueError("k and v must be [Tk, Hkv, D] matching q")
+    if cu_seqlens_q.shape != cu_seqlens_k.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both have batch + 1 entries")
+    if sinks is not None:
+        _need(sinks, "sinks", torch.float32, 1)
+        if sinks.shape[0] != hq:
+            raise ValueError("sinks must have num_q_heads entries")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.bfloat16, 3)
+        if out.shape != q.shape:
+            raise ValueError("out must match q")
+    if return_lse and lse is None:
+        lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2)
+        if lse.shape != (tq, hq):
+            raise ValueError("lse must be [Tq, Hq]")
+    _check(library().sinkattn_prefill_append(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), cu_seqlens_q.shape[0] - 1,
+        int(max_seqlen_q), int(max_seqlen_k), tq, tk, hq, hkv, d, int(window), float(softmax_scale), _ptr(out),
+        _ptr(lse), _stream(q.device)))
     return (out, lse) if (return_lse or lse is not None) else out
 
 

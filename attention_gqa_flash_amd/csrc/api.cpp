@@ -76,6 +76,7 @@ sinkattn_status check_failed(unsigned flags) {
       {sinkattn::kCheckK, "k holds NaN or Inf"},
       {sinkattn::kCheckV, "v holds NaN or Inf"},
       {sinkattn::kCheckParts, "o_parts holds NaN or Inf, or lse_parts NaN or +inf"},
+      {sinkattn::kCheckAppend, "a sequence has fewer keys than queries (cu_seqlens_k vs cu_seqlens_q)"},
   };
   std::string msg = "debug checks failed:";
   for (const auto& n : kNames)
@@ -106,6 +107,53 @@ const char* sinkattn_last_error(void) { return g_last_error.c_str(); }
 
 const char* sinkattn_version(void) { return "sinkattn 0.1.0 (gfx950)"; }
 
+// Self-attention prefill (cu_q == cu_k) and append prefill share one kernel.
+static sinkattn_status prefill_common(const void* q, const void* k, const void* v, const float* sinks,
+                                      const int32_t* cu_q, const int32_t* cu_k, int32_t batch, int32_t max_q,
+                                      int32_t max_k, int32_t total_q, int32_t total_k, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t window, float softmax_scale,
+                                      void* o, float* lse, void* stream) {
+  const bool append = cu_k != cu_q;
+  sinkattn_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
+  if (st != SINKATTN_OK) return st;
+  if ((st = check_scale(softmax_scale)) != SINKATTN_OK) return st;
+  if (batch == 0 || max_q == 0 || total_q == 0) return ok();
+  if (!q || !k || !v || !o || !cu_q || !cu_k)
+    return fail(SINKATTN_ERR_INVALID_ARG, "q, k, v, o and the sequence offsets must not be NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(SINKATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if (max_q > total_q)
+    return fail(SINKATTN_ERR_INVALID_ARG, "max_seqlen (%d) exceeds total_tokens (%d)", max_q, total_q);
+  if (max_k > total_k)
+    return fail(SINKATTN_ERR_INVALID_ARG, "max_seqlen_k (%d) exceeds total_k (%d)", max_k, total_k);
+  if (max_k == 0) return fail(SINKATTN_ERR_INVALID_ARG, "queries need keys: max_seqlen_k is 0");
+  const int group = num_q_heads / num_kv_heads;
+  if (sinkattn::prefill_blocks(batch, total_q, num_kv_heads, group) > sinkattn::prefill_max_blocks())
+    return fail(SINKATTN_ERR_UNSUPPORTED, "too many (query tile, head) work items for one launch");
+  // K/V rows of one sequence are addressed with 32-bit byte offsets.
+  if (static_cast<long long>(max_k) * num_kv_heads * head_dim * 2 >= (1LL << 31))
+    return fail(SINKATTN_ERR_UNSUPPORTED, "max_seqlen_k * num_kv_heads * head_dim * 2 must stay below 2^31");
+  if (debug_checks()) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t qn = static_cast<size_t>(total_q) * num_q_heads * head_dim;
+    const size_t kvn = static_cast<size_t>(total_k) * num_kv_heads * head_dim;
+    if ((st = hip_queue(sinkattn::check_clear(s))) != SINKATTN_OK) return st;
+    if ((st = hip_queue(sinkattn::check_offsets(cu_q, batch, max_q, 0, total_q, s))) != SINKATTN_OK) return st;
+    if (append) {
+      if ((st = hip_queue(sinkattn::check_offsets(cu_k, batch, max_k, 0, total_k, s))) != SINKATTN_OK) return st;
+      if ((st = hip_queue(sinkattn::check_append(cu_q, cu_k, batch, s))) != SINKATTN_OK) return st;
+    }
+    if ((st = hip_queue(sinkattn::check_sinks(sinks, num_q_heads, s))) != SINKATTN_OK) return st;
+    if ((st = hip_queue(sinkattn::check_bf16(q, qn, sinkattn::kCheckQ, s))) != SINKATTN_OK) return st;
+    if ((st = hip_queue(sinkattn::check_bf16(k, kvn, sinkattn::kCheckK, s))) != SINKATTN_OK) return st;
+    if ((st = hip_queue(sinkattn::check_bf16(v, kvn, sinkattn::kCheckV, s))) != SINKATTN_OK) return st;
+    if ((st = check_result(s, nullptr)) != SINKATTN_OK) return st;
+  }
+  sinkattn::PrefillLaunch a{q, k, v, sinks, cu_q, cu_k, batch, max_q, max_k, total_q, num_q_heads,
+                            num_kv_heads, window, softmax_scale, o, lse};
+  return hip_status(sinkattn::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
+}
+
 sinkattn_status sinkattn_prefill_varlen(const void* q, const void* k, const void* v, const float* sinks,
                                         const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
                                         int32_t total_tokens, int32_t num_q_heads, int32_t num_kv_heads,
@@ -113,38 +161,26 @@ sinkattn_status sinkattn_prefill_varlen(const void* q, const void* k, const void
                                         float* lse, void* stream) {
   if (batch < 0 || max_seqlen < 0 || total_tokens < 0)
     return fail(SINKATTN_ERR_INVALID_ARG, "batch, max_seqlen and total_tokens must be >= 0");
-  sinkattn_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
-  if (st != SINKATTN_OK) return st;
-  if ((st = check_scale(softmax_scale)) != SINKATTN_OK) return st;
-  if (batch == 0 || max_seqlen == 0 || total_tokens == 0) return ok();
-  if (!q || !k || !v || !o || !cu_seqlens)
-    return fail(SINKATTN_ERR_INVALID_ARG, "q, k, v, o and cu_seqlens must not be NULL");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-    return fail(SINKATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
-  if (max_seqlen > total_tokens)
-    return fail(SINKATTN_ERR_INVALID_ARG, "max_seqlen (%d) exceeds total_tokens (%d)", max_seqlen, total_tokens);
-  const int group = num_q_heads / num_kv_heads;
-  if (sinkattn::prefill_blocks(batch, total_tokens, num_kv_heads, group) > sinkattn::prefill_max_blocks())
-    return fail(SINKATTN_ERR_UNSUPPORTED, "too many (query tile, head) work items for one launch");
-  // K/V rows of one sequence are addressed with 32-bit byte offsets.
-  if (static_cast<long long>(max_seqlen) * num_kv_heads * head_dim * 2 >= (1LL << 31))
-    return fail(SINKATTN_ERR_UNSUPPORTED, "max_seqlen * num_kv_heads * head_dim * 2 must stay below 2^31");
-  if (debug_checks()) {
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const size_t qn = static_cast<size_t>(total_tokens) * num_q_heads * head_dim;
-    const size_t kvn = static_cast<size_t>(total_tokens) * num_kv_heads * head_dim;
-    if ((st = hip_queue(sinkattn::check_clear(s))) != SINKATTN_OK) return st;
-    if ((st = hip_queue(sinkattn::check_offsets(cu_seqlens, batch, max_seqlen, 0, total_tokens, s))) != SINKATTN_OK)
-      return st;
-    if ((st = hip_queue(sinkattn::check_sinks(sinks, num_q_heads, s))) != SINKATTN_OK) return st;
-    if ((st = hip_queue(sinkattn::check_bf16(q, qn, sinkattn::kCheckQ, s))) != SINKATTN_OK) return st;
-    if ((st = hip_queue(sinkattn::check_bf16(k, kvn, sinkattn::kCheckK, s))) != SINKATTN_OK) return st;
-    if ((st = hip_queue(sinkattn::check_bf16(v, kvn, sinkattn::kCheckV, s))) != SINKATTN_OK) return st;
-    if ((st = check_result(s, nullptr)) != SINKATTN_OK) return st;
-  }
-  sinkattn::PrefillLaunch a{q, k, v, sinks, cu_seqlens, batch, max_seqlen, total_tokens, num_q_heads,
-                            num_kv_heads, window, softmax_scale, o, lse};
-  return hip_status(sinkattn::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
+  return prefill_common(q, k, v, sinks, cu_seqlens, cu_seqlens, batch, max_seqlen, max_seqlen, total_tokens,
+                        total_tokens, num_q_heads, num_kv_heads, head_dim, window, softmax_scale, o, lse, stream);
+}
+
+sinkattn_status sinkattn_prefill_append(const void* q, const void* k, const void* v, const float* sinks,
+                                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+                                        int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t total_q,
+                                        int32_t total_k, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t window, float softmax_scale, void* o, float* lse,
+                                        void* stream) {
+  if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
+    return fail(SINKATTN_ERR_INVALID_ARG, "batch, lengths and totals must be >= 0");
+  if (cu_seqlens_q != nullptr && cu_seqlens_q == cu_seqlens_k && max_seqlen_q == max_seqlen_k &&
+      total_q == total_k)
+    return sinkattn_prefill_varlen(q, k, v, sinks, cu_seqlens_q, batch, max_seqlen_q, total_q, num_q_heads,
+                                   num_kv_heads, head_dim, window, softmax_scale, o, lse, stream);
+  if (cu_seqlens_q != nullptr && cu_seqlens_q == cu_seqlens_k)
+    return fail(SINKATTN_ERR_INVALID_ARG, "one offsets array for queries and keys needs equal maxima and totals");
+  return prefill_common(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k, total_q,
+                        total_k, num_q_heads, num_kv_heads, head_dim, window, softmax_scale, o, lse, stream);
 }
 
 size_t sinkattn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t num_splits) {

@@ -1,7 +1,8 @@
 // Device-side precondition checks, run by the C ABI before a launch when
 // SINKATTN_DEBUG_CHECKS=1 is set in the environment.  They cover what the
 // host cannot see without reading device memory: sequence offsets (monotone,
-// starting at 0, lengths within the declared maximum, decode lengths >= 1),
+// starting at 0, lengths within the declared maximum, decode lengths >= 1,
+// append prefill: at least as many keys as queries per sequence),
 // sinks (finite or -inf; NaN and +inf are undefined), and NaN / Inf in the
 // bf16 inputs (NaN codes in E4M3 caches) and in merge partials.
 //
@@ -37,6 +38,15 @@ __global__ void check_offsets_kernel(const int32_t* __restrict__ cu, int batch, 
       g_check_total = hi;
     }
   }
+  if (bits != 0u) atomicOr(&g_check_flags, bits);
+}
+
+// Append prefill: no sequence may have fewer key rows than query rows.
+__global__ void check_append_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+                                    int batch) {
+  unsigned bits = 0;
+  for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < batch; b += gridDim.x * blockDim.x)
+    if (cu_k[b + 1] - cu_k[b] < cu_q[b + 1] - cu_q[b]) bits |= kCheckAppend;
   if (bits != 0u) atomicOr(&g_check_flags, bits);
 }
 
@@ -101,6 +111,12 @@ hipError_t check_offsets(const int32_t* cu, int batch, int max_len, int min_len,
   if (batch <= 0) return hipSuccess;
   hipLaunchKernelGGL(check_offsets_kernel, dim3(grid_for(batch)), dim3(256), 0, stream, cu, batch, max_len,
                      min_len, total_limit);
+  return hipGetLastError();
+}
+
+hipError_t check_append(const int32_t* cu_q, const int32_t* cu_k, int batch, hipStream_t stream) {
+  if (batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(check_append_kernel, dim3(grid_for(batch)), dim3(256), 0, stream, cu_q, cu_k, batch);
   return hipGetLastError();
 }
 

@@ -7,13 +7,17 @@
 
 namespace sinkattn {
 
+// Prefill: queries packed by cu_seqlens, keys / values by cu_seqlens_k
+// (the same array for self-attention); per sequence the queries are the last
+// Lq_b of its Lk_b >= Lq_b tokens (bottom-right causal alignment).
 struct PrefillLaunch {
   const void* q;
   const void* k;
   const void* v;
   const float* sinks;
   const int32_t* cu_seqlens;
-  int batch, max_seqlen, total_tokens, num_q_heads, num_kv_heads, window;
+  const int32_t* cu_seqlens_k;
+  int batch, max_seqlen, max_seqlen_k, total_tokens, num_q_heads, num_kv_heads, window;
   float softmax_scale;
   void* o;
   float* lse;
@@ -63,12 +67,15 @@ enum CheckBits : unsigned {
   kCheckK = 1u << 7,             // NaN / Inf in k
   kCheckV = 1u << 8,             // NaN / Inf in v
   kCheckParts = 1u << 9,         // NaN / Inf in o_parts, NaN / +inf in lse_parts
-  kCheckAll = (1u << 10) - 1u,
+  kCheckAppend = 1u << 10,       // append prefill: a sequence with fewer keys than queries
+  kCheckAll = (1u << 11) - 1u,
 };
 hipError_t check_clear(hipStream_t stream);
 hipError_t check_offsets(const int32_t* cu, int batch, int max_len, int min_len, int total_limit,
                          hipStream_t stream);
 hipError_t check_sinks(const float* sinks, int n, hipStream_t stream);
+// Append prefill: every sequence has cu_k[b+1] - cu_k[b] >= cu_q[b+1] - cu_q[b].
+hipError_t check_append(const int32_t* cu_q, const int32_t* cu_k, int batch, hipStream_t stream);
 hipError_t check_bf16(const void* x, size_t n, unsigned bit, hipStream_t stream);
 // E4M3 codes: NaN (all exponent and mantissa bits set).
 hipError_t check_e4m3(const void* x, size_t n, unsigned bit, hipStream_t stream);

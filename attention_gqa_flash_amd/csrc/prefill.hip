@@ -5,6 +5,16 @@
 // its running max at the sink and its denominator at 1), with the 128-token
 // window layers of the NVIDIA gpt-oss announcement (model description).
 //
+// Append prefill (chunked prefill, multi-token-query decode): sequence b has
+// Lk_b key rows (cu_seqlens_k) and its last Lq_b <= Lk_b tokens are the
+// queries (cu_seqlens_q), so query row r sits at position off + r with
+// off = Lk_b - Lq_b, and the causal / window mask is aligned at the bottom
+// right.  Self-attention prefill is the case cu_seqlens_k = cu_seqlens_q
+// (off = 0).  Draft tokens of a speculative or multi-token-prediction decoder
+// are verified this way (Perplexity, "GPT-OSS on day 0", in-house inference
+// engine; Baseten, "How to run GPT OSS 120B at 500+ tokens per second on
+// NVIDIA GPUs", next performance optimizations).
+//
 // Work decomposition: one workgroup per (sequence, KV head, chunk of up to 8
 // query heads of that KV head's group, tile of 32 query tokens).  The four
 // waves of a workgroup share every K/V tile staged in LDS; wave w owns two
@@ -156,9 +166,9 @@ template <bool kWindow, int kCols>
 __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_per_eu(4 / kCols, 4 / kCols))) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ sinks,
-    const int32_t* __restrict__ cu_seqlens, int hq, int hkv, int group, int n_hchunk,
-    int batch, int max_seqlen, int window, float scale_log2, uint16_t* __restrict__ o,
-    float* __restrict__ lse) {
+    const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ cu_seqlens_k, int hq, int hkv, int group,
+    int n_hchunk, int batch, int max_seqlen, int max_seqlen_k, int window, float scale_log2,
+    uint16_t* __restrict__ o, float* __restrict__ lse) {
   // Ring of LDS tile buffers, each K rows then V rows.  Tile t lives in
   // buffer (t - t_begin) % kBufs; the loop below is unrolled over the ring so
   // every LDS address is a per-lane base plus an immediate offset.
@@ -189,34 +199,39 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
   if (b < 0) return;  // uniform over the workgroup
 
   const int seq0 = cu_seqlens[b];
-  // Lengths above max_seqlen break a precondition; clamping keeps every
-  // access inside the bounds the host checked.
+  const int seq0_k = cu_seqlens_k[b];
+  // Lengths above the declared maxima, or fewer keys than queries, break a
+  // precondition; clamping keeps every access inside the bounds the host
+  // checked (such a sequence's rows are left unwritten).
   const int len = min(cu_seqlens[b + 1] - seq0, max_seqlen);
+  const int len_k = min(cu_seqlens_k[b + 1] - seq0_k, max_seqlen_k);
   const int n_tiles = len > 0 ? (len + kQTile - 1) / kQTile : 0;
   const int j = w - item_start(seq0, b);
-  if (j >= n_tiles) return;  // a spare item between two sequences
+  if (j >= n_tiles || len_k < len) return;  // a spare item between two sequences
+  const int off = len_k - len;  // position of query row 0 in the sequence
   const int qt = n_tiles - 1 - j;
   const int q0 = qt * kQTile;
 
   const int last_q = min(len - 1, q0 + kQTile - 1);
-  const int first_key = kWindow ? max(0, q0 - window + 1) : 0;
+  const int last_pos = last_q + off;  // the last key any query of the tile sees
+  const int first_key = kWindow ? max(0, q0 + off - window + 1) : 0;
   const int t_begin = first_key / kKTile;
-  const int t_end = last_q / kKTile;
+  const int t_end = last_pos / kKTile;
   // 32-key steps h_begin..h_end: every one holds a key some query of the
   // tile sees.
   const int h_begin = first_key >> 5;
-  const int h_end = last_q >> 5;
+  const int h_end = last_pos >> 5;
 
   // K / V rows of this sequence and KV head; a key's row is hkv * 64
   // elements further on.
-  const size_t kv0 = (static_cast<size_t>(seq0) * hkv + g) * kHeadDim;
+  const size_t kv0 = (static_cast<size_t>(seq0_k) * hkv + g) * kHeadDim;
   const uint16_t* k_seq = k + kv0;
   const uint16_t* v_seq = v + kv0;
   // LDS byte address of the ring (uniform).
   const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_address(&kv_lds[0][0]));
   auto issue = [&](int tt, int buf) {
     const uint32_t dst = ring + static_cast<uint32_t>(buf) * (2 * kKTile * kHeadDim * 2);
-    issue_tile<kThreads>(k_seq, v_seq, dst, dst + kKTile * kHeadDim * 2, len, hkv * kHeadDim, tt * kKTile,
+    issue_tile<kThreads>(k_seq, v_seq, dst, dst + kKTile * kHeadDim * 2, len_k, hkv * kHeadDim, tt * kKTile,
                          wave, lane);
   };
   // The first two tiles go out before anything else, then the workgroup's
@@ -249,7 +264,7 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
     head[c] = g * group + (head_ok[c] ? slot : 0);
   }
   const bool wave_active = head_ok[0];
-  const int qtok = q0 + col;
+  const int qpos = q0 + off + col;  // this lane's query position in the sequence
 
   // Q^T as the B operand (lane holds query column `col`, d = 16 s + 8 half
   // + t), read from the Q block in LDS once it has landed.
@@ -335,10 +350,10 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
   // 32 hh + key_of_reg(r, half).
   auto need_mask = [&](int hh) {
     const int kbase = hh * 32;
-    return (kbase + 31 > q0) || (kWindow && kbase <= last_q - window);
+    return (kbase + 31 > q0 + off) || (kWindow && kbase <= last_pos - window);
   };
   auto mask = [&](int hh, f32x16_t& s_c) {
-    const int lim = qtok - hh * 32 - 8 * half;
+    const int lim = qpos - hh * 32 - 8 * half;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int off = key_of_reg(r, 0);
@@ -549,12 +564,12 @@ hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream) {
   const long long blocks = prefill_blocks(a.batch, a.total_tokens, a.num_kv_heads, group);
   if (blocks <= 0) return hipSuccess;
   dim3 grid(static_cast<unsigned>(blocks), 1, 1);
-  const bool windowed = a.window > 0 && a.window < a.max_seqlen;
+  const bool windowed = a.window > 0 && a.window < a.max_seqlen_k;
   auto kernel = windowed ? prefill_kernel<true, kColsPerWave> : prefill_kernel<false, kColsPerWave>;
   hipLaunchKernelGGL(kernel, grid, dim3(threads_for<kColsPerWave>()), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), a.sinks, a.cu_seqlens, a.num_q_heads,
-                     a.num_kv_heads, group, n_hchunk, a.batch, a.max_seqlen, a.window,
+                     static_cast<const uint16_t*>(a.v), a.sinks, a.cu_seqlens, a.cu_seqlens_k, a.num_q_heads,
+                     a.num_kv_heads, group, n_hchunk, a.batch, a.max_seqlen, a.max_seqlen_k, a.window,
                      a.softmax_scale * kLog2e, static_cast<uint16_t*>(a.o), a.lse);
   return hipGetLastError();
 }

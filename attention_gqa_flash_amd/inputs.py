@@ -118,6 +118,37 @@ def make_decode(lengths, hq: int, hkv: int, d: int = 64, seed: int = 0,
 
 
 @dataclass
+class AppendInputs:
+    q: np.ndarray             # uint16 bf16 bits [Tq, Hq, D]
+    k: np.ndarray             # uint16 bf16 bits [Tk, Hkv, D]
+    v: np.ndarray             # uint16 bf16 bits [Tk, Hkv, D]
+    sinks: np.ndarray         # float32 [Hq]
+    cu_seqlens_q: np.ndarray  # int32 [B+1]
+    cu_seqlens_k: np.ndarray  # int32 [B+1]
+    scale: float
+    q_lens: list = field(default_factory=list)
+    k_lens: list = field(default_factory=list)
+
+
+def make_append(q_lens, k_lens, hq: int, hkv: int, d: int = 64, seed: int = 0, scale: float = 0.125,
+                sink_std: float = 1.0, rng: Optional[np.random.Generator] = None):
+    """Queries appended to cached sequences: sequence b has k_lens[b] key rows
+    and its last q_lens[b] <= k_lens[b] tokens are queries.  Draw order
+    q -> k -> v -> sinks, N(0,1) rounded to bf16; sinks N(0, sink_std^2)."""
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    q_lens = [int(x) for x in q_lens]
+    k_lens = [int(x) for x in k_lens]
+    assert len(q_lens) == len(k_lens) and all(0 <= a <= b for a, b in zip(q_lens, k_lens))
+    q = _normal_bf16(rng, (sum(q_lens), hq, d))
+    k = _normal_bf16(rng, (sum(k_lens), hkv, d))
+    v = _normal_bf16(rng, (sum(k_lens), hkv, d))
+    sinks = rng.standard_normal(size=hq, dtype=np.float32)
+    if sink_std != 1.0:
+        sinks = sinks * np.float32(sink_std)
+    return AppendInputs(q, k, v, sinks.astype(np.float32), _cu(q_lens), _cu(k_lens), scale, q_lens, k_lens)
+
+
+@dataclass
 class DecodeFp8Inputs:
     q: np.ndarray            # uint16 bf16 bits [B, Hq, D]
     k: np.ndarray            # uint8 E4M3 codes [Tk, Hkv, D]

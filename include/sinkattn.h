@@ -107,6 +107,51 @@ SINKATTN_API sinkattn_status sinkattn_prefill_varlen(
     void* o, float* lse, void* stream);
 
 /*
+ * Append prefill with sinks: chunked prefill against a cache that already
+ * holds a sequence's earlier tokens, and multi-token-query decode (the draft
+ * tokens a speculative or multi-token-prediction decoder hands to the target
+ * model for verification: Perplexity, "GPT-OSS on day 0", in-house inference
+ * engine; Baseten, "How to run GPT OSS 120B at 500+ tokens per second on
+ * NVIDIA GPUs", next performance optimizations).
+ *
+ * Sequence b has Lk_b = cu_seqlens_k[b+1] - cu_seqlens_k[b] key/value rows
+ * (every token up to and including its newest) and Lq_b = cu_seqlens_q[b+1]
+ * - cu_seqlens_q[b] <= Lk_b queries, its newest tokens: query r sits at
+ * position p = Lk_b - Lq_b + r and sees key j iff j <= p and (W <= 0 or
+ * j > p - W), the causal mask aligned at the bottom right.  Lq_b = Lk_b is
+ * sinkattn_prefill_varlen; Lq_b = 1 is the single-token decode.
+ *
+ *   q             bf16 [total_q, num_q_heads, head_dim]
+ *   k, v          bf16 [total_k, num_kv_heads, head_dim]
+ *   sinks         fp32 [num_q_heads], or NULL for "no sink" on every head
+ *   cu_seqlens_q  int32 [batch + 1], device, offsets of the query rows
+ *   cu_seqlens_k  int32 [batch + 1], device, offsets of the key/value rows
+ *                 (the same array as cu_seqlens_q only together with equal
+ *                 maxima and totals: that is self-attention prefill)
+ *   max_seqlen_q, max_seqlen_k   host ints, >= every Lq_b, resp. Lk_b
+ *   total_q, total_k             host ints, rows of q/o, resp. k/v
+ *   window        <= 0: full causal; W > 0: p - W < j <= p
+ *   o             bf16 [total_q, num_q_heads, head_dim] (written)
+ *   lse           fp32 [total_q, num_q_heads], natural log, sink included;
+ *                 NULL to skip
+ *
+ * Device-side preconditions besides the shared ones (for both offset
+ * arrays): Lq_b <= Lk_b for every b; a sequence that breaks it is skipped
+ * (its rows are not written) and SINKATTN_DEBUG_CHECKS=1 reports it.
+ * max_seqlen_k == 0 with queries present is SINKATTN_ERR_INVALID_ARG.
+ * Shape limits as sinkattn_prefill_varlen, with max_seqlen_k in the 2^31
+ * bound and total_q in the workgroup bound.
+ */
+SINKATTN_API sinkattn_status sinkattn_prefill_append(
+    const void* q, const void* k, const void* v,
+    const float* sinks,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+    int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t total_q, int32_t total_k,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t window, float softmax_scale,
+    void* o, float* lse, void* stream);
+
+/*
  * Bytes of workspace sinkattn_decode_splitkv needs for num_splits > 1:
  * fp32 partial outputs [num_splits, batch, num_q_heads, head_dim] and fp32
  * partial lse [num_splits, batch, num_q_heads], each 256-byte aligned.

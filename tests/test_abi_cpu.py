@@ -28,7 +28,8 @@ def _lib():
 def test_header_declares_the_entry_points():
     assert _declared() == sorted([
         "sinkattn_decode_splitkv", "sinkattn_decode_splitkv_fp8", "sinkattn_decode_workspace_bytes",
-        "sinkattn_last_error", "sinkattn_merge_lse", "sinkattn_prefill_varlen", "sinkattn_version"])
+        "sinkattn_last_error", "sinkattn_merge_lse", "sinkattn_prefill_append", "sinkattn_prefill_varlen",
+        "sinkattn_version"])
 
 
 def test_every_declared_symbol_is_exported():
@@ -87,6 +88,46 @@ def test_prefill_empty_is_ok_without_launch():
     lib = _lib()
     assert _prefill(lib, batch=0) == 0
     assert _prefill(lib, total=0, max_seqlen=0) == 0
+
+
+FAKE2 = ctypes.c_void_p(2 << 20)  # a second offsets array, likewise never read
+
+
+def _append(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, sinks=None, cuq=FAKE, cuk=FAKE2, batch=2, mq=16, mk=64, tq=20, tk=100,
+             hq=8, hkv=2, d=64, window=0, scale=0.125, o=FAKE, lse=None)
+    a.update(kw)
+    return lib.sinkattn_prefill_append(a["q"], a["k"], a["v"], a["sinks"], a["cuq"], a["cuk"], a["batch"], a["mq"],
+                                       a["mk"], a["tq"], a["tk"], a["hq"], a["hkv"], a["d"], a["window"],
+                                       a["scale"], a["o"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=128), 2),
+    (dict(hq=6, hkv=4), 1),
+    (dict(scale=0.0), 1),
+    (dict(batch=-1), 1),
+    (dict(mk=-1), 1),
+    (dict(cuk=None), 1),
+    (dict(k=None), 1),
+    (dict(v=ctypes.c_void_p((1 << 20) + 4)), 1),
+    (dict(mq=32, tq=16), 1),                     # max_seqlen_q above total_q
+    (dict(mk=200, tk=100), 1),                   # max_seqlen_k above total_k
+    (dict(mk=0, tk=0), 1),                       # queries without keys
+    (dict(cuk=FAKE, mk=16, tk=100), 1),          # one offsets array, different maxima or totals
+    # one sequence's K/V rows past 2^31 bytes (32-bit row offsets)
+    (dict(mk=1 << 20, tk=1 << 20, hq=128, hkv=128), 2),
+])
+def test_append_rejects(kw, status):
+    lib = _lib()
+    assert _append(lib, **kw) == status
+    assert lib.sinkattn_last_error()
+
+
+def test_append_empty_is_ok_without_launch():
+    lib = _lib()
+    assert _append(lib, batch=0) == 0
+    assert _append(lib, tq=0, mq=0) == 0
 
 
 def _decode(lib, **kw):

@@ -51,6 +51,9 @@ def library() -> ctypes.CDLL:
     lib.sinkattn_decode_splitkv_fp8.argtypes = [vp, vp, vp, f32, f32, vp, i32, i32, vp, i32, i32, i32, i32, f32,
                                                 i32, vp, sz, vp, vp, vp]
     lib.sinkattn_decode_splitkv_fp8.restype = ctypes.c_int
+    lib.sinkattn_decode_splitkv_multi.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, i32, i32, i32,
+                                                  f32, i32, vp, sz, vp, vp, vp]
+    lib.sinkattn_decode_splitkv_multi.restype = ctypes.c_int
     lib.sinkattn_merge_lse.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.sinkattn_merge_lse.restype = ctypes.c_int
     lib.sinkattn_last_error.argtypes = []
@@ -242,6 +245,45 @@ def decode_splitkv_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
         _ptr(q), _ptr(k_cache), _ptr(v_cache), float(k_scale), float(v_scale), _ptr(cu_seqlens_k), bsz,
         int(max_seqlen_k), _ptr(sinks), hq, hkv, d, int(window), float(softmax_scale), int(num_splits),
         _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(q.device)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def decode_splitkv_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                         cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                         sinks: Optional[torch.Tensor], window: int = 0, softmax_scale: float = 0.125,
+                         num_splits: int = 1, workspace: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         return_lse: bool = False):
+    """Multi-token-query split-KV decode: q [Tq, Hq, 64] bf16 packed by
+    cu_seqlens_q, caches [Tk, Hkv, 64] bf16 packed by cu_seqlens_k; each
+    sequence's queries are its newest tokens (bottom-right causal)."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 3)
+    _need(v_cache, "v_cache", torch.bfloat16, 3)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    tq, hq, d = q.shape
+    hkv = k_cache.shape[1]
+    if v_cache.shape != k_cache.shape or k_cache.shape[2] != d:
+        raise ValueError("k_cache and v_cache must be [Tk, Hkv, D] matching q")
+    if cu_seqlens_q.shape != cu_seqlens_k.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both have batch + 1 entries")
+    if sinks is not None:
+        _need(sinks, "sinks", torch.float32, 1)
+        if sinks.shape[0] != hq:
+            raise ValueError("sinks must have num_q_heads entries")
+    need = decode_workspace_bytes(tq, hq, d, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
+    _check(library().sinkattn_decode_splitkv_multi(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), cu_seqlens_q.shape[0] - 1,
+        int(max_seqlen_q), int(max_seqlen_k), tq, _ptr(sinks), hq, hkv, d, int(window), float(softmax_scale),
+        int(num_splits), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(q.device)))
     return (out, lse) if (return_lse or lse is not None) else out
 
 

@@ -195,8 +195,12 @@ static sinkattn_status decode_common(const void* q, const void* k_cache, const v
                                      const float* sinks, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                      int32_t window, float softmax_scale, int32_t num_splits, void* workspace,
                                      size_t workspace_bytes, void* o, float* lse, void* stream, bool fp8,
-                                     float k_scale, float v_scale) {
+                                     float k_scale, float v_scale, const int32_t* cu_seqlens_q = nullptr,
+                                     int32_t max_seqlen_q = 1, int32_t total_q = 0) {
+  const bool multi = cu_seqlens_q != nullptr;
   if (batch < 0 || max_seqlen_k < 0) return fail(SINKATTN_ERR_INVALID_ARG, "batch and max_seqlen_k must be >= 0");
+  if (multi && (max_seqlen_q < 0 || total_q < 0))
+    return fail(SINKATTN_ERR_INVALID_ARG, "max_seqlen_q and total_q must be >= 0");
   sinkattn_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
   if (st != SINKATTN_OK) return st;
   if ((st = check_scale(softmax_scale)) != SINKATTN_OK) return st;
@@ -208,7 +212,12 @@ static sinkattn_status decode_common(const void* q, const void* k_cache, const v
   if (num_q_heads / num_kv_heads > sinkattn::decode_max_group())
     return fail(SINKATTN_ERR_UNSUPPORTED, "decode supports at most %d query heads per KV head",
                 sinkattn::decode_max_group());
-  if (batch == 0) return ok();
+  if (multi && static_cast<long long>(max_seqlen_q) * (num_q_heads / num_kv_heads) > 32)
+    return fail(SINKATTN_ERR_UNSUPPORTED, "max_seqlen_q * (num_q_heads / num_kv_heads) must be at most 32 (got %d * %d)",
+                max_seqlen_q, num_q_heads / num_kv_heads);
+  if (multi && max_seqlen_q > total_q)
+    return fail(SINKATTN_ERR_INVALID_ARG, "max_seqlen_q (%d) exceeds total_q (%d)", max_seqlen_q, total_q);
+  if (batch == 0 || (multi && (max_seqlen_q == 0 || total_q == 0))) return ok();
   if (!q || !k_cache || !v_cache || !o || !cu_seqlens_k)
     return fail(SINKATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, o and cu_seqlens_k must not be NULL");
   if (max_seqlen_k < 1) return fail(SINKATTN_ERR_INVALID_ARG, "decode needs max_seqlen_k >= 1");
@@ -221,10 +230,15 @@ static sinkattn_status decode_common(const void* q, const void* k_cache, const v
     // Offsets first: they size the K/V scan.
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = hip_queue(sinkattn::check_clear(s))) != SINKATTN_OK) return st;
+    if (multi) {
+      if ((st = hip_queue(sinkattn::check_offsets(cu_seqlens_q, batch, max_seqlen_q, 0, total_q, s))) != SINKATTN_OK)
+        return st;
+      if ((st = hip_queue(sinkattn::check_append(cu_seqlens_q, cu_seqlens_k, batch, s))) != SINKATTN_OK) return st;
+    }
     if ((st = hip_queue(sinkattn::check_offsets(cu_seqlens_k, batch, max_seqlen_k, 1, -1, s))) != SINKATTN_OK)
       return st;
     if ((st = hip_queue(sinkattn::check_sinks(sinks, num_q_heads, s))) != SINKATTN_OK) return st;
-    const size_t qn = static_cast<size_t>(batch) * num_q_heads * head_dim;
+    const size_t qn = static_cast<size_t>(multi ? total_q : batch) * num_q_heads * head_dim;
     if ((st = hip_queue(sinkattn::check_bf16(q, qn, sinkattn::kCheckQ, s))) != SINKATTN_OK) return st;
     int total_kv = 0;
     if ((st = check_result(s, &total_kv)) != SINKATTN_OK) return st;
@@ -240,22 +254,24 @@ static sinkattn_status decode_common(const void* q, const void* k_cache, const v
   }
   sinkattn::DecodeLaunch a{q, k_cache, v_cache, sinks, cu_seqlens_k, batch, max_seqlen_k, num_q_heads, num_kv_heads,
                            window, num_splits, softmax_scale, o, lse, nullptr, nullptr, fp8,
-                           fp8 ? k_scale : 1.0f, fp8 ? v_scale : 1.0f};
+                           fp8 ? k_scale : 1.0f, fp8 ? v_scale : 1.0f, cu_seqlens_q, max_seqlen_q, total_q};
+  // Output rows: one per sequence, or (multi) one per query token.
+  const int32_t rows_out = multi ? total_q : batch;
   if (num_splits == 1) return hip_status(sinkattn::launch_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
 
-  const size_t need = sinkattn_decode_workspace_bytes(batch, num_q_heads, head_dim, num_splits);
+  const size_t need = sinkattn_decode_workspace_bytes(rows_out, num_q_heads, head_dim, num_splits);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(SINKATTN_ERR_WORKSPACE, "workspace of %zu bytes is too small (need %zu)", workspace_bytes, need);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(SINKATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  const size_t rows = static_cast<size_t>(num_splits) * batch * num_q_heads;
+  const size_t rows = static_cast<size_t>(num_splits) * rows_out * num_q_heads;
   char* ws = static_cast<char*>(workspace);
   a.o_part = reinterpret_cast<float*>(ws);
   a.lse_part = reinterpret_cast<float*>(ws + round_up(rows * head_dim * sizeof(float), 256));
   hipError_t e = sinkattn::launch_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_status(e, "decode launch");
   if (sinkattn::decode_merges_in_kernel(a)) return ok();
-  sinkattn::MergeLaunch m{a.o_part, a.lse_part, num_splits, batch, num_q_heads, o, lse};
+  sinkattn::MergeLaunch m{a.o_part, a.lse_part, num_splits, rows_out, num_q_heads, o, lse};
   return hip_status(sinkattn::launch_merge(m, static_cast<hipStream_t>(stream)), "merge launch");
 }
 
@@ -279,6 +295,21 @@ sinkattn_status sinkattn_decode_splitkv_fp8(const void* q, const void* k_cache, 
   return decode_common(q, k_cache, v_cache, cu_seqlens_k, batch, max_seqlen_k, sinks, num_q_heads, num_kv_heads,
                        head_dim, window, softmax_scale, num_splits, workspace, workspace_bytes, o, lse, stream, true,
                        k_scale, v_scale);
+}
+
+sinkattn_status sinkattn_decode_splitkv_multi(const void* q, const void* k_cache, const void* v_cache,
+                                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+                                              int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t total_q,
+                                              const float* sinks, int32_t num_q_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t window, float softmax_scale,
+                                              int32_t num_splits, void* workspace, size_t workspace_bytes, void* o,
+                                              float* lse, void* stream) {
+  // (with batch 0 and no offsets the call validates its arguments and returns)
+  if (cu_seqlens_q == nullptr && batch > 0)
+    return fail(SINKATTN_ERR_INVALID_ARG, "cu_seqlens_q must not be NULL");
+  return decode_common(q, k_cache, v_cache, cu_seqlens_k, batch, max_seqlen_k, sinks, num_q_heads, num_kv_heads,
+                       head_dim, window, softmax_scale, num_splits, workspace, workspace_bytes, o, lse, stream, false,
+                       1.0f, 1.0f, cu_seqlens_q, max_seqlen_q, total_q);
 }
 
 sinkattn_status sinkattn_merge_lse(const float* o_parts, const float* lse_parts, int32_t num_parts, int32_t n,

@@ -149,14 +149,23 @@ __device__ __forceinline__ void stage_tile(const TileRegs<kFp8>& cur, uint16_t* 
 // separate workgroups (6.9 against 6.2 TB/s, measured with plain loads);
 // otherwise the waves of the workgroup interleave over one split and merge
 // through LDS.
-template <int kDecWaves, bool kSplitPerWave, bool kHeadPerWave = false, int kHeadsPerWG = 1, bool kFp8 = false>
+//
+// kMulti (multi-token-query decode): sequence b's last nq_b tokens are
+// queries (rows cu_seqlens_q[b] .. of q, o and the partials), and MFMA
+// column c = t * group + h serves token t and query head h of the group, so
+// one pass over the keys serves every query token (nq_b * group <= ncols <=
+// 32 columns).  Token t sits at position len - nq_b + t and sees the keys at
+// or before it (and, with a window W, after position - W): the causal mask
+// aligned at the bottom right, applied per column.
+template <int kDecWaves, bool kSplitPerWave, bool kHeadPerWave = false, int kHeadsPerWG = 1, bool kFp8 = false,
+          bool kMulti = false>
 __device__ __forceinline__ void decode_body(
     const uint16_t* __restrict__ q, const void* __restrict__ k,
     const void* __restrict__ v, const float* __restrict__ sinks,
     const int32_t* __restrict__ cu_seqlens_k, int batch, int hq, int hkv, int group,
     int window, float scale_log2, int num_splits, uint16_t* __restrict__ o,
-    float* __restrict__ lse, float* __restrict__ o_part, float* __restrict__ lse_part, int splits_per_wg = 1,
-    float v_scale = 1.0f) {
+    float* __restrict__ lse, float* __restrict__ o_part, float* __restrict__ lse_part, int splits_per_wg,
+    float v_scale, const int32_t* __restrict__ cu_seqlens_q, int ncols, int out_rows) {
   // Wave-private K and V staging tiles (2 x 4 KiB per wave); the whole
   // buffer is reused for the cross-wave merge of up to 32 heads x 64 d per
   // wave (index (wave * group + head) * 64 + d).
@@ -202,7 +211,15 @@ __device__ __forceinline__ void decode_body(
 
   const int base = cu_seqlens_k[b];
   const int len = cu_seqlens_k[b + 1] - base;
-  const int lo = window > 0 ? max(0, len - window) : 0;
+  // Query tokens of this sequence (one unless kMulti); more than len breaks
+  // a precondition and is clamped.
+  int q_row0 = b, nq = 1;
+  if constexpr (kMulti) {
+    q_row0 = cu_seqlens_q[b];
+    nq = min(cu_seqlens_q[b + 1] - q_row0, len);
+    if (nq <= 0) return;  // uniform over the workgroup: no query, no output row
+  }
+  const int lo = window > 0 ? max(0, len - nq - window + 1) : 0;
   const int n = len - lo;
   const int chunk = n > 0 ? (n + num_splits - 1) / num_splits : 0;
   auto split_end = [&](int sp) { return sp < num_splits ? min(len, lo + (sp + 1) * chunk) : len; };
@@ -210,8 +227,12 @@ __device__ __forceinline__ void decode_body(
   const int a = split < num_splits ? min(len, lo + split * chunk) : len;
   int e = split_end(split);
 
-  const bool col_ok = col < group;
-  const int head = g * group + (col_ok ? col : 0);
+  // Column -> (query token, head of the group); single-token: token 0.
+  const int tok = kMulti ? col / group : 0;
+  const bool col_ok = kMulti ? tok < nq : col < group;
+  const int head = g * group + (col_ok ? col - tok * group : 0);
+  const int qrow = kMulti ? q_row0 + (col_ok ? tok : 0) : b;  // row of q / o / partials
+  const int qpos = len - nq + (col_ok ? tok : 0);              // the query's position (kMulti masks)
 
   uint16_t* kt = reinterpret_cast<uint16_t*>(lds_buf) + wave * 2 * kKeys * kHeadDim;
   uint16_t* vt = kt + kKeys * kHeadDim;
@@ -232,7 +253,7 @@ __device__ __forceinline__ void decode_body(
   for (int s = 0; s < 4; ++s) {
     // (every lane loads; columns past the group repeat the group's first
     // head: S columns are independent, and theirs are never written)
-    const u32x4_t val = load16(q + (static_cast<size_t>(b) * hq + head) * kHeadDim + 16 * s + 8 * half);
+    const u32x4_t val = load16(q + (static_cast<size_t>(qrow) * hq + head) * kHeadDim + 16 * s + 8 * half);
     qreg[s] = __builtin_bit_cast(bf16x8_t, val);
   }
   // The sink belongs to split 0 only (its wave 0 when the waves share a
@@ -262,7 +283,7 @@ __device__ __forceinline__ void decode_body(
     if (sp >= num_splits || !col_ok) return;
     float inv = den > 0.0f ? 1.0f / den : 0.0f;
     if constexpr (kFp8) inv *= v_scale;  // V = v_scale * e4m3(code)
-    const size_t prow = (static_cast<size_t>(sp) * batch + b) * hq + head;
+    const size_t prow = (static_cast<size_t>(sp) * out_rows + qrow) * hq + head;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -291,6 +312,17 @@ __device__ __forceinline__ void decode_body(
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (k0 + key_of_reg(r, half) >= end) sacc[r] = kNegInf;
+    }
+    if constexpr (kMulti) {
+      // Per-column causal / window mask where the tile reaches past the
+      // first query's position or below the last query's window.
+      if (k0 + kKeys - 1 > len - nq || (window > 0 && k0 <= len - 1 - window)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + key_of_reg(r, half);
+          if (key > qpos || (window > 0 && key <= qpos - window)) sacc[r] = kNegInf;
+        }
+      }
     }
 
     float mx = sacc[0];
@@ -379,21 +411,24 @@ __device__ __forceinline__ void decode_body(
     red_m[wave][col] = m2;
     red_l[wave][col] = den;
   }
+  const int cols = kMulti ? ncols : group;  // columns per wave in red_o
   if (col_ok) {
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int d = 32 * db + 8 * (r >> 2) + 4 * half + (r & 3);
-        red_o[(wave * group + col) * kHeadDim + d] = acc[db][r];
+        red_o[(wave * cols + col) * kHeadDim + d] = acc[db][r];
       }
   }
   __syncthreads();
 
-  for (int idx = tid; idx < kHeadsPerWG * group * kHeadDim; idx += 64 * kDecWaves) {
-    const int hs = idx / (group * kHeadDim);  // KV head within the workgroup
-    const int hc = (idx / kHeadDim) % group;
+  for (int idx = tid; idx < kHeadsPerWG * cols * kHeadDim; idx += 64 * kDecWaves) {
+    const int hs = idx / (cols * kHeadDim);  // KV head within the workgroup
+    const int hc = (idx / kHeadDim) % cols;  // column
     const int d = idx % kHeadDim;
+    const int ct = kMulti ? hc / group : 0;  // its query token
+    if (kMulti && ct >= nq) continue;
     float big_m = kNegInf;
 #pragma unroll
     for (int i = 0; i < kIl; ++i) big_m = fmaxf(big_m, red_m[hs + kHeadsPerWG * i][hc]);
@@ -405,18 +440,19 @@ __device__ __forceinline__ void decode_body(
         const int w = hs + kHeadsPerWG * i;
         const float sc = fast_exp2(red_m[w][hc] - big_m);
         tot += sc * red_l[w][hc];
-        num += sc * red_o[(w * group + hc) * kHeadDim + d];
+        num += sc * red_o[(w * cols + hc) * kHeadDim + d];
       }
       out = num / tot;
       if constexpr (kFp8) out *= v_scale;  // V = v_scale * e4m3(code)
       out_lse = (big_m + __log2f(tot)) * kLn2;
     }
-    const int h = (g - hsub + hs) * group + hc;
+    const int h = (g - hsub + hs) * group + (hc - ct * group);
+    const int row = kMulti ? q_row0 + ct : b;
     if (num_splits == 1) {
-      o[(static_cast<size_t>(b) * hq + h) * kHeadDim + d] = to_bf16_bits(out);
-      if (lse != nullptr && d == 0) lse[static_cast<size_t>(b) * hq + h] = out_lse;
+      o[(static_cast<size_t>(row) * hq + h) * kHeadDim + d] = to_bf16_bits(out);
+      if (lse != nullptr && d == 0) lse[static_cast<size_t>(row) * hq + h] = out_lse;
     } else {
-      const size_t prow = (static_cast<size_t>(split) * batch + b) * hq + h;
+      const size_t prow = (static_cast<size_t>(split) * out_rows + row) * hq + h;
       o_part[prow * kHeadDim + d] = out;
       if (d == 0) lse_part[prow] = out_lse;
     }
@@ -449,31 +485,32 @@ __device__ __forceinline__ float wave_sum(float x) {
   const uint16_t *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,                  \
       const float *__restrict__ sinks, const int32_t *__restrict__ cu_seqlens_k, int batch, int hq, int hkv, \
       int group, int window, float scale_log2, int num_splits, uint16_t *__restrict__ o, float *__restrict__ lse, \
-      float *__restrict__ o_part, float *__restrict__ lse_part, int splits_per_wg, float v_scale
+      float *__restrict__ o_part, float *__restrict__ lse_part, int splits_per_wg, float v_scale,             \
+      const int32_t *__restrict__ cu_seqlens_q, int ncols, int out_rows
 #define SINKATTN_DECODE_ARGS                                                                                  \
   q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, group, window, scale_log2, num_splits, o, lse, o_part, lse_part, \
-      splits_per_wg, v_scale
+      splits_per_wg, v_scale, cu_seqlens_q, ncols, out_rows
 
 // Short splits (at most kShortChunk keys): two-wave workgroups at three
 // waves per SIMD, i.e. more workgroups and so more loads in flight.
-template <bool kFp8>
+template <bool kFp8, bool kMulti>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3, 3))) void decode_kernel_w2(
     SINKATTN_DECODE_PARAMS) {
-  decode_body<2, false, false, 1, kFp8>(SINKATTN_DECODE_ARGS);
+  decode_body<2, false, false, 1, kFp8, kMulti>(SINKATTN_DECODE_ARGS);
 }
 
 // Four or more long splits: four-wave workgroups, one split per wave (each
 // wave writes its split's partial; no cross-wave merge).
-template <bool kFp8>
+template <bool kFp8, bool kMulti>
 __global__ __launch_bounds__(256) void decode_kernel_ps(SINKATTN_DECODE_PARAMS) {
-  decode_body<4, true, false, 1, kFp8>(SINKATTN_DECODE_ARGS);
+  decode_body<4, true, false, 1, kFp8, kMulti>(SINKATTN_DECODE_ARGS);
 }
 
 // Four or more splits over 4 to 8 KV heads: one workgroup per (sequence,
 // split), one wave per KV head.
-template <bool kFp8>
+template <bool kFp8, bool kMulti>
 __global__ __launch_bounds__(512) void decode_kernel_hw(SINKATTN_DECODE_PARAMS) {
-  decode_body<8, false, true, 1, kFp8>(SINKATTN_DECODE_ARGS);
+  decode_body<8, false, true, 1, kFp8, kMulti>(SINKATTN_DECODE_ARGS);
 }
 
 // One split of more than kShortChunk keys over an even number of KV heads:
@@ -481,17 +518,17 @@ __global__ __launch_bounds__(512) void decode_kernel_hw(SINKATTN_DECODE_PARAMS) 
 // waves each, so that a workgroup reads 256 contiguous bytes of every token
 // row it touches (a plain-load probe: 6.4-6.6 TB/s against 6.0-6.2 for one
 // head per workgroup; 64 x 8192 at S = 1 from 180 to 165 us).
-template <bool kFp8>
+template <bool kFp8, bool kMulti>
 __global__ __launch_bounds__(512) void decode_kernel_w8p(SINKATTN_DECODE_PARAMS) {
-  decode_body<8, false, false, 2, kFp8>(SINKATTN_DECODE_ARGS);
+  decode_body<8, false, false, 2, kFp8, kMulti>(SINKATTN_DECODE_ARGS);
 }
 
 // Long splits: four-wave workgroups at the compiler's own register budget
 // (two waves per SIMD; at three, S = 4 on 64 x 8192 would end on a
 // two-thirds-full round of workgroups).
-template <bool kFp8>
+template <bool kFp8, bool kMulti>
 __global__ __launch_bounds__(256) void decode_kernel_w4(SINKATTN_DECODE_PARAMS) {
-  decode_body<4, false, false, 1, kFp8>(SINKATTN_DECODE_ARGS);
+  decode_body<4, false, false, 1, kFp8, kMulti>(SINKATTN_DECODE_ARGS);
 }
 
 #undef SINKATTN_DECODE_PARAMS
@@ -540,8 +577,11 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
 }  // namespace
 
 // Keys of the longest range a decode query attends.
+// The most keys one sequence's queries see together (the first query's
+// window start to the end).
 static long long max_range(const DecodeLaunch& a) {
-  return a.window > 0 ? std::min<long long>(a.max_seqlen_k, a.window) : a.max_seqlen_k;
+  const long long nq = a.cu_seqlens_q != nullptr ? a.max_q : 1;
+  return a.window > 0 ? std::min<long long>(a.max_seqlen_k, a.window + nq - 1) : a.max_seqlen_k;
 }
 
 bool decode_merges_in_kernel(const DecodeLaunch& a) {
@@ -549,7 +589,7 @@ bool decode_merges_in_kernel(const DecodeLaunch& a) {
   return a.num_splits > 1 && keys_per_split <= kKeys && max_range(a) <= kDirectMaxKeys;
 }
 
-template <bool kFp8>
+template <bool kFp8, bool kMulti>
 static hipError_t launch_decode_t(const DecodeLaunch& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
   // Splits of at most 32 keys: the whole range in one workgroup per
@@ -561,34 +601,36 @@ static hipError_t launch_decode_t(const DecodeLaunch& a, hipStream_t stream) {
   unsigned grid = static_cast<unsigned>(a.batch) * a.num_kv_heads * splits;
   unsigned threads = 128;
   int per_wg = 1;
-  decltype(&decode_kernel_w4<kFp8>) kernel = decode_kernel_w2<kFp8>;
+  decltype(&decode_kernel_w4<kFp8, kMulti>) kernel = decode_kernel_w2<kFp8, kMulti>;
   if (splits >= kHeadPerWaveMinSplits && a.num_kv_heads >= 4 && a.num_kv_heads <= 8 &&
       keys_per_split >= kHeadPerWaveMinKeys) {
     const long long units = static_cast<long long>(a.batch) * splits;
     per_wg = static_cast<int>(std::max<long long>(1, std::min<long long>(splits, units / kHeadPerWaveTarget)));
     grid = static_cast<unsigned>(static_cast<long long>(a.batch) * ((splits + per_wg - 1) / per_wg));
     threads = 64 * a.num_kv_heads;
-    kernel = decode_kernel_hw<kFp8>;
+    kernel = decode_kernel_hw<kFp8, kMulti>;
   } else if (splits == 1 && !short_chunks && a.num_kv_heads % 2 == 0) {
     grid = static_cast<unsigned>(a.batch) * (a.num_kv_heads / 2);
     threads = 512;
-    kernel = decode_kernel_w8p<kFp8>;
+    kernel = decode_kernel_w8p<kFp8, kMulti>;
   } else if (splits >= kSplitPerWaveMin && !short_chunks) {
     grid = static_cast<unsigned>(a.batch) * a.num_kv_heads * ((splits + 3) / 4);
     threads = 256;
-    kernel = decode_kernel_ps<kFp8>;
+    kernel = decode_kernel_ps<kFp8, kMulti>;
   } else if (!short_chunks) {
     threads = 256;
-    kernel = decode_kernel_w4<kFp8>;
+    kernel = decode_kernel_w4<kFp8, kMulti>;
   }
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, stream, static_cast<const uint16_t*>(a.q), a.k, a.v,
                      a.sinks, a.cu_seqlens_k, a.batch, a.num_q_heads, a.num_kv_heads, group, a.window, scale_log2,
-                     splits, static_cast<uint16_t*>(a.o), a.lse, a.o_part, a.lse_part, per_wg, a.v_scale);
+                     splits, static_cast<uint16_t*>(a.o), a.lse, a.o_part, a.lse_part, per_wg, a.v_scale,
+                     a.cu_seqlens_q, kMulti ? a.max_q * group : group, kMulti ? a.total_q : a.batch);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
-  return a.fp8 ? launch_decode_t<true>(a, stream) : launch_decode_t<false>(a, stream);
+  if (a.cu_seqlens_q != nullptr) return launch_decode_t<false, true>(a, stream);
+  return a.fp8 ? launch_decode_t<true, false>(a, stream) : launch_decode_t<false, false>(a, stream);
 }
 
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream) {

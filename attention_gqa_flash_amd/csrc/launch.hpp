@@ -38,6 +38,13 @@ struct DecodeLaunch {
   bool fp8 = false;       // K/V caches hold E4M3 codes
   float k_scale = 1.0f;   // K = k_scale * e4m3(code)
   float v_scale = 1.0f;   // V = v_scale * e4m3(code)
+  // Multi-token-query decode (bf16 cache): sequence b's last
+  // cu_seqlens_q[b+1] - cu_seqlens_q[b] <= max_q tokens are queries, rows of
+  // q / o / lse / partials indexed by cu_seqlens_q (total_q rows);
+  // max_q * group <= 32.
+  const int32_t* cu_seqlens_q = nullptr;
+  int max_q = 1;
+  int total_q = 0;
 };
 
 struct MergeLaunch {

@@ -20,7 +20,10 @@ Infinity Cache between steps.  Each leg reports mean, median and min.
 Also reported (not part of the step or of `value`): decode at 1, 4 and 16
 splits, also against an FP8 (E4M3) cache with per-tensor scales; the tiny 256-token prefill; the long-context decode pair (16 x 32768
 cached tokens, 32 splits, full then 128-window); the ragged 32-sequence
-varlen prefill (causal and 128-window); a streaming-read and a copy
+varlen prefill (causal and 128-window); the append prefill (the last
+2048-token chunk of an 8192-token prompt; 64 x 4 draft tokens verified
+against 8192 cached tokens, also through the multi-token-query decode at 1
+and 4 splits); a streaming-read and a copy
 bandwidth reference; the engine clock (sysfs pp_dpm_sclk) sampled during the step.
 Small working sets are timed after a 512 MiB cache scrub.  The long-decode
 and ragged inputs are drawn on the device from a seeded generator (same
@@ -81,6 +84,28 @@ def decode_bytes(lengths, window, hq=HQ, hkv=HKV, kv_elem_bytes=2) -> float:
     keys = sum(min(n, window) if window > 0 else n for n in lengths)
     return float(2 * len(lengths) * hq * D * 2 + 2 * keys * hkv * D * kv_elem_bytes + hq * 4
                  + (len(lengths) + 1) * 4)
+
+
+def append_pairs(q_len: int, k_len: int, window: int) -> int:
+    """Sum of |J(p)| over the query positions p = k_len - q_len .. k_len - 1
+    (bottom-right causal, optional window)."""
+    def upto(n):  # sum over p < n of |J(p)|
+        return visible_pairs(n, window) if n > 0 else 0
+    return upto(k_len) - upto(k_len - q_len)
+
+
+def append_flops(q_lens, k_lens, window, hq=HQ) -> float:
+    return 4.0 * D * hq * sum(append_pairs(a, b, window) for a, b in zip(q_lens, k_lens))
+
+
+def append_bytes(q_lens, k_lens, window, hq=HQ, hkv=HKV) -> float:
+    """Q + O + every K/V row some query sees + sinks + both offset arrays."""
+    keys = 0
+    for a, b in zip(q_lens, k_lens):
+        first = max(0, b - a - window + 1) if window > 0 else 0
+        keys += b - first if a > 0 else 0
+    tq = sum(q_lens)
+    return float(2 * tq * hq * D * 2 + 2 * keys * hkv * D * 2 + hq * 4 + 2 * (len(q_lens) + 1) * 4)
 
 
 def decode_flops(lengths, window, hq=HQ) -> float:
@@ -580,6 +605,43 @@ def _other_configs(torch, np, binding, inputs, dev, bf16, timed, hbm_entry, mfma
         e["bound"] = "mfma" if window == 0 else "hbm"
         out["ragged_prefill_%s" % ("causal" if window == 0 else "w128")] = e
     del rq, rk, rv, ro
+    torch.cuda.synchronize()
+
+    # append prefill: the last 2048-token chunk of an 8192-token prompt, and
+    # draft-token verification (64 sequences x 4 queries against 8192 cached)
+    gen.manual_seed(4)
+    for name, q_lens, k_lens in (("chunked_prefill_last_2048_of_8192", [2048], [8192]),
+                                 ("draft_verify_64x4_ctx8192", [4] * 64, [8192] * 64)):
+        aq = _device_normal_bf16(torch, (sum(q_lens), HQ, D), gen, dev)
+        ak = _device_normal_bf16(torch, (sum(k_lens), HKV, D), gen, dev)
+        av = _device_normal_bf16(torch, (sum(k_lens), HKV, D), gen, dev)
+        asinks = torch.randn(HQ, generator=gen, device=dev, dtype=torch.float32)
+        acq = torch.tensor(np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32), device=dev)
+        ack = torch.tensor(np.concatenate([[0], np.cumsum(k_lens)]).astype(np.int32), device=dev)
+        ao = torch.empty_like(aq)
+        for window in (0, WINDOW):
+            st = timed(lambda: binding.prefill_append(aq, ak, av, asinks, acq, ack, max(q_lens), max(k_lens), window,
+                                                      scale, out=ao), scrub_each=(sum(k_lens) < 100000))
+            f, b = append_flops(q_lens, k_lens, window), append_bytes(q_lens, k_lens, window)
+            mfma_bound = name.startswith("chunked") and window == 0
+            e = mfma_entry(st, f, b) if mfma_bound else hbm_entry(st, b, f)
+            e["bound"] = "mfma" if mfma_bound else "hbm"
+            e["shape"] = "%d sequences, %s queries, %s keys, 64/8 heads, window %d" % (
+                len(q_lens), sorted(set(q_lens)), sorted(set(k_lens)), window)
+            out["%s_%s" % (name, "causal" if window == 0 else "w128")] = e
+            if name.startswith("draft"):
+                # the same verification through the multi-token-query decode
+                for s_count in (1, 4):
+                    aws = torch.empty(binding.decode_workspace_bytes(sum(q_lens), HQ, D, s_count), dtype=torch.uint8,
+                                      device=dev)
+                    st = timed(lambda: binding.decode_splitkv_multi(aq, ak, av, acq, ack, max(q_lens), max(k_lens),
+                                                                    asinks, window, scale, s_count, workspace=aws,
+                                                                    out=ao), scrub_each=(window > 0))
+                    e = hbm_entry(st, b, f)
+                    e["bound"] = "hbm"
+                    e["shape"] = "64 sequences, 4 queries, 8192 keys, 64/8 heads, window %d, S=%d" % (window, s_count)
+                    out["%s_multi_decode_s%d_%s" % (name, s_count, "causal" if window == 0 else "w128")] = e
+        del aq, ak, av, ao
     torch.cuda.synchronize()
 
     # achievable bandwidth: a 2 GiB streaming read (torch sum over fp32) and a

@@ -237,6 +237,47 @@ SINKATTN_API sinkattn_status sinkattn_decode_splitkv_fp8(
     void* o, float* lse, void* stream);
 
 /*
+ * Multi-token-query split-KV decode: each sequence's newest tokens are
+ * queries against its cache, the draft tokens a speculative or
+ * multi-token-prediction decoder hands to the target model for verification
+ * (Perplexity, "GPT-OSS on day 0", in-house inference engine; Baseten, "How
+ * to run GPT OSS 120B at 500+ tokens per second on NVIDIA GPUs", next
+ * performance optimizations).  The result equals sinkattn_prefill_append on
+ * the same arguments (query r of sequence b at position Lk_b - Lq_b + r,
+ * bottom-right causal, optional window), computed by the decode kernels: one
+ * pass over each split of the keys serves all Lq_b tokens and the query
+ * heads of a KV head together, so the cache is read once per KV head.
+ *
+ *   q             bf16 [total_q, num_q_heads, head_dim], packed by
+ *                 cu_seqlens_q (int32 [batch + 1], device)
+ *   k_cache,
+ *   v_cache       bf16 [total_kv, num_kv_heads, head_dim], packed by
+ *                 cu_seqlens_k (int32 [batch + 1], device)
+ *   max_seqlen_q  host int >= every Lq_b; max_seqlen_q * (num_q_heads /
+ *                 num_kv_heads) <= 32 (else SINKATTN_ERR_UNSUPPORTED)
+ *   max_seqlen_k  host int >= every Lk_b (>= 1)
+ *   total_q       rows of q / o / lse
+ *   num_splits,
+ *   workspace     as sinkattn_decode_splitkv, sized by
+ *                 sinkattn_decode_workspace_bytes(total_q, num_q_heads,
+ *                 head_dim, num_splits); the sink enters split 0 only
+ *   o, lse        bf16 [total_q, num_q_heads, head_dim]; fp32
+ *                 [total_q, num_q_heads] or NULL
+ *
+ * Device-side preconditions besides the shared ones: 0 <= Lq_b <= Lk_b and
+ * Lk_b >= 1 (SINKATTN_DEBUG_CHECKS=1 reports violations).
+ */
+SINKATTN_API sinkattn_status sinkattn_decode_splitkv_multi(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+    int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t total_q,
+    const float* sinks,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t window, float softmax_scale, int32_t num_splits,
+    void* workspace, size_t workspace_bytes,
+    void* o, float* lse, void* stream);
+
+/*
  * Log-sum-exp merge of num_parts partial results, each normalised by its own
  * denominator (the combination step that the split-KV form of the
  * Perplexity page's online softmax implies; the page does not print it):

@@ -27,7 +27,8 @@ def _lib():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted([
-        "sinkattn_decode_splitkv", "sinkattn_decode_splitkv_fp8", "sinkattn_decode_workspace_bytes",
+        "sinkattn_decode_splitkv", "sinkattn_decode_splitkv_fp8", "sinkattn_decode_splitkv_multi",
+        "sinkattn_decode_workspace_bytes",
         "sinkattn_last_error", "sinkattn_merge_lse", "sinkattn_prefill_append", "sinkattn_prefill_varlen",
         "sinkattn_version"])
 
@@ -202,3 +203,36 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(binding.SinkAttnError):
         binding.library()
+
+
+def _decode_multi(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cuq=FAKE, cuk=FAKE2, batch=4, mq=4, mk=100, tq=16, sinks=None, hq=64, hkv=8,
+             d=64, window=0, scale=0.125, splits=1, ws=None, ws_bytes=0, o=FAKE, lse=None)
+    a.update(kw)
+    return lib.sinkattn_decode_splitkv_multi(a["q"], a["k"], a["v"], a["cuq"], a["cuk"], a["batch"], a["mq"],
+                                             a["mk"], a["tq"], a["sinks"], a["hq"], a["hkv"], a["d"], a["window"],
+                                             a["scale"], a["splits"], a["ws"], a["ws_bytes"], a["o"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mq=5), 2),                  # 5 tokens x 8 heads > 32 columns
+    (dict(hq=64, hkv=2, mq=2), 2),    # a group of 32 leaves room for one token only
+    (dict(cuq=None), 1),
+    (dict(hq=8, hkv=8, mq=20, tq=16), 1),  # max_seqlen_q above total_q
+    (dict(mq=-1), 1),
+    (dict(splits=4), 3),              # no workspace
+    (dict(splits=4, ws=FAKE, ws_bytes=4 * 16 * 64 * 65 * 4 - 1), 3),  # sized for the batch, not total_q
+    (dict(mk=0), 1),
+    (dict(d=128), 2),
+])
+def test_decode_multi_rejects(kw, status):
+    lib = _lib()
+    assert _decode_multi(lib, **kw) == status
+    assert lib.sinkattn_last_error()
+
+
+def test_decode_multi_empty_is_ok_without_launch():
+    lib = _lib()
+    assert _decode_multi(lib, batch=0) == 0
+    assert _decode_multi(lib, batch=0, cuq=None) == 0
+    assert _decode_multi(lib, tq=0, mq=0) == 0

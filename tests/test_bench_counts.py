@@ -63,3 +63,16 @@ def test_gpus_above_one_exits():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("q_len,k_len", [(1, 1), (1, 9), (3, 9), (9, 9), (5, 300), (0, 7)])
+@pytest.mark.parametrize("window", [0, 1, 4, 128])
+def test_append_counts_by_enumeration(q_len, k_len, window):
+    """Append pairs and attended K/V rows (bottom-right causal) by brute force."""
+    b = _bench()
+    pos = range(k_len - q_len, k_len)
+    brute = sum(1 for p in pos for j in range(p + 1) if window <= 0 or j > p - window)
+    assert b.append_pairs(q_len, k_len, window) == brute
+    rows = {j for p in pos for j in range(p + 1) if window <= 0 or j > p - window}
+    expect = 2 * q_len * 64 * 64 * 2 + 2 * len(rows) * 8 * 64 * 2 + 64 * 4 + 2 * 2 * 4
+    assert b.append_bytes([q_len], [k_len], window) == expect

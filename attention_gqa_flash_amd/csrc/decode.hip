@@ -60,6 +60,11 @@ constexpr long long kHeadPerWaveTarget = 512;
 // the time the partials and their merge take (16 x 32768 cached tokens,
 // 128-key window, 32 splits: 4.9 against 13.5 us back to back).
 constexpr int kDirectMaxKeys = 1024;
+// A range of at most kDirectWholeKeys keys (a 128-key window layer, also
+// with a few query tokens before it) is evaluated whole at any split count:
+// 64 x 4 draft tokens with a 128-key window, 4 splits of 33 keys, took
+// 0.040 ms split and merged against 0.019 ms as one range.
+constexpr int kDirectWholeKeys = 256;
 
 // One 32-key tile of one wave, in registers, K and V rows in coalesced
 // order.  bf16 cache: lane l holds the 16-byte chunk l % 8 of rows
@@ -586,7 +591,8 @@ static long long max_range(const DecodeLaunch& a) {
 
 bool decode_merges_in_kernel(const DecodeLaunch& a) {
   const long long keys_per_split = (max_range(a) + a.num_splits - 1) / a.num_splits;
-  return a.num_splits > 1 && keys_per_split <= kKeys && max_range(a) <= kDirectMaxKeys;
+  return a.num_splits > 1 && max_range(a) <= kDirectMaxKeys &&
+         (keys_per_split <= kKeys || max_range(a) <= kDirectWholeKeys);
 }
 
 template <bool kFp8, bool kMulti>

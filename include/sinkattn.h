@@ -181,10 +181,11 @@ SINKATTN_API size_t sinkattn_decode_workspace_bytes(int32_t batch, int32_t num_q
  *                  partials are combined with the log-sum-exp merge
  *                  (sinkattn_merge_lse) before returning.  The merge is
  *                  exact, so every S gives the same result up to fp32
- *                  rounding; when the chunks would hold at most 32 keys of a
- *                  range of at most 1024 (window layers with many splits),
- *                  the range is evaluated whole (as S = 1) and the workspace
- *                  is not touched.
+ *                  rounding; when the range is at most 256 keys, or the
+ *                  chunks would hold at most 32 keys of a range of at most
+ *                  1024 (window layers with several splits), the range is
+ *                  evaluated whole (as S = 1) and the workspace is not
+ *                  touched.
  *   workspace      device buffer of >= sinkattn_decode_workspace_bytes(...)
  *                  bytes when S > 1 (SINKATTN_ERR_WORKSPACE otherwise); may
  *                  be NULL when S == 1

@@ -9,7 +9,9 @@ too wide, the wrong GQA grouping, a base-2 lse, an unweighted merge; and
 for the FP8 oracle (checked by tests/test_oracle_fp8.py): exponent bias 8
 instead of 7, subnormals scaled like normals, the two scales swapped; and
 for the append oracle (tests/test_oracle_append.py): top-left causal
-alignment, the window one key too wide, queries one position late.
+alignment, the window one key too wide, queries one position late; and for
+the paged oracle (tests/test_oracle_paged.py): page and slot swapped, the
+slot off by one.
 """
 
 import os
@@ -48,6 +50,12 @@ APPEND_MUTATIONS = [
 ]
 
 
+PAGED_MUTATIONS = [
+    ("pages[bt[b, j // page_size], j % page_size]", "pages[bt[b, j % page_size], j // page_size]"),
+    ("pages[bt[b, j // page_size], j % page_size]", "pages[bt[b, j // page_size], (j + 1) % page_size]"),
+]
+
+
 def _run_pins(tmp_path, module, old, new, pin_file):
     for sub in ("oracle", "tests", "attention_gqa_flash_amd"):
         shutil.copytree(os.path.join(ROOT, sub), tmp_path / sub,
@@ -75,3 +83,8 @@ def test_fp8_pins_catch_planted_mistake(tmp_path, old, new):
 @pytest.mark.parametrize("old,new", APPEND_MUTATIONS, ids=["append_%d" % i for i in range(len(APPEND_MUTATIONS))])
 def test_append_pins_catch_planted_mistake(tmp_path, old, new):
     _run_pins(tmp_path, "append.py", old, new, "tests/test_oracle_append.py")
+
+
+@pytest.mark.parametrize("old,new", PAGED_MUTATIONS, ids=["paged_%d" % i for i in range(len(PAGED_MUTATIONS))])
+def test_paged_pins_catch_planted_mistake(tmp_path, old, new):
+    _run_pins(tmp_path, "paged.py", old, new, "tests/test_oracle_paged.py")

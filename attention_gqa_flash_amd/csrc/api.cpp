@@ -77,6 +77,7 @@ sinkattn_status check_failed(unsigned flags) {
       {sinkattn::kCheckV, "v holds NaN or Inf"},
       {sinkattn::kCheckParts, "o_parts holds NaN or Inf, or lse_parts NaN or +inf"},
       {sinkattn::kCheckAppend, "a sequence has fewer keys than queries (cu_seqlens_k vs cu_seqlens_q)"},
+      {sinkattn::kCheckPages, "a page id is outside the pool, or a block table row is too short"},
   };
   std::string msg = "debug checks failed:";
   for (const auto& n : kNames)
@@ -196,8 +197,11 @@ static sinkattn_status decode_common(const void* q, const void* k_cache, const v
                                      int32_t window, float softmax_scale, int32_t num_splits, void* workspace,
                                      size_t workspace_bytes, void* o, float* lse, void* stream, bool fp8,
                                      float k_scale, float v_scale, const int32_t* cu_seqlens_q = nullptr,
-                                     int32_t max_seqlen_q = 1, int32_t total_q = 0) {
+                                     int32_t max_seqlen_q = 1, int32_t total_q = 0,
+                                     const int32_t* block_table = nullptr, int32_t max_pages = 0,
+                                     int32_t page_size = 0, int32_t num_pages = 0) {
   const bool multi = cu_seqlens_q != nullptr;
+  const bool paged = block_table != nullptr;  // cu_seqlens_k then holds the lengths [batch]
   if (batch < 0 || max_seqlen_k < 0) return fail(SINKATTN_ERR_INVALID_ARG, "batch and max_seqlen_k must be >= 0");
   if (multi && (max_seqlen_q < 0 || total_q < 0))
     return fail(SINKATTN_ERR_INVALID_ARG, "max_seqlen_q and total_q must be >= 0");
@@ -219,7 +223,7 @@ static sinkattn_status decode_common(const void* q, const void* k_cache, const v
     return fail(SINKATTN_ERR_INVALID_ARG, "max_seqlen_q (%d) exceeds total_q (%d)", max_seqlen_q, total_q);
   if (batch == 0 || (multi && (max_seqlen_q == 0 || total_q == 0))) return ok();
   if (!q || !k_cache || !v_cache || !o || !cu_seqlens_k)
-    return fail(SINKATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, o and cu_seqlens_k must not be NULL");
+    return fail(SINKATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, o and the sequence offsets / lengths must not be NULL");
   if (max_seqlen_k < 1) return fail(SINKATTN_ERR_INVALID_ARG, "decode needs max_seqlen_k >= 1");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
     return fail(SINKATTN_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be 16-byte aligned");
@@ -235,13 +239,20 @@ static sinkattn_status decode_common(const void* q, const void* k_cache, const v
         return st;
       if ((st = hip_queue(sinkattn::check_append(cu_seqlens_q, cu_seqlens_k, batch, s))) != SINKATTN_OK) return st;
     }
-    if ((st = hip_queue(sinkattn::check_offsets(cu_seqlens_k, batch, max_seqlen_k, 1, -1, s))) != SINKATTN_OK)
+    if (paged) {
+      if ((st = hip_queue(sinkattn::check_paged(cu_seqlens_k, block_table, batch, max_pages, page_size, num_pages,
+                                                max_seqlen_k, s))) != SINKATTN_OK)
+        return st;
+    } else if ((st = hip_queue(sinkattn::check_offsets(cu_seqlens_k, batch, max_seqlen_k, 1, -1, s))) !=
+               SINKATTN_OK) {
       return st;
+    }
     if ((st = hip_queue(sinkattn::check_sinks(sinks, num_q_heads, s))) != SINKATTN_OK) return st;
     const size_t qn = static_cast<size_t>(multi ? total_q : batch) * num_q_heads * head_dim;
     if ((st = hip_queue(sinkattn::check_bf16(q, qn, sinkattn::kCheckQ, s))) != SINKATTN_OK) return st;
     int total_kv = 0;
     if ((st = check_result(s, &total_kv)) != SINKATTN_OK) return st;
+    if (paged) total_kv = num_pages * page_size;  // the whole pool
     const size_t kvn = static_cast<size_t>(total_kv) * num_kv_heads * head_dim;
     if (fp8) {
       if ((st = hip_queue(sinkattn::check_e4m3(k_cache, kvn, sinkattn::kCheckK, s))) != SINKATTN_OK) return st;
@@ -254,7 +265,10 @@ static sinkattn_status decode_common(const void* q, const void* k_cache, const v
   }
   sinkattn::DecodeLaunch a{q, k_cache, v_cache, sinks, cu_seqlens_k, batch, max_seqlen_k, num_q_heads, num_kv_heads,
                            window, num_splits, softmax_scale, o, lse, nullptr, nullptr, fp8,
-                           fp8 ? k_scale : 1.0f, fp8 ? v_scale : 1.0f, cu_seqlens_q, max_seqlen_q, total_q};
+                           fp8 ? k_scale : 1.0f, fp8 ? v_scale : 1.0f, cu_seqlens_q, max_seqlen_q, total_q,
+                           block_table, max_pages, 0, num_pages};
+  if (paged)
+    while ((1 << a.page_shift) < page_size) ++a.page_shift;
   // Output rows: one per sequence, or (multi) one per query token.
   const int32_t rows_out = multi ? total_q : batch;
   if (num_splits == 1) return hip_status(sinkattn::launch_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
@@ -310,6 +324,31 @@ sinkattn_status sinkattn_decode_splitkv_multi(const void* q, const void* k_cache
   return decode_common(q, k_cache, v_cache, cu_seqlens_k, batch, max_seqlen_k, sinks, num_q_heads, num_kv_heads,
                        head_dim, window, softmax_scale, num_splits, workspace, workspace_bytes, o, lse, stream, false,
                        1.0f, 1.0f, cu_seqlens_q, max_seqlen_q, total_q);
+}
+
+sinkattn_status sinkattn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                                      const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                                      int32_t max_pages, int32_t page_size, int32_t num_pages, int32_t max_seqlen_k,
+                                      const float* sinks, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t window, float softmax_scale, int32_t num_splits, void* workspace,
+                                      size_t workspace_bytes, void* o, float* lse, void* stream) {
+  if (page_size < 16 || page_size > (1 << 20) || (page_size & (page_size - 1)) != 0)
+    return fail(SINKATTN_ERR_UNSUPPORTED, "page_size must be a power of two in [16, 2^20] (got %d)", page_size);
+  if (batch < 0 || max_pages < 0 || num_pages < 0)
+    return fail(SINKATTN_ERR_INVALID_ARG, "batch, max_pages and num_pages must be >= 0");
+  if (batch > 0 && (max_pages < 1 || num_pages < 1))
+    return fail(SINKATTN_ERR_INVALID_ARG, "max_pages and num_pages must be >= 1");
+  if (static_cast<long long>(max_pages) * page_size < max_seqlen_k)
+    return fail(SINKATTN_ERR_INVALID_ARG, "max_pages * page_size (%lld) is below max_seqlen_k (%d)",
+                static_cast<long long>(max_pages) * page_size, max_seqlen_k);
+  if (static_cast<long long>(num_pages) * page_size > 0x7fffffffLL)
+    return fail(SINKATTN_ERR_UNSUPPORTED, "num_pages * page_size must stay below 2^31 tokens");
+  if (batch > 0 && (block_table == nullptr || seq_lens == nullptr))
+    return fail(SINKATTN_ERR_INVALID_ARG, "block_table and seq_lens must not be NULL");
+  // (batch 0 validates the remaining arguments and returns)
+  return decode_common(q, k_pages, v_pages, seq_lens, batch, max_seqlen_k, sinks, num_q_heads, num_kv_heads,
+                       head_dim, window, softmax_scale, num_splits, workspace, workspace_bytes, o, lse, stream, false,
+                       1.0f, 1.0f, nullptr, 1, 0, block_table, max_pages, page_size, num_pages);
 }
 
 sinkattn_status sinkattn_merge_lse(const float* o_parts, const float* lse_parts, int32_t num_parts, int32_t n,

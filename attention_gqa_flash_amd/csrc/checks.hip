@@ -50,6 +50,25 @@ __global__ void check_append_kernel(const int32_t* __restrict__ cu_q, const int3
   if (bits != 0u) atomicOr(&g_check_flags, bits);
 }
 
+// Paged decode: lengths within [1, max_len], tables long enough, page ids
+// inside the pool.  One thread per sequence.
+__global__ void check_paged_kernel(const int32_t* __restrict__ lens, const int32_t* __restrict__ table, int batch,
+                                   int max_pages, int page_size, int num_pages, int max_len) {
+  unsigned bits = 0;
+  for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < batch; b += gridDim.x * blockDim.x) {
+    const int n = lens[b];
+    if (n < 1) bits |= kCheckLengthMin;
+    if (n > max_len) bits |= kCheckLengthMax;
+    const int pages = n > 0 ? (min(n, max_len) + page_size - 1) / page_size : 0;
+    if (pages > max_pages) bits |= kCheckPages;
+    for (int p = 0; p < min(pages, max_pages); ++p) {
+      const int id = table[static_cast<size_t>(b) * max_pages + p];
+      if (id < 0 || id >= num_pages) bits |= kCheckPages;
+    }
+  }
+  if (bits != 0u) atomicOr(&g_check_flags, bits);
+}
+
 // Floating-point classes are tested on the bit patterns: the library is
 // built without NaN semantics (-fno-honor-nans), so x != x would fold away.
 __device__ __forceinline__ bool is_nan_bits(uint32_t u) { return (u & 0x7fffffffu) > 0x7f800000u; }
@@ -117,6 +136,14 @@ hipError_t check_offsets(const int32_t* cu, int batch, int max_len, int min_len,
 hipError_t check_append(const int32_t* cu_q, const int32_t* cu_k, int batch, hipStream_t stream) {
   if (batch <= 0) return hipSuccess;
   hipLaunchKernelGGL(check_append_kernel, dim3(grid_for(batch)), dim3(256), 0, stream, cu_q, cu_k, batch);
+  return hipGetLastError();
+}
+
+hipError_t check_paged(const int32_t* seq_lens, const int32_t* block_table, int batch, int max_pages,
+                       int page_size, int num_pages, int max_len, hipStream_t stream) {
+  if (batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(check_paged_kernel, dim3(grid_for(batch)), dim3(256), 0, stream, seq_lens, block_table, batch,
+                     max_pages, page_size, num_pages, max_len);
   return hipGetLastError();
 }
 

@@ -106,6 +106,39 @@ __device__ __forceinline__ void load_tile(TileRegs<kFp8>& t, const void* __restr
   }
 }
 
+// Paged cache (bf16): pages [num_pages, 1 << page_shift, hkv, 64]; key j
+// of the sequence is slot j & (page_size - 1) of page row[j >> page_shift].
+// A 32-key tile spans at most three pages when page_size >= 16; their ids
+// are uniform over the wave (scalar loads), clamped to the pool so that a bad
+// table cannot move an access out of bounds.  Rows at or beyond `end` repeat
+// row end - 1, as in load_tile.
+__device__ __forceinline__ void load_tile_paged(TileRegs<false>& t, const void* __restrict__ k,
+                                                const void* __restrict__ v, const int32_t* __restrict__ row,
+                                                int max_pages, int page_shift, int num_pages, int hkv, int g,
+                                                int k0, int end, int lane) {
+  const uint16_t* kh = static_cast<const uint16_t*>(k);
+  const uint16_t* vh = static_cast<const uint16_t*>(v);
+  const int p0 = k0 >> page_shift;
+  const int plast = min((end - 1) >> page_shift, max_pages - 1);
+  int pid[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int id = row[min(p0 + j, plast)];
+    pid[j] = min(max(id, 0), num_pages - 1);
+  }
+  const int slot_mask = (1 << page_shift) - 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = min(k0 + (lane >> 3) + 8 * i, end - 1);
+    const int rel = (key >> page_shift) - p0;
+    const int id = rel == 0 ? pid[0] : (rel == 1 ? pid[1] : pid[2]);
+    const size_t tok = (static_cast<size_t>(id) << page_shift) + (key & slot_mask);
+    const size_t off = (tok * hkv + g) * kHeadDim + (lane & 7) * 8;
+    t.k[i] = load16_stream(kh + off);
+    t.v[i] = load16_stream(vh + off);
+  }
+}
+
 // 16 E4M3 codes (one 16-byte chunk) -> 16 bf16 in two 16-byte halves.  E4M3
 // values are exactly representable in bf16; the conversion runs with scale 1.
 __device__ __forceinline__ void e4m3x16_to_bf16(u32x4_t c, u32x4_t& lo, u32x4_t& hi) {
@@ -162,15 +195,19 @@ __device__ __forceinline__ void stage_tile(const TileRegs<kFp8>& cur, uint16_t* 
 // 32 columns).  Token t sits at position len - nq_b + t and sees the keys at
 // or before it (and, with a window W, after position - W): the causal mask
 // aligned at the bottom right, applied per column.
+//
+// kPaged: the cache is paged (load_tile_paged); cu_seqlens_k then holds the
+// sequence lengths [batch] instead of offsets.
 template <int kDecWaves, bool kSplitPerWave, bool kHeadPerWave = false, int kHeadsPerWG = 1, bool kFp8 = false,
-          bool kMulti = false>
+          bool kMulti = false, bool kPaged = false>
 __device__ __forceinline__ void decode_body(
     const uint16_t* __restrict__ q, const void* __restrict__ k,
     const void* __restrict__ v, const float* __restrict__ sinks,
     const int32_t* __restrict__ cu_seqlens_k, int batch, int hq, int hkv, int group,
     int window, float scale_log2, int num_splits, uint16_t* __restrict__ o,
     float* __restrict__ lse, float* __restrict__ o_part, float* __restrict__ lse_part, int splits_per_wg,
-    float v_scale, const int32_t* __restrict__ cu_seqlens_q, int ncols, int out_rows) {
+    float v_scale, const int32_t* __restrict__ cu_seqlens_q, int ncols, int out_rows,
+    const int32_t* __restrict__ block_table, int max_pages, int page_shift, int num_pages) {
   // Wave-private K and V staging tiles (2 x 4 KiB per wave); the whole
   // buffer is reused for the cross-wave merge of up to 32 heads x 64 d per
   // wave (index (wave * group + head) * 64 + d).
@@ -214,8 +251,15 @@ __device__ __forceinline__ void decode_body(
   const int g = x % hkv;
   const int b = x / hkv;
 
-  const int base = cu_seqlens_k[b];
-  const int len = cu_seqlens_k[b + 1] - base;
+  const int base = kPaged ? 0 : cu_seqlens_k[b];
+  const int len = kPaged ? cu_seqlens_k[b] : cu_seqlens_k[b + 1] - base;
+  const int32_t* bt_row = kPaged ? block_table + static_cast<size_t>(b) * max_pages : nullptr;
+  auto load = [&](TileRegs<kFp8>& t, int k_first, int k_end) {
+    if constexpr (kPaged)
+      load_tile_paged(t, k, v, bt_row, max_pages, page_shift, num_pages, hkv, g, k_first, k_end, lane);
+    else
+      load_tile(t, k, v, base, hkv, g, k_first, k_end, lane);
+  };
   // Query tokens of this sequence (one unless kMulti); more than len breaks
   // a precondition and is clamped.
   int q_row0 = b, nq = 1;
@@ -251,7 +295,7 @@ __device__ __forceinline__ void decode_body(
   TileRegs<kFp8> cur, nxt;
   constexpr int kStride = kOwnSplit ? kKeys : kKeys * kIl;
   int k0 = kOwnSplit ? a : a + kKeys * wl;
-  if (k0 < e) load_tile(cur, k, v, base, hkv, g, k0, e, lane);
+  if (k0 < e) load(cur, k0, e);
 
   bf16x8_t qreg[4];
 #pragma unroll
@@ -376,9 +420,9 @@ __device__ __forceinline__ void decode_body(
       for (; k0 < e; k0 += kKeys) {
         const int k1 = k0 + kKeys;
         if (k1 < e)
-          load_tile(nxt, k, v, base, hkv, g, k1, e, lane);
+          load(nxt, k1, e);
         else if (sp + 1 < split_stop && e < split_end(sp + 1))
-          load_tile(nxt, k, v, base, hkv, g, e, split_end(sp + 1), lane);
+          load(nxt, e, split_end(sp + 1));
         tile_step(cur, k0, e);
         cur = nxt;
       }
@@ -397,7 +441,7 @@ __device__ __forceinline__ void decode_body(
 
   for (; k0 < e; k0 += kStride) {
     const int k1 = k0 + kStride;
-    if (k1 < e) load_tile(nxt, k, v, base, hkv, g, k1, e, lane);
+    if (k1 < e) load(nxt, k1, e);
     tile_step(cur, k0, e);
     cur = nxt;
   }
@@ -491,31 +535,32 @@ __device__ __forceinline__ float wave_sum(float x) {
       const float *__restrict__ sinks, const int32_t *__restrict__ cu_seqlens_k, int batch, int hq, int hkv, \
       int group, int window, float scale_log2, int num_splits, uint16_t *__restrict__ o, float *__restrict__ lse, \
       float *__restrict__ o_part, float *__restrict__ lse_part, int splits_per_wg, float v_scale,             \
-      const int32_t *__restrict__ cu_seqlens_q, int ncols, int out_rows
+      const int32_t *__restrict__ cu_seqlens_q, int ncols, int out_rows, const int32_t *__restrict__ block_table, \
+      int max_pages, int page_shift, int num_pages
 #define SINKATTN_DECODE_ARGS                                                                                  \
   q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, group, window, scale_log2, num_splits, o, lse, o_part, lse_part, \
-      splits_per_wg, v_scale, cu_seqlens_q, ncols, out_rows
+      splits_per_wg, v_scale, cu_seqlens_q, ncols, out_rows, block_table, max_pages, page_shift, num_pages
 
 // Short splits (at most kShortChunk keys): two-wave workgroups at three
 // waves per SIMD, i.e. more workgroups and so more loads in flight.
-template <bool kFp8, bool kMulti>
+template <bool kFp8, bool kMulti, bool kPaged>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3, 3))) void decode_kernel_w2(
     SINKATTN_DECODE_PARAMS) {
-  decode_body<2, false, false, 1, kFp8, kMulti>(SINKATTN_DECODE_ARGS);
+  decode_body<2, false, false, 1, kFp8, kMulti, kPaged>(SINKATTN_DECODE_ARGS);
 }
 
 // Four or more long splits: four-wave workgroups, one split per wave (each
 // wave writes its split's partial; no cross-wave merge).
-template <bool kFp8, bool kMulti>
+template <bool kFp8, bool kMulti, bool kPaged>
 __global__ __launch_bounds__(256) void decode_kernel_ps(SINKATTN_DECODE_PARAMS) {
-  decode_body<4, true, false, 1, kFp8, kMulti>(SINKATTN_DECODE_ARGS);
+  decode_body<4, true, false, 1, kFp8, kMulti, kPaged>(SINKATTN_DECODE_ARGS);
 }
 
 // Four or more splits over 4 to 8 KV heads: one workgroup per (sequence,
 // split), one wave per KV head.
-template <bool kFp8, bool kMulti>
+template <bool kFp8, bool kMulti, bool kPaged>
 __global__ __launch_bounds__(512) void decode_kernel_hw(SINKATTN_DECODE_PARAMS) {
-  decode_body<8, false, true, 1, kFp8, kMulti>(SINKATTN_DECODE_ARGS);
+  decode_body<8, false, true, 1, kFp8, kMulti, kPaged>(SINKATTN_DECODE_ARGS);
 }
 
 // One split of more than kShortChunk keys over an even number of KV heads:
@@ -523,17 +568,17 @@ __global__ __launch_bounds__(512) void decode_kernel_hw(SINKATTN_DECODE_PARAMS) 
 // waves each, so that a workgroup reads 256 contiguous bytes of every token
 // row it touches (a plain-load probe: 6.4-6.6 TB/s against 6.0-6.2 for one
 // head per workgroup; 64 x 8192 at S = 1 from 180 to 165 us).
-template <bool kFp8, bool kMulti>
+template <bool kFp8, bool kMulti, bool kPaged>
 __global__ __launch_bounds__(512) void decode_kernel_w8p(SINKATTN_DECODE_PARAMS) {
-  decode_body<8, false, false, 2, kFp8, kMulti>(SINKATTN_DECODE_ARGS);
+  decode_body<8, false, false, 2, kFp8, kMulti, kPaged>(SINKATTN_DECODE_ARGS);
 }
 
 // Long splits: four-wave workgroups at the compiler's own register budget
 // (two waves per SIMD; at three, S = 4 on 64 x 8192 would end on a
 // two-thirds-full round of workgroups).
-template <bool kFp8, bool kMulti>
+template <bool kFp8, bool kMulti, bool kPaged>
 __global__ __launch_bounds__(256) void decode_kernel_w4(SINKATTN_DECODE_PARAMS) {
-  decode_body<4, false, false, 1, kFp8, kMulti>(SINKATTN_DECODE_ARGS);
+  decode_body<4, false, false, 1, kFp8, kMulti, kPaged>(SINKATTN_DECODE_ARGS);
 }
 
 #undef SINKATTN_DECODE_PARAMS
@@ -595,7 +640,7 @@ bool decode_merges_in_kernel(const DecodeLaunch& a) {
          (keys_per_split <= kKeys || max_range(a) <= kDirectWholeKeys);
 }
 
-template <bool kFp8, bool kMulti>
+template <bool kFp8, bool kMulti, bool kPaged>
 static hipError_t launch_decode_t(const DecodeLaunch& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
   // Splits of at most 32 keys: the whole range in one workgroup per
@@ -607,36 +652,38 @@ static hipError_t launch_decode_t(const DecodeLaunch& a, hipStream_t stream) {
   unsigned grid = static_cast<unsigned>(a.batch) * a.num_kv_heads * splits;
   unsigned threads = 128;
   int per_wg = 1;
-  decltype(&decode_kernel_w4<kFp8, kMulti>) kernel = decode_kernel_w2<kFp8, kMulti>;
+  decltype(&decode_kernel_w4<kFp8, kMulti, kPaged>) kernel = decode_kernel_w2<kFp8, kMulti, kPaged>;
   if (splits >= kHeadPerWaveMinSplits && a.num_kv_heads >= 4 && a.num_kv_heads <= 8 &&
       keys_per_split >= kHeadPerWaveMinKeys) {
     const long long units = static_cast<long long>(a.batch) * splits;
     per_wg = static_cast<int>(std::max<long long>(1, std::min<long long>(splits, units / kHeadPerWaveTarget)));
     grid = static_cast<unsigned>(static_cast<long long>(a.batch) * ((splits + per_wg - 1) / per_wg));
     threads = 64 * a.num_kv_heads;
-    kernel = decode_kernel_hw<kFp8, kMulti>;
+    kernel = decode_kernel_hw<kFp8, kMulti, kPaged>;
   } else if (splits == 1 && !short_chunks && a.num_kv_heads % 2 == 0) {
     grid = static_cast<unsigned>(a.batch) * (a.num_kv_heads / 2);
     threads = 512;
-    kernel = decode_kernel_w8p<kFp8, kMulti>;
+    kernel = decode_kernel_w8p<kFp8, kMulti, kPaged>;
   } else if (splits >= kSplitPerWaveMin && !short_chunks) {
     grid = static_cast<unsigned>(a.batch) * a.num_kv_heads * ((splits + 3) / 4);
     threads = 256;
-    kernel = decode_kernel_ps<kFp8, kMulti>;
+    kernel = decode_kernel_ps<kFp8, kMulti, kPaged>;
   } else if (!short_chunks) {
     threads = 256;
-    kernel = decode_kernel_w4<kFp8, kMulti>;
+    kernel = decode_kernel_w4<kFp8, kMulti, kPaged>;
   }
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, stream, static_cast<const uint16_t*>(a.q), a.k, a.v,
                      a.sinks, a.cu_seqlens_k, a.batch, a.num_q_heads, a.num_kv_heads, group, a.window, scale_log2,
                      splits, static_cast<uint16_t*>(a.o), a.lse, a.o_part, a.lse_part, per_wg, a.v_scale,
-                     a.cu_seqlens_q, kMulti ? a.max_q * group : group, kMulti ? a.total_q : a.batch);
+                     a.cu_seqlens_q, kMulti ? a.max_q * group : group, kMulti ? a.total_q : a.batch, a.block_table,
+                     a.max_pages, a.page_shift, a.num_pages);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
-  if (a.cu_seqlens_q != nullptr) return launch_decode_t<false, true>(a, stream);
-  return a.fp8 ? launch_decode_t<true, false>(a, stream) : launch_decode_t<false, false>(a, stream);
+  if (a.block_table != nullptr) return launch_decode_t<false, false, true>(a, stream);
+  if (a.cu_seqlens_q != nullptr) return launch_decode_t<false, true, false>(a, stream);
+  return a.fp8 ? launch_decode_t<true, false, false>(a, stream) : launch_decode_t<false, false, false>(a, stream);
 }
 
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream) {

@@ -45,6 +45,11 @@ struct DecodeLaunch {
   const int32_t* cu_seqlens_q = nullptr;
   int max_q = 1;
   int total_q = 0;
+  // Paged cache (bf16, one token per sequence): k / v are pages
+  // [num_pages, 1 << page_shift, num_kv_heads, 64], block_table [batch,
+  // max_pages] page ids, and cu_seqlens_k holds the lengths [batch].
+  const int32_t* block_table = nullptr;
+  int max_pages = 0, page_shift = 0, num_pages = 0;
 };
 
 struct MergeLaunch {
@@ -75,7 +80,8 @@ enum CheckBits : unsigned {
   kCheckV = 1u << 8,             // NaN / Inf in v
   kCheckParts = 1u << 9,         // NaN / Inf in o_parts, NaN / +inf in lse_parts
   kCheckAppend = 1u << 10,       // append prefill: a sequence with fewer keys than queries
-  kCheckAll = (1u << 11) - 1u,
+  kCheckPages = 1u << 11,        // paged decode: a page id outside the pool or a table too short
+  kCheckAll = (1u << 12) - 1u,
 };
 hipError_t check_clear(hipStream_t stream);
 hipError_t check_offsets(const int32_t* cu, int batch, int max_len, int min_len, int total_limit,
@@ -83,6 +89,10 @@ hipError_t check_offsets(const int32_t* cu, int batch, int max_len, int min_len,
 hipError_t check_sinks(const float* sinks, int n, hipStream_t stream);
 // Append prefill: every sequence has cu_k[b+1] - cu_k[b] >= cu_q[b+1] - cu_q[b].
 hipError_t check_append(const int32_t* cu_q, const int32_t* cu_k, int batch, hipStream_t stream);
+// Paged decode: 1 <= seq_lens[b] <= max_len and every page id a sequence
+// uses (the first ceil(L_b / page_size) of its table row) in [0, num_pages).
+hipError_t check_paged(const int32_t* seq_lens, const int32_t* block_table, int batch, int max_pages,
+                       int page_size, int num_pages, int max_len, hipStream_t stream);
 hipError_t check_bf16(const void* x, size_t n, unsigned bit, hipStream_t stream);
 // E4M3 codes: NaN (all exponent and mantissa bits set).
 hipError_t check_e4m3(const void* x, size_t n, unsigned bit, hipStream_t stream);

@@ -149,6 +149,49 @@ def make_append(q_lens, k_lens, hq: int, hkv: int, d: int = 64, seed: int = 0, s
 
 
 @dataclass
+class PagedDecodeInputs:
+    q: np.ndarray            # uint16 bf16 bits [B, Hq, D]
+    k_pages: np.ndarray      # uint16 bf16 bits [P, page_size, Hkv, D]
+    v_pages: np.ndarray
+    block_table: np.ndarray  # int32 [B, max_pages] (-1 past a sequence's pages)
+    seq_lens: np.ndarray     # int32 [B]
+    sinks: np.ndarray        # float32 [Hq]
+    page_size: int
+    scale: float
+    lengths: list = field(default_factory=list)
+
+
+def make_paged_decode(lengths, page_size: int, hq: int, hkv: int, d: int = 64, seed: int = 0,
+                      scale: float = 0.125, spare_pages: int = 3, fill_bits: int = 0x7FC0,
+                      sink_std: float = 1.0, rng: Optional[np.random.Generator] = None):
+    """A paged cache holding the same draws as make_decode (q -> k -> v ->
+    sinks, N(0,1) rounded to bf16), scattered into pages in a random physical
+    order (drawn after the sinks) with spare pages; slots no sequence owns hold
+    ``fill_bits`` (a bf16 NaN by default, so that a read outside a sequence's
+    tokens shows in its output)."""
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    dec = make_decode(lengths, hq, hkv, d, rng=rng, scale=scale, sink_std=sink_std)
+    n_pages = [-(-int(n) // page_size) for n in dec.lengths]
+    total = sum(n_pages) + spare_pages
+    order = rng.permutation(total)
+    kp = np.full((total, page_size, hkv, d), fill_bits, dtype=np.uint16)
+    vp = np.full((total, page_size, hkv, d), fill_bits, dtype=np.uint16)
+    bt = np.full((len(dec.lengths), max(n_pages) + 1), -1, dtype=np.int32)
+    nxt = 0
+    for b, n in enumerate(dec.lengths):
+        base = int(dec.cu_seqlens_k[b])
+        for p in range(n_pages[b]):
+            phys = int(order[nxt])
+            nxt += 1
+            bt[b, p] = phys
+            lo, hi = p * page_size, min(n, (p + 1) * page_size)
+            kp[phys, :hi - lo] = dec.k[base + lo:base + hi]
+            vp[phys, :hi - lo] = dec.v[base + lo:base + hi]
+    return PagedDecodeInputs(dec.q, kp, vp, bt, np.asarray(dec.lengths, dtype=np.int32), dec.sinks, page_size,
+                             scale, list(dec.lengths))
+
+
+@dataclass
 class DecodeFp8Inputs:
     q: np.ndarray            # uint16 bf16 bits [B, Hq, D]
     k: np.ndarray            # uint8 E4M3 codes [Tk, Hkv, D]

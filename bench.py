@@ -23,7 +23,8 @@ cached tokens, 32 splits, full then 128-window); the ragged 32-sequence
 varlen prefill (causal and 128-window); the append prefill (the last
 2048-token chunk of an 8192-token prompt; 64 x 4 draft tokens verified
 against 8192 cached tokens, also through the multi-token-query decode at 1
-and 4 splits); a streaming-read and a copy
+and 4 splits); the 64 x 8192 decode against a paged cache (16- and 64-token
+pages, shuffled); a streaming-read and a copy
 bandwidth reference; the engine clock (sysfs pp_dpm_sclk) sampled during the step.
 Small working sets are timed after a 512 MiB cache scrub.  The long-decode
 and ragged inputs are drawn on the device from a seeded generator (same
@@ -605,6 +606,31 @@ def _other_configs(torch, np, binding, inputs, dev, bf16, timed, hbm_entry, mfma
         e["bound"] = "mfma" if window == 0 else "hbm"
         out["ragged_prefill_%s" % ("causal" if window == 0 else "w128")] = e
     del rq, rk, rv, ro
+    torch.cuda.synchronize()
+
+    # paged cache: the 64 x 8192 decode with 16- and 64-token pages in a
+    # shuffled physical order (page table from a seeded host permutation)
+    gen.manual_seed(5)
+    pq = _device_normal_bf16(torch, (DEC_BATCH, HQ, D), gen, dev)
+    psinks = torch.randn(HQ, generator=gen, device=dev, dtype=torch.float32)
+    plens = torch.full((DEC_BATCH,), DEC_CTX, dtype=torch.int32, device=dev)
+    po = torch.empty_like(pq)
+    pws = torch.empty(binding.decode_workspace_bytes(DEC_BATCH, HQ, D, 16), dtype=torch.uint8, device=dev)
+    for page_size in (16, 64):
+        per_seq = DEC_CTX // page_size
+        n_pages = DEC_BATCH * per_seq
+        kp = _device_normal_bf16(torch, (n_pages, page_size, HKV, D), gen, dev)
+        vp = _device_normal_bf16(torch, (n_pages, page_size, HKV, D), gen, dev)
+        perm = np.random.default_rng(page_size).permutation(n_pages).astype(np.int32)
+        table = torch.tensor(perm.reshape(DEC_BATCH, per_seq), device=dev)
+        for s_count in (1, 4, 16):
+            st = timed(lambda: binding.decode_paged(pq, kp, vp, table, plens, DEC_CTX, psinks, 0, scale, s_count,
+                                                    workspace=pws, out=po))
+            e = hbm_entry(st, decode_bytes([DEC_CTX] * DEC_BATCH, 0))
+            e["shape"] = "B=64, ctx 8192, 64/8 heads, %d-token pages (shuffled), S=%d" % (page_size, s_count)
+            out["paged_decode_ps%d_s%d" % (page_size, s_count)] = e
+        del kp, vp
+    del pq, po, pws
     torch.cuda.synchronize()
 
     # append prefill: the last 2048-token chunk of an 8192-token prompt, and

@@ -238,6 +238,45 @@ SINKATTN_API sinkattn_status sinkattn_decode_splitkv_fp8(
     void* o, float* lse, void* stream);
 
 /*
+ * Split-KV decode against a paged KV cache: keys and values live in
+ * fixed-size pages of a shared pool, addressed per sequence through a block
+ * table (the serving layout around the decode that the Perplexity page's
+ * in-house inference engine and the FlashInfer decode template it extends
+ * read from; Baseten, "How to run GPT OSS 120B at 500+ tokens per second on
+ * NVIDIA GPUs": KV-cache-aware routing).  Token j of sequence b is slot
+ * j % page_size of page block_table[b][j / page_size]; otherwise the result
+ * is exactly sinkattn_decode_splitkv's on the gathered cache.
+ *
+ *   q              bf16 [batch, num_q_heads, head_dim]
+ *   k_pages,
+ *   v_pages        bf16 [num_pages, page_size, num_kv_heads, head_dim]
+ *   block_table    int32 [batch, max_pages], device: page ids in
+ *                  [0, num_pages); entries past a sequence's last page are
+ *                  not read
+ *   seq_lens       int32 [batch], device: L_b >= 1, <= max_seqlen_k
+ *   page_size      a power of two in [16, 2^20] (SINKATTN_ERR_UNSUPPORTED
+ *                  otherwise); max_pages * page_size >= max_seqlen_k;
+ *                  num_pages * page_size < 2^31
+ *   window, softmax_scale, num_splits, workspace, o, lse
+ *                  as sinkattn_decode_splitkv (workspace sized by
+ *                  sinkattn_decode_workspace_bytes(batch, ...))
+ *
+ * Device-side preconditions: the lengths and the page ids a sequence uses
+ * (SINKATTN_DEBUG_CHECKS=1 checks them).  Page ids outside the pool are
+ * clamped into it, so a bad table gives wrong values, never an access
+ * outside k_pages / v_pages.
+ */
+SINKATTN_API sinkattn_status sinkattn_decode_paged(
+    const void* q, const void* k_pages, const void* v_pages,
+    const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+    int32_t max_pages, int32_t page_size, int32_t num_pages, int32_t max_seqlen_k,
+    const float* sinks,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t window, float softmax_scale, int32_t num_splits,
+    void* workspace, size_t workspace_bytes,
+    void* o, float* lse, void* stream);
+
+/*
  * Multi-token-query split-KV decode: each sequence's newest tokens are
  * queries against its cache, the draft tokens a speculative or
  * multi-token-prediction decoder hands to the target model for verification

@@ -27,7 +27,8 @@ def _lib():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted([
-        "sinkattn_decode_splitkv", "sinkattn_decode_splitkv_fp8", "sinkattn_decode_splitkv_multi",
+        "sinkattn_decode_paged", "sinkattn_decode_splitkv", "sinkattn_decode_splitkv_fp8",
+        "sinkattn_decode_splitkv_multi",
         "sinkattn_decode_workspace_bytes",
         "sinkattn_last_error", "sinkattn_merge_lse", "sinkattn_prefill_append", "sinkattn_prefill_varlen",
         "sinkattn_version"])
@@ -236,3 +237,37 @@ def test_decode_multi_empty_is_ok_without_launch():
     assert _decode_multi(lib, batch=0) == 0
     assert _decode_multi(lib, batch=0, cuq=None) == 0
     assert _decode_multi(lib, tq=0, mq=0) == 0
+
+
+def _decode_paged(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE2, batch=4, mp=8, ps=16, npg=40, mk=100, sinks=None, hq=64,
+             hkv=8, d=64, window=0, scale=0.125, splits=1, ws=None, ws_bytes=0, o=FAKE, lse=None)
+    a.update(kw)
+    return lib.sinkattn_decode_paged(a["q"], a["k"], a["v"], a["bt"], a["lens"], a["batch"], a["mp"], a["ps"],
+                                     a["npg"], a["mk"], a["sinks"], a["hq"], a["hkv"], a["d"], a["window"],
+                                     a["scale"], a["splits"], a["ws"], a["ws_bytes"], a["o"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ps=8), 2),                  # below 16
+    (dict(ps=24), 2),                 # not a power of two
+    (dict(mp=0), 1),
+    (dict(npg=0), 1),
+    (dict(mp=6), 1),                  # 6 x 16 < max_seqlen_k
+    (dict(bt=None), 1),
+    (dict(lens=None), 1),
+    (dict(npg=1 << 27, ps=32), 2),    # pool past 2^31 tokens
+    (dict(splits=4), 3),              # no workspace
+    (dict(d=128), 2),
+    (dict(k=ctypes.c_void_p((1 << 20) + 2)), 1),
+])
+def test_decode_paged_rejects(kw, status):
+    lib = _lib()
+    assert _decode_paged(lib, **kw) == status
+    assert lib.sinkattn_last_error()
+
+
+def test_decode_paged_empty_is_ok_without_launch():
+    lib = _lib()
+    assert _decode_paged(lib, batch=0) == 0
+    assert _decode_paged(lib, batch=0, bt=None, lens=None) == 0

@@ -177,7 +177,9 @@ def _cpu_other_configs(cores: int) -> dict:
     tiny prefill; 2 of the 16 long-decode sequences (both layers); for the
     ragged prefill, 3 of its sequences (the longest, a middle and a short
     one; all rows of the two shorter, 256 evenly spaced rows of the
-    longest), both layers.  Rates are float64 GFLOP/s (or GB/s of the
+    longest), both layers; 2 of the 64 decode sequences against the E4M3 and
+    the paged cache; 256 query rows of the 2048-token append chunk (both
+    layers); 2 of the 64 draft-token sequences.  Rates are float64 GFLOP/s (or GB/s of the
     algorithmic bytes); `seconds_full` extrapolates to the whole workload."""
     import numpy as np
 
@@ -225,6 +227,49 @@ def _cpu_other_configs(cores: int) -> dict:
             "seconds": t, "gflops_f64": fl / t / 1e9, "seconds_full": total / (fl / t),
             "sample": "%d rows of sequences of %s tokens, %d processes (pool start-up included)"
                       % (len(rows), pick, cores)}
+
+    from oracle import decode_fp8_ref, decode_paged_ref, prefill_append_ref
+
+    # FP8 (E4M3) decode and paged decode: 2 of the 64 sequences x 8192 keys
+    f8 = inputs.make_decode_fp8([DEC_CTX] * 2, HQ, HKV, D, seed=0)
+    t0 = time.perf_counter()
+    decode_fp8_ref(inputs.bf16_bits_to_f32(f8.q), f8.k, f8.v, f8.k_scale, f8.v_scale, f8.cu_seqlens_k, f8.sinks, 0,
+                   f8.scale)
+    t = time.perf_counter() - t0
+    out["fp8_decode"] = {"seconds": t, "gbs_f64": decode_bytes([DEC_CTX] * 2, 0, kv_elem_bytes=1) / t / 1e9,
+                         "seconds_full": t * DEC_BATCH / 2, "sample": "2 of 64 sequences x 8192 keys, 1 process"}
+    pg = inputs.make_paged_decode([DEC_CTX] * 2, 16, HQ, HKV, D, seed=0)
+    kp, vp = inputs.bf16_bits_to_f32(pg.k_pages), inputs.bf16_bits_to_f32(pg.v_pages)
+    t0 = time.perf_counter()
+    decode_paged_ref(inputs.bf16_bits_to_f32(pg.q), kp, vp, pg.block_table, pg.seq_lens, 16, pg.sinks, 0, pg.scale)
+    t = time.perf_counter() - t0
+    out["paged_decode_ps16"] = {"seconds": t, "gbs_f64": decode_bytes([DEC_CTX] * 2, 0) / t / 1e9,
+                                "seconds_full": t * DEC_BATCH / 2,
+                                "sample": "2 of 64 sequences x 8192 keys, 16-token pages, 1 process"}
+    del kp, vp
+
+    # append prefill (last 2048 of 8192 tokens): 256 evenly spaced query rows;
+    # draft verification: 2 of the 64 sequences x 4 queries x 8192 keys
+    a = inputs.make_append([2048], [8192], HQ, HKV, D, seed=0)
+    qf, kf, vf = (inputs.bf16_bits_to_f32(x) for x in (a.q, a.k, a.v))
+    rows = list(np.linspace(0, 2047, 256).astype(np.int64))
+    for window in (0, WINDOW):
+        fl = sum(4.0 * D * HQ * (min(6144 + r + 1, window) if window > 0 else 6144 + r + 1) for r in rows)
+        t0 = time.perf_counter()
+        prefill_append_ref(qf, kf, vf, a.sinks, a.cu_seqlens_q, a.cu_seqlens_k, window, a.scale, rows=rows)
+        t = time.perf_counter() - t0
+        total = append_flops([2048], [8192], window)
+        out["chunked_prefill_last_2048_of_8192_%s" % ("causal" if window == 0 else "w128")] = {
+            "seconds": t, "gflops_f64": fl / t / 1e9, "seconds_full": total / (fl / t),
+            "sample": "256 of 2048 query rows, 1 process"}
+    a = inputs.make_append([4, 4], [DEC_CTX] * 2, HQ, HKV, D, seed=0)
+    qf, kf, vf = (inputs.bf16_bits_to_f32(x) for x in (a.q, a.k, a.v))
+    t0 = time.perf_counter()
+    prefill_append_ref(qf, kf, vf, a.sinks, a.cu_seqlens_q, a.cu_seqlens_k, 0, a.scale)
+    t = time.perf_counter() - t0
+    out["draft_verify_64x4_ctx8192_causal"] = {
+        "seconds": t, "gbs_f64": append_bytes([4, 4], [DEC_CTX] * 2, 0) / t / 1e9, "seconds_full": t * DEC_BATCH / 2,
+        "sample": "2 of 64 sequences x 4 queries x 8192 keys, 1 process"}
     return out
 
 

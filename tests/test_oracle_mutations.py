@@ -11,7 +11,9 @@ instead of 7, subnormals scaled like normals, the two scales swapped; and
 for the append oracle (tests/test_oracle_append.py): top-left causal
 alignment, the window one key too wide, queries one position late; and for
 the paged oracle (tests/test_oracle_paged.py): page and slot swapped, the
-slot off by one.
+slot off by one; and for the rotary oracle (tests/test_oracle_rope.py): the
+rotation the wrong way, the YaRN ramp reversed, the temperature without its
+0.1, V rotated as well.
 """
 
 import os
@@ -56,6 +58,16 @@ PAGED_MUTATIONS = [
 ]
 
 
+ROPE_MUTATIONS = [
+    ("out = np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)",
+     "out = np.concatenate([x1 * c + x2 * s, x2 * c - x1 * s], axis=-1)"),      # rotation the wrong way
+    ("freq = (1.0 - gamma) * base / factor + gamma * base",
+     "freq = gamma * base / factor + (1.0 - gamma) * base"),                     # ramp reversed
+    ("return freq, 0.1 * math.log(factor) + 1.0", "return freq, math.log(factor) + 1.0"),
+    ("vc[slot] = v[t]", "vc[slot] = rope_ref(v[t:t + 1], positions[t:t + 1], inv_freq, attention_factor)[0]"),
+]
+
+
 def _run_pins(tmp_path, module, old, new, pin_file):
     for sub in ("oracle", "tests", "attention_gqa_flash_amd"):
         shutil.copytree(os.path.join(ROOT, sub), tmp_path / sub,
@@ -88,3 +100,8 @@ def test_append_pins_catch_planted_mistake(tmp_path, old, new):
 @pytest.mark.parametrize("old,new", PAGED_MUTATIONS, ids=["paged_%d" % i for i in range(len(PAGED_MUTATIONS))])
 def test_paged_pins_catch_planted_mistake(tmp_path, old, new):
     _run_pins(tmp_path, "paged.py", old, new, "tests/test_oracle_paged.py")
+
+
+@pytest.mark.parametrize("old,new", ROPE_MUTATIONS, ids=["rope_%d" % i for i in range(len(ROPE_MUTATIONS))])
+def test_rope_pins_catch_planted_mistake(tmp_path, old, new):
+    _run_pins(tmp_path, "rope.py", old, new, "tests/test_oracle_rope.py")

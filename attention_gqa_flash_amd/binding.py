@@ -57,6 +57,10 @@ def library() -> ctypes.CDLL:
     lib.sinkattn_decode_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, i32, i32, i32, f32,
                                           i32, vp, sz, vp, vp, vp]
     lib.sinkattn_decode_paged.restype = ctypes.c_int
+    f64 = ctypes.c_double
+    lib.sinkattn_rope_qkv_append.argtypes = [vp, vp, vp, i32, i32, i32, i32, f64, f64, i32, f64, f64, vp, vp, vp, i32,
+                                             vp]
+    lib.sinkattn_rope_qkv_append.restype = ctypes.c_int
     lib.sinkattn_merge_lse.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.sinkattn_merge_lse.restype = ctypes.c_int
     lib.sinkattn_last_error.argtypes = []
@@ -325,6 +329,35 @@ def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, 
         page_size, num_pages, int(max_seqlen_k), _ptr(sinks), hq, hkv, d, int(window), float(softmax_scale),
         int(num_splits), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(q.device)))
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def rope_qkv_append(qkv: torch.Tensor, positions: torch.Tensor, slot_mapping: torch.Tensor, num_q_heads: int,
+                    num_kv_heads: int, k_cache: torch.Tensor, v_cache: torch.Tensor, rope_theta: float = 10000.0,
+                    yarn_factor: float = 1.0, yarn_original_max_position: int = 4096, yarn_beta_fast: float = 32.0,
+                    yarn_beta_slow: float = 1.0, q_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The fused rotary step: qkv [T, Hq + 2 Hkv, 64] bf16, positions and
+    slot_mapping [T] int32; writes the rotated K and the V of token t into
+    k_cache / v_cache [rows, Hkv, 64] row slot_mapping[t] (-1: none) and
+    returns the rotated Q [T, Hq, 64]."""
+    _need(qkv, "qkv", torch.bfloat16, 3)
+    _need(positions, "positions", torch.int32, 1)
+    _need(slot_mapping, "slot_mapping", torch.int32, 1)
+    _need(k_cache, "k_cache", torch.bfloat16, 3)
+    _need(v_cache, "v_cache", torch.bfloat16, 3)
+    t, heads, d = qkv.shape
+    if heads != num_q_heads + 2 * num_kv_heads:
+        raise ValueError("qkv must hold num_q_heads + 2 * num_kv_heads heads")
+    if positions.shape[0] != t or slot_mapping.shape[0] != t:
+        raise ValueError("positions and slot_mapping need one entry per token")
+    if k_cache.shape != v_cache.shape or k_cache.shape[1:] != (num_kv_heads, d):
+        raise ValueError("k_cache and v_cache must be [rows, num_kv_heads, head_dim]")
+    if q_out is None:
+        q_out = torch.empty((t, num_q_heads, d), dtype=torch.bfloat16, device=qkv.device)
+    _check(library().sinkattn_rope_qkv_append(
+        _ptr(qkv), _ptr(positions), _ptr(slot_mapping), t, int(num_q_heads), int(num_kv_heads), d,
+        float(rope_theta), float(yarn_factor), int(yarn_original_max_position), float(yarn_beta_fast),
+        float(yarn_beta_slow), _ptr(q_out), _ptr(k_cache), _ptr(v_cache), k_cache.shape[0], _stream(qkv.device)))
+    return q_out
 
 
 def merge_lse(o_parts: torch.Tensor, lse_parts: torch.Tensor, out: Optional[torch.Tensor] = None,

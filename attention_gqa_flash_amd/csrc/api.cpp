@@ -3,6 +3,7 @@
 // the contract of every entry point.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -78,6 +79,7 @@ sinkattn_status check_failed(unsigned flags) {
       {sinkattn::kCheckParts, "o_parts holds NaN or Inf, or lse_parts NaN or +inf"},
       {sinkattn::kCheckAppend, "a sequence has fewer keys than queries (cu_seqlens_k vs cu_seqlens_q)"},
       {sinkattn::kCheckPages, "a page id is outside the pool, or a block table row is too short"},
+      {sinkattn::kCheckSlots, "a slot is outside [-1, cache_rows) or names a cache row twice"},
   };
   std::string msg = "debug checks failed:";
   for (const auto& n : kNames)
@@ -349,6 +351,68 @@ sinkattn_status sinkattn_decode_paged(const void* q, const void* k_pages, const 
   return decode_common(q, k_pages, v_pages, seq_lens, batch, max_seqlen_k, sinks, num_q_heads, num_kv_heads,
                        head_dim, window, softmax_scale, num_splits, workspace, workspace_bytes, o, lse, stream, false,
                        1.0f, 1.0f, nullptr, 1, 0, block_table, max_pages, page_size, num_pages);
+}
+
+// Rotary frequencies of the pairs (i, i + 32): theta^(-2i/64), rescaled by
+// YaRN's NTK-by-parts rule when factor > 1 (a frequency that turns more than
+// beta_fast times over the original context is kept, fewer than beta_slow
+// times divided by the factor, linear in the turn count between), and YaRN's
+// temperature 0.1 ln(factor) + 1.
+static sinkattn::RopeTable rope_table(double theta, double factor, int original_max_position, double beta_fast,
+                                      double beta_slow) {
+  sinkattn::RopeTable t{};
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < 32; ++i) {
+    const double f = std::pow(theta, -static_cast<double>(2 * i) / 64.0);
+    double g = 1.0;
+    if (factor > 1.0) {
+      const double turns = original_max_position * f / two_pi;
+      g = std::min(1.0, std::max(0.0, (turns - beta_slow) / (beta_fast - beta_slow)));
+    }
+    t.freq[i] = factor > 1.0 ? (1.0 - g) * f / factor + g * f : f;
+  }
+  t.attention_factor = factor > 1.0 ? static_cast<float>(0.1 * std::log(factor) + 1.0) : 1.0f;
+  return t;
+}
+
+sinkattn_status sinkattn_rope_qkv_append(const void* qkv, const int32_t* positions, const int32_t* slot_mapping,
+                                         int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, double rope_theta, double yarn_factor,
+                                         int32_t yarn_original_max_position, double yarn_beta_fast,
+                                         double yarn_beta_slow, void* q_out, void* k_cache, void* v_cache,
+                                         int32_t cache_rows, void* stream) {
+  if (num_tokens < 0 || cache_rows < 0) return fail(SINKATTN_ERR_INVALID_ARG, "num_tokens and cache_rows must be >= 0");
+  if (num_q_heads < 1 || num_kv_heads < 1)
+    return fail(SINKATTN_ERR_INVALID_ARG, "head counts must be >= 1 (got %d, %d)", num_q_heads, num_kv_heads);
+  if (head_dim != 64) return fail(SINKATTN_ERR_UNSUPPORTED, "head_dim %d is not supported (only 64)", head_dim);
+  if (!std::isfinite(rope_theta) || !(rope_theta > 1.0))
+    return fail(SINKATTN_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
+  if (!std::isfinite(yarn_factor) || !(yarn_factor > 0.0))
+    return fail(SINKATTN_ERR_INVALID_ARG, "yarn_factor must be finite and > 0");
+  if (yarn_factor > 1.0 &&
+      (yarn_original_max_position < 1 || !std::isfinite(yarn_beta_fast) || !std::isfinite(yarn_beta_slow) ||
+       !(yarn_beta_fast > yarn_beta_slow)))
+    return fail(SINKATTN_ERR_INVALID_ARG,
+                "YaRN needs original_max_position >= 1 and finite beta_fast > beta_slow");
+  if (num_tokens == 0) return ok();
+  if (!qkv || !positions || !slot_mapping || !q_out || !k_cache || !v_cache)
+    return fail(SINKATTN_ERR_INVALID_ARG, "qkv, positions, slot_mapping, q_out, k_cache and v_cache must not be NULL");
+  if (!aligned16(qkv) || !aligned16(q_out) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(SINKATTN_ERR_INVALID_ARG, "qkv, q_out, k_cache and v_cache must be 16-byte aligned");
+  sinkattn_status st;
+  if (debug_checks()) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t n = static_cast<size_t>(num_tokens) * (num_q_heads + 2 * num_kv_heads) * head_dim;
+    if ((st = hip_queue(sinkattn::check_clear(s))) != SINKATTN_OK) return st;
+    if ((st = hip_queue(sinkattn::check_slots(slot_mapping, num_tokens, cache_rows, s))) != SINKATTN_OK) return st;
+    if ((st = hip_queue(sinkattn::check_bf16(qkv, n, sinkattn::kCheckQ, s))) != SINKATTN_OK) return st;
+    if ((st = check_result(s, nullptr)) != SINKATTN_OK) return st;
+  }
+  sinkattn::RopeLaunch a{qkv, positions, slot_mapping, num_tokens, num_q_heads, num_kv_heads, cache_rows,
+                         rope_table(rope_theta, yarn_factor, yarn_original_max_position, yarn_beta_fast,
+                                    yarn_beta_slow),
+                         q_out, k_cache, v_cache};
+  return hip_status(sinkattn::launch_rope_qkv_append(a, static_cast<hipStream_t>(stream)), "rope launch");
 }
 
 sinkattn_status sinkattn_merge_lse(const float* o_parts, const float* lse_parts, int32_t num_parts, int32_t n,

@@ -69,6 +69,20 @@ __global__ void check_paged_kernel(const int32_t* __restrict__ lens, const int32
   if (bits != 0u) atomicOr(&g_check_flags, bits);
 }
 
+// Rotary append: slots in [-1, cache_rows) and pairwise distinct (the check
+// compares every pair: debug mode only, quadratic in the tokens).
+__global__ void check_slots_kernel(const int32_t* __restrict__ slots, int n, int cache_rows) {
+  unsigned bits = 0;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const int s = slots[i];
+    if (s < -1 || s >= cache_rows) bits |= kCheckSlots;
+    if (s >= 0)
+      for (int j = i + 1; j < n; ++j)
+        if (slots[j] == s) bits |= kCheckSlots;
+  }
+  if (bits != 0u) atomicOr(&g_check_flags, bits);
+}
+
 // Floating-point classes are tested on the bit patterns: the library is
 // built without NaN semantics (-fno-honor-nans), so x != x would fold away.
 __device__ __forceinline__ bool is_nan_bits(uint32_t u) { return (u & 0x7fffffffu) > 0x7f800000u; }
@@ -144,6 +158,12 @@ hipError_t check_paged(const int32_t* seq_lens, const int32_t* block_table, int 
   if (batch <= 0) return hipSuccess;
   hipLaunchKernelGGL(check_paged_kernel, dim3(grid_for(batch)), dim3(256), 0, stream, seq_lens, block_table, batch,
                      max_pages, page_size, num_pages, max_len);
+  return hipGetLastError();
+}
+
+hipError_t check_slots(const int32_t* slots, int n, int cache_rows, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(check_slots_kernel, dim3(grid_for(n)), dim3(256), 0, stream, slots, n, cache_rows);
   return hipGetLastError();
 }
 

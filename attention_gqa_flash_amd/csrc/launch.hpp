@@ -60,7 +60,26 @@ struct MergeLaunch {
   float* lse;
 };
 
+// Fused rotary step: frequencies f_i of dimension pairs (i, i + 32) and the
+// temperature factor, computed on the host.
+struct RopeTable {
+  double freq[32];
+  float attention_factor;
+};
+
+struct RopeLaunch {
+  const void* qkv;             // bf16 [num_tokens, num_q_heads + 2 num_kv_heads, 64]
+  const int32_t* positions;    // [num_tokens]
+  const int32_t* slot_mapping; // [num_tokens], cache row or -1
+  int num_tokens, num_q_heads, num_kv_heads, cache_rows;
+  RopeTable table;
+  void* q_out;                 // bf16 [num_tokens, num_q_heads, 64]
+  void* k_cache;               // bf16 [cache_rows, num_kv_heads, 64]
+  void* v_cache;
+};
+
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream);
+hipError_t launch_rope_qkv_append(const RopeLaunch& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 // True when launch_decode writes o (and lse) itself although num_splits > 1
 // (splits of at most 32 keys are evaluated as one range): no merge follows.
@@ -81,12 +100,15 @@ enum CheckBits : unsigned {
   kCheckParts = 1u << 9,         // NaN / Inf in o_parts, NaN / +inf in lse_parts
   kCheckAppend = 1u << 10,       // append prefill: a sequence with fewer keys than queries
   kCheckPages = 1u << 11,        // paged decode: a page id outside the pool or a table too short
-  kCheckAll = (1u << 12) - 1u,
+  kCheckSlots = 1u << 12,        // rotary append: a slot outside [-1, cache_rows) or used twice
+  kCheckAll = (1u << 13) - 1u,
 };
 hipError_t check_clear(hipStream_t stream);
 hipError_t check_offsets(const int32_t* cu, int batch, int max_len, int min_len, int total_limit,
                          hipStream_t stream);
 hipError_t check_sinks(const float* sinks, int n, hipStream_t stream);
+// Rotary append: every slot in [-1, cache_rows), and no cache row named twice.
+hipError_t check_slots(const int32_t* slots, int n, int cache_rows, hipStream_t stream);
 // Append prefill: every sequence has cu_k[b+1] - cu_k[b] >= cu_q[b+1] - cu_q[b].
 hipError_t check_append(const int32_t* cu_q, const int32_t* cu_k, int batch, hipStream_t stream);
 // Paged decode: 1 <= seq_lens[b] <= max_len and every page id a sequence

@@ -192,6 +192,32 @@ def make_paged_decode(lengths, page_size: int, hq: int, hkv: int, d: int = 64, s
 
 
 @dataclass
+class RopeInputs:
+    qkv: np.ndarray           # uint16 bf16 bits [T, Hq + 2 Hkv, D]
+    positions: np.ndarray     # int32 [T]
+    slot_mapping: np.ndarray  # int32 [T], distinct rows or -1
+    k_cache: np.ndarray       # uint16 bf16 bits [rows, Hkv, D] (initial contents)
+    v_cache: np.ndarray
+
+
+def make_rope(num_tokens: int, hq: int, hkv: int, cache_rows: int, d: int = 64, seed: int = 0,
+              max_position: int = 131072, skip_every: int = 7, rng: Optional[np.random.Generator] = None):
+    """Inputs of the fused rotary step: qkv and the caches N(0,1) rounded to
+    bf16; positions uniform in [0, max_position); distinct cache rows drawn
+    without replacement, every skip_every-th token without a row (-1)."""
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    assert cache_rows >= num_tokens
+    qkv = _normal_bf16(rng, (num_tokens, hq + 2 * hkv, d))
+    positions = rng.integers(0, max_position, size=num_tokens).astype(np.int32)
+    slots = rng.permutation(cache_rows)[:num_tokens].astype(np.int32)
+    if skip_every > 0:
+        slots[::skip_every] = -1
+    kc = _normal_bf16(rng, (cache_rows, hkv, d))
+    vc = _normal_bf16(rng, (cache_rows, hkv, d))
+    return RopeInputs(qkv, positions, slots, kc, vc)
+
+
+@dataclass
 class DecodeFp8Inputs:
     q: np.ndarray            # uint16 bf16 bits [B, Hq, D]
     k: np.ndarray            # uint8 E4M3 codes [Tk, Hkv, D]

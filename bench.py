@@ -24,7 +24,8 @@ varlen prefill (causal and 128-window); the append prefill (the last
 2048-token chunk of an 8192-token prompt; 64 x 4 draft tokens verified
 against 8192 cached tokens, also through the multi-token-query decode at 1
 and 4 splits); the 64 x 8192 decode against a paged cache (16- and 64-token
-pages, shuffled); a streaming-read and a copy
+pages, shuffled); the fused rotary step (YaRN; Q out, K/V appended) for 8192
+and 64 tokens; a streaming-read and a copy
 bandwidth reference; the engine clock (sysfs pp_dpm_sclk) sampled during the step.
 Small working sets are timed after a 512 MiB cache scrub.  The long-decode
 and ragged inputs are drawn on the device from a seeded generator (same
@@ -109,6 +110,12 @@ def append_bytes(q_lens, k_lens, window, hq=HQ, hkv=HKV) -> float:
     return float(2 * tq * hq * D * 2 + 2 * keys * hkv * D * 2 + hq * 4 + 2 * (len(q_lens) + 1) * 4)
 
 
+def rope_bytes(num_tokens: int, hq=HQ, hkv=HKV) -> float:
+    """Fused rotary step: read qkv, positions and slots; write q, k and v."""
+    row = D * 2
+    return float(num_tokens * ((hq + 2 * hkv) * row * 2 + 8))
+
+
 def decode_flops(lengths, window, hq=HQ) -> float:
     keys = sum(min(n, window) if window > 0 else n for n in lengths)
     return 4.0 * D * hq * keys
@@ -179,7 +186,8 @@ def _cpu_other_configs(cores: int) -> dict:
     one; all rows of the two shorter, 256 evenly spaced rows of the
     longest), both layers; 2 of the 64 decode sequences against the E4M3 and
     the paged cache; 256 query rows of the 2048-token append chunk (both
-    layers); 2 of the 64 draft-token sequences.  Rates are float64 GFLOP/s (or GB/s of the
+    layers); 2 of the 64 draft-token sequences; 1024 of the 8192 tokens of
+    the fused rotary step.  Rates are float64 GFLOP/s (or GB/s of the
     algorithmic bytes); `seconds_full` extrapolates to the whole workload."""
     import numpy as np
 
@@ -267,6 +275,16 @@ def _cpu_other_configs(cores: int) -> dict:
     t0 = time.perf_counter()
     prefill_append_ref(qf, kf, vf, a.sinks, a.cu_seqlens_q, a.cu_seqlens_k, 0, a.scale)
     t = time.perf_counter() - t0
+    # fused rotary step: 1024 of the 8192 prefill tokens
+    from oracle import rope_qkv_append_ref, yarn_inv_freq_ref
+    r = inputs.make_rope(1024, HQ, HKV, cache_rows=2048, seed=0)
+    t0 = time.perf_counter()
+    f_rope, m_rope = yarn_inv_freq_ref(D, 150000.0, 32.0, 4096, 32.0, 1.0)
+    rope_qkv_append_ref(inputs.bf16_bits_to_f32(r.qkv), r.positions, HQ, HKV, f_rope, m_rope, r.slot_mapping,
+                        inputs.bf16_bits_to_f32(r.k_cache), inputs.bf16_bits_to_f32(r.v_cache))
+    t = time.perf_counter() - t0
+    out["rope_qkv_append_8192"] = {"seconds": t, "gbs_f64": rope_bytes(1024) / t / 1e9, "seconds_full": t * 8,
+                                   "sample": "1024 of 8192 tokens (cache copies included), 1 process"}
     out["draft_verify_64x4_ctx8192_causal"] = {
         "seconds": t, "gbs_f64": append_bytes([4, 4], [DEC_CTX] * 2, 0) / t / 1e9, "seconds_full": t * DEC_BATCH / 2,
         "sample": "2 of 64 sequences x 4 queries x 8192 keys, 1 process"}
@@ -676,6 +694,29 @@ def _other_configs(torch, np, binding, inputs, dev, bf16, timed, hbm_entry, mfma
             out["paged_decode_ps%d_s%d" % (page_size, s_count)] = e
         del kp, vp
     del pq, po, pws
+    torch.cuda.synchronize()
+
+    # fused rotary step (YaRN, theta 150000, factor 32 over a 4096-token
+    # original context, beta 32 / 1): the 8192 tokens of the prefill and the
+    # 64 tokens of one decode step, K/V appended to distinct cache rows
+    gen.manual_seed(6)
+    for n_tok, rows_cache in ((PREFILL_LEN, 2 * PREFILL_LEN), (DEC_BATCH, DEC_BATCH * DEC_CTX)):
+        rqkv = _device_normal_bf16(torch, (n_tok, HQ + 2 * HKV, D), gen, dev)
+        rpos = torch.randint(0, 131072, (n_tok,), generator=gen, device=dev, dtype=torch.int32)
+        rslots = torch.randperm(rows_cache, generator=gen, device=dev)[:n_tok].to(torch.int32)
+        rkc = torch.empty((rows_cache, HKV, D), dtype=torch.bfloat16, device=dev)
+        rvc = torch.empty_like(rkc)
+        rq = torch.empty((n_tok, HQ, D), dtype=torch.bfloat16, device=dev)
+        st = timed(lambda: binding.rope_qkv_append(rqkv, rpos, rslots, HQ, HKV, rkc, rvc, rope_theta=150000.0,
+                                                   yarn_factor=32.0, yarn_original_max_position=4096,
+                                                   yarn_beta_fast=32.0, yarn_beta_slow=1.0, q_out=rq),
+                   scrub_each=(n_tok < 1024))
+        nbytes = rope_bytes(n_tok)
+        e = hbm_entry(st, nbytes)
+        e["bound"] = "hbm"
+        e["shape"] = "%d tokens, 64/8 heads, YaRN, K/V to distinct rows of a %d-row cache" % (n_tok, rows_cache)
+        out["rope_qkv_append_%d" % n_tok] = e
+        del rqkv, rkc, rvc, rq
     torch.cuda.synchronize()
 
     # append prefill: the last 2048-token chunk of an 8192-token prompt, and

@@ -318,6 +318,48 @@ SINKATTN_API sinkattn_status sinkattn_decode_splitkv_multi(
     void* o, float* lse, void* stream);
 
 /*
+ * The rotary step before attention, fused: rotate the query heads into q_out
+ * and write the rotated key heads and the value heads of each new token into
+ * its cache row (vLLM, "GPT-OSS performance optimizations on NVIDIA
+ * Blackwell", minimum latency: RoPE + Q + cache fusion; NVIDIA gpt-oss
+ * announcement, model description: RoPE; Perplexity, "GPT-OSS on day 0",
+ * Hopper section: YaRN position encoding).  The pages give no formula; the
+ * rotation is the RoFormer one with dimension i pairing with i + head_dim/2:
+ *     (x_i, x_{i+32}) -> m * (x_i cos a - x_{i+32} sin a, x_{i+32} cos a + x_i sin a),
+ *     a = position * f_i,  f_i = rope_theta^(-2i/64),
+ * and for yarn_factor s > 1 YaRN's NTK-by-parts rescaling (Peng et al.): with
+ * r_i = yarn_original_max_position * f_i / (2 pi) turns over the original
+ * context, gamma_i = clamp((r_i - yarn_beta_slow) / (yarn_beta_fast -
+ * yarn_beta_slow), 0, 1), f_i -> (1 - gamma_i) f_i / s + gamma_i f_i, and the
+ * temperature m = 0.1 ln s + 1 (m = 1 for s <= 1).
+ *
+ *   qkv           bf16 [num_tokens, num_q_heads + 2 num_kv_heads, head_dim]:
+ *                 the q heads, then the k heads, then the v heads of a token
+ *   positions     int32 [num_tokens], device: each token's position
+ *   slot_mapping  int32 [num_tokens], device: the cache row of the token's k
+ *                 and v (for a paged cache, page * page_size + slot), or -1
+ *                 to write none; rows must be distinct
+ *   q_out         bf16 [num_tokens, num_q_heads, head_dim] (written)
+ *   k_cache,
+ *   v_cache       bf16 [cache_rows, num_kv_heads, head_dim]; only the rows
+ *                 named by slot_mapping are written (k rotated, v copied)
+ *
+ * Angles are reduced modulo 2 pi in fp64 before sin / cos in fp32, so the
+ * phase of large positions is kept.  Errors: rope_theta must be finite and
+ * > 1, yarn_factor finite and > 0, and with yarn_factor > 1 the original
+ * context >= 1 and finite yarn_beta_fast > yarn_beta_slow
+ * (SINKATTN_ERR_INVALID_ARG); head_dim 64 only.  Slots outside
+ * [-1, cache_rows) are skipped; slots out of range or repeated are reported
+ * under SINKATTN_DEBUG_CHECKS=1.
+ */
+SINKATTN_API sinkattn_status sinkattn_rope_qkv_append(
+    const void* qkv, const int32_t* positions, const int32_t* slot_mapping, int32_t num_tokens,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    double rope_theta, double yarn_factor, int32_t yarn_original_max_position,
+    double yarn_beta_fast, double yarn_beta_slow,
+    void* q_out, void* k_cache, void* v_cache, int32_t cache_rows, void* stream);
+
+/*
  * Log-sum-exp merge of num_parts partial results, each normalised by its own
  * denominator (the combination step that the split-KV form of the
  * Perplexity page's online softmax implies; the page does not print it):

@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
     assert _declared() == sorted([
         "sinkattn_decode_paged", "sinkattn_decode_splitkv", "sinkattn_decode_splitkv_fp8",
         "sinkattn_decode_splitkv_multi",
-        "sinkattn_decode_workspace_bytes",
+        "sinkattn_decode_workspace_bytes", "sinkattn_rope_qkv_append",
         "sinkattn_last_error", "sinkattn_merge_lse", "sinkattn_prefill_append", "sinkattn_prefill_varlen",
         "sinkattn_version"])
 
@@ -271,3 +271,39 @@ def test_decode_paged_empty_is_ok_without_launch():
     lib = _lib()
     assert _decode_paged(lib, batch=0) == 0
     assert _decode_paged(lib, batch=0, bt=None, lens=None) == 0
+
+
+def _rope(lib, **kw):
+    a = dict(qkv=FAKE, pos=FAKE2, slots=FAKE2, t=16, hq=64, hkv=8, d=64, theta=150000.0, s=32.0, L=4096, bf=32.0,
+             bs=1.0, q=FAKE, kc=FAKE, vc=FAKE, rows=100)
+    a.update(kw)
+    return lib.sinkattn_rope_qkv_append(a["qkv"], a["pos"], a["slots"], a["t"], a["hq"], a["hkv"], a["d"],
+                                        ctypes.c_double(a["theta"]), ctypes.c_double(a["s"]), a["L"],
+                                        ctypes.c_double(a["bf"]), ctypes.c_double(a["bs"]), a["q"], a["kc"], a["vc"],
+                                        a["rows"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=128), 2),
+    (dict(t=-1), 1),
+    (dict(hkv=0), 1),
+    (dict(theta=1.0), 1),
+    (dict(theta=float("inf")), 1),
+    (dict(s=0.0), 1),
+    (dict(s=float("nan")), 1),
+    (dict(L=0), 1),                   # YaRN without an original context
+    (dict(bf=1.0, bs=1.0), 1),        # empty ramp
+    (dict(qkv=None), 1),
+    (dict(slots=None), 1),
+    (dict(kc=ctypes.c_void_p((1 << 20) + 8)), 1),
+])
+def test_rope_rejects(kw, status):
+    lib = _lib()
+    assert _rope(lib, **kw) == status
+    assert lib.sinkattn_last_error()
+
+
+def test_rope_empty_and_plain_rope_arguments():
+    lib = _lib()
+    assert _rope(lib, t=0) == 0
+    assert _rope(lib, t=0, s=1.0, L=0, bf=0.0, bs=0.0) == 0   # no YaRN: its parameters are not read

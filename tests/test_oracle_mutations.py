@@ -13,7 +13,8 @@ alignment, the window one key too wide, queries one position late; and for
 the paged oracle (tests/test_oracle_paged.py): page and slot swapped, the
 slot off by one; and for the rotary oracle (tests/test_oracle_rope.py): the
 rotation the wrong way, the YaRN ramp reversed, the temperature without its
-0.1, V rotated as well.
+0.1, V rotated as well; and for the projection oracle
+(tests/test_oracle_oproj.py): output features reversed, the bias reversed.
 """
 
 import os
@@ -68,6 +69,12 @@ ROPE_MUTATIONS = [
 ]
 
 
+OPROJ_MUTATIONS = [
+    ("y = o @ w.T", "y = o @ w.T[::-1]"),                          # output features reversed
+    ("y = y + np.asarray(bias, dtype=np.float64)[None, :]", "y = y + np.asarray(bias, dtype=np.float64)[None, ::-1]"),
+]
+
+
 def _run_pins(tmp_path, module, old, new, pin_file):
     for sub in ("oracle", "tests", "attention_gqa_flash_amd"):
         shutil.copytree(os.path.join(ROOT, sub), tmp_path / sub,
@@ -105,3 +112,8 @@ def test_paged_pins_catch_planted_mistake(tmp_path, old, new):
 @pytest.mark.parametrize("old,new", ROPE_MUTATIONS, ids=["rope_%d" % i for i in range(len(ROPE_MUTATIONS))])
 def test_rope_pins_catch_planted_mistake(tmp_path, old, new):
     _run_pins(tmp_path, "rope.py", old, new, "tests/test_oracle_rope.py")
+
+
+@pytest.mark.parametrize("old,new", OPROJ_MUTATIONS, ids=["oproj_%d" % i for i in range(len(OPROJ_MUTATIONS))])
+def test_oproj_pins_catch_planted_mistake(tmp_path, old, new):
+    _run_pins(tmp_path, "oproj.py", old, new, "tests/test_oracle_oproj.py")

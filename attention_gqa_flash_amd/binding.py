@@ -61,6 +61,10 @@ def library() -> ctypes.CDLL:
     lib.sinkattn_rope_qkv_append.argtypes = [vp, vp, vp, i32, i32, i32, i32, f64, f64, i32, f64, f64, vp, vp, vp, i32,
                                              vp]
     lib.sinkattn_rope_qkv_append.restype = ctypes.c_int
+    lib.sinkattn_oproj_bias.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
+    lib.sinkattn_oproj_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.sinkattn_oproj_workspace_bytes.restype = sz
+    lib.sinkattn_oproj_bias.restype = ctypes.c_int
     lib.sinkattn_merge_lse.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.sinkattn_merge_lse.restype = ctypes.c_int
     lib.sinkattn_last_error.argtypes = []
@@ -358,6 +362,33 @@ def rope_qkv_append(qkv: torch.Tensor, positions: torch.Tensor, slot_mapping: to
         float(rope_theta), float(yarn_factor), int(yarn_original_max_position), float(yarn_beta_fast),
         float(yarn_beta_slow), _ptr(q_out), _ptr(k_cache), _ptr(v_cache), k_cache.shape[0], _stream(qkv.device)))
     return q_out
+
+
+def oproj_bias(o: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor],
+               out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Output projection with bias: o [N, K] bf16 (or [N, Hq, D], viewed as
+    [N, Hq * D]), w [E, K] bf16, bias [E] fp32 or None -> y [N, E] bf16."""
+    if o.dim() == 3:
+        o = o.reshape(o.shape[0], -1)
+    _need(o, "o", torch.bfloat16, 2)
+    _need(w, "w", torch.bfloat16, 2)
+    n, k = o.shape
+    e = w.shape[0]
+    if w.shape[1] != k:
+        raise ValueError("w must be [out_features, in_features] matching o")
+    if bias is not None:
+        _need(bias, "bias", torch.float32, 1)
+        if bias.shape[0] != e:
+            raise ValueError("bias must have out_features entries")
+    if out is None:
+        out = torch.empty((n, e), dtype=torch.bfloat16, device=o.device)
+    need = int(library().sinkattn_oproj_workspace_bytes(n, k, e))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=o.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().sinkattn_oproj_bias(_ptr(o), _ptr(w), _ptr(bias), n, k, e, _ptr(out), _ptr(workspace), ws_bytes,
+                                         _stream(o.device)))
+    return out
 
 
 def merge_lse(o_parts: torch.Tensor, lse_parts: torch.Tensor, out: Optional[torch.Tensor] = None,

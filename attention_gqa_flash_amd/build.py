@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsinkattn.so")
-SOURCES = ["prefill.hip", "decode.hip", "rope.hip", "checks.hip", "api.cpp"]
+SOURCES = ["prefill.hip", "decode.hip", "rope.hip", "oproj.hip", "checks.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

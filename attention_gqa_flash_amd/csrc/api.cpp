@@ -415,6 +415,48 @@ sinkattn_status sinkattn_rope_qkv_append(const void* qkv, const int32_t* positio
   return hip_status(sinkattn::launch_rope_qkv_append(a, static_cast<hipStream_t>(stream)), "rope launch");
 }
 
+size_t sinkattn_oproj_workspace_bytes(int32_t num_rows, int32_t in_features, int32_t out_features) {
+  if (num_rows <= 0 || in_features < 128 || in_features % 128 != 0 || out_features < 32 || out_features % 32 != 0)
+    return 0;
+  const int splits = sinkattn::oproj_splits(num_rows, in_features, out_features);
+  return splits > 1 ? round_up(static_cast<size_t>(splits) * num_rows * out_features * sizeof(float), 256) : 0;
+}
+
+sinkattn_status sinkattn_oproj_bias(const void* o, const void* w, const float* bias, int32_t num_rows,
+                                    int32_t in_features, int32_t out_features, void* y, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (num_rows < 0 || in_features < 1 || out_features < 1)
+    return fail(SINKATTN_ERR_INVALID_ARG, "need num_rows >= 0 and positive feature counts");
+  if (in_features % 128 != 0 || out_features % 32 != 0)
+    return fail(SINKATTN_ERR_UNSUPPORTED, "in_features must be a multiple of 128 and out_features of 32 (got %d, %d)",
+                in_features, out_features);
+  if ((static_cast<long long>(num_rows) + 63) / 64 > 65535)
+    return fail(SINKATTN_ERR_UNSUPPORTED, "at most 65535 * 64 rows per call");
+  if (num_rows == 0) return ok();
+  if (!o || !w || !y) return fail(SINKATTN_ERR_INVALID_ARG, "o, w and y must not be NULL");
+  if (!aligned16(o) || !aligned16(w) || !aligned16(y))
+    return fail(SINKATTN_ERR_INVALID_ARG, "o, w and y must be 16-byte aligned");
+  if (debug_checks()) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    sinkattn_status st;
+    if ((st = hip_queue(sinkattn::check_clear(s))) != SINKATTN_OK) return st;
+    if ((st = hip_queue(sinkattn::check_bf16(o, static_cast<size_t>(num_rows) * in_features, sinkattn::kCheckQ,
+                                             s))) != SINKATTN_OK)
+      return st;
+    if ((st = hip_queue(sinkattn::check_bf16(w, static_cast<size_t>(out_features) * in_features,
+                                             sinkattn::kCheckK, s))) != SINKATTN_OK)
+      return st;
+    if ((st = check_result(s, nullptr)) != SINKATTN_OK) return st;
+  }
+  const size_t need = sinkattn_oproj_workspace_bytes(num_rows, in_features, out_features);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(SINKATTN_ERR_WORKSPACE, "workspace of %zu bytes is too small (need %zu)", workspace_bytes, need);
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SINKATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  sinkattn::OprojLaunch a{o, w, bias, num_rows, in_features, out_features, y, static_cast<float*>(workspace)};
+  return hip_status(sinkattn::launch_oproj(a, static_cast<hipStream_t>(stream)), "projection launch");
+}
+
 sinkattn_status sinkattn_merge_lse(const float* o_parts, const float* lse_parts, int32_t num_parts, int32_t n,
                                    int32_t num_heads, int32_t head_dim, void* o, float* lse, void* stream) {
   if (num_parts < 1 || n < 0 || num_heads < 1)

@@ -78,7 +78,21 @@ struct RopeLaunch {
   void* v_cache;
 };
 
+// Output projection with bias: y [num_rows, out_features] = o W^T + b,
+// o [num_rows, in_features], W [out_features, in_features] (bf16), b fp32.
+struct OprojLaunch {
+  const void* o;
+  const void* w;
+  const float* bias;
+  int num_rows, in_features, out_features;
+  void* y;
+  float* part;  // fp32 [splits, num_rows, out_features] when oproj_splits(...) > 1
+};
+// K ranges one projection launch splits into (1: no partials).
+int oproj_splits(int num_rows, int in_features, int out_features);
+
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream);
+hipError_t launch_oproj(const OprojLaunch& a, hipStream_t stream);
 hipError_t launch_rope_qkv_append(const RopeLaunch& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 // True when launch_decode writes o (and lse) itself although num_splits > 1

@@ -1,0 +1,159 @@
+// Output projection with bias after attention (gfx950):
+//     y[n, e] = sum_k o[n, k] * W[e, k] + b[e]
+// o is the attention output with its query heads concatenated (k = h * 64 +
+// d), W one row per output feature; bf16 in, fp32 accumulation, bf16 out
+// (Perplexity, "GPT-OSS on day 0", section "GPT-OSS on Hopper": the output
+// projection carries a bias).
+//
+// Shaped for the decode step, where the rows are few and the weight is the
+// traffic: computed transposed, y^T = W o^T, with v_mfma_f32_32x32x16_bf16
+// (A = 32 rows of W, B = 32 rows of o, both 16-byte loads of 8 consecutive
+// k straight from memory: no LDS staging).  A workgroup owns 32 output
+// features and 64 rows; its 8 waves split K into 8 slices, so W is streamed
+// from HBM once per 64 rows while o stays in L2, and the slices are summed
+// through LDS, where the bias is added and the result rounded to bf16.  The
+// split-KV merge is not fused in: every 32-feature tile would re-read all of
+// the split partials, so the merge writes o once (bf16) and this kernel reads
+// it from L2.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace sinkattn {
+
+namespace {
+
+constexpr int kOprojWaves = 8;
+constexpr int kOprojCols = 32;  // output features per workgroup
+constexpr int kOprojRows = 64;  // rows per workgroup (two MFMA column blocks)
+constexpr int kOprojUnroll = 8;
+
+// blockIdx.z takes K range [z K / gridDim.z, (z + 1) K / gridDim.z) (its 8
+// waves split it again); with more than one K range each workgroup writes
+// fp32 partial sums to part[z] and oproj_finish_kernel adds them up.
+__global__ __launch_bounds__(64 * kOprojWaves) void oproj_kernel(const uint16_t* __restrict__ o,
+                                                                 const uint16_t* __restrict__ w,
+                                                                 const float* __restrict__ bias,
+                                                                 uint16_t* __restrict__ y, float* __restrict__ part,
+                                                                 int n_rows, int k_dim, int e_dim) {
+  __shared__ float red[kOprojWaves][2][16][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int e0 = blockIdx.x * kOprojCols;
+  const int n0 = blockIdx.y * kOprojRows;
+  const int k_range = k_dim / gridDim.z;       // a multiple of 128
+  const int slice = k_range / kOprojWaves;     // a multiple of 16
+  const int k_begin = blockIdx.z * k_range + wave * slice;
+  const int kh = 8 * (lane >> 5);
+  // Rows past n_rows repeat the last row: their columns of y^T are dropped.
+  const int nr0 = min(n0 + (lane & 31), n_rows - 1);
+  const int nr1 = min(n0 + 32 + (lane & 31), n_rows - 1);
+  const bool two = n0 + 32 < n_rows;  // uniform: a second block of 32 rows
+  const uint16_t* wp = w + static_cast<size_t>(e0 + (lane & 31)) * k_dim + k_begin + kh;
+  const uint16_t* op0 = o + static_cast<size_t>(nr0) * k_dim + k_begin + kh;
+  const uint16_t* op1 = o + static_cast<size_t>(nr1) * k_dim + k_begin + kh;
+
+  f32x16_t acc0 = zero16(), acc1 = zero16();
+  for (int k = 0; k < slice; k += 16 * kOprojUnroll) {
+    const int steps = min(kOprojUnroll, (slice - k) / 16);
+    bf16x8_t a[kOprojUnroll], b0[kOprojUnroll], b1[kOprojUnroll];
+#pragma unroll
+    for (int u = 0; u < kOprojUnroll; ++u) {
+      if (u < steps) {
+        a[u] = __builtin_bit_cast(bf16x8_t, load16_stream(wp + k + 16 * u));
+        b0[u] = __builtin_bit_cast(bf16x8_t, load16(op0 + k + 16 * u));
+        if (two) b1[u] = __builtin_bit_cast(bf16x8_t, load16(op1 + k + 16 * u));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kOprojUnroll; ++u) {
+      if (u < steps) {
+        acc0 = mfma_32x32x16(a[u], b0[u], acc0);
+        if (two) acc1 = mfma_32x32x16(a[u], b1[u], acc1);
+      }
+    }
+  }
+
+  // Sum the K slices: register r of lane l holds y^T[e0 + 8 (r / 4) +
+  // 4 (l / 32) + r % 4][row block + l % 32].
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    red[wave][0][r][lane] = acc0[r];
+    red[wave][1][r][lane] = two ? acc1[r] : 0.0f;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 2 * 16 * 64; idx += 64 * kOprojWaves) {
+    const int nb = idx >> 10;
+    const int r = (idx >> 6) & 15;
+    const int ln = idx & 63;
+    const int n = n0 + 32 * nb + (ln & 31);
+    if (n >= n_rows) continue;
+    float sum = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < kOprojWaves; ++wv) sum += red[wv][nb][r][ln];
+    const int e = e0 + 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
+    if (gridDim.z > 1) {
+      part[(static_cast<size_t>(blockIdx.z) * n_rows + n) * e_dim + e] = sum;
+      continue;
+    }
+    if (bias != nullptr) sum += bias[e];
+    y[static_cast<size_t>(n) * e_dim + e] = to_bf16_bits(sum);
+  }
+}
+
+// y = bf16(sum of the K-range partials + bias), four outputs per thread.
+__global__ __launch_bounds__(256) void oproj_finish_kernel(const float* __restrict__ part, const float* __restrict__ bias,
+                                                           uint16_t* __restrict__ y, int splits, long long count,
+                                                           int e_dim) {
+  const long long i = (static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
+  if (i >= count) return;  // count is a multiple of 32 (e_dim is)
+  float4 acc = *reinterpret_cast<const float4*>(part + i);
+  for (int z = 1; z < splits; ++z) {
+    const float4 p = *reinterpret_cast<const float4*>(part + z * count + i);
+    acc.x += p.x;
+    acc.y += p.y;
+    acc.z += p.z;
+    acc.w += p.w;
+  }
+  if (bias != nullptr) {
+    const int e = static_cast<int>(i % e_dim);
+    acc.x += bias[e];
+    acc.y += bias[e + 1];
+    acc.z += bias[e + 2];
+    acc.w += bias[e + 3];
+  }
+  u16x4_t out;
+  out[0] = to_bf16_bits(acc.x);
+  out[1] = to_bf16_bits(acc.y);
+  out[2] = to_bf16_bits(acc.z);
+  out[3] = to_bf16_bits(acc.w);
+  *reinterpret_cast<u16x4_t*>(y + i) = out;
+}
+
+}  // namespace
+
+// K ranges per launch: enough workgroups to fill the chip twice (512) when
+// the row blocks alone do not, each range a multiple of 128 of K.
+int oproj_splits(int num_rows, int in_features, int out_features) {
+  const long long tiles = static_cast<long long>(out_features / kOprojCols) * ((num_rows + kOprojRows - 1) / kOprojRows);
+  int splits = 1;
+  while (tiles * splits < 512 && in_features % (128 * splits * 2) == 0 && splits < 32) splits *= 2;
+  return splits;
+}
+
+hipError_t launch_oproj(const OprojLaunch& a, hipStream_t stream) {
+  if (a.num_rows <= 0) return hipSuccess;
+  const int splits = oproj_splits(a.num_rows, a.in_features, a.out_features);
+  const dim3 grid(static_cast<unsigned>(a.out_features / kOprojCols),
+                  static_cast<unsigned>((a.num_rows + kOprojRows - 1) / kOprojRows), static_cast<unsigned>(splits));
+  hipLaunchKernelGGL(oproj_kernel, grid, dim3(64 * kOprojWaves), 0, stream, static_cast<const uint16_t*>(a.o),
+                     static_cast<const uint16_t*>(a.w), a.bias, static_cast<uint16_t*>(a.y), a.part, a.num_rows,
+                     a.in_features, a.out_features);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const long long count = static_cast<long long>(a.num_rows) * a.out_features;
+  hipLaunchKernelGGL(oproj_finish_kernel, dim3(static_cast<unsigned>((count / 4 + 255) / 256)), dim3(256), 0, stream,
+                     a.part, a.bias, static_cast<uint16_t*>(a.y), splits, count, a.out_features);
+  return hipGetLastError();
+}
+
+}  // namespace sinkattn

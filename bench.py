@@ -25,7 +25,8 @@ varlen prefill (causal and 128-window); the append prefill (the last
 against 8192 cached tokens, also through the multi-token-query decode at 1
 and 4 splits); the 64 x 8192 decode against a paged cache (16- and 64-token
 pages, shuffled); the fused rotary step (YaRN; Q out, K/V appended) for 8192
-and 64 tokens; a streaming-read and a copy
+and 64 tokens; the output projection with bias (64 and 8192 rows, 4096 ->
+2880); a streaming-read and a copy
 bandwidth reference; the engine clock (sysfs pp_dpm_sclk) sampled during the step.
 Small working sets are timed after a 512 MiB cache scrub.  The long-decode
 and ragged inputs are drawn on the device from a seeded generator (same
@@ -114,6 +115,15 @@ def rope_bytes(num_tokens: int, hq=HQ, hkv=HKV) -> float:
     """Fused rotary step: read qkv, positions and slots; write q, k and v."""
     row = D * 2
     return float(num_tokens * ((hq + 2 * hkv) * row * 2 + 8))
+
+
+OPROJ_OUT = 2880  # synthetic output width of the projection
+
+
+def oproj_bytes(num_rows: int, out_features: int = OPROJ_OUT, hq=HQ) -> float:
+    """Output projection: o and W read once, y written, bias read."""
+    k = hq * D
+    return float(2 * (num_rows * k + out_features * k + num_rows * out_features) + 4 * out_features)
 
 
 def decode_flops(lengths, window, hq=HQ) -> float:
@@ -717,6 +727,30 @@ def _other_configs(torch, np, binding, inputs, dev, bf16, timed, hbm_entry, mfma
         e["shape"] = "%d tokens, 64/8 heads, YaRN, K/V to distinct rows of a %d-row cache" % (n_tok, rows_cache)
         out["rope_qkv_append_%d" % n_tok] = e
         del rqkv, rkc, rvc, rq
+    torch.cuda.synchronize()
+
+    # output projection with bias (synthetic 2880-wide projection of the
+    # 64 x 64 concatenated heads): the 64 rows of a decode step and the 8192
+    # rows of the prefill
+    gen.manual_seed(7)
+    ow = (torch.randn((OPROJ_OUT, HQ * D), generator=gen, device=dev) / math.sqrt(HQ * D)).to(torch.bfloat16)
+    ob = torch.randn(OPROJ_OUT, generator=gen, device=dev, dtype=torch.float32)
+    for n_rows in (DEC_BATCH, PREFILL_LEN):
+        oo = _device_normal_bf16(torch, (n_rows, HQ * D), gen, dev)
+        oy = torch.empty((n_rows, OPROJ_OUT), dtype=torch.bfloat16, device=dev)
+        st = timed(lambda: binding.oproj_bias(oo, ow, ob, out=oy), scrub_each=True)
+        f = 2.0 * n_rows * HQ * D * OPROJ_OUT
+        b = oproj_bytes(n_rows)
+        if n_rows == DEC_BATCH:
+            e = hbm_entry(st, b, f)
+            e["bound"] = "hbm"
+        else:
+            e = mfma_entry(st, f, b)
+            e["bound"] = "mfma"
+        e["shape"] = "%d rows x 4096 -> 2880, bias" % n_rows
+        out["oproj_bias_%d" % n_rows] = e
+        del oo, oy
+    del ow, ob
     torch.cuda.synchronize()
 
     # append prefill: the last 2048-token chunk of an 8192-token prompt, and

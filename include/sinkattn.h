@@ -360,6 +360,39 @@ SINKATTN_API sinkattn_status sinkattn_rope_qkv_append(
     void* q_out, void* k_cache, void* v_cache, int32_t cache_rows, void* stream);
 
 /*
+ * Output projection with bias, the step after attention (Perplexity,
+ * "GPT-OSS on day 0", section "GPT-OSS on Hopper": the output projection
+ * carries a bias):
+ *     y[n, e] = sum_k o[n, k] * W[e, k] + bias[e]
+ *
+ *   o             bf16 [num_rows, in_features]: attention outputs with the
+ *                 query heads concatenated (the o of the attention entry
+ *                 points viewed as [rows, num_q_heads * head_dim])
+ *   w             bf16 [out_features, in_features]: one row per output
+ *                 feature
+ *   bias          fp32 [out_features], or NULL for none
+ *   y             bf16 [num_rows, out_features] (written; fp32 accumulation,
+ *                 rounded to nearest even once)
+ *
+ * in_features must be a multiple of 128 and out_features of 32, and
+ * num_rows at most 65535 * 64 (SINKATTN_ERR_UNSUPPORTED otherwise).  Shaped
+ * for decode-sized row counts, where the weight is the traffic: the weight is
+ * read from memory once per 64 rows, and when the (64-row, 32-feature) tiles
+ * alone would leave the chip idle, K is split across workgroups whose fp32
+ * partial sums go to the workspace (device, 256-byte aligned, at least
+ * sinkattn_oproj_workspace_bytes(num_rows, in_features, out_features) bytes,
+ * 0 when no split is made; SINKATTN_ERR_WORKSPACE otherwise) and a second
+ * kernel adds them and the bias.  Under SINKATTN_DEBUG_CHECKS=1 NaN / Inf in
+ * o or w is reported.
+ */
+SINKATTN_API size_t sinkattn_oproj_workspace_bytes(int32_t num_rows, int32_t in_features,
+                                                  int32_t out_features);
+SINKATTN_API sinkattn_status sinkattn_oproj_bias(
+    const void* o, const void* w, const float* bias,
+    int32_t num_rows, int32_t in_features, int32_t out_features,
+    void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Log-sum-exp merge of num_parts partial results, each normalised by its own
  * denominator (the combination step that the split-KV form of the
  * Perplexity page's online softmax implies; the page does not print it):

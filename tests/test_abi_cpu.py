@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
     assert _declared() == sorted([
         "sinkattn_decode_paged", "sinkattn_decode_splitkv", "sinkattn_decode_splitkv_fp8",
         "sinkattn_decode_splitkv_multi",
-        "sinkattn_decode_workspace_bytes", "sinkattn_rope_qkv_append",
+        "sinkattn_decode_workspace_bytes", "sinkattn_oproj_bias", "sinkattn_oproj_workspace_bytes",
+        "sinkattn_rope_qkv_append",
         "sinkattn_last_error", "sinkattn_merge_lse", "sinkattn_prefill_append", "sinkattn_prefill_varlen",
         "sinkattn_version"])
 
@@ -307,3 +308,28 @@ def test_rope_empty_and_plain_rope_arguments():
     lib = _lib()
     assert _rope(lib, t=0) == 0
     assert _rope(lib, t=0, s=1.0, L=0, bf=0.0, bs=0.0) == 0   # no YaRN: its parameters are not read
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE, None, 64, 4000, 2880, FAKE), 2),    # in_features not a multiple of 128
+    ((FAKE, FAKE, None, 64, 4096, 2890, FAKE), 2),    # out_features not a multiple of 32
+    ((FAKE, FAKE, None, -1, 4096, 2880, FAKE), 1),
+    ((FAKE, FAKE, None, 64, 0, 2880, FAKE), 1),
+    ((None, FAKE, None, 64, 4096, 2880, FAKE), 1),
+    ((FAKE, ctypes.c_void_p((1 << 20) + 2), None, 64, 4096, 2880, FAKE), 1),
+    ((FAKE, FAKE, None, 65536 * 64, 4096, 2880, FAKE), 2),
+    ((FAKE, FAKE, None, 64, 4096, 2880, FAKE), 3),    # split K needs a workspace
+])
+def test_oproj_rejects(args, status):
+    lib = _lib()
+    assert lib.sinkattn_oproj_bias(*args, None, 0, None) == status
+    assert lib.sinkattn_last_error()
+    assert lib.sinkattn_oproj_bias(FAKE, FAKE, None, 0, 4096, 2880, FAKE, None, 0, None) == 0
+
+
+def test_oproj_workspace_size():
+    lib = _lib()
+    # 64 rows: 90 tiles, K split 8 ways (720 workgroups); 8192 rows: no split
+    assert lib.sinkattn_oproj_workspace_bytes(64, 4096, 2880) == 8 * 64 * 2880 * 4
+    assert lib.sinkattn_oproj_workspace_bytes(8192, 4096, 2880) == 0
+    assert lib.sinkattn_oproj_workspace_bytes(0, 4096, 2880) == 0

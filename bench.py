@@ -197,7 +197,7 @@ def _cpu_other_configs(cores: int) -> dict:
     longest), both layers; 2 of the 64 decode sequences against the E4M3 and
     the paged cache; 256 query rows of the 2048-token append chunk (both
     layers); 2 of the 64 draft-token sequences; 1024 of the 8192 tokens of
-    the fused rotary step.  Rates are float64 GFLOP/s (or GB/s of the
+    the fused rotary step; the whole 64-row output projection.  Rates are float64 GFLOP/s (or GB/s of the
     algorithmic bytes); `seconds_full` extrapolates to the whole workload."""
     import numpy as np
 
@@ -295,6 +295,19 @@ def _cpu_other_configs(cores: int) -> dict:
     t = time.perf_counter() - t0
     out["rope_qkv_append_8192"] = {"seconds": t, "gbs_f64": rope_bytes(1024) / t / 1e9, "seconds_full": t * 8,
                                    "sample": "1024 of 8192 tokens (cache copies included), 1 process"}
+    # output projection with bias: the 64 rows of a decode step (whole)
+    from oracle import oproj_ref
+    rng = np.random.default_rng(0)
+    o_rows = inputs.bf16_bits_to_f32(inputs.round_to_bf16_bits(rng.standard_normal((DEC_BATCH, HQ * D),
+                                                                                   dtype=np.float32)))
+    w_rows = inputs.bf16_bits_to_f32(inputs.round_to_bf16_bits(
+        (rng.standard_normal((OPROJ_OUT, HQ * D)) / math.sqrt(HQ * D)).astype(np.float32)))
+    t0 = time.perf_counter()
+    oproj_ref(o_rows, w_rows, rng.standard_normal(OPROJ_OUT))
+    t = time.perf_counter() - t0
+    out["oproj_bias_64"] = {"seconds": t, "gbs_f64": oproj_bytes(DEC_BATCH) / t / 1e9,
+                            "gflops_f64": 2.0 * DEC_BATCH * HQ * D * OPROJ_OUT / t / 1e9,
+                            "sample": "whole workload (64 rows), 1 process"}
     out["draft_verify_64x4_ctx8192_causal"] = {
         "seconds": t, "gbs_f64": append_bytes([4, 4], [DEC_CTX] * 2, 0) / t / 1e9, "seconds_full": t * DEC_BATCH / 2,
         "sample": "2 of 64 sequences x 4 queries x 8192 keys, 1 process"}

@@ -8,10 +8,12 @@
 // Shaped for the decode step, where the rows are few and the weight is the
 // traffic: computed transposed, y^T = W o^T, with v_mfma_f32_32x32x16_bf16
 // (A = 32 rows of W, B = 32 rows of o, both 16-byte loads of 8 consecutive
-// k straight from memory: no LDS staging).  A workgroup owns 32 output
-// features and 64 rows; its 8 waves split K into 8 slices, so W is streamed
-// from HBM once per 64 rows while o stays in L2, and the slices are summed
-// through LDS, where the bias is added and the result rounded to bf16.  The
+// k straight from memory: no LDS staging).  A workgroup owns 32 kOprojTiles
+// output features and 64 rows, each wave all of them (its o loads feed
+// kOprojTiles weight tiles); the 8 waves split K into 8 slices, so W is
+// streamed from HBM once per 64 rows while o stays in L2, and the slices are
+// summed through LDS, where the bias is added and the result rounded to
+// bf16.  The
 // split-KV merge is not fused in: every 32-feature tile would re-read all of
 // the split partials, so the merge writes o once (bf16) and this kernel reads
 // it from L2.
@@ -23,9 +25,13 @@ namespace sinkattn {
 namespace {
 
 constexpr int kOprojWaves = 8;
-constexpr int kOprojCols = 32;  // output features per workgroup
-constexpr int kOprojRows = 64;  // rows per workgroup (two MFMA column blocks)
-constexpr int kOprojUnroll = 8;
+// 32-feature MFMA tiles per wave (they share each o load).  Measured at
+// 64 / 256 / 8192 rows x 4096 -> 2880: one tile 0.032 / 0.088 / 2.18 ms, two
+// 0.033 / 0.076 / 1.91 ms, four 0.044 / 0.085 / 1.82 ms.
+constexpr int kOprojTiles = 2;
+constexpr int kOprojCols = 32 * kOprojTiles;       // output features per workgroup
+constexpr int kOprojRows = 64;                     // rows per workgroup (two MFMA column blocks)
+constexpr int kOprojUnroll = 8 / kOprojTiles;
 
 // blockIdx.z takes K range [z K / gridDim.z, (z + 1) K / gridDim.z) (its 8
 // waves split it again); with more than one K range each workgroup writes
@@ -48,18 +54,26 @@ __global__ __launch_bounds__(64 * kOprojWaves) void oproj_kernel(const uint16_t*
   const int nr0 = min(n0 + (lane & 31), n_rows - 1);
   const int nr1 = min(n0 + 32 + (lane & 31), n_rows - 1);
   const bool two = n0 + 32 < n_rows;  // uniform: a second block of 32 rows
-  const uint16_t* wp = w + static_cast<size_t>(e0 + (lane & 31)) * k_dim + k_begin + kh;
+  // Feature rows past e_dim (the last tile of an e_dim not a multiple of
+  // kOprojCols) repeat row e_dim - 1 and are not stored.
+  const uint16_t* wp[kOprojTiles];
+#pragma unroll
+  for (int c = 0; c < kOprojTiles; ++c)
+    wp[c] = w + static_cast<size_t>(min(e0 + 32 * c + (lane & 31), e_dim - 1)) * k_dim + k_begin + kh;
   const uint16_t* op0 = o + static_cast<size_t>(nr0) * k_dim + k_begin + kh;
   const uint16_t* op1 = o + static_cast<size_t>(nr1) * k_dim + k_begin + kh;
 
-  f32x16_t acc0 = zero16(), acc1 = zero16();
+  f32x16_t acc[kOprojTiles][2];
+#pragma unroll
+  for (int c = 0; c < kOprojTiles; ++c) acc[c][0] = acc[c][1] = zero16();
   for (int k = 0; k < slice; k += 16 * kOprojUnroll) {
     const int steps = min(kOprojUnroll, (slice - k) / 16);
-    bf16x8_t a[kOprojUnroll], b0[kOprojUnroll], b1[kOprojUnroll];
+    bf16x8_t a[kOprojUnroll][kOprojTiles], b0[kOprojUnroll], b1[kOprojUnroll];
 #pragma unroll
     for (int u = 0; u < kOprojUnroll; ++u) {
       if (u < steps) {
-        a[u] = __builtin_bit_cast(bf16x8_t, load16_stream(wp + k + 16 * u));
+#pragma unroll
+        for (int c = 0; c < kOprojTiles; ++c) a[u][c] = __builtin_bit_cast(bf16x8_t, load16_stream(wp[c] + k + 16 * u));
         b0[u] = __builtin_bit_cast(bf16x8_t, load16(op0 + k + 16 * u));
         if (two) b1[u] = __builtin_bit_cast(bf16x8_t, load16(op1 + k + 16 * u));
       }
@@ -67,36 +81,43 @@ __global__ __launch_bounds__(64 * kOprojWaves) void oproj_kernel(const uint16_t*
 #pragma unroll
     for (int u = 0; u < kOprojUnroll; ++u) {
       if (u < steps) {
-        acc0 = mfma_32x32x16(a[u], b0[u], acc0);
-        if (two) acc1 = mfma_32x32x16(a[u], b1[u], acc1);
+#pragma unroll
+        for (int c = 0; c < kOprojTiles; ++c) {
+          acc[c][0] = mfma_32x32x16(a[u][c], b0[u], acc[c][0]);
+          if (two) acc[c][1] = mfma_32x32x16(a[u][c], b1[u], acc[c][1]);
+        }
       }
     }
   }
 
-  // Sum the K slices: register r of lane l holds y^T[e0 + 8 (r / 4) +
-  // 4 (l / 32) + r % 4][row block + l % 32].
+  // Sum the K slices, one 32-feature tile at a time: register r of lane l
+  // holds y^T[tile + 8 (r / 4) + 4 (l / 32) + r % 4][row block + l % 32].
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    red[wave][0][r][lane] = acc0[r];
-    red[wave][1][r][lane] = two ? acc1[r] : 0.0f;
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < 2 * 16 * 64; idx += 64 * kOprojWaves) {
-    const int nb = idx >> 10;
-    const int r = (idx >> 6) & 15;
-    const int ln = idx & 63;
-    const int n = n0 + 32 * nb + (ln & 31);
-    if (n >= n_rows) continue;
-    float sum = 0.0f;
+  for (int c = 0; c < kOprojTiles; ++c) {
+    if (c > 0) __syncthreads();  // the previous tile's sums are read
 #pragma unroll
-    for (int wv = 0; wv < kOprojWaves; ++wv) sum += red[wv][nb][r][ln];
-    const int e = e0 + 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
-    if (gridDim.z > 1) {
-      part[(static_cast<size_t>(blockIdx.z) * n_rows + n) * e_dim + e] = sum;
-      continue;
+    for (int r = 0; r < 16; ++r) {
+      red[wave][0][r][lane] = acc[c][0][r];
+      red[wave][1][r][lane] = two ? acc[c][1][r] : 0.0f;
     }
-    if (bias != nullptr) sum += bias[e];
-    y[static_cast<size_t>(n) * e_dim + e] = to_bf16_bits(sum);
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 2 * 16 * 64; idx += 64 * kOprojWaves) {
+      const int nb = idx >> 10;
+      const int r = (idx >> 6) & 15;
+      const int ln = idx & 63;
+      const int n = n0 + 32 * nb + (ln & 31);
+      const int e = e0 + 32 * c + 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
+      if (n >= n_rows || e >= e_dim) continue;
+      float sum = 0.0f;
+#pragma unroll
+      for (int wv = 0; wv < kOprojWaves; ++wv) sum += red[wv][nb][r][ln];
+      if (gridDim.z > 1) {
+        part[(static_cast<size_t>(blockIdx.z) * n_rows + n) * e_dim + e] = sum;
+        continue;
+      }
+      if (bias != nullptr) sum += bias[e];
+      y[static_cast<size_t>(n) * e_dim + e] = to_bf16_bits(sum);
+    }
   }
 }
 
@@ -134,7 +155,8 @@ __global__ __launch_bounds__(256) void oproj_finish_kernel(const float* __restri
 // K ranges per launch: enough workgroups to fill the chip twice (512) when
 // the row blocks alone do not, each range a multiple of 128 of K.
 int oproj_splits(int num_rows, int in_features, int out_features) {
-  const long long tiles = static_cast<long long>(out_features / kOprojCols) * ((num_rows + kOprojRows - 1) / kOprojRows);
+  const long long tiles = static_cast<long long>((out_features + kOprojCols - 1) / kOprojCols) *
+                          ((num_rows + kOprojRows - 1) / kOprojRows);
   int splits = 1;
   while (tiles * splits < 512 && in_features % (128 * splits * 2) == 0 && splits < 32) splits *= 2;
   return splits;
@@ -143,7 +165,7 @@ int oproj_splits(int num_rows, int in_features, int out_features) {
 hipError_t launch_oproj(const OprojLaunch& a, hipStream_t stream) {
   if (a.num_rows <= 0) return hipSuccess;
   const int splits = oproj_splits(a.num_rows, a.in_features, a.out_features);
-  const dim3 grid(static_cast<unsigned>(a.out_features / kOprojCols),
+  const dim3 grid(static_cast<unsigned>((a.out_features + kOprojCols - 1) / kOprojCols),
                   static_cast<unsigned>((a.num_rows + kOprojRows - 1) / kOprojRows), static_cast<unsigned>(splits));
   hipLaunchKernelGGL(oproj_kernel, grid, dim3(64 * kOprojWaves), 0, stream, static_cast<const uint16_t*>(a.o),
                      static_cast<const uint16_t*>(a.w), a.bias, static_cast<uint16_t*>(a.y), a.part, a.num_rows,

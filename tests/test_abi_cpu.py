@@ -329,7 +329,7 @@ def test_oproj_rejects(args, status):
 
 def test_oproj_workspace_size():
     lib = _lib()
-    # 64 rows: 45 tiles of 64 features, K split 16 ways (720 workgroups); 8192 rows: no split
-    assert lib.sinkattn_oproj_workspace_bytes(64, 4096, 2880) == 16 * 64 * 2880 * 4
+    # 64 rows: 45 tiles of 64 features, K split 4 ways (180 workgroups); 8192 rows: no split
+    assert lib.sinkattn_oproj_workspace_bytes(64, 4096, 2880) == 4 * 64 * 2880 * 4
     assert lib.sinkattn_oproj_workspace_bytes(8192, 4096, 2880) == 0
     assert lib.sinkattn_oproj_workspace_bytes(0, 4096, 2880) == 0

@@ -377,13 +377,14 @@ SINKATTN_API sinkattn_status sinkattn_rope_qkv_append(
  * in_features must be a multiple of 128 and out_features of 32, and
  * num_rows at most 65535 * 64 (SINKATTN_ERR_UNSUPPORTED otherwise).  Shaped
  * for decode-sized row counts, where the weight is the traffic: the weight is
- * read from memory once per 64 rows, and when the (64-row, 32-feature) tiles
+ * read from memory once per 64 rows, and when the (64-row, 64-feature) tiles
  * alone would leave the chip idle, K is split across workgroups whose fp32
  * partial sums go to the workspace (device, 256-byte aligned, at least
  * sinkattn_oproj_workspace_bytes(num_rows, in_features, out_features) bytes,
  * 0 when no split is made; SINKATTN_ERR_WORKSPACE otherwise) and a second
- * kernel adds them and the bias.  Under SINKATTN_DEBUG_CHECKS=1 NaN / Inf in
- * o or w is reported.
+ * kernel adds them and the bias.  Above 256 rows an LDS-tiled GEMM runs
+ * instead (no workspace).  Under SINKATTN_DEBUG_CHECKS=1 NaN / Inf in o or w
+ * is reported.
  */
 SINKATTN_API size_t sinkattn_oproj_workspace_bytes(int32_t num_rows, int32_t in_features,
                                                   int32_t out_features);

@@ -163,66 +163,73 @@ __global__ __launch_bounds__(256) void oproj_finish_kernel(const float* __restri
 // operand element is read from memory once per tile instead of once per
 // 32 x 32 MFMA block.  LDS rows are padded by 8 elements (16 bytes) so that
 // the 16-byte reads of 32 consecutive rows spread over the banks.
-constexpr int kGemmTile = 128;
 // K per LDS step (8192 rows x 4096 -> 2880: 32 -> 0.316 ms, 64 -> 0.277,
 // 128 -> 0.287)
 constexpr int kGemmK = 64;
-constexpr int kGemmPad = kGemmK + 8;  // LDS row stride in elements
-constexpr int kGemmChunks = kGemmK / 8;                 // 16-byte chunks per tile row
-constexpr int kGemmPassRows = 256 / kGemmChunks;        // tile rows one pass of 256 threads copies
-constexpr int kGemmPasses = kGemmTile / kGemmPassRows;
+constexpr int kGemmPad = kGemmK + 8;      // LDS row stride in elements
+constexpr int kGemmChunks = kGemmK / 8;   // 16-byte chunks per tile row
+// Rows and output features per workgroup (8192 rows: 128 x 128 0.281 ms,
+// 256 x 128 0.290, 128 x 256 0.295 with 8 waves).
+constexpr int kGemmTN = 128;
+constexpr int kGemmTE = 128;
+constexpr int kGemmWaves = (kGemmTN / 64) * (kGemmTE / 64);
+constexpr int kGemmThreads = 64 * kGemmWaves;
+constexpr int kGemmPassRows = kGemmThreads / kGemmChunks;  // tile rows one pass of the threads copies
+constexpr int kGemmPassesO = kGemmTN / kGemmPassRows;
+constexpr int kGemmPassesW = kGemmTE / kGemmPassRows;
 
-__global__ __launch_bounds__(256) void oproj_gemm_kernel(const uint16_t* __restrict__ o,
-                                                         const uint16_t* __restrict__ w,
-                                                         const float* __restrict__ bias, uint16_t* __restrict__ y,
-                                                         int n_rows, int k_dim, int e_dim) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_o[kGemmTile * kGemmPad];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_w[kGemmTile * kGemmPad];
+__global__ __launch_bounds__(kGemmThreads) void oproj_gemm_kernel(const uint16_t* __restrict__ o,
+                                                                  const uint16_t* __restrict__ w,
+                                                                  const float* __restrict__ bias,
+                                                                  uint16_t* __restrict__ y, int n_rows, int k_dim,
+                                                                  int e_dim) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds_o[kGemmTN * kGemmPad];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_w[kGemmTE * kGemmPad];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int n0 = blockIdx.x * kGemmTile;
-  const int e0 = blockIdx.y * kGemmTile;
+  const int n0 = blockIdx.x * kGemmTN;
+  const int e0 = blockIdx.y * kGemmTE;
   // Copy assignment: thread t moves 16-byte chunk t % kGemmChunks of tile
   // rows t / kGemmChunks + kGemmPassRows i (rows past the matrix repeat its
   // last row).
   const int crow = tid / kGemmChunks;
   const int cchunk = 8 * (tid % kGemmChunks);
-  const uint16_t* og[kGemmPasses];
-  const uint16_t* wg[kGemmPasses];
+  const uint16_t* og[kGemmPassesO];
+  const uint16_t* wg[kGemmPassesW];
 #pragma unroll
-  for (int i = 0; i < kGemmPasses; ++i) {
+  for (int i = 0; i < kGemmPassesO; ++i)
     og[i] = o + static_cast<size_t>(min(n0 + crow + kGemmPassRows * i, n_rows - 1)) * k_dim + cchunk;
+#pragma unroll
+  for (int i = 0; i < kGemmPassesW; ++i)
     wg[i] = w + static_cast<size_t>(min(e0 + crow + kGemmPassRows * i, e_dim - 1)) * k_dim + cchunk;
-  }
   // Wave (we, wn) computes features e0 + 64 we .. + 63 and rows n0 + 64 wn ..
-  const int we = wave & 1;
-  const int wn = wave >> 1;
+  const int we = wave % (kGemmTE / 64);
+  const int wn = wave / (kGemmTE / 64);
   const int kh = 8 * (lane >> 5);
   f32x16_t acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = zero16();
 
-  u32x4_t ro[kGemmPasses], rw[kGemmPasses];
+  u32x4_t ro[kGemmPassesO], rw[kGemmPassesW];
 #pragma unroll
-  for (int i = 0; i < kGemmPasses; ++i) {
-    ro[i] = load16(og[i]);
-    rw[i] = load16(wg[i]);
-  }
+  for (int i = 0; i < kGemmPassesO; ++i) ro[i] = load16(og[i]);
+#pragma unroll
+  for (int i = 0; i < kGemmPassesW; ++i) rw[i] = load16(wg[i]);
   for (int k = 0; k < k_dim; k += kGemmK) {
     __syncthreads();  // the previous tiles' LDS reads are done
 #pragma unroll
-    for (int i = 0; i < kGemmPasses; ++i) {
+    for (int i = 0; i < kGemmPassesO; ++i)
       *reinterpret_cast<u32x4_t*>(lds_o + (crow + kGemmPassRows * i) * kGemmPad + cchunk) = ro[i];
+#pragma unroll
+    for (int i = 0; i < kGemmPassesW; ++i)
       *reinterpret_cast<u32x4_t*>(lds_w + (crow + kGemmPassRows * i) * kGemmPad + cchunk) = rw[i];
-    }
     __syncthreads();
     if (k + kGemmK < k_dim) {
 #pragma unroll
-      for (int i = 0; i < kGemmPasses; ++i) {
-        ro[i] = load16(og[i] + k + kGemmK);
-        rw[i] = load16(wg[i] + k + kGemmK);
-      }
+      for (int i = 0; i < kGemmPassesO; ++i) ro[i] = load16(og[i] + k + kGemmK);
+#pragma unroll
+      for (int i = 0; i < kGemmPassesW; ++i) rw[i] = load16(wg[i] + k + kGemmK);
     }
 #pragma unroll
     for (int ks = 0; ks < kGemmK; ks += 16) {
@@ -276,9 +283,9 @@ int oproj_splits(int num_rows, int in_features, int out_features) {
 hipError_t launch_oproj(const OprojLaunch& a, hipStream_t stream) {
   if (a.num_rows <= 0) return hipSuccess;
   if (a.num_rows > kOprojGemmMinRows) {
-    const dim3 grid(static_cast<unsigned>((a.num_rows + kGemmTile - 1) / kGemmTile),
-                    static_cast<unsigned>((a.out_features + kGemmTile - 1) / kGemmTile));
-    hipLaunchKernelGGL(oproj_gemm_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(a.o),
+    const dim3 grid(static_cast<unsigned>((a.num_rows + kGemmTN - 1) / kGemmTN),
+                    static_cast<unsigned>((a.out_features + kGemmTE - 1) / kGemmTE));
+    hipLaunchKernelGGL(oproj_gemm_kernel, grid, dim3(kGemmThreads), 0, stream, static_cast<const uint16_t*>(a.o),
                        static_cast<const uint16_t*>(a.w), a.bias, static_cast<uint16_t*>(a.y), a.num_rows,
                        a.in_features, a.out_features);
     return hipGetLastError();

@@ -20,7 +20,8 @@ sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
 import numpy as np  # noqa: E402
 
 from attention_gqa_flash_amd import inputs  # noqa: E402
-from oracle import decode_ref, decode_split_partials_ref, prefill_varlen_ref  # noqa: E402
+from oracle import (decode_fp8_ref, decode_paged_ref, decode_ref, decode_split_partials_ref, oproj_ref,  # noqa: E402
+                    prefill_append_ref, prefill_varlen_ref, rope_qkv_append_ref, yarn_inv_freq_ref)
 
 PREFILL = dict(lengths=[33, 70], hq=4, hkv=2, d=64, seed=7)
 PREFILL_ROWS = [0, 32, 102]
@@ -49,8 +50,53 @@ def build():
     return out
 
 
+APPEND = dict(q_lens=[3, 1, 20], k_lens=[40, 1, 20], hq=8, hkv=2, seed=9)
+PAGED = dict(lengths=[5, 70], page_size=16, hq=8, hkv=2, seed=10)
+FP8 = dict(lengths=[30, 90], hq=8, hkv=2, seed=11)
+ROPE = dict(tokens=6, hq=4, hkv=2, cache_rows=10, seed=12)
+YARN = dict(theta=150000.0, factor=32.0, original=4096, beta_fast=32.0, beta_slow=1.0)
+
+
+def build_next():
+    """The oracle functions of the appended-query, paged, FP8, rotary and
+    projection workloads (oracle/append.py, paged.py, fp8.py, rope.py,
+    oproj.py) on small seeded inputs."""
+    out = {"source": "oracle/{append,paged,fp8,rope,oproj}.py on seeded inputs (see make_golden.py)"}
+    a = inputs.make_append(APPEND["q_lens"], APPEND["k_lens"], APPEND["hq"], APPEND["hkv"], seed=APPEND["seed"])
+    q, k, v = (inputs.bf16_bits_to_f32(x) for x in (a.q, a.k, a.v))
+    out["append"] = {"inputs": APPEND, "cases": []}
+    for window in (0, 8):
+        o, lse = prefill_append_ref(q, k, v, a.sinks, a.cu_seqlens_q, a.cu_seqlens_k, window, a.scale)
+        out["append"]["cases"].append({"window": window, "o_d8": _f(o[..., :8]), "lse": _f(lse)})
+    p = inputs.make_paged_decode(PAGED["lengths"], PAGED["page_size"], PAGED["hq"], PAGED["hkv"], seed=PAGED["seed"])
+    o, lse = decode_paged_ref(inputs.bf16_bits_to_f32(p.q), inputs.bf16_bits_to_f32(p.k_pages),
+                              inputs.bf16_bits_to_f32(p.v_pages), p.block_table, p.seq_lens, p.page_size, p.sinks, 0,
+                              p.scale)
+    out["paged"] = {"inputs": PAGED, "o_d8": _f(o[..., :8]), "lse": _f(lse)}
+    f8 = inputs.make_decode_fp8(FP8["lengths"], FP8["hq"], FP8["hkv"], seed=FP8["seed"])
+    o, lse = decode_fp8_ref(inputs.bf16_bits_to_f32(f8.q), f8.k, f8.v, f8.k_scale, f8.v_scale, f8.cu_seqlens_k,
+                            f8.sinks, 0, f8.scale)
+    out["fp8"] = {"inputs": FP8, "o_d8": _f(o[..., :8]), "lse": _f(lse)}
+    r = inputs.make_rope(ROPE["tokens"], ROPE["hq"], ROPE["hkv"], ROPE["cache_rows"], seed=ROPE["seed"])
+    freq, m = yarn_inv_freq_ref(64, YARN["theta"], YARN["factor"], YARN["original"], YARN["beta_fast"],
+                                YARN["beta_slow"])
+    q_out, kc, _ = rope_qkv_append_ref(inputs.bf16_bits_to_f32(r.qkv), r.positions, ROPE["hq"], ROPE["hkv"], freq, m,
+                                       r.slot_mapping, inputs.bf16_bits_to_f32(r.k_cache),
+                                       inputs.bf16_bits_to_f32(r.v_cache))
+    out["rope"] = {"inputs": ROPE, "yarn": YARN, "freq": _f(freq), "temperature": float(m),
+                   "q_d8": _f(q_out[..., :8]), "k_cache_d8": _f(kc[..., :8])}
+    rng = np.random.default_rng(13)
+    o_in = rng.standard_normal((3, 128))
+    w_in = rng.standard_normal((32, 128)) / np.sqrt(128)
+    b_in = rng.standard_normal(32)
+    out["oproj"] = {"seed": 13, "y": _f(oproj_ref(o_in, w_in, b_in))}
+    return out
+
+
 if __name__ == "__main__":
     data = build()
     with open(os.path.join(HERE, "oracle_regression.json"), "w") as f:
         json.dump(data, f)
-    print("wrote oracle_regression.json")
+    with open(os.path.join(HERE, "oracle_regression_next.json"), "w") as f:
+        json.dump(build_next(), f)
+    print("wrote oracle_regression.json, oracle_regression_next.json")

@@ -38,3 +38,29 @@ def test_decode_fixture():
         np.testing.assert_allclose(o[..., :8].ravel(), case["o_d8"], rtol=1e-10, atol=1e-13)
         np.testing.assert_allclose(lse.ravel(), case["lse"], rtol=1e-12)
         np.testing.assert_allclose(lp.ravel(), case["split4_lse"], rtol=1e-12)
+
+
+def _load_next():
+    with open(os.path.join(HERE, "oracle_regression_next.json")) as f:
+        return json.load(f)
+
+
+def test_next_fixture_against_the_current_oracle():
+    """Appended queries, paged decode, FP8 decode, rotary step and projection
+    reproduce their stored values (written by tests/golden/make_golden.py)."""
+    import sys
+    sys.path.insert(0, HERE)
+    import make_golden
+    stored = _load_next()
+    fresh = make_golden.build_next()
+    for key in ("append", "paged", "fp8", "rope", "oproj"):
+        a, b = stored[key], fresh[key]
+        for field, value in a.items():
+            if field in ("inputs", "yarn", "seed"):
+                assert value == b[field]
+            elif field == "cases":
+                for ca, cb in zip(value, b[field]):
+                    for f2 in ca:
+                        np.testing.assert_allclose(cb[f2], ca[f2], rtol=1e-10, atol=1e-13)
+            else:
+                np.testing.assert_allclose(b[field], value, rtol=1e-10, atol=1e-13)

@@ -80,6 +80,8 @@ sinkattn_status check_failed(unsigned flags) {
       {sinkattn::kCheckAppend, "a sequence has fewer keys than queries (cu_seqlens_k vs cu_seqlens_q)"},
       {sinkattn::kCheckPages, "a page id is outside the pool, or a block table row is too short"},
       {sinkattn::kCheckSlots, "a slot is outside [-1, cache_rows) or names a cache row twice"},
+      {sinkattn::kCheckO, "o holds NaN or Inf"},
+      {sinkattn::kCheckW, "w holds NaN or Inf"},
   };
   std::string msg = "debug checks failed:";
   for (const auto& n : kNames)
@@ -440,11 +442,11 @@ sinkattn_status sinkattn_oproj_bias(const void* o, const void* w, const float* b
     hipStream_t s = static_cast<hipStream_t>(stream);
     sinkattn_status st;
     if ((st = hip_queue(sinkattn::check_clear(s))) != SINKATTN_OK) return st;
-    if ((st = hip_queue(sinkattn::check_bf16(o, static_cast<size_t>(num_rows) * in_features, sinkattn::kCheckQ,
+    if ((st = hip_queue(sinkattn::check_bf16(o, static_cast<size_t>(num_rows) * in_features, sinkattn::kCheckO,
                                              s))) != SINKATTN_OK)
       return st;
     if ((st = hip_queue(sinkattn::check_bf16(w, static_cast<size_t>(out_features) * in_features,
-                                             sinkattn::kCheckK, s))) != SINKATTN_OK)
+                                             sinkattn::kCheckW, s))) != SINKATTN_OK)
       return st;
     if ((st = check_result(s, nullptr)) != SINKATTN_OK) return st;
   }

@@ -115,7 +115,9 @@ enum CheckBits : unsigned {
   kCheckAppend = 1u << 10,       // append prefill: a sequence with fewer keys than queries
   kCheckPages = 1u << 11,        // paged decode: a page id outside the pool or a table too short
   kCheckSlots = 1u << 12,        // rotary append: a slot outside [-1, cache_rows) or used twice
-  kCheckAll = (1u << 13) - 1u,
+  kCheckO = 1u << 13,            // output projection: NaN / Inf in o
+  kCheckW = 1u << 14,            // output projection: NaN / Inf in w
+  kCheckAll = (1u << 15) - 1u,
 };
 hipError_t check_clear(hipStream_t stream);
 hipError_t check_offsets(const int32_t* cu, int batch, int max_len, int min_len, int total_limit,

@@ -61,3 +61,16 @@ def test_oproj_of_a_decode_output():
     torch.cuda.synchronize()
     o_bits = o.view(torch.int16).cpu().numpy().view(np.uint16).reshape(64, 4096)
     _check(o_bits, w, b, y)
+
+
+def test_oproj_debug_check_names_the_operand(monkeypatch):
+    monkeypatch.setenv("SINKATTN_DEBUG_CHECKS", "1")
+    o, w, b = _case(64, 4096, 2880, seed=8)
+    y = binding.oproj_bias(bf16_to_device(o), bf16_to_device(w), f32_to_device(b))
+    torch.cuda.synchronize()
+    _check(o, w, b, y)
+    w_bad = w.copy()
+    w_bad[5, 17] = 0x7FC0  # bf16 NaN
+    with pytest.raises(binding.SinkAttnError) as err:
+        binding.oproj_bias(bf16_to_device(o), bf16_to_device(w_bad), f32_to_device(b))
+    assert err.value.status == 1 and "w holds NaN" in str(err.value)

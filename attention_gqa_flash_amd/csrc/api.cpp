@@ -77,7 +77,7 @@ sinkattn_status check_failed(unsigned flags) {
       {sinkattn::kCheckK, "k holds NaN or Inf"},
       {sinkattn::kCheckV, "v holds NaN or Inf"},
       {sinkattn::kCheckParts, "o_parts holds NaN or Inf, or lse_parts NaN or +inf"},
-      {sinkattn::kCheckAppend, "a sequence has fewer keys than queries (cu_seqlens_k vs cu_seqlens_q)"},
+      {sinkattn::kCheckAppend, "a sequence has fewer keys than queries (its key length vs cu_seqlens_q)"},
       {sinkattn::kCheckPages, "a page id is outside the pool, or a block table row is too short"},
       {sinkattn::kCheckSlots, "a slot is outside [-1, cache_rows) or names a cache row twice"},
       {sinkattn::kCheckO, "o holds NaN or Inf"},
@@ -146,7 +146,7 @@ static sinkattn_status prefill_common(const void* q, const void* k, const void* 
     if ((st = hip_queue(sinkattn::check_offsets(cu_q, batch, max_q, 0, total_q, s))) != SINKATTN_OK) return st;
     if (append) {
       if ((st = hip_queue(sinkattn::check_offsets(cu_k, batch, max_k, 0, total_k, s))) != SINKATTN_OK) return st;
-      if ((st = hip_queue(sinkattn::check_append(cu_q, cu_k, batch, s))) != SINKATTN_OK) return st;
+      if ((st = hip_queue(sinkattn::check_append(cu_q, cu_k, false, batch, s))) != SINKATTN_OK) return st;
     }
     if ((st = hip_queue(sinkattn::check_sinks(sinks, num_q_heads, s))) != SINKATTN_OK) return st;
     if ((st = hip_queue(sinkattn::check_bf16(q, qn, sinkattn::kCheckQ, s))) != SINKATTN_OK) return st;
@@ -241,7 +241,8 @@ static sinkattn_status decode_common(const void* q, const void* k_cache, const v
     if (multi) {
       if ((st = hip_queue(sinkattn::check_offsets(cu_seqlens_q, batch, max_seqlen_q, 0, total_q, s))) != SINKATTN_OK)
         return st;
-      if ((st = hip_queue(sinkattn::check_append(cu_seqlens_q, cu_seqlens_k, batch, s))) != SINKATTN_OK) return st;
+      if ((st = hip_queue(sinkattn::check_append(cu_seqlens_q, cu_seqlens_k, paged, batch, s))) != SINKATTN_OK)
+        return st;
     }
     if (paged) {
       if ((st = hip_queue(sinkattn::check_paged(cu_seqlens_k, block_table, batch, max_pages, page_size, num_pages,
@@ -330,12 +331,9 @@ sinkattn_status sinkattn_decode_splitkv_multi(const void* q, const void* k_cache
                        1.0f, 1.0f, cu_seqlens_q, max_seqlen_q, total_q);
 }
 
-sinkattn_status sinkattn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
-                                      const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
-                                      int32_t max_pages, int32_t page_size, int32_t num_pages, int32_t max_seqlen_k,
-                                      const float* sinks, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                      int32_t window, float softmax_scale, int32_t num_splits, void* workspace,
-                                      size_t workspace_bytes, void* o, float* lse, void* stream) {
+// Arguments of the paged cache, shared by the paged decode entry points.
+static sinkattn_status check_pages(const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                                   int32_t max_pages, int32_t page_size, int32_t num_pages, int32_t max_seqlen_k) {
   if (page_size < 16 || page_size > (1 << 20) || (page_size & (page_size - 1)) != 0)
     return fail(SINKATTN_ERR_UNSUPPORTED, "page_size must be a power of two in [16, 2^20] (got %d)", page_size);
   if (batch < 0 || max_pages < 0 || num_pages < 0)
@@ -349,10 +347,37 @@ sinkattn_status sinkattn_decode_paged(const void* q, const void* k_pages, const 
     return fail(SINKATTN_ERR_UNSUPPORTED, "num_pages * page_size must stay below 2^31 tokens");
   if (batch > 0 && (block_table == nullptr || seq_lens == nullptr))
     return fail(SINKATTN_ERR_INVALID_ARG, "block_table and seq_lens must not be NULL");
+  return ok();
+}
+
+sinkattn_status sinkattn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                                      const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                                      int32_t max_pages, int32_t page_size, int32_t num_pages, int32_t max_seqlen_k,
+                                      const float* sinks, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t window, float softmax_scale, int32_t num_splits, void* workspace,
+                                      size_t workspace_bytes, void* o, float* lse, void* stream) {
+  sinkattn_status st = check_pages(block_table, seq_lens, batch, max_pages, page_size, num_pages, max_seqlen_k);
+  if (st != SINKATTN_OK) return st;
   // (batch 0 validates the remaining arguments and returns)
   return decode_common(q, k_pages, v_pages, seq_lens, batch, max_seqlen_k, sinks, num_q_heads, num_kv_heads,
                        head_dim, window, softmax_scale, num_splits, workspace, workspace_bytes, o, lse, stream, false,
                        1.0f, 1.0f, nullptr, 1, 0, block_table, max_pages, page_size, num_pages);
+}
+
+sinkattn_status sinkattn_decode_paged_multi(const void* q, const void* k_pages, const void* v_pages,
+                                            const int32_t* block_table, const int32_t* seq_lens,
+                                            const int32_t* cu_seqlens_q, int32_t batch, int32_t max_pages,
+                                            int32_t page_size, int32_t num_pages, int32_t max_seqlen_q,
+                                            int32_t max_seqlen_k, int32_t total_q, const float* sinks,
+                                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                            int32_t window, float softmax_scale, int32_t num_splits, void* workspace,
+                                            size_t workspace_bytes, void* o, float* lse, void* stream) {
+  sinkattn_status st = check_pages(block_table, seq_lens, batch, max_pages, page_size, num_pages, max_seqlen_k);
+  if (st != SINKATTN_OK) return st;
+  if (cu_seqlens_q == nullptr && batch > 0) return fail(SINKATTN_ERR_INVALID_ARG, "cu_seqlens_q must not be NULL");
+  return decode_common(q, k_pages, v_pages, seq_lens, batch, max_seqlen_k, sinks, num_q_heads, num_kv_heads,
+                       head_dim, window, softmax_scale, num_splits, workspace, workspace_bytes, o, lse, stream, false,
+                       1.0f, 1.0f, cu_seqlens_q, max_seqlen_q, total_q, block_table, max_pages, page_size, num_pages);
 }
 
 // Rotary frequencies of the pairs (i, i + 32): theta^(-2i/64), rescaled by

@@ -43,10 +43,12 @@ __global__ void check_offsets_kernel(const int32_t* __restrict__ cu, int batch, 
 
 // Append prefill: no sequence may have fewer key rows than query rows.
 __global__ void check_append_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
-                                    int batch) {
+                                    bool k_lengths, int batch) {
   unsigned bits = 0;
-  for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < batch; b += gridDim.x * blockDim.x)
-    if (cu_k[b + 1] - cu_k[b] < cu_q[b + 1] - cu_q[b]) bits |= kCheckAppend;
+  for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < batch; b += gridDim.x * blockDim.x) {
+    const int lk = k_lengths ? cu_k[b] : cu_k[b + 1] - cu_k[b];
+    if (lk < cu_q[b + 1] - cu_q[b]) bits |= kCheckAppend;
+  }
   if (bits != 0u) atomicOr(&g_check_flags, bits);
 }
 
@@ -147,9 +149,9 @@ hipError_t check_offsets(const int32_t* cu, int batch, int max_len, int min_len,
   return hipGetLastError();
 }
 
-hipError_t check_append(const int32_t* cu_q, const int32_t* cu_k, int batch, hipStream_t stream) {
+hipError_t check_append(const int32_t* cu_q, const int32_t* cu_k, bool k_lengths, int batch, hipStream_t stream) {
   if (batch <= 0) return hipSuccess;
-  hipLaunchKernelGGL(check_append_kernel, dim3(grid_for(batch)), dim3(256), 0, stream, cu_q, cu_k, batch);
+  hipLaunchKernelGGL(check_append_kernel, dim3(grid_for(batch)), dim3(256), 0, stream, cu_q, cu_k, k_lengths, batch);
   return hipGetLastError();
 }
 

@@ -685,7 +685,9 @@ static hipError_t launch_decode_t(const DecodeLaunch& a, hipStream_t stream) {
 }
 
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
-  if (a.block_table != nullptr) return launch_decode_t<false, false, true>(a, stream);
+  if (a.block_table != nullptr)
+    return a.cu_seqlens_q != nullptr ? launch_decode_t<false, true, true>(a, stream)
+                                     : launch_decode_t<false, false, true>(a, stream);
   if (a.cu_seqlens_q != nullptr) return launch_decode_t<false, true, false>(a, stream);
   return a.fp8 ? launch_decode_t<true, false, false>(a, stream) : launch_decode_t<false, false, false>(a, stream);
 }

@@ -126,7 +126,8 @@ hipError_t check_sinks(const float* sinks, int n, hipStream_t stream);
 // Rotary append: every slot in [-1, cache_rows), and no cache row named twice.
 hipError_t check_slots(const int32_t* slots, int n, int cache_rows, hipStream_t stream);
 // Append prefill: every sequence has cu_k[b+1] - cu_k[b] >= cu_q[b+1] - cu_q[b].
-hipError_t check_append(const int32_t* cu_q, const int32_t* cu_k, int batch, hipStream_t stream);
+// cu_k holds offsets [batch + 1], or (k_lengths) the lengths [batch].
+hipError_t check_append(const int32_t* cu_q, const int32_t* cu_k, bool k_lengths, int batch, hipStream_t stream);
 // Paged decode: 1 <= seq_lens[b] <= max_len and every page id a sequence
 // uses (the first ceil(L_b / page_size) of its table row) in [0, num_pages).
 hipError_t check_paged(const int32_t* seq_lens, const int32_t* block_table, int batch, int max_pages,

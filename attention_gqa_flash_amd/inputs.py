@@ -171,24 +171,61 @@ def make_paged_decode(lengths, page_size: int, hq: int, hkv: int, d: int = 64, s
     tokens shows in its output)."""
     rng = rng if rng is not None else np.random.default_rng(seed)
     dec = make_decode(lengths, hq, hkv, d, rng=rng, scale=scale, sink_std=sink_std)
-    n_pages = [-(-int(n) // page_size) for n in dec.lengths]
+    kp, vp, bt = _scatter_pages(dec.k, dec.v, dec.cu_seqlens_k, dec.lengths, page_size, rng, spare_pages, fill_bits)
+    return PagedDecodeInputs(dec.q, kp, vp, bt, np.asarray(dec.lengths, dtype=np.int32), dec.sinks, page_size,
+                             scale, list(dec.lengths))
+
+
+def _scatter_pages(k, v, cu, lengths, page_size, rng, spare_pages, fill_bits):
+    """Packed rows -> pages in a random physical order (one permutation drawn
+    from rng) with spare pages; unowned slots hold fill_bits.  Returns
+    (k_pages, v_pages, block_table with -1 past each sequence's pages)."""
+    hkv, d = k.shape[1], k.shape[2]
+    n_pages = [-(-int(n) // page_size) for n in lengths]
     total = sum(n_pages) + spare_pages
     order = rng.permutation(total)
     kp = np.full((total, page_size, hkv, d), fill_bits, dtype=np.uint16)
     vp = np.full((total, page_size, hkv, d), fill_bits, dtype=np.uint16)
-    bt = np.full((len(dec.lengths), max(n_pages) + 1), -1, dtype=np.int32)
+    bt = np.full((len(lengths), max(n_pages) + 1), -1, dtype=np.int32)
     nxt = 0
-    for b, n in enumerate(dec.lengths):
-        base = int(dec.cu_seqlens_k[b])
+    for b, n in enumerate(lengths):
+        base = int(cu[b])
         for p in range(n_pages[b]):
             phys = int(order[nxt])
             nxt += 1
             bt[b, p] = phys
             lo, hi = p * page_size, min(n, (p + 1) * page_size)
-            kp[phys, :hi - lo] = dec.k[base + lo:base + hi]
-            vp[phys, :hi - lo] = dec.v[base + lo:base + hi]
-    return PagedDecodeInputs(dec.q, kp, vp, bt, np.asarray(dec.lengths, dtype=np.int32), dec.sinks, page_size,
-                             scale, list(dec.lengths))
+            kp[phys, :hi - lo] = k[base + lo:base + hi]
+            vp[phys, :hi - lo] = v[base + lo:base + hi]
+    return kp, vp, bt
+
+
+@dataclass
+class PagedAppendInputs:
+    q: np.ndarray             # uint16 bf16 bits [Tq, Hq, D]
+    k_pages: np.ndarray       # uint16 bf16 bits [P, page_size, Hkv, D]
+    v_pages: np.ndarray
+    block_table: np.ndarray   # int32 [B, max_pages] (-1 past a sequence's pages)
+    seq_lens: np.ndarray      # int32 [B] (Lk_b)
+    cu_seqlens_q: np.ndarray  # int32 [B+1]
+    sinks: np.ndarray         # float32 [Hq]
+    page_size: int
+    scale: float
+    q_lens: list = field(default_factory=list)
+    k_lens: list = field(default_factory=list)
+
+
+def make_paged_append(q_lens, k_lens, page_size: int, hq: int, hkv: int, d: int = 64, seed: int = 0,
+                      scale: float = 0.125, spare_pages: int = 3, fill_bits: int = 0x7FC0,
+                      rng: Optional[np.random.Generator] = None):
+    """The draws of make_append (q -> k -> v -> sinks) with the cache
+    scattered into pages as make_paged_decode does (permutation drawn after
+    the sinks, unowned slots NaN)."""
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    a = make_append(q_lens, k_lens, hq, hkv, d, rng=rng, scale=scale)
+    kp, vp, bt = _scatter_pages(a.k, a.v, a.cu_seqlens_k, a.k_lens, page_size, rng, spare_pages, fill_bits)
+    return PagedAppendInputs(a.q, kp, vp, bt, np.asarray(a.k_lens, dtype=np.int32), a.cu_seqlens_q, a.sinks,
+                             page_size, scale, list(a.q_lens), list(a.k_lens))
 
 
 @dataclass

@@ -24,7 +24,7 @@ varlen prefill (causal and 128-window); the append prefill (the last
 2048-token chunk of an 8192-token prompt; 64 x 4 draft tokens verified
 against 8192 cached tokens, also through the multi-token-query decode at 1
 and 4 splits); the 64 x 8192 decode against a paged cache (16- and 64-token
-pages, shuffled); the fused rotary step (YaRN; Q out, K/V appended) for 8192
+pages, shuffled), also with 4 draft tokens per sequence; the fused rotary step (YaRN; Q out, K/V appended) for 8192
 and 64 tokens; the output projection with bias (64 and 8192 rows, 4096 ->
 2880); a streaming-read and a copy
 bandwidth reference; the engine clock (sysfs pp_dpm_sclk) sampled during the step.
@@ -702,6 +702,11 @@ def _other_configs(torch, np, binding, inputs, dev, bf16, timed, hbm_entry, mfma
     plens = torch.full((DEC_BATCH,), DEC_CTX, dtype=torch.int32, device=dev)
     po = torch.empty_like(pq)
     pws = torch.empty(binding.decode_workspace_bytes(DEC_BATCH, HQ, D, 16), dtype=torch.uint8, device=dev)
+    pm_lens = [4] * DEC_BATCH
+    pmq = _device_normal_bf16(torch, (sum(pm_lens), HQ, D), gen, dev)
+    pmcq = torch.tensor(np.concatenate([[0], np.cumsum(pm_lens)]).astype(np.int32), device=dev)
+    pmo = torch.empty_like(pmq)
+    pmws = torch.empty(binding.decode_workspace_bytes(sum(pm_lens), HQ, D, 4), dtype=torch.uint8, device=dev)
     for page_size in (16, 64):
         per_seq = DEC_CTX // page_size
         n_pages = DEC_BATCH * per_seq
@@ -715,8 +720,23 @@ def _other_configs(torch, np, binding, inputs, dev, bf16, timed, hbm_entry, mfma
             e = hbm_entry(st, decode_bytes([DEC_CTX] * DEC_BATCH, 0))
             e["shape"] = "B=64, ctx 8192, 64/8 heads, %d-token pages (shuffled), S=%d" % (page_size, s_count)
             out["paged_decode_ps%d_s%d" % (page_size, s_count)] = e
+        # draft-token verification against the same paged cache: the 4
+        # newest tokens of each sequence are its queries
+        for window in (0, WINDOW):
+            f, b = append_flops(pm_lens, [DEC_CTX] * DEC_BATCH, window), append_bytes(pm_lens, [DEC_CTX] * DEC_BATCH,
+                                                                                      window)
+            for s_count in (1, 4):
+                st = timed(lambda: binding.decode_paged_multi(pmq, kp, vp, table, plens, pmcq, 4, DEC_CTX, psinks,
+                                                              window, scale, s_count, workspace=pmws, out=pmo),
+                           scrub_each=(window > 0))
+                e = hbm_entry(st, b, f)
+                e["bound"] = "hbm"
+                e["shape"] = "64 sequences, 4 queries, ctx 8192, 64/8 heads, %d-token pages (shuffled), window %d, " \
+                             "S=%d" % (page_size, window, s_count)
+                out["paged_draft_verify_64x4_ps%d_s%d_%s" % (page_size, s_count,
+                                                              "causal" if window == 0 else "w128")] = e
         del kp, vp
-    del pq, po, pws
+    del pq, po, pws, pmq, pmo, pmws, pmcq
     torch.cuda.synchronize()
 
     # fused rotary step (YaRN, theta 150000, factor 32 over a 4096-token

@@ -318,6 +318,38 @@ SINKATTN_API sinkattn_status sinkattn_decode_splitkv_multi(
     void* o, float* lse, void* stream);
 
 /*
+ * Multi-token-query decode against a paged cache: the draft-token
+ * verification of sinkattn_decode_splitkv_multi, with the keys and values in
+ * the pages of sinkattn_decode_paged.  The result equals
+ * sinkattn_decode_splitkv_multi's on the gathered cache (sequence b's newest
+ * Lq_b tokens are its queries, bottom-right causal, optional window).
+ *
+ *   q, cu_seqlens_q, max_seqlen_q, total_q, o, lse
+ *                  as sinkattn_decode_splitkv_multi
+ *   k_pages, v_pages, block_table, seq_lens, max_pages, page_size,
+ *   num_pages, max_seqlen_k
+ *                  as sinkattn_decode_paged (seq_lens holds Lk_b)
+ *   window, softmax_scale, num_splits
+ *                  as sinkattn_decode_splitkv
+ *   workspace      sized by sinkattn_decode_workspace_bytes(total_q,
+ *                  num_q_heads, head_dim, num_splits)
+ *
+ * Device-side preconditions: those of both entry points, 0 <= Lq_b <= Lk_b
+ * among them (SINKATTN_DEBUG_CHECKS=1 reports violations).  Page ids outside
+ * the pool are clamped into it.
+ */
+SINKATTN_API sinkattn_status sinkattn_decode_paged_multi(
+    const void* q, const void* k_pages, const void* v_pages,
+    const int32_t* block_table, const int32_t* seq_lens, const int32_t* cu_seqlens_q, int32_t batch,
+    int32_t max_pages, int32_t page_size, int32_t num_pages,
+    int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t total_q,
+    const float* sinks,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t window, float softmax_scale, int32_t num_splits,
+    void* workspace, size_t workspace_bytes,
+    void* o, float* lse, void* stream);
+
+/*
  * The rotary step before attention, fused: rotate the query heads into q_out
  * and write the rotated key heads and the value heads of each new token into
  * its cache row (vLLM, "GPT-OSS performance optimizations on NVIDIA

@@ -15,14 +15,22 @@ NVIDIA GPUs", KV-cache-aware routing).  The pages name the KV cache but not
 its layout; fixed-size pages addressed through a per-sequence table is the
 layout of the inference engines they name (vLLM, SGLang, TensorRT-LLM).
 
+Several query tokens per sequence (draft-token verification against a paged
+cache) follow the same rule: the gathered rows go through the append prefill
+(``prefill_append_ref``: the newest tokens are the queries, bottom-right
+causal).
+
 Parity status: pinned by CPU tests (tests/test_oracle_paged.py) against the
-contiguous decode (identity table), page permutations, and brute force.
+contiguous decode (identity table), page permutations, and brute force; the
+multi-token form against the contiguous append prefill under shuffled pages,
+the single-token paged decode, and brute force.
 """
 
 from __future__ import annotations
 
 import numpy as np
 
+from .append import prefill_append_ref
 from .sink_attention import decode_ref
 
 
@@ -49,3 +57,14 @@ def decode_paged_ref(q, k_pages, v_pages, block_table, seq_lens, page_size: int,
     k, cu = gather_pages(k_pages, block_table, seq_lens, page_size)
     v, _ = gather_pages(v_pages, block_table, seq_lens, page_size)
     return decode_ref(q, k, v, cu, sinks, window, scale)
+
+
+def decode_paged_multi_ref(q, k_pages, v_pages, block_table, seq_lens, cu_seqlens_q, page_size: int, sinks,
+                           window: int, scale: float, rows=None):
+    """Several query tokens per sequence against a paged cache (float64):
+    q [Tq, Hq, D], sequence b's queries are rows cu_seqlens_q[b] ..
+    cu_seqlens_q[b+1] - 1, its newest Lq_b <= seq_lens[b] tokens; pages and
+    table as ``decode_paged_ref``.  Returns o [Tq, Hq, D], lse [Tq, Hq]."""
+    k, cu = gather_pages(k_pages, block_table, seq_lens, page_size)
+    v, _ = gather_pages(v_pages, block_table, seq_lens, page_size)
+    return prefill_append_ref(q, k, v, sinks, cu_seqlens_q, cu, window, scale, rows=rows)

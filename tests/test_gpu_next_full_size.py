@@ -3,8 +3,8 @@ against the float64 oracle on host-generated inputs of the same shapes.
 
 Outputs the oracle can produce in seconds are compared in full (the fused
 rotary step and the 64-row projection); otherwise on samples: whole decode
-sequences (every query head of 8 of the 64 sequences, chosen by a seeded
-generator) and query rows of the long append chunk.  Bars as in the rest of
+sequences (every query head and draft token of 8 of the 64 sequences, chosen
+by a seeded generator) and query rows of the long append chunk.  Bars as in the rest of
 the suite: attention outputs max |err| <= 2e-2, mean |err| <= 2e-3, lse
 within 4e-3; the rotary step and the projection within half a bf16 ulp (plus
 1e-5, resp. 1e-3 for fp32 accumulation over K = 4096).
@@ -17,7 +17,7 @@ import pytest
 import torch
 
 from attention_gqa_flash_amd import binding, inputs
-from oracle import (decode_fp8_ref, decode_paged_ref, oproj_ref, prefill_append_ref, rope_qkv_append_ref,
+from oracle import (decode_fp8_ref, decode_paged_multi_ref, decode_paged_ref, oproj_ref, prefill_append_ref, rope_qkv_append_ref,
                     yarn_inv_freq_ref)
 from tests.helpers import (assert_close_lse, assert_close_out, bf16_to_device, f32_to_device, i32_to_device,
                            to_f64)
@@ -101,6 +101,24 @@ def test_draft_verification_64x4_over_8192(window):
         assert_close_lse(got_m[1].cpu().numpy()[rows], rl, "multi decode")
     assert_close_out(to_f64(got[0])[rows], ro, "append prefill W=%d" % window)
     assert_close_lse(got[1].cpu().numpy()[rows], rl, "append prefill")
+
+
+@pytest.mark.parametrize("window", [0, 128])
+def test_draft_verification_64x4_over_8192_paged(window):
+    """The multi-token decode against 16-token pages (S = 1 and 4)."""
+    p = inputs.make_paged_append([4] * B, [CTX] * B, 16, hq=HQ, hkv=HKV, seed=0)
+    args = [bf16_to_device(x) for x in (p.q, p.k_pages, p.v_pages)]
+    table, lens, cq = (i32_to_device(x) for x in (p.block_table, p.seq_lens, p.cu_seqlens_q))
+    rows = np.concatenate([np.arange(4 * b, 4 * b + 4) for b in SAMPLE])
+    ro, rl = decode_paged_multi_ref(inputs.bf16_bits_to_f32(p.q)[rows], inputs.bf16_bits_to_f32(p.k_pages),
+                                    inputs.bf16_bits_to_f32(p.v_pages), p.block_table[SAMPLE], p.seq_lens[SAMPLE],
+                                    np.arange(0, 4 * len(SAMPLE) + 1, 4), 16, p.sinks, window, p.scale)
+    for splits in (1, 4):
+        o, lse = binding.decode_paged_multi(*args, table, lens, cq, 4, CTX, f32_to_device(p.sinks), window, p.scale,
+                                            splits, return_lse=True)
+        torch.cuda.synchronize()
+        assert_close_out(to_f64(o)[rows], ro, "paged draft S=%d W=%d" % (splits, window))
+        assert_close_lse(lse.cpu().numpy()[rows], rl, "paged draft")
 
 
 @pytest.mark.parametrize("window", [0, 128])

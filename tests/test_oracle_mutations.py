@@ -56,6 +56,10 @@ APPEND_MUTATIONS = [
 PAGED_MUTATIONS = [
     ("pages[bt[b, j // page_size], j % page_size]", "pages[bt[b, j % page_size], j // page_size]"),
     ("pages[bt[b, j // page_size], j % page_size]", "pages[bt[b, j // page_size], (j + 1) % page_size]"),
+    ("return prefill_append_ref(q, k, v, sinks, cu_seqlens_q, cu, window, scale, rows=rows)",
+     "return prefill_append_ref(q, v, k, sinks, cu_seqlens_q, cu, window, scale, rows=rows)"),
+    ("return prefill_append_ref(q, k, v, sinks, cu_seqlens_q, cu, window, scale, rows=rows)",
+     "return prefill_append_ref(q, k, v, sinks, cu_seqlens_q, cu, 0, scale, rows=rows)"),
 ]
 
 

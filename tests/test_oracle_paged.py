@@ -4,7 +4,9 @@ K/V pages [P, page_size, Hkv, D]; token j of sequence b is page
 block_table[b, j // page_size], slot j % page_size.  Pinned against the
 contiguous decode (identity tables), invariance under any permutation of the
 physical pages, page sizes that do and do not divide the lengths, and brute
-force with Python loops.
+force with Python loops.  The multi-token form (each sequence's newest tokens
+are its queries) against the contiguous append prefill, the single-token paged
+decode, and brute force with the bottom-right mask written out.
 """
 
 import math
@@ -12,7 +14,7 @@ import math
 import numpy as np
 import pytest
 
-from oracle import decode_paged_ref, decode_ref, gather_pages
+from oracle import decode_paged_multi_ref, decode_paged_ref, decode_ref, gather_pages, prefill_append_ref
 
 
 def _paged_from_contiguous(k, v, lens, page_size, rng=None, spare=3):
@@ -87,3 +89,67 @@ def test_brute_force():
                 want = math.fsum(wj * vp[p, s, g, c] for wj, (p, s) in zip(w, rows)) / den
                 assert abs(o[b, h, c] - want) < 1e-12
             assert abs(lse[b, h] - (mx + math.log(den))) < 1e-12
+
+
+@pytest.mark.parametrize("page_size", [1, 16, 48])
+@pytest.mark.parametrize("window", [0, 5, 128])
+def test_multi_equals_contiguous_append_under_any_page_order(page_size, window):
+    rng = np.random.default_rng(100 + page_size + window)
+    k_lens, q_lens = [1, 17, 300, 64, 129], [1, 3, 4, 0, 2]
+    hq, hkv, d = 8, 2, 8
+    q = rng.standard_normal((sum(q_lens), hq, d))
+    k = rng.standard_normal((sum(k_lens), hkv, d))
+    v = rng.standard_normal((sum(k_lens), hkv, d))
+    sinks = rng.standard_normal(hq)
+    cu_q = np.concatenate([[0], np.cumsum(q_lens)])
+    cu_k = np.concatenate([[0], np.cumsum(k_lens)])
+    ro, rl = prefill_append_ref(q, k, v, sinks, cu_q, cu_k, window, 0.3)
+    for shuffle in (None, rng):
+        kp, vp, bt = _paged_from_contiguous(k, v, k_lens, page_size, shuffle)
+        o, lse = decode_paged_multi_ref(q, kp, vp, bt, k_lens, cu_q, page_size, sinks, window, 0.3)
+        assert np.max(np.abs(o - ro)) < 1e-13 and np.max(np.abs(lse - rl)) < 1e-13
+
+
+def test_multi_with_one_query_is_the_paged_decode():
+    rng = np.random.default_rng(11)
+    lens, page_size = [9, 33, 2], 4
+    hq, hkv, d = 4, 2, 5
+    k = rng.standard_normal((sum(lens), hkv, d))
+    v = rng.standard_normal((sum(lens), hkv, d))
+    q = rng.standard_normal((len(lens), hq, d))
+    sinks = rng.standard_normal(hq)
+    kp, vp, bt = _paged_from_contiguous(k, v, lens, page_size, rng)
+    for window in (0, 3):
+        ro, rl = decode_paged_ref(q, kp, vp, bt, lens, page_size, sinks, window, 0.4)
+        o, lse = decode_paged_multi_ref(q, kp, vp, bt, lens, np.arange(len(lens) + 1), page_size, sinks, window,
+                                        0.4)
+        assert np.max(np.abs(o - ro)) < 1e-13 and np.max(np.abs(lse - rl)) < 1e-13
+
+
+def test_multi_brute_force():
+    rng = np.random.default_rng(12)
+    page_size, k_lens, q_lens, window = 3, [7, 4], [3, 2], 4
+    hq, hkv, d = 4, 2, 3
+    kp = rng.standard_normal((6, page_size, hkv, d))
+    vp = rng.standard_normal((6, page_size, hkv, d))
+    bt = np.array([[4, 0, 5], [2, 1, 3]])
+    cu_q = [0, 3, 5]
+    q = rng.standard_normal((5, hq, d))
+    sinks = rng.standard_normal(hq)
+    o, lse = decode_paged_multi_ref(q, kp, vp, bt, k_lens, cu_q, page_size, sinks, window, 0.7)
+    for b in range(2):
+        for i in range(q_lens[b]):
+            r = cu_q[b] + i
+            pos = k_lens[b] - q_lens[b] + i          # the query is the sequence's token `pos`
+            seen = [j for j in range(k_lens[b]) if pos - window < j <= pos]
+            for h in range(hq):
+                g = h // (hq // hkv)
+                slots = [(bt[b, j // page_size], j % page_size) for j in seen]
+                logits = [0.7 * math.fsum(q[r, h, c] * kp[p, s, g, c] for c in range(d)) for p, s in slots]
+                mx = max(logits + [sinks[h]])
+                w = [math.exp(x - mx) for x in logits]
+                den = math.fsum(w + [math.exp(sinks[h] - mx)])
+                for c in range(d):
+                    want = math.fsum(wj * vp[p, s, g, c] for wj, (p, s) in zip(w, slots)) / den
+                    assert abs(o[r, h, c] - want) < 1e-12
+                assert abs(lse[r, h] - (mx + math.log(den))) < 1e-12

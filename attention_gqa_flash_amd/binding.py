@@ -57,6 +57,9 @@ def library() -> ctypes.CDLL:
     lib.sinkattn_decode_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, i32, i32, i32, f32,
                                           i32, vp, sz, vp, vp, vp]
     lib.sinkattn_decode_paged.restype = ctypes.c_int
+    lib.sinkattn_decode_paged_fp8.argtypes = [vp, vp, vp, f32, f32, vp, vp, i32, i32, i32, i32, i32, vp, i32, i32,
+                                              i32, i32, f32, i32, vp, sz, vp, vp, vp]
+    lib.sinkattn_decode_paged_fp8.restype = ctypes.c_int
     lib.sinkattn_decode_paged_multi.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, i32,
                                                 i32, i32, i32, f32, i32, vp, sz, vp, vp, vp]
     lib.sinkattn_decode_paged_multi.restype = ctypes.c_int
@@ -335,6 +338,45 @@ def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, 
         _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), bsz, block_table.shape[1],
         page_size, num_pages, int(max_seqlen_k), _ptr(sinks), hq, hkv, d, int(window), float(softmax_scale),
         int(num_splits), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(q.device)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def decode_paged_fp8(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, k_scale: float, v_scale: float,
+                     block_table: torch.Tensor, seq_lens: torch.Tensor, max_seqlen_k: int,
+                     sinks: Optional[torch.Tensor], window: int = 0, softmax_scale: float = 0.125,
+                     num_splits: int = 1, workspace: Optional[torch.Tensor] = None,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     return_lse: bool = False):
+    """Split-KV decode against a paged FP8 cache: q [B, Hq, 64] bf16; k/v
+    pages [P, page_size, Hkv, 64] uint8 E4M3 codes with host scales;
+    block_table [B, max_pages] int32; seq_lens [B] int32 (all device)."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_pages, "k_pages", torch.uint8, 4)
+    _need(v_pages, "v_pages", torch.uint8, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    bsz, hq, d = q.shape
+    num_pages, page_size, hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    if v_pages.shape != k_pages.shape or k_pages.shape[3] != d:
+        raise ValueError("k_pages and v_pages must be [P, page_size, Hkv, D] matching q")
+    if block_table.shape[0] != bsz or seq_lens.shape[0] != bsz:
+        raise ValueError("block_table and seq_lens need one row / entry per sequence")
+    if sinks is not None:
+        _need(sinks, "sinks", torch.float32, 1)
+        if sinks.shape[0] != hq:
+            raise ValueError("sinks must have num_q_heads entries")
+    need = decode_workspace_bytes(bsz, hq, d, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((bsz, hq), dtype=torch.float32, device=q.device)
+    _check(library().sinkattn_decode_paged_fp8(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), float(k_scale), float(v_scale), _ptr(block_table), _ptr(seq_lens), bsz,
+        block_table.shape[1], page_size, num_pages, int(max_seqlen_k), _ptr(sinks), hq, hkv, d, int(window),
+        float(softmax_scale), int(num_splits), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(q.device)))
     return (out, lse) if (return_lse or lse is not None) else out
 
 

@@ -364,6 +364,20 @@ sinkattn_status sinkattn_decode_paged(const void* q, const void* k_pages, const 
                        1.0f, 1.0f, nullptr, 1, 0, block_table, max_pages, page_size, num_pages);
 }
 
+sinkattn_status sinkattn_decode_paged_fp8(const void* q, const void* k_pages, const void* v_pages, float k_scale,
+                                          float v_scale, const int32_t* block_table, const int32_t* seq_lens,
+                                          int32_t batch, int32_t max_pages, int32_t page_size, int32_t num_pages,
+                                          int32_t max_seqlen_k, const float* sinks, int32_t num_q_heads,
+                                          int32_t num_kv_heads, int32_t head_dim, int32_t window,
+                                          float softmax_scale, int32_t num_splits, void* workspace,
+                                          size_t workspace_bytes, void* o, float* lse, void* stream) {
+  sinkattn_status st = check_pages(block_table, seq_lens, batch, max_pages, page_size, num_pages, max_seqlen_k);
+  if (st != SINKATTN_OK) return st;
+  return decode_common(q, k_pages, v_pages, seq_lens, batch, max_seqlen_k, sinks, num_q_heads, num_kv_heads,
+                       head_dim, window, softmax_scale, num_splits, workspace, workspace_bytes, o, lse, stream, true,
+                       k_scale, v_scale, nullptr, 1, 0, block_table, max_pages, page_size, num_pages);
+}
+
 sinkattn_status sinkattn_decode_paged_multi(const void* q, const void* k_pages, const void* v_pages,
                                             const int32_t* block_table, const int32_t* seq_lens,
                                             const int32_t* cu_seqlens_q, int32_t batch, int32_t max_pages,

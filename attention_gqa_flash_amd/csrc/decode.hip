@@ -110,18 +110,18 @@ __device__ __forceinline__ void load_tile(TileRegs<kFp8>& t, const void* __restr
   }
 }
 
-// Paged cache (bf16): pages [num_pages, 1 << page_shift, hkv, 64]; key j
-// of the sequence is slot j & (page_size - 1) of page row[j >> page_shift].
-// A 32-key tile spans at most three pages when page_size >= 16; their ids
-// are uniform over the wave (scalar loads), clamped to the pool so that a bad
-// table cannot move an access out of bounds.  Rows at or beyond `end` repeat
-// row end - 1, as in load_tile.
-__device__ __forceinline__ void load_tile_paged(TileRegs<false>& t, const void* __restrict__ k,
+// Paged cache: pages [num_pages, 1 << page_shift, hkv, 64] (bf16, or E4M3
+// codes with kFp8); key j of the sequence is slot j & (page_size - 1) of page
+// row[j >> page_shift].  A 32-key tile spans at most three pages when
+// page_size >= 16; their ids are uniform over the wave (scalar loads),
+// clamped to the pool so that a bad table cannot move an access out of
+// bounds.  Lanes take the same keys and 16-byte pieces as load_tile; rows at
+// or beyond `end` repeat row end - 1.
+template <bool kFp8>
+__device__ __forceinline__ void load_tile_paged(TileRegs<kFp8>& t, const void* __restrict__ k,
                                                 const void* __restrict__ v, const int32_t* __restrict__ row,
                                                 int max_pages, int page_shift, int num_pages, int hkv, int g,
                                                 int k0, int end, int lane) {
-  const uint16_t* kh = static_cast<const uint16_t*>(k);
-  const uint16_t* vh = static_cast<const uint16_t*>(v);
   const int p0 = k0 >> page_shift;
   const int plast = min((end - 1) >> page_shift, max_pages - 1);
   int pid[3];
@@ -131,15 +131,31 @@ __device__ __forceinline__ void load_tile_paged(TileRegs<false>& t, const void* 
     pid[j] = min(max(id, 0), num_pages - 1);
   }
   const int slot_mask = (1 << page_shift) - 1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = min(k0 + (lane >> 3) + 8 * i, end - 1);
+  auto token = [&](int key) {
     const int rel = (key >> page_shift) - p0;
     const int id = rel == 0 ? pid[0] : (rel == 1 ? pid[1] : pid[2]);
-    const size_t tok = (static_cast<size_t>(id) << page_shift) + (key & slot_mask);
-    const size_t off = (tok * hkv + g) * kHeadDim + (lane & 7) * 8;
-    t.k[i] = load16_stream(kh + off);
-    t.v[i] = load16_stream(vh + off);
+    return (static_cast<size_t>(id) << page_shift) + (key & slot_mask);
+  };
+  if constexpr (kFp8) {
+    const uint8_t* kb = static_cast<const uint8_t*>(k);
+    const uint8_t* vb = static_cast<const uint8_t*>(v);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int key = min(k0 + (lane >> 2) + 16 * i, end - 1);
+      const size_t off = (token(key) * hkv + g) * kHeadDim + (lane & 3) * 16;  // bytes
+      t.k[i] = load16(reinterpret_cast<const uint16_t*>(kb + off));
+      t.v[i] = load16(reinterpret_cast<const uint16_t*>(vb + off));
+    }
+  } else {
+    const uint16_t* kh = static_cast<const uint16_t*>(k);
+    const uint16_t* vh = static_cast<const uint16_t*>(v);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = min(k0 + (lane >> 3) + 8 * i, end - 1);
+      const size_t off = (token(key) * hkv + g) * kHeadDim + (lane & 7) * 8;
+      t.k[i] = load16_stream(kh + off);
+      t.v[i] = load16_stream(vh + off);
+    }
   }
 }
 
@@ -685,9 +701,10 @@ static hipError_t launch_decode_t(const DecodeLaunch& a, hipStream_t stream) {
 }
 
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
-  if (a.block_table != nullptr)
-    return a.cu_seqlens_q != nullptr ? launch_decode_t<false, true, true>(a, stream)
-                                     : launch_decode_t<false, false, true>(a, stream);
+  if (a.block_table != nullptr) {
+    if (a.cu_seqlens_q != nullptr) return launch_decode_t<false, true, true>(a, stream);
+    return a.fp8 ? launch_decode_t<true, false, true>(a, stream) : launch_decode_t<false, false, true>(a, stream);
+  }
   if (a.cu_seqlens_q != nullptr) return launch_decode_t<false, true, false>(a, stream);
   return a.fp8 ? launch_decode_t<true, false, false>(a, stream) : launch_decode_t<false, false, false>(a, stream);
 }

@@ -177,15 +177,16 @@ def make_paged_decode(lengths, page_size: int, hq: int, hkv: int, d: int = 64, s
 
 
 def _scatter_pages(k, v, cu, lengths, page_size, rng, spare_pages, fill_bits):
-    """Packed rows -> pages in a random physical order (one permutation drawn
-    from rng) with spare pages; unowned slots hold fill_bits.  Returns
+    """Packed rows (bf16 bits or E4M3 codes) -> pages in a random physical
+    order (one permutation drawn from rng) with spare pages; unowned slots
+    hold fill_bits.  Returns
     (k_pages, v_pages, block_table with -1 past each sequence's pages)."""
     hkv, d = k.shape[1], k.shape[2]
     n_pages = [-(-int(n) // page_size) for n in lengths]
     total = sum(n_pages) + spare_pages
     order = rng.permutation(total)
-    kp = np.full((total, page_size, hkv, d), fill_bits, dtype=np.uint16)
-    vp = np.full((total, page_size, hkv, d), fill_bits, dtype=np.uint16)
+    kp = np.full((total, page_size, hkv, d), fill_bits, dtype=k.dtype)
+    vp = np.full((total, page_size, hkv, d), fill_bits, dtype=k.dtype)
     bt = np.full((len(lengths), max(n_pages) + 1), -1, dtype=np.int32)
     nxt = 0
     for b, n in enumerate(lengths):
@@ -299,6 +300,34 @@ def make_decode_fp8(lengths, hq: int, hkv: int, d: int = 64, seed: int = 0,
         sinks = sinks * np.float32(sink_std)
     return DecodeFp8Inputs(q, k, v, float(k_scale), float(v_scale), sinks.astype(np.float32), _cu(lengths), scale,
                            lengths)
+
+
+@dataclass
+class PagedDecodeFp8Inputs:
+    q: np.ndarray            # uint16 bf16 bits [B, Hq, D]
+    k_pages: np.ndarray      # uint8 E4M3 codes [P, page_size, Hkv, D]
+    v_pages: np.ndarray
+    k_scale: float
+    v_scale: float
+    block_table: np.ndarray  # int32 [B, max_pages] (-1 past a sequence's pages)
+    seq_lens: np.ndarray     # int32 [B]
+    sinks: np.ndarray        # float32 [Hq]
+    page_size: int
+    scale: float
+    lengths: list = field(default_factory=list)
+
+
+def make_paged_decode_fp8(lengths, page_size: int, hq: int, hkv: int, d: int = 64, seed: int = 0,
+                          scale: float = 0.125, spare_pages: int = 3, fill_code: int = 0x7F,
+                          rng: Optional[np.random.Generator] = None):
+    """The draws of make_decode_fp8 (q -> k -> v -> sinks) with the cache
+    scattered into pages as make_paged_decode does (permutation drawn after
+    the sinks); unowned slots hold ``fill_code`` (an E4M3 NaN by default)."""
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    dec = make_decode_fp8(lengths, hq, hkv, d, rng=rng, scale=scale)
+    kp, vp, bt = _scatter_pages(dec.k, dec.v, dec.cu_seqlens_k, dec.lengths, page_size, rng, spare_pages, fill_code)
+    return PagedDecodeFp8Inputs(dec.q, kp, vp, dec.k_scale, dec.v_scale, bt, np.asarray(dec.lengths, dtype=np.int32),
+                                dec.sinks, page_size, scale, list(dec.lengths))
 
 
 def ragged_lengths(rng: np.random.Generator, n: int = 32, lo: int = 128, hi: int = 32768):

@@ -24,7 +24,8 @@ varlen prefill (causal and 128-window); the append prefill (the last
 2048-token chunk of an 8192-token prompt; 64 x 4 draft tokens verified
 against 8192 cached tokens, also through the multi-token-query decode at 1
 and 4 splits); the 64 x 8192 decode against a paged cache (16- and 64-token
-pages, shuffled), also with 4 draft tokens per sequence; the fused rotary step (YaRN; Q out, K/V appended) for 8192
+pages, shuffled), also with 4 draft tokens per sequence and over E4M3 pages;
+the fused rotary step (YaRN; Q out, K/V appended) for 8192
 and 64 tokens; the output projection with bias (64 and 8192 rows, 4096 ->
 2880); a streaming-read and a copy
 bandwidth reference; the engine clock (sysfs pp_dpm_sclk) sampled during the step.
@@ -735,6 +736,18 @@ def _other_configs(torch, np, binding, inputs, dev, bf16, timed, hbm_entry, mfma
                              "S=%d" % (page_size, window, s_count)
                 out["paged_draft_verify_64x4_ps%d_s%d_%s" % (page_size, s_count,
                                                               "causal" if window == 0 else "w128")] = e
+        if page_size == 16:
+            # the same table over pages of E4M3 codes (N(0,1) / scale rounded
+            # on the device; one byte per cached element)
+            fkp = (torch.randn(kp.shape, generator=gen, device=dev) * 16.0).to(torch.float8_e4m3fn).view(torch.uint8)
+            fvp = (torch.randn(kp.shape, generator=gen, device=dev) * 16.0).to(torch.float8_e4m3fn).view(torch.uint8)
+            for s_count in (1, 4, 16):
+                st = timed(lambda: binding.decode_paged_fp8(pq, fkp, fvp, 1.0 / 16, 1.0 / 16, table, plens, DEC_CTX,
+                                                            psinks, 0, scale, s_count, workspace=pws, out=po))
+                e = hbm_entry(st, decode_bytes([DEC_CTX] * DEC_BATCH, 0, kv_elem_bytes=1))
+                e["shape"] = "B=64, ctx 8192, 64/8 heads, E4M3 K/V in 16-token pages (shuffled), S=%d" % s_count
+                out["paged_fp8_decode_ps16_s%d" % s_count] = e
+            del fkp, fvp
         del kp, vp
     del pq, po, pws, pmq, pmo, pmws, pmcq
     torch.cuda.synchronize()

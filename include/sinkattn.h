@@ -318,6 +318,35 @@ SINKATTN_API sinkattn_status sinkattn_decode_splitkv_multi(
     void* o, float* lse, void* stream);
 
 /*
+ * Split-KV decode against a paged FP8 cache: the pages and block table of
+ * sinkattn_decode_paged holding the E4M3 codes and per-tensor scales of
+ * sinkattn_decode_splitkv_fp8.  The result equals sinkattn_decode_splitkv_fp8's
+ * on the gathered cache.
+ *
+ *   k_pages,
+ *   v_pages        uint8 E4M3 codes [num_pages, page_size, num_kv_heads,
+ *                  head_dim], 16-byte aligned
+ *   k_scale,
+ *   v_scale        as sinkattn_decode_splitkv_fp8
+ *   everything else
+ *                  as sinkattn_decode_paged (workspace sized by
+ *                  sinkattn_decode_workspace_bytes(batch, ...))
+ *
+ * Device-side preconditions: those of both entry points (SINKATTN_DEBUG_CHECKS=1
+ * checks the table, the lengths and every code of the pool).
+ */
+SINKATTN_API sinkattn_status sinkattn_decode_paged_fp8(
+    const void* q, const void* k_pages, const void* v_pages,
+    float k_scale, float v_scale,
+    const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+    int32_t max_pages, int32_t page_size, int32_t num_pages, int32_t max_seqlen_k,
+    const float* sinks,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t window, float softmax_scale, int32_t num_splits,
+    void* workspace, size_t workspace_bytes,
+    void* o, float* lse, void* stream);
+
+/*
  * Multi-token-query decode against a paged cache: the draft-token
  * verification of sinkattn_decode_splitkv_multi, with the keys and values in
  * the pages of sinkattn_decode_paged.  The result equals

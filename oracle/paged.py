@@ -15,15 +15,19 @@ NVIDIA GPUs", KV-cache-aware routing).  The pages name the KV cache but not
 its layout; fixed-size pages addressed through a per-sequence table is the
 layout of the inference engines they name (vLLM, SGLang, TensorRT-LLM).
 
-Several query tokens per sequence (draft-token verification against a paged
-cache) follow the same rule: the gathered rows go through the append prefill
+An FP8 paged cache holds E4M3 codes in the same layout; the gathered codes go
+through the FP8 decode (``decode_fp8_ref``, per-tensor scales).  Several
+query tokens per sequence (draft-token verification against a paged cache)
+follow the same rule: the gathered rows go through the append prefill
 (``prefill_append_ref``: the newest tokens are the queries, bottom-right
 causal).
 
 Parity status: pinned by CPU tests (tests/test_oracle_paged.py) against the
 contiguous decode (identity table), page permutations, and brute force; the
 multi-token form against the contiguous append prefill under shuffled pages,
-the single-token paged decode, and brute force.
+the single-token paged decode, and brute force; the FP8 form against the
+contiguous FP8 decode under shuffled pages and the paged decode of the
+decoded values.
 """
 
 from __future__ import annotations
@@ -31,6 +35,7 @@ from __future__ import annotations
 import numpy as np
 
 from .append import prefill_append_ref
+from .fp8 import decode_fp8_ref
 from .sink_attention import decode_ref
 
 
@@ -68,3 +73,13 @@ def decode_paged_multi_ref(q, k_pages, v_pages, block_table, seq_lens, cu_seqlen
     k, cu = gather_pages(k_pages, block_table, seq_lens, page_size)
     v, _ = gather_pages(v_pages, block_table, seq_lens, page_size)
     return prefill_append_ref(q, k, v, sinks, cu_seqlens_q, cu, window, scale, rows=rows)
+
+
+def decode_paged_fp8_ref(q, k_pages, v_pages, k_scale: float, v_scale: float, block_table, seq_lens,
+                         page_size: int, sinks, window: int, scale: float):
+    """Single-token decode against a paged cache of E4M3 codes (float64):
+    k_pages / v_pages uint8 [P, page_size, Hkv, D]; K = k_scale * e4m3(code),
+    V = v_scale * e4m3(code); everything else as ``decode_paged_ref``."""
+    k, cu = gather_pages(k_pages, block_table, seq_lens, page_size)
+    v, _ = gather_pages(v_pages, block_table, seq_lens, page_size)
+    return decode_fp8_ref(q, k, v, k_scale, v_scale, cu, sinks, window, scale)

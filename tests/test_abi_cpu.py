@@ -27,7 +27,7 @@ def _lib():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted([
-        "sinkattn_decode_paged", "sinkattn_decode_paged_multi", "sinkattn_decode_splitkv", "sinkattn_decode_splitkv_fp8",
+        "sinkattn_decode_paged", "sinkattn_decode_paged_fp8", "sinkattn_decode_paged_multi", "sinkattn_decode_splitkv", "sinkattn_decode_splitkv_fp8",
         "sinkattn_decode_splitkv_multi",
         "sinkattn_decode_workspace_bytes", "sinkattn_oproj_bias", "sinkattn_oproj_workspace_bytes",
         "sinkattn_rope_qkv_append",
@@ -272,6 +272,37 @@ def test_decode_paged_empty_is_ok_without_launch():
     lib = _lib()
     assert _decode_paged(lib, batch=0) == 0
     assert _decode_paged(lib, batch=0, bt=None, lens=None) == 0
+
+
+def _decode_paged_fp8(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=0.5, vs=0.5, bt=FAKE, lens=FAKE2, batch=4, mp=8, ps=16, npg=40, mk=100,
+             sinks=None, hq=64, hkv=8, d=64, window=0, scale=0.125, splits=1, ws=None, ws_bytes=0, o=FAKE, lse=None)
+    a.update(kw)
+    return lib.sinkattn_decode_paged_fp8(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["bt"], a["lens"], a["batch"],
+                                         a["mp"], a["ps"], a["npg"], a["mk"], a["sinks"], a["hq"], a["hkv"], a["d"],
+                                         a["window"], a["scale"], a["splits"], a["ws"], a["ws_bytes"], a["o"],
+                                         a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ps=24), 2),                 # page size not a power of two
+    (dict(mp=6), 1),                  # 6 x 16 < max_seqlen_k
+    (dict(lens=None), 1),
+    (dict(ks=0.0), 1),
+    (dict(vs=float("inf")), 1),
+    (dict(ks=float("nan")), 1),
+    (dict(splits=4), 3),              # no workspace
+    (dict(v=ctypes.c_void_p((1 << 20) + 8)), 1),
+])
+def test_decode_paged_fp8_rejects(kw, status):
+    lib = _lib()
+    assert _decode_paged_fp8(lib, **kw) == status
+    assert lib.sinkattn_last_error()
+
+
+def test_decode_paged_fp8_empty_is_ok_without_launch():
+    lib = _lib()
+    assert _decode_paged_fp8(lib, batch=0) == 0
 
 
 def _decode_paged_multi(lib, **kw):

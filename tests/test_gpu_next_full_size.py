@@ -17,7 +17,7 @@ import pytest
 import torch
 
 from attention_gqa_flash_amd import binding, inputs
-from oracle import (decode_fp8_ref, decode_paged_multi_ref, decode_paged_ref, oproj_ref, prefill_append_ref, rope_qkv_append_ref,
+from oracle import (decode_fp8_ref, decode_paged_fp8_ref, decode_paged_multi_ref, decode_paged_ref, oproj_ref, prefill_append_ref, rope_qkv_append_ref,
                     yarn_inv_freq_ref)
 from tests.helpers import (assert_close_lse, assert_close_out, bf16_to_device, f32_to_device, i32_to_device,
                            to_f64)
@@ -77,6 +77,20 @@ def test_paged_decode_64x8192(page_size, splits):
                               p.block_table[SAMPLE], p.seq_lens[SAMPLE], page_size, p.sinks, 0, p.scale)
     assert_close_out(to_f64(o)[SAMPLE], ro, "paged ps=%d S=%d" % (page_size, splits))
     assert_close_lse(lse.cpu().numpy()[SAMPLE], rl, "paged")
+
+
+@pytest.mark.parametrize("splits", [1, 4, 16])
+def test_paged_fp8_decode_64x8192(splits):
+    p = inputs.make_paged_decode_fp8([CTX] * B, 16, hq=HQ, hkv=HKV, seed=0)
+    o, lse = binding.decode_paged_fp8(bf16_to_device(p.q), torch.from_numpy(p.k_pages).cuda(),
+                                      torch.from_numpy(p.v_pages).cuda(), p.k_scale, p.v_scale,
+                                      i32_to_device(p.block_table), i32_to_device(p.seq_lens), CTX,
+                                      f32_to_device(p.sinks), 0, p.scale, splits, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = decode_paged_fp8_ref(inputs.bf16_bits_to_f32(p.q)[SAMPLE], p.k_pages, p.v_pages, p.k_scale, p.v_scale,
+                                  p.block_table[SAMPLE], p.seq_lens[SAMPLE], 16, p.sinks, 0, p.scale)
+    assert_close_out(to_f64(o)[SAMPLE], ro, "paged fp8 64x8192 S=%d" % splits)
+    assert_close_lse(lse.cpu().numpy()[SAMPLE], rl, "paged fp8 64x8192")
 
 
 @pytest.mark.parametrize("window", [0, 128])

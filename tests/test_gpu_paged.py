@@ -7,7 +7,8 @@ would show in its output.  Cases: page sizes 16 to 256 (a 32-key tile then
 spans up to three pages), lengths on and off page and tile boundaries, every
 decode kernel shape through the split counts, windows, GQA groups 4 to 32,
 without sinks, agreement with the contiguous decode bit for bit, and the
-debug check of the page table.  Bar: max |err| <= 2e-2, mean |err| <= 2e-3,
+debug check of the page table; the same over pages of FP8 (E4M3) codes,
+with an E4M3 NaN in every unowned slot.  Bar: max |err| <= 2e-2, mean |err| <= 2e-3,
 lse within 4e-3 with an identical -inf pattern.
 """
 
@@ -16,7 +17,7 @@ import pytest
 import torch
 
 from attention_gqa_flash_amd import binding, inputs
-from oracle import decode_paged_ref
+from oracle import decode_paged_fp8_ref, decode_paged_ref
 from tests.helpers import (assert_close_lse, assert_close_out, bf16_to_device, f32_to_device, i32_to_device,
                            to_f64)
 
@@ -105,3 +106,62 @@ def test_paged_debug_checks(monkeypatch):
         binding.decode_paged(bf16_to_device(p.q), _pages_to_device(p.k_pages), _pages_to_device(p.v_pages),
                              i32_to_device(p.block_table), short, 70, f32_to_device(p.sinks), 0, p.scale, 1)
     assert err.value.status == 1 and "empty" in str(err.value)
+
+
+def _run_fp8(p, window, splits):
+    o, lse = binding.decode_paged_fp8(bf16_to_device(p.q), torch.from_numpy(p.k_pages).cuda(),
+                                      torch.from_numpy(p.v_pages).cuda(), p.k_scale, p.v_scale,
+                                      i32_to_device(p.block_table), i32_to_device(p.seq_lens), max(p.lengths),
+                                      f32_to_device(p.sinks), window, p.scale, splits, return_lse=True)
+    torch.cuda.synchronize()
+    return to_f64(o), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("page_size", [16, 64, 256])
+@pytest.mark.parametrize("hq,hkv", [(64, 8), (32, 1), (16, 4)])
+@pytest.mark.parametrize("splits", [1, 4, 16])
+def test_paged_fp8_decode(page_size, hq, hkv, splits):
+    p = inputs.make_paged_decode_fp8(LENGTHS, page_size, hq=hq, hkv=hkv, seed=90 + page_size + hq + splits)
+    p.sinks[2] = -np.inf
+    for window in (0, 128):
+        o, lse = _run_fp8(p, window, splits)
+        ro, rl = decode_paged_fp8_ref(inputs.bf16_bits_to_f32(p.q), p.k_pages, p.v_pages, p.k_scale, p.v_scale,
+                                      p.block_table, p.seq_lens, page_size, p.sinks, window, p.scale)
+        what = "paged fp8 ps=%d G=%d S=%d W=%d" % (page_size, hq // hkv, splits, window)
+        assert_close_out(o, ro, what)
+        assert_close_lse(lse, rl, what)
+
+
+def test_paged_fp8_equals_contiguous_fp8_bitwise():
+    lengths = [700, 1, 4096, 33]
+    p = inputs.make_paged_decode_fp8(lengths, 16, hq=64, hkv=8, seed=91)
+    d = inputs.make_decode_fp8(lengths, hq=64, hkv=8, seed=91)
+    assert np.array_equal(p.q, d.q)
+    q = bf16_to_device(d.q)
+    sinks = f32_to_device(d.sinks)
+    for window in (0, 128):
+        for splits in (1, 4, 16):
+            o1 = binding.decode_paged_fp8(q, torch.from_numpy(p.k_pages).cuda(), torch.from_numpy(p.v_pages).cuda(),
+                                          p.k_scale, p.v_scale, i32_to_device(p.block_table),
+                                          i32_to_device(p.seq_lens), 4096, sinks, window, d.scale, splits)
+            o2 = binding.decode_splitkv_fp8(q, torch.from_numpy(d.k).cuda(), torch.from_numpy(d.v).cuda(), d.k_scale,
+                                            d.v_scale, i32_to_device(d.cu_seqlens_k), 4096, sinks, window, d.scale,
+                                            splits)
+            torch.cuda.synchronize()
+            assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), (window, splits)
+
+
+def test_paged_fp8_debug_checks(monkeypatch):
+    monkeypatch.setenv("SINKATTN_DEBUG_CHECKS", "1")
+    p = inputs.make_paged_decode_fp8([40, 70], 16, hq=8, hkv=2, seed=92, fill_code=0x38)  # finite fill: 1.0
+    o, _ = _run_fp8(p, 0, 1)
+    ro, _ = decode_paged_fp8_ref(inputs.bf16_bits_to_f32(p.q), p.k_pages, p.v_pages, p.k_scale, p.v_scale,
+                                 p.block_table, p.seq_lens, 16, p.sinks, 0, p.scale)
+    assert_close_out(o, ro, "paged fp8 debug valid")
+    bad = p.v_pages.copy()
+    bad[p.block_table[1, 3], 5, 1, 7] = 0xFF  # an E4M3 NaN in a slot sequence 1 uses
+    with pytest.raises(binding.SinkAttnError) as err:
+        binding.decode_paged_fp8(bf16_to_device(p.q), torch.from_numpy(p.k_pages).cuda(), torch.from_numpy(bad).cuda(),
+                                 p.k_scale, p.v_scale, i32_to_device(p.block_table), i32_to_device(p.seq_lens), 70,
+                                 f32_to_device(p.sinks), 0, p.scale, 1)
+    assert err.value.status == 1 and "v holds" in str(err.value)

@@ -60,6 +60,8 @@ PAGED_MUTATIONS = [
      "return prefill_append_ref(q, v, k, sinks, cu_seqlens_q, cu, window, scale, rows=rows)"),
     ("return prefill_append_ref(q, k, v, sinks, cu_seqlens_q, cu, window, scale, rows=rows)",
      "return prefill_append_ref(q, k, v, sinks, cu_seqlens_q, cu, 0, scale, rows=rows)"),
+    ("return decode_fp8_ref(q, k, v, k_scale, v_scale, cu, sinks, window, scale)",
+     "return decode_fp8_ref(q, k, v, v_scale, k_scale, cu, sinks, window, scale)"),
 ]
 
 

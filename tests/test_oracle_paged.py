@@ -6,7 +6,9 @@ contiguous decode (identity tables), invariance under any permutation of the
 physical pages, page sizes that do and do not divide the lengths, and brute
 force with Python loops.  The multi-token form (each sequence's newest tokens
 are its queries) against the contiguous append prefill, the single-token paged
-decode, and brute force with the bottom-right mask written out.
+decode, and brute force with the bottom-right mask written out.  The FP8 form
+(E4M3 codes in the pages) against the contiguous FP8 decode under any page
+order, and the paged decode of the scaled decoded values.
 """
 
 import math
@@ -14,7 +16,8 @@ import math
 import numpy as np
 import pytest
 
-from oracle import decode_paged_multi_ref, decode_paged_ref, decode_ref, gather_pages, prefill_append_ref
+from oracle import (decode_fp8_ref, decode_paged_fp8_ref, decode_paged_multi_ref, decode_paged_ref, decode_ref,
+                    e4m3_to_float64, gather_pages, prefill_append_ref)
 
 
 def _paged_from_contiguous(k, v, lens, page_size, rng=None, spare=3):
@@ -153,3 +156,28 @@ def test_multi_brute_force():
                     want = math.fsum(wj * vp[p, s, g, c] for wj, (p, s) in zip(w, slots)) / den
                     assert abs(o[r, h, c] - want) < 1e-12
                 assert abs(lse[r, h] - (mx + math.log(den))) < 1e-12
+
+
+@pytest.mark.parametrize("page_size", [1, 16, 48])
+@pytest.mark.parametrize("window", [0, 5])
+def test_fp8_equals_contiguous_fp8_decode_and_the_decoded_paged_decode(page_size, window):
+    rng = np.random.default_rng(200 + page_size + window)
+    lens = [1, 17, 300, 64]
+    hq, hkv, d = 8, 2, 8
+    q = rng.standard_normal((len(lens), hq, d))
+    codes = rng.integers(0, 256, size=(2, sum(lens), hkv, d)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38  # no NaN codes (0x38 is 1.0)
+    kc, vc = codes
+    sinks = rng.standard_normal(hq)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    ks, vs = 0.03, 0.5
+    ro, rl = decode_fp8_ref(q, kc, vc, ks, vs, cu, sinks, window, 0.3)
+    for shuffle in (None, rng):
+        kp, vp, bt = _paged_from_contiguous(kc.astype(np.float64), vc.astype(np.float64), lens, page_size, shuffle)
+        kp = np.nan_to_num(kp, nan=0.0).astype(np.uint8)
+        vp = np.nan_to_num(vp, nan=0.0).astype(np.uint8)
+        o, lse = decode_paged_fp8_ref(q, kp, vp, ks, vs, bt, lens, page_size, sinks, window, 0.3)
+        assert np.max(np.abs(o - ro)) < 1e-13 and np.max(np.abs(lse - rl)) < 1e-13
+        o2, lse2 = decode_paged_ref(q, ks * e4m3_to_float64(kp), vs * e4m3_to_float64(vp), bt, lens, page_size,
+                                    sinks, window, 0.3)
+        assert np.max(np.abs(o - o2)) < 1e-12 and np.max(np.abs(lse - lse2)) < 1e-12

@@ -113,27 +113,33 @@ __device__ __forceinline__ void load_tile(TileRegs<kFp8>& t, const void* __restr
 // Paged cache: pages [num_pages, 1 << page_shift, hkv, 64] (bf16, or E4M3
 // codes with kFp8); key j of the sequence is slot j & (page_size - 1) of page
 // row[j >> page_shift].  A 32-key tile spans at most three pages when
-// page_size >= 16; their ids are uniform over the wave (scalar loads),
-// clamped to the pool so that a bad table cannot move an access out of
-// bounds.  Lanes take the same keys and 16-byte pieces as load_tile; rows at
-// or beyond `end` repeat row end - 1.
+// page_size >= 16: PageIds holds the ids of pages p0, p0 + 1, p0 + 2 of one
+// sequence, uniform over the wave, clamped to the pool so that a bad table
+// cannot move an access out of bounds.
+struct PageIds {
+  int p0;
+  int id[3];
+};
+
+// Reads the ids of pages p0 .. p0 + 2 (entries past the sequence's last page
+// `plast` repeat it, so no entry past the table row is read).
+__device__ __forceinline__ void fetch_page_ids(PageIds& p, const int32_t* __restrict__ row, int p0, int plast,
+                                               int num_pages) {
+  p.p0 = p0;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) p.id[j] = min(max(row[min(p0 + j, plast)], 0), num_pages - 1);
+}
+
+// Lanes take the same keys and 16-byte pieces as load_tile; rows at or beyond
+// `end` repeat row end - 1.  pid covers page k0 >> page_shift.
 template <bool kFp8>
 __device__ __forceinline__ void load_tile_paged(TileRegs<kFp8>& t, const void* __restrict__ k,
-                                                const void* __restrict__ v, const int32_t* __restrict__ row,
-                                                int max_pages, int page_shift, int num_pages, int hkv, int g,
-                                                int k0, int end, int lane) {
-  const int p0 = k0 >> page_shift;
-  const int plast = min((end - 1) >> page_shift, max_pages - 1);
-  int pid[3];
-#pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    const int id = row[min(p0 + j, plast)];
-    pid[j] = min(max(id, 0), num_pages - 1);
-  }
+                                                const void* __restrict__ v, const PageIds& pid, int page_shift,
+                                                int hkv, int g, int k0, int end, int lane) {
   const int slot_mask = (1 << page_shift) - 1;
   auto token = [&](int key) {
-    const int rel = (key >> page_shift) - p0;
-    const int id = rel == 0 ? pid[0] : (rel == 1 ? pid[1] : pid[2]);
+    const int rel = (key >> page_shift) - pid.p0;
+    const int id = rel == 0 ? pid.id[0] : (rel == 1 ? pid.id[1] : pid.id[2]);
     return (static_cast<size_t>(id) << page_shift) + (key & slot_mask);
   };
   if constexpr (kFp8) {
@@ -274,11 +280,26 @@ __device__ __forceinline__ void decode_body(
   const int base = kPaged ? 0 : cu_seqlens_k[b];
   const int len = kPaged ? cu_seqlens_k[b] : cu_seqlens_k[b + 1] - base;
   const int32_t* bt_row = kPaged ? block_table + static_cast<size_t>(b) * max_pages : nullptr;
+  const int plast = kPaged ? min(max(len - 1, 0) >> page_shift, max_pages - 1) : 0;
+  constexpr int kStride = kOwnSplit ? kKeys : kKeys * kIl;  // keys between a wave's tiles
+  // Paged bf16: the ids of the pages a tile needs are read one tile ahead (a
+  // wave's next tile normally starts kStride keys on), so that the address
+  // of each K/V row does not wait for a table read; a tile that starts
+  // elsewhere (the next split's first) reads its ids first.  64 x 8192,
+  // 16-token pages: S = 1 0.200 -> 0.186 ms, S = 16 0.215 -> 0.203 ms.  The
+  // E4M3 tiles read their ids when they are loaded: ahead, S = 4 and 16 took
+  // 6-9% longer (0.142 -> 0.155 ms at S = 4).
+  constexpr bool kIdsAhead = kPaged && !kFp8;
+  PageIds pids{-1, {0, 0, 0}};
   auto load = [&](TileRegs<kFp8>& t, int k_first, int k_end) {
-    if constexpr (kPaged)
-      load_tile_paged(t, k, v, bt_row, max_pages, page_shift, num_pages, hkv, g, k_first, k_end, lane);
-    else
+    if constexpr (kPaged) {
+      const int p0 = k_first >> page_shift;
+      if (!kIdsAhead || p0 != pids.p0) fetch_page_ids(pids, bt_row, p0, plast, num_pages);
+      load_tile_paged(t, k, v, pids, page_shift, hkv, g, k_first, k_end, lane);
+      if constexpr (kIdsAhead) fetch_page_ids(pids, bt_row, (k_first + kStride) >> page_shift, plast, num_pages);
+    } else {
       load_tile(t, k, v, base, hkv, g, k_first, k_end, lane);
+    }
   };
   // Query tokens of this sequence (one unless kMulti); more than len breaks
   // a precondition and is clamped.
@@ -313,7 +334,6 @@ __device__ __forceinline__ void decode_body(
   // flight while the current one is computed.  The first tile is requested
   // before Q and the sink, so the three latencies overlap.
   TileRegs<kFp8> cur, nxt;
-  constexpr int kStride = kOwnSplit ? kKeys : kKeys * kIl;
   int k0 = kOwnSplit ? a : a + kKeys * wl;
   if (k0 < e) load(cur, k0, e);
 

@@ -115,19 +115,23 @@ __device__ __forceinline__ void load_tile(TileRegs<kFp8>& t, const void* __restr
 // row[j >> page_shift].  A 32-key tile spans at most three pages when
 // page_size >= 16: PageIds holds the ids of pages p0, p0 + 1, p0 + 2 of one
 // sequence, uniform over the wave, clamped to the pool so that a bad table
-// cannot move an access out of bounds.
+// cannot move an access out of bounds.  The ids must stay in registers: a
+// choice among them by index makes the compiler keep them in memory, one
+// copy per work-item (8 KB of LDS per 512-thread workgroup, or scratch when
+// LDS is full), so a row's page id is formed from their differences.
 struct PageIds {
-  int p0;
-  int id[3];
+  int p0, id0, id1, id2;
 };
 
 // Reads the ids of pages p0 .. p0 + 2 (entries past the sequence's last page
 // `plast` repeat it, so no entry past the table row is read).
 __device__ __forceinline__ void fetch_page_ids(PageIds& p, const int32_t* __restrict__ row, int p0, int plast,
                                                int num_pages) {
+  auto id = [&](int page) { return min(max(row[min(page, plast)], 0), num_pages - 1); };
   p.p0 = p0;
-#pragma unroll
-  for (int j = 0; j < 3; ++j) p.id[j] = min(max(row[min(p0 + j, plast)], 0), num_pages - 1);
+  p.id0 = id(p0);
+  p.id1 = id(p0 + 1);
+  p.id2 = id(p0 + 2);
 }
 
 // Lanes take the same keys and 16-byte pieces as load_tile; rows at or beyond
@@ -138,8 +142,10 @@ __device__ __forceinline__ void load_tile_paged(TileRegs<kFp8>& t, const void* _
                                                 int hkv, int g, int k0, int end, int lane) {
   const int slot_mask = (1 << page_shift) - 1;
   auto token = [&](int key) {
-    const int rel = (key >> page_shift) - pid.p0;
-    const int id = rel == 0 ? pid.id[0] : (rel == 1 ? pid.id[1] : pid.id[2]);
+    const int rel = (key >> page_shift) - pid.p0;  // 0, 1 or 2
+    // (as differences: written as a choice among the three ids, the
+    // compiler builds a per-work-item table in memory to index)
+    const int id = pid.id0 + (rel >= 1 ? pid.id1 - pid.id0 : 0) + (rel >= 2 ? pid.id2 - pid.id1 : 0);
     return (static_cast<size_t>(id) << page_shift) + (key & slot_mask);
   };
   if constexpr (kFp8) {
@@ -290,7 +296,7 @@ __device__ __forceinline__ void decode_body(
   // E4M3 tiles read their ids when they are loaded: ahead, S = 4 and 16 took
   // 6-9% longer (0.142 -> 0.155 ms at S = 4).
   constexpr bool kIdsAhead = kPaged && !kFp8;
-  PageIds pids{-1, {0, 0, 0}};
+  PageIds pids{-1, 0, 0, 0};
   auto load = [&](TileRegs<kFp8>& t, int k_first, int k_end) {
     if constexpr (kPaged) {
       const int p0 = k_first >> page_shift;

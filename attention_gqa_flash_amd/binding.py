@@ -60,6 +60,9 @@ def library() -> ctypes.CDLL:
     lib.sinkattn_decode_paged_fp8.argtypes = [vp, vp, vp, f32, f32, vp, vp, i32, i32, i32, i32, i32, vp, i32, i32,
                                               i32, i32, f32, i32, vp, sz, vp, vp, vp]
     lib.sinkattn_decode_paged_fp8.restype = ctypes.c_int
+    lib.sinkattn_prefill_append_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp,
+                                                  i32, i32, i32, i32, f32, vp, vp, vp]
+    lib.sinkattn_prefill_append_paged.restype = ctypes.c_int
     lib.sinkattn_decode_paged_multi.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, i32,
                                                 i32, i32, i32, f32, i32, vp, sz, vp, vp, vp]
     lib.sinkattn_decode_paged_multi.restype = ctypes.c_int
@@ -377,6 +380,42 @@ def decode_paged_fp8(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tens
         _ptr(q), _ptr(k_pages), _ptr(v_pages), float(k_scale), float(v_scale), _ptr(block_table), _ptr(seq_lens), bsz,
         block_table.shape[1], page_size, num_pages, int(max_seqlen_k), _ptr(sinks), hq, hkv, d, int(window),
         float(softmax_scale), int(num_splits), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(q.device)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def prefill_append_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
+                         seq_lens_k: torch.Tensor, cu_seqlens_q: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                         sinks: Optional[torch.Tensor], window: int = 0, softmax_scale: float = 0.125,
+                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         return_lse: bool = False):
+    """Append (chunked) prefill against a paged cache: q [Tq, Hq, 64] bf16
+    packed by cu_seqlens_q; k/v pages [P, page_size, Hkv, 64] bf16;
+    block_table [B, max_pages] int32; seq_lens_k [B] int32 (all device)."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_pages, "k_pages", torch.bfloat16, 4)
+    _need(v_pages, "v_pages", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens_k, "seq_lens_k", torch.int32, 1)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    tq, hq, d = q.shape
+    bsz = seq_lens_k.shape[0]
+    num_pages, page_size, hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    if v_pages.shape != k_pages.shape or k_pages.shape[3] != d:
+        raise ValueError("k_pages and v_pages must be [P, page_size, Hkv, D] matching q")
+    if block_table.shape[0] != bsz or cu_seqlens_q.shape[0] != bsz + 1:
+        raise ValueError("block_table needs one row per sequence and cu_seqlens_q batch + 1 entries")
+    if sinks is not None:
+        _need(sinks, "sinks", torch.float32, 1)
+        if sinks.shape[0] != hq:
+            raise ValueError("sinks must have num_q_heads entries")
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
+    _check(library().sinkattn_prefill_append_paged(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens_k), _ptr(cu_seqlens_q), bsz,
+        block_table.shape[1], page_size, num_pages, int(max_seqlen_q), int(max_seqlen_k), tq, _ptr(sinks), hq, hkv, d,
+        int(window), float(softmax_scale), _ptr(out), _ptr(lse), _stream(q.device)))
     return (out, lse) if (return_lse or lse is not None) else out
 
 

@@ -117,8 +117,10 @@ static sinkattn_status prefill_common(const void* q, const void* k, const void* 
                                       const int32_t* cu_q, const int32_t* cu_k, int32_t batch, int32_t max_q,
                                       int32_t max_k, int32_t total_q, int32_t total_k, int32_t num_q_heads,
                                       int32_t num_kv_heads, int32_t head_dim, int32_t window, float softmax_scale,
-                                      void* o, float* lse, void* stream) {
+                                      void* o, float* lse, void* stream, const int32_t* block_table = nullptr,
+                                      int32_t max_pages = 0, int32_t page_size = 0, int32_t num_pages = 0) {
   const bool append = cu_k != cu_q;
+  const bool paged = block_table != nullptr;  // k / v are page pools, cu_k the key lengths [batch]
   sinkattn_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
   if (st != SINKATTN_OK) return st;
   if ((st = check_scale(softmax_scale)) != SINKATTN_OK) return st;
@@ -144,7 +146,12 @@ static sinkattn_status prefill_common(const void* q, const void* k, const void* 
     const size_t kvn = static_cast<size_t>(total_k) * num_kv_heads * head_dim;
     if ((st = hip_queue(sinkattn::check_clear(s))) != SINKATTN_OK) return st;
     if ((st = hip_queue(sinkattn::check_offsets(cu_q, batch, max_q, 0, total_q, s))) != SINKATTN_OK) return st;
-    if (append) {
+    if (paged) {
+      if ((st = hip_queue(sinkattn::check_paged(cu_k, block_table, batch, max_pages, page_size, num_pages, max_k,
+                                                s))) != SINKATTN_OK)
+        return st;
+      if ((st = hip_queue(sinkattn::check_append(cu_q, cu_k, true, batch, s))) != SINKATTN_OK) return st;
+    } else if (append) {
       if ((st = hip_queue(sinkattn::check_offsets(cu_k, batch, max_k, 0, total_k, s))) != SINKATTN_OK) return st;
       if ((st = hip_queue(sinkattn::check_append(cu_q, cu_k, false, batch, s))) != SINKATTN_OK) return st;
     }
@@ -156,6 +163,12 @@ static sinkattn_status prefill_common(const void* q, const void* k, const void* 
   }
   sinkattn::PrefillLaunch a{q, k, v, sinks, cu_q, cu_k, batch, max_q, max_k, total_q, num_q_heads,
                             num_kv_heads, window, softmax_scale, o, lse};
+  if (paged) {
+    a.block_table = block_table;
+    a.max_pages = max_pages;
+    a.num_pages = num_pages;
+    while ((1 << a.page_shift) < page_size) ++a.page_shift;
+  }
   return hip_status(sinkattn::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
 }
 
@@ -392,6 +405,25 @@ sinkattn_status sinkattn_decode_paged_multi(const void* q, const void* k_pages, 
   return decode_common(q, k_pages, v_pages, seq_lens, batch, max_seqlen_k, sinks, num_q_heads, num_kv_heads,
                        head_dim, window, softmax_scale, num_splits, workspace, workspace_bytes, o, lse, stream, false,
                        1.0f, 1.0f, cu_seqlens_q, max_seqlen_q, total_q, block_table, max_pages, page_size, num_pages);
+}
+
+sinkattn_status sinkattn_prefill_append_paged(const void* q, const void* k_pages, const void* v_pages,
+                                              const int32_t* block_table, const int32_t* seq_lens_k,
+                                              const int32_t* cu_seqlens_q, int32_t batch, int32_t max_pages,
+                                              int32_t page_size, int32_t num_pages, int32_t max_seqlen_q,
+                                              int32_t max_seqlen_k, int32_t total_q, const float* sinks,
+                                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                              int32_t window, float softmax_scale, void* o, float* lse,
+                                              void* stream) {
+  if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0)
+    return fail(SINKATTN_ERR_INVALID_ARG, "batch, lengths and totals must be >= 0");
+  sinkattn_status st = check_pages(block_table, seq_lens_k, batch, max_pages, page_size, num_pages, max_seqlen_k);
+  if (st != SINKATTN_OK) return st;
+  if (cu_seqlens_q == nullptr && batch > 0) return fail(SINKATTN_ERR_INVALID_ARG, "cu_seqlens_q must not be NULL");
+  // (the pool's rows stand for total_k)
+  return prefill_common(q, k_pages, v_pages, sinks, cu_seqlens_q, seq_lens_k, batch, max_seqlen_q, max_seqlen_k,
+                        total_q, num_pages * page_size, num_q_heads, num_kv_heads, head_dim, window, softmax_scale, o,
+                        lse, stream, block_table, max_pages, page_size, num_pages);
 }
 
 // Rotary frequencies of the pairs (i, i + 32): theta^(-2i/64), rescaled by

@@ -21,6 +21,10 @@ struct PrefillLaunch {
   float softmax_scale;
   void* o;
   float* lse;
+  // Paged K/V (block_table non-null): k / v are the page pools and
+  // cu_seqlens_k holds the key lengths [batch].
+  const int32_t* block_table = nullptr;
+  int max_pages = 0, page_shift = 0, num_pages = 0;
 };
 
 struct DecodeLaunch {

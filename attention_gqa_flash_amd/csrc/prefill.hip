@@ -93,6 +93,39 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ k_seq, c
   }
 }
 
+// The same copy from a paged cache: pages [num_pages, 1 << page_shift, hkv,
+// 64], key j of the sequence in slot j & (page_size - 1) of page
+// row[j >> page_shift].  A tile's 64 keys (key0 a multiple of 64) lie in at
+// most four pages when page_size >= 16; their ids are read once per tile,
+// uniform over the workgroup and clamped to the pool (a bad table cannot move
+// a copy out of bounds), and a row's id is formed from their differences so
+// that they stay in registers.  k_pool / v_pool point at head g of token 0.
+template <int kThreads>
+__device__ __forceinline__ void issue_tile_paged(const uint16_t* __restrict__ k_pool,
+                                                 const uint16_t* __restrict__ v_pool, uint32_t k_dst, uint32_t v_dst,
+                                                 int len, int hkv, int key0, int wave, int lane,
+                                                 const int32_t* __restrict__ row, int page_shift, int plast,
+                                                 int num_pages) {
+  constexpr int kPer = kKTile * 8 / kThreads;
+  const int p0 = key0 >> page_shift;
+  auto id_of = [&](int page) { return min(max(row[min(page, plast)], 0), num_pages - 1); };
+  const int id0 = id_of(p0), id1 = id_of(p0 + 1), id2 = id_of(p0 + 2), id3 = id_of(p0 + 3);
+  const int slot_mask = (1 << page_shift) - 1;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int slot0 = 64 * (kPer * wave + i);
+    const int r = (slot0 >> 3) + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz_f(r);
+    const int key = min(key0 + r, len - 1);
+    const int rel = (key >> page_shift) - p0;  // 0 .. 3
+    const int id = id0 + (rel >= 1 ? id1 - id0 : 0) + (rel >= 2 ? id2 - id1 : 0) + (rel >= 3 ? id3 - id2 : 0);
+    const size_t tok = (static_cast<size_t>(id) << page_shift) + (key & slot_mask);
+    const size_t off = tok * static_cast<size_t>(hkv) * kHeadDim + chunk * 8;  // elements
+    load16_to_lds_untracked(k_pool + off, k_dst + slot0 * 16);
+    load16_to_lds_untracked(v_pool + off, v_dst + slot0 * 16);
+  }
+}
+
 // P (bf16, the B operand of O^T) for one 32-key half of one column block
 // against the reference max m_use (log2 units); returns this lane's partial
 // sum of the bf16-rounded probabilities (two independent chains, one per
@@ -162,13 +195,14 @@ __device__ __forceinline__ int find_sequence(const int32_t* __restrict__ cu, int
   }
 }
 
-template <bool kWindow, int kCols>
+template <bool kWindow, int kCols, bool kPaged>
 __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_per_eu(4 / kCols, 4 / kCols))) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ sinks,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ cu_seqlens_k, int hq, int hkv, int group,
     int n_hchunk, int batch, int max_seqlen, int max_seqlen_k, int window, float scale_log2,
-    uint16_t* __restrict__ o, float* __restrict__ lse) {
+    uint16_t* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ block_table, int max_pages,
+    int page_shift, int num_pages) {
   // Ring of LDS tile buffers, each K rows then V rows.  Tile t lives in
   // buffer (t - t_begin) % kBufs; the loop below is unrolled over the ring so
   // every LDS address is a per-lane base plus an immediate offset.
@@ -199,12 +233,13 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
   if (b < 0) return;  // uniform over the workgroup
 
   const int seq0 = cu_seqlens[b];
-  const int seq0_k = cu_seqlens_k[b];
+  // kPaged: the keys live in pages; cu_seqlens_k then holds the lengths.
+  const int seq0_k = kPaged ? 0 : cu_seqlens_k[b];
   // Lengths above the declared maxima, or fewer keys than queries, break a
   // precondition; clamping keeps every access inside the bounds the host
   // checked (such a sequence's rows are left unwritten).
   const int len = min(cu_seqlens[b + 1] - seq0, max_seqlen);
-  const int len_k = min(cu_seqlens_k[b + 1] - seq0_k, max_seqlen_k);
+  const int len_k = min(kPaged ? cu_seqlens_k[b] : cu_seqlens_k[b + 1] - seq0_k, max_seqlen_k);
   const int n_tiles = len > 0 ? (len + kQTile - 1) / kQTile : 0;
   const int j = w - item_start(seq0, b);
   if (j >= n_tiles || len_k < len) return;  // a spare item between two sequences
@@ -229,10 +264,16 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
   const uint16_t* v_seq = v + kv0;
   // LDS byte address of the ring (uniform).
   const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_address(&kv_lds[0][0]));
+  const int32_t* bt_row = kPaged ? block_table + static_cast<size_t>(b) * max_pages : nullptr;
+  const int plast = kPaged ? min((len_k - 1) >> page_shift, max_pages - 1) : 0;  // len_k >= len >= 1 here
   auto issue = [&](int tt, int buf) {
     const uint32_t dst = ring + static_cast<uint32_t>(buf) * (2 * kKTile * kHeadDim * 2);
-    issue_tile<kThreads>(k_seq, v_seq, dst, dst + kKTile * kHeadDim * 2, len_k, hkv * kHeadDim, tt * kKTile,
-                         wave, lane);
+    if constexpr (kPaged)
+      issue_tile_paged<kThreads>(k_seq, v_seq, dst, dst + kKTile * kHeadDim * 2, len_k, hkv, tt * kKTile, wave,
+                                 lane, bt_row, page_shift, plast, num_pages);
+    else
+      issue_tile<kThreads>(k_seq, v_seq, dst, dst + kKTile * kHeadDim * 2, len_k, hkv * kHeadDim, tt * kKTile,
+                           wave, lane);
   };
   // The first two tiles go out before anything else, then the workgroup's
   // Q block (32 tokens x 8 head slots x 128 B, 1 KB contiguous per token)
@@ -565,12 +606,15 @@ hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream) {
   if (blocks <= 0) return hipSuccess;
   dim3 grid(static_cast<unsigned>(blocks), 1, 1);
   const bool windowed = a.window > 0 && a.window < a.max_seqlen_k;
-  auto kernel = windowed ? prefill_kernel<true, kColsPerWave> : prefill_kernel<false, kColsPerWave>;
+  const bool paged = a.block_table != nullptr;
+  auto kernel = paged ? (windowed ? prefill_kernel<true, kColsPerWave, true> : prefill_kernel<false, kColsPerWave, true>)
+                      : (windowed ? prefill_kernel<true, kColsPerWave, false> : prefill_kernel<false, kColsPerWave, false>);
   hipLaunchKernelGGL(kernel, grid, dim3(threads_for<kColsPerWave>()), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.sinks, a.cu_seqlens, a.cu_seqlens_k, a.num_q_heads,
                      a.num_kv_heads, group, n_hchunk, a.batch, a.max_seqlen, a.max_seqlen_k, a.window,
-                     a.softmax_scale * kLog2e, static_cast<uint16_t*>(a.o), a.lse);
+                     a.softmax_scale * kLog2e, static_cast<uint16_t*>(a.o), a.lse, a.block_table, a.max_pages,
+                     a.page_shift, a.num_pages);
   return hipGetLastError();
 }
 

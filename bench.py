@@ -24,8 +24,8 @@ varlen prefill (causal and 128-window); the append prefill (the last
 2048-token chunk of an 8192-token prompt; 64 x 4 draft tokens verified
 against 8192 cached tokens, also through the multi-token-query decode at 1
 and 4 splits); the 64 x 8192 decode against a paged cache (16- and 64-token
-pages, shuffled), also with 4 draft tokens per sequence and over E4M3 pages;
-the fused rotary step (YaRN; Q out, K/V appended) for 8192
+pages, shuffled), also with 4 draft tokens per sequence, over E4M3 pages, and
+as the keys of a 2048-token prompt chunk (append prefill over pages); the fused rotary step (YaRN; Q out, K/V appended) for 8192
 and 64 tokens; the output projection with bias (64 and 8192 rows, 4096 ->
 2880); a streaming-read and a copy
 bandwidth reference; the engine clock (sysfs pp_dpm_sclk) sampled during the step.
@@ -737,6 +737,21 @@ def _other_configs(torch, np, binding, inputs, dev, bf16, timed, hbm_entry, mfma
                 out["paged_draft_verify_64x4_ps%d_s%d_%s" % (page_size, s_count,
                                                               "causal" if window == 0 else "w128")] = e
         if page_size == 16:
+            # the last 2048-token chunk of an 8192-token prompt whose keys
+            # are the first sequence's pages
+            cq2 = torch.tensor([0, 2048], dtype=torch.int32, device=dev)
+            q2 = _device_normal_bf16(torch, (2048, HQ, D), gen, dev)
+            o2 = torch.empty_like(q2)
+            for window in (0, WINDOW):
+                st = timed(lambda: binding.prefill_append_paged(q2, kp, vp, table[:1], plens[:1], cq2, 2048, DEC_CTX,
+                                                                psinks, window, scale, out=o2),
+                           scrub_each=(window > 0))
+                f, b = append_flops([2048], [DEC_CTX], window), append_bytes([2048], [DEC_CTX], window)
+                e = mfma_entry(st, f, b) if window == 0 else hbm_entry(st, b, f)
+                e["bound"] = "mfma" if window == 0 else "hbm"
+                e["shape"] = "last 2048 of 8192 tokens, keys in 16-token pages (shuffled), 64/8 heads, window %d" % window
+                out["paged_chunked_prefill_last_2048_of_8192_%s" % ("causal" if window == 0 else "w128")] = e
+            del q2, o2
             # the same table over pages of E4M3 codes (N(0,1) / scale rounded
             # on the device; one byte per cached element)
             fkp = (torch.randn(kp.shape, generator=gen, device=dev) * 16.0).to(torch.float8_e4m3fn).view(torch.uint8)

@@ -318,6 +318,34 @@ SINKATTN_API sinkattn_status sinkattn_decode_splitkv_multi(
     void* o, float* lse, void* stream);
 
 /*
+ * Append (chunked) prefill against a paged cache: the queries, offsets,
+ * masks and outputs of sinkattn_prefill_append with the keys and values in
+ * the pages of sinkattn_decode_paged.  The result equals
+ * sinkattn_prefill_append's on the gathered cache (sequence b's Lq_b queries
+ * are its newest tokens, bottom-right causal, optional window): a prompt
+ * chunk, or draft tokens, attending to a paged KV cache.
+ *
+ *   q, cu_seqlens_q, max_seqlen_q, total_q, sinks, window, softmax_scale,
+ *   o, lse         as sinkattn_prefill_append
+ *   k_pages, v_pages, block_table, max_pages, page_size, num_pages
+ *                  as sinkattn_decode_paged
+ *   seq_lens_k     int32 [batch], device: Lk_b >= Lq_b, <= max_seqlen_k
+ *
+ * Device-side preconditions: those of both entry points (SINKATTN_DEBUG_CHECKS=1
+ * checks the offsets, lengths, table and operands).  Page ids outside the pool
+ * are clamped into it.
+ */
+SINKATTN_API sinkattn_status sinkattn_prefill_append_paged(
+    const void* q, const void* k_pages, const void* v_pages,
+    const int32_t* block_table, const int32_t* seq_lens_k, const int32_t* cu_seqlens_q, int32_t batch,
+    int32_t max_pages, int32_t page_size, int32_t num_pages,
+    int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t total_q,
+    const float* sinks,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t window, float softmax_scale,
+    void* o, float* lse, void* stream);
+
+/*
  * Split-KV decode against a paged FP8 cache: the pages and block table of
  * sinkattn_decode_paged holding the E4M3 codes and per-tensor scales of
  * sinkattn_decode_splitkv_fp8.  The result equals sinkattn_decode_splitkv_fp8's

@@ -66,7 +66,9 @@ def decode_paged_ref(q, k_pages, v_pages, block_table, seq_lens, page_size: int,
 
 def decode_paged_multi_ref(q, k_pages, v_pages, block_table, seq_lens, cu_seqlens_q, page_size: int, sinks,
                            window: int, scale: float, rows=None):
-    """Several query tokens per sequence against a paged cache (float64):
+    """Several query tokens per sequence against a paged cache (float64),
+    whether a few draft tokens or a prompt chunk (the append prefill over
+    pages computes the same thing):
     q [Tq, Hq, D], sequence b's queries are rows cu_seqlens_q[b] ..
     cu_seqlens_q[b+1] - 1, its newest Lq_b <= seq_lens[b] tokens; pages and
     table as ``decode_paged_ref``.  Returns o [Tq, Hq, D], lse [Tq, Hq]."""

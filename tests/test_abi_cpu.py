@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
         "sinkattn_decode_splitkv_multi",
         "sinkattn_decode_workspace_bytes", "sinkattn_oproj_bias", "sinkattn_oproj_workspace_bytes",
         "sinkattn_rope_qkv_append",
-        "sinkattn_last_error", "sinkattn_merge_lse", "sinkattn_prefill_append", "sinkattn_prefill_varlen",
+        "sinkattn_last_error", "sinkattn_merge_lse", "sinkattn_prefill_append", "sinkattn_prefill_append_paged",
+        "sinkattn_prefill_varlen",
         "sinkattn_version"])
 
 
@@ -338,6 +339,38 @@ def test_decode_paged_multi_empty_is_ok_without_launch():
     assert _decode_paged_multi(lib, batch=0) == 0
     assert _decode_paged_multi(lib, batch=0, bt=None, lens=None, cuq=None) == 0
     assert _decode_paged_multi(lib, tq=0, mq=0) == 0
+
+
+def _prefill_paged(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE2, cuq=FAKE2, batch=4, mp=8, ps=16, npg=40, mq=64, mk=100,
+             tq=200, sinks=None, hq=64, hkv=8, d=64, window=0, scale=0.125, o=FAKE, lse=None)
+    a.update(kw)
+    return lib.sinkattn_prefill_append_paged(a["q"], a["k"], a["v"], a["bt"], a["lens"], a["cuq"], a["batch"],
+                                             a["mp"], a["ps"], a["npg"], a["mq"], a["mk"], a["tq"], a["sinks"],
+                                             a["hq"], a["hkv"], a["d"], a["window"], a["scale"], a["o"], a["lse"],
+                                             None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ps=24), 2),                 # page size not a power of two
+    (dict(mp=6), 1),                  # 6 x 16 < max_seqlen_k
+    (dict(bt=None), 1),
+    (dict(cuq=None), 1),
+    (dict(mq=300), 1),                # more than total_q
+    (dict(mk=0), 1),                  # queries need keys
+    (dict(d=128), 2),
+    (dict(o=ctypes.c_void_p((1 << 20) + 2)), 1),
+])
+def test_prefill_append_paged_rejects(kw, status):
+    lib = _lib()
+    assert _prefill_paged(lib, **kw) == status
+    assert lib.sinkattn_last_error()
+
+
+def test_prefill_append_paged_empty_is_ok_without_launch():
+    lib = _lib()
+    assert _prefill_paged(lib, batch=0) == 0
+    assert _prefill_paged(lib, tq=0, mq=0) == 0
 
 
 def _rope(lib, **kw):

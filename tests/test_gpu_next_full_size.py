@@ -136,6 +136,22 @@ def test_draft_verification_64x4_over_8192_paged(window):
 
 
 @pytest.mark.parametrize("window", [0, 128])
+def test_chunked_prefill_last_2048_of_8192_paged(window):
+    p = inputs.make_paged_append([2048], [8192], 16, hq=HQ, hkv=HKV, seed=0)
+    o, lse = binding.prefill_append_paged(bf16_to_device(p.q), bf16_to_device(p.k_pages), bf16_to_device(p.v_pages),
+                                          i32_to_device(p.block_table), i32_to_device(p.seq_lens),
+                                          i32_to_device(p.cu_seqlens_q), 2048, 8192, f32_to_device(p.sinks), window,
+                                          p.scale, return_lse=True)
+    torch.cuda.synchronize()
+    rows = sorted(set(int(x) for x in np.random.default_rng(3).integers(0, 2048, 40)) | {0, 2047})
+    ro, rl = decode_paged_multi_ref(inputs.bf16_bits_to_f32(p.q), inputs.bf16_bits_to_f32(p.k_pages),
+                                    inputs.bf16_bits_to_f32(p.v_pages), p.block_table, p.seq_lens, p.cu_seqlens_q, 16,
+                                    p.sinks, window, p.scale, rows=rows)
+    assert_close_out(to_f64(o)[rows], ro[rows], "paged chunk W=%d" % window)
+    assert_close_lse(lse.cpu().numpy()[rows], rl[rows], "paged chunk")
+
+
+@pytest.mark.parametrize("window", [0, 128])
 def test_chunked_prefill_last_2048_of_8192(window):
     a = inputs.make_append([2048], [8192], hq=HQ, hkv=HKV, seed=0)
     o, lse = binding.prefill_append(*(bf16_to_device(x) for x in (a.q, a.k, a.v)), f32_to_device(a.sinks),

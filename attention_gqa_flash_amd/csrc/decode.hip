@@ -293,8 +293,8 @@ __device__ __forceinline__ void decode_body(
   // of each K/V row does not wait for a table read; a tile that starts
   // elsewhere (the next split's first) reads its ids first.  64 x 8192,
   // 16-token pages: S = 1 0.200 -> 0.186 ms, S = 16 0.215 -> 0.203 ms.  The
-  // E4M3 tiles read their ids when they are loaded: ahead, S = 4 and 16 took
-  // 6-9% longer (0.142 -> 0.155 ms at S = 4).
+  // E4M3 tiles read their ids when they are loaded: reading them ahead made
+  // no measurable difference there.
   constexpr bool kIdsAhead = kPaged && !kFp8;
   PageIds pids{-1, 0, 0, 0};
   auto load = [&](TileRegs<kFp8>& t, int k_first, int k_end) {

@@ -67,7 +67,7 @@ def library() -> ctypes.CDLL:
                                                 i32, i32, i32, f32, i32, vp, sz, vp, vp, vp]
     lib.sinkattn_decode_paged_multi.restype = ctypes.c_int
     f64 = ctypes.c_double
-    lib.sinkattn_rope_qkv_append.argtypes = [vp, vp, vp, i32, i32, i32, i32, f64, f64, i32, f64, f64, vp, vp, vp, i32,
+    lib.sinkattn_rope_qkv_append.argtypes = [vp, vp, vp, i32, i32, i32, i32, f64, f64, i32, f64, f64, i32, vp, vp, vp, i32,
                                              vp]
     lib.sinkattn_rope_qkv_append.restype = ctypes.c_int
     lib.sinkattn_oproj_bias.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
@@ -464,7 +464,8 @@ def decode_paged_multi(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Te
 def rope_qkv_append(qkv: torch.Tensor, positions: torch.Tensor, slot_mapping: torch.Tensor, num_q_heads: int,
                     num_kv_heads: int, k_cache: torch.Tensor, v_cache: torch.Tensor, rope_theta: float = 10000.0,
                     yarn_factor: float = 1.0, yarn_original_max_position: int = 4096, yarn_beta_fast: float = 32.0,
-                    yarn_beta_slow: float = 1.0, q_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    yarn_beta_slow: float = 1.0, yarn_truncate: bool = False,
+                    q_out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The fused rotary step: qkv [T, Hq + 2 Hkv, 64] bf16, positions and
     slot_mapping [T] int32; writes the rotated K and the V of token t into
     k_cache / v_cache [rows, Hkv, 64] row slot_mapping[t] (-1: none) and
@@ -486,7 +487,8 @@ def rope_qkv_append(qkv: torch.Tensor, positions: torch.Tensor, slot_mapping: to
     _check(library().sinkattn_rope_qkv_append(
         _ptr(qkv), _ptr(positions), _ptr(slot_mapping), t, int(num_q_heads), int(num_kv_heads), d,
         float(rope_theta), float(yarn_factor), int(yarn_original_max_position), float(yarn_beta_fast),
-        float(yarn_beta_slow), _ptr(q_out), _ptr(k_cache), _ptr(v_cache), k_cache.shape[0], _stream(qkv.device)))
+        float(yarn_beta_slow), int(bool(yarn_truncate)), _ptr(q_out), _ptr(k_cache), _ptr(v_cache), k_cache.shape[0],
+        _stream(qkv.device)))
     return q_out
 
 

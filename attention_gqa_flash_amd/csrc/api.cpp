@@ -157,8 +157,18 @@ static sinkattn_status prefill_common(const void* q, const void* k, const void* 
     }
     if ((st = hip_queue(sinkattn::check_sinks(sinks, num_q_heads, s))) != SINKATTN_OK) return st;
     if ((st = hip_queue(sinkattn::check_bf16(q, qn, sinkattn::kCheckQ, s))) != SINKATTN_OK) return st;
-    if ((st = hip_queue(sinkattn::check_bf16(k, kvn, sinkattn::kCheckK, s))) != SINKATTN_OK) return st;
-    if ((st = hip_queue(sinkattn::check_bf16(v, kvn, sinkattn::kCheckV, s))) != SINKATTN_OK) return st;
+    if (paged) {  // only the pool rows the table and lengths reach
+      const int row = num_kv_heads * head_dim;
+      if ((st = hip_queue(sinkattn::check_paged_values(k, cu_k, block_table, batch, max_pages, page_size, num_pages,
+                                                       max_k, row, 2, sinkattn::kCheckK, s))) != SINKATTN_OK)
+        return st;
+      if ((st = hip_queue(sinkattn::check_paged_values(v, cu_k, block_table, batch, max_pages, page_size, num_pages,
+                                                       max_k, row, 2, sinkattn::kCheckV, s))) != SINKATTN_OK)
+        return st;
+    } else {
+      if ((st = hip_queue(sinkattn::check_bf16(k, kvn, sinkattn::kCheckK, s))) != SINKATTN_OK) return st;
+      if ((st = hip_queue(sinkattn::check_bf16(v, kvn, sinkattn::kCheckV, s))) != SINKATTN_OK) return st;
+    }
     if ((st = check_result(s, nullptr)) != SINKATTN_OK) return st;
   }
   sinkattn::PrefillLaunch a{q, k, v, sinks, cu_q, cu_k, batch, max_q, max_k, total_q, num_q_heads,
@@ -270,9 +280,18 @@ static sinkattn_status decode_common(const void* q, const void* k_cache, const v
     if ((st = hip_queue(sinkattn::check_bf16(q, qn, sinkattn::kCheckQ, s))) != SINKATTN_OK) return st;
     int total_kv = 0;
     if ((st = check_result(s, &total_kv)) != SINKATTN_OK) return st;
-    if (paged) total_kv = num_pages * page_size;  // the whole pool
     const size_t kvn = static_cast<size_t>(total_kv) * num_kv_heads * head_dim;
-    if (fp8) {
+    if (paged) {  // only the pool rows the table and lengths reach
+      const int row = num_kv_heads * head_dim, eb = fp8 ? 1 : 2;
+      if ((st = hip_queue(sinkattn::check_paged_values(k_cache, cu_seqlens_k, block_table, batch, max_pages, page_size,
+                                                       num_pages, max_seqlen_k, row, eb, sinkattn::kCheckK, s))) !=
+          SINKATTN_OK)
+        return st;
+      if ((st = hip_queue(sinkattn::check_paged_values(v_cache, cu_seqlens_k, block_table, batch, max_pages, page_size,
+                                                       num_pages, max_seqlen_k, row, eb, sinkattn::kCheckV, s))) !=
+          SINKATTN_OK)
+        return st;
+    } else if (fp8) {
       if ((st = hip_queue(sinkattn::check_e4m3(k_cache, kvn, sinkattn::kCheckK, s))) != SINKATTN_OK) return st;
       if ((st = hip_queue(sinkattn::check_e4m3(v_cache, kvn, sinkattn::kCheckV, s))) != SINKATTN_OK) return st;
     } else {
@@ -427,22 +446,40 @@ sinkattn_status sinkattn_prefill_append_paged(const void* q, const void* k_pages
 }
 
 // Rotary frequencies of the pairs (i, i + 32): theta^(-2i/64), rescaled by
-// YaRN's NTK-by-parts rule when factor > 1 (a frequency that turns more than
-// beta_fast times over the original context is kept, fewer than beta_slow
-// times divided by the factor, linear in the turn count between), and YaRN's
-// temperature 0.1 ln(factor) + 1.
+// YaRN's NTK-by-parts rule when factor > 1, with the ramp over the pair index
+// that YaRN's own code and the GPT-OSS / DeepSeek-V3 models use: the index at
+// which a frequency turns `beta` times over the original context is
+// 32 ln(L / (2 pi beta)) / ln(theta); between the indices of beta_fast and
+// beta_slow (rounded outwards when `truncate` is set; clamped to [0, 63])
+// the frequency moves linearly in the index from f to f / factor.  YaRN's
+// temperature is 0.1 ln(factor) + 1.
 static sinkattn::RopeTable rope_table(double theta, double factor, int original_max_position, double beta_fast,
-                                      double beta_slow) {
+                                      double beta_slow, bool truncate) {
   sinkattn::RopeTable t{};
   const double two_pi = 6.283185307179586476925286766559;
+  double low = 0.0, high = 1.0;
+  if (factor > 1.0) {
+    auto index_of = [&](double turns) {
+      return 32.0 * std::log(original_max_position / (two_pi * turns)) / std::log(theta);
+    };
+    low = index_of(beta_fast);
+    high = index_of(beta_slow);
+    if (truncate) {
+      low = std::floor(low);
+      high = std::ceil(high);
+    }
+    low = std::max(low, 0.0);
+    high = std::min(high, 63.0);
+    if (high == low) high += 0.001;  // a zero-width ramp is a step
+  }
   for (int i = 0; i < 32; ++i) {
     const double f = std::pow(theta, -static_cast<double>(2 * i) / 64.0);
-    double g = 1.0;
     if (factor > 1.0) {
-      const double turns = original_max_position * f / two_pi;
-      g = std::min(1.0, std::max(0.0, (turns - beta_slow) / (beta_fast - beta_slow)));
+      const double g = std::min(1.0, std::max(0.0, (i - low) / (high - low)));
+      t.freq[i] = f * (1.0 - g) + g * f / factor;
+    } else {
+      t.freq[i] = f;
     }
-    t.freq[i] = factor > 1.0 ? (1.0 - g) * f / factor + g * f : f;
   }
   t.attention_factor = factor > 1.0 ? static_cast<float>(0.1 * std::log(factor) + 1.0) : 1.0f;
   return t;
@@ -452,8 +489,8 @@ sinkattn_status sinkattn_rope_qkv_append(const void* qkv, const int32_t* positio
                                          int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
                                          int32_t head_dim, double rope_theta, double yarn_factor,
                                          int32_t yarn_original_max_position, double yarn_beta_fast,
-                                         double yarn_beta_slow, void* q_out, void* k_cache, void* v_cache,
-                                         int32_t cache_rows, void* stream) {
+                                         double yarn_beta_slow, int32_t yarn_truncate, void* q_out, void* k_cache,
+                                         void* v_cache, int32_t cache_rows, void* stream) {
   if (num_tokens < 0 || cache_rows < 0) return fail(SINKATTN_ERR_INVALID_ARG, "num_tokens and cache_rows must be >= 0");
   if (num_q_heads < 1 || num_kv_heads < 1)
     return fail(SINKATTN_ERR_INVALID_ARG, "head counts must be >= 1 (got %d, %d)", num_q_heads, num_kv_heads);
@@ -464,9 +501,9 @@ sinkattn_status sinkattn_rope_qkv_append(const void* qkv, const int32_t* positio
     return fail(SINKATTN_ERR_INVALID_ARG, "yarn_factor must be finite and > 0");
   if (yarn_factor > 1.0 &&
       (yarn_original_max_position < 1 || !std::isfinite(yarn_beta_fast) || !std::isfinite(yarn_beta_slow) ||
-       !(yarn_beta_fast > yarn_beta_slow)))
+       !(yarn_beta_fast > yarn_beta_slow) || !(yarn_beta_slow > 0.0)))
     return fail(SINKATTN_ERR_INVALID_ARG,
-                "YaRN needs original_max_position >= 1 and finite beta_fast > beta_slow");
+                "YaRN needs original_max_position >= 1 and finite beta_fast > beta_slow > 0");
   if (num_tokens == 0) return ok();
   if (!qkv || !positions || !slot_mapping || !q_out || !k_cache || !v_cache)
     return fail(SINKATTN_ERR_INVALID_ARG, "qkv, positions, slot_mapping, q_out, k_cache and v_cache must not be NULL");
@@ -483,7 +520,7 @@ sinkattn_status sinkattn_rope_qkv_append(const void* qkv, const int32_t* positio
   }
   sinkattn::RopeLaunch a{qkv, positions, slot_mapping, num_tokens, num_q_heads, num_kv_heads, cache_rows,
                          rope_table(rope_theta, yarn_factor, yarn_original_max_position, yarn_beta_fast,
-                                    yarn_beta_slow),
+                                    yarn_beta_slow, yarn_truncate != 0),
                          q_out, k_cache, v_cache};
   return hip_status(sinkattn::launch_rope_qkv_append(a, static_cast<hipStream_t>(stream)), "rope launch");
 }

@@ -129,6 +129,41 @@ __global__ void check_f32_kernel(const float* __restrict__ x, size_t n, unsigned
   if (bad != 0u) atomicOr(&g_check_flags, bit);
 }
 
+// NaN / Inf (bf16, elem_bytes 2) or NaN codes (E4M3, elem_bytes 1) in the
+// page-pool rows a paged call can read: the first lens[b] slots of sequence
+// b through its table row.  Free or unowned pages are not inspected.  A
+// length or page id that check_paged reports is skipped here, so a broken
+// table cannot move this scan out of the pool.  Work is (sequence, page)
+// pairs in a grid-stride loop, one page per workgroup at a time.
+__global__ void check_paged_values_kernel(const void* __restrict__ pool, const int32_t* __restrict__ lens,
+                                          const int32_t* __restrict__ table, int batch, int max_pages,
+                                          int page_size, int num_pages, int max_len, int row_elems, int elem_bytes,
+                                          unsigned bit) {
+  unsigned bad = 0;
+  const long long pairs = static_cast<long long>(batch) * max_pages;
+  for (long long pr = blockIdx.x; pr < pairs; pr += gridDim.x) {
+    const int b = static_cast<int>(pr / max_pages);
+    const int p = static_cast<int>(pr % max_pages);
+    const int n = lens[b];
+    if (n < 1 || n > max_len) continue;
+    const long long first = static_cast<long long>(p) * page_size;
+    if (first >= n) continue;
+    const int id = table[pr];
+    if (id < 0 || id >= num_pages) continue;
+    const int rows = static_cast<int>(min(static_cast<long long>(page_size), n - first));
+    const size_t base = static_cast<size_t>(id) * page_size * row_elems;
+    const size_t count = static_cast<size_t>(rows) * row_elems;
+    if (elem_bytes == 2) {
+      const uint16_t* x = static_cast<const uint16_t*>(pool) + base;
+      for (size_t i = threadIdx.x; i < count; i += blockDim.x) bad |= (x[i] & 0x7f80u) == 0x7f80u;
+    } else {
+      const uint8_t* x = static_cast<const uint8_t*>(pool) + base;
+      for (size_t i = threadIdx.x; i < count; i += blockDim.x) bad |= (x[i] & 0x7fu) == 0x7fu;
+    }
+  }
+  if (bad != 0u) atomicOr(&g_check_flags, bit);
+}
+
 unsigned grid_for(size_t n) {
   const size_t blocks = (n + 255) / 256;
   return static_cast<unsigned>(blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks));
@@ -160,6 +195,17 @@ hipError_t check_paged(const int32_t* seq_lens, const int32_t* block_table, int 
   if (batch <= 0) return hipSuccess;
   hipLaunchKernelGGL(check_paged_kernel, dim3(grid_for(batch)), dim3(256), 0, stream, seq_lens, block_table, batch,
                      max_pages, page_size, num_pages, max_len);
+  return hipGetLastError();
+}
+
+hipError_t check_paged_values(const void* pool, const int32_t* seq_lens, const int32_t* block_table, int batch,
+                              int max_pages, int page_size, int num_pages, int max_len, int row_elems, int elem_bytes,
+                              unsigned bit, hipStream_t stream) {
+  if (pool == nullptr || batch <= 0 || max_pages <= 0) return hipSuccess;
+  const long long pairs = static_cast<long long>(batch) * max_pages;
+  const unsigned blocks = static_cast<unsigned>(pairs < 4096 ? pairs : 4096);
+  hipLaunchKernelGGL(check_paged_values_kernel, dim3(blocks), dim3(256), 0, stream, pool, seq_lens, block_table,
+                     batch, max_pages, page_size, num_pages, max_len, row_elems, elem_bytes, bit);
   return hipGetLastError();
 }
 

@@ -120,9 +120,8 @@ __device__ __forceinline__ void load16_to_lds(const uint16_t* src, uint16_t* lds
 // about it: it adds no vmcnt waits of its own before LDS reads (it would
 // otherwise make every transposing read wait for every copy in flight).  The
 // caller orders each read of the destination after the copy with a vmcnt
-// wait and a barrier.  The LDS address goes through M0, which the kernels
-// using this do not otherwise use (checked on their assembly when the
-// library is built).
+// wait and a barrier.  The LDS address goes through M0; the asm names M0 as
+// clobbered, so the compiler reloads any value of its own it keeps there.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void load16_to_lds_untracked(const uint16_t* src, uint32_t lds_addr) {

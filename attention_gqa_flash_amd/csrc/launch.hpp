@@ -137,6 +137,11 @@ hipError_t check_append(const int32_t* cu_q, const int32_t* cu_k, bool k_lengths
 hipError_t check_paged(const int32_t* seq_lens, const int32_t* block_table, int batch, int max_pages,
                        int page_size, int num_pages, int max_len, hipStream_t stream);
 hipError_t check_bf16(const void* x, size_t n, unsigned bit, hipStream_t stream);
+// The rows of a page pool that the table and lengths of a paged call reach
+// (row_elems elements of elem_bytes bytes each: 2 = bf16, 1 = E4M3).
+hipError_t check_paged_values(const void* pool, const int32_t* seq_lens, const int32_t* block_table, int batch,
+                              int max_pages, int page_size, int num_pages, int max_len, int row_elems, int elem_bytes,
+                              unsigned bit, hipStream_t stream);
 // E4M3 codes: NaN (all exponent and mantissa bits set).
 hipError_t check_e4m3(const void* x, size_t n, unsigned bit, hipStream_t stream);
 hipError_t check_f32(const float* x, size_t n, unsigned bit, bool allow_neg_inf, hipStream_t stream);

@@ -8,7 +8,9 @@ input with GPT-OSS attention shapes (64 query heads, 8 KV heads, head_dim
   * split-KV decode, batch 64 x 8192 cached tokens, 16 splits, including
     the log-sum-exp merge.
 
-Printed: ONE JSON line.  `value` is the mean of the two roofline fractions
+Printed: ONE compact JSON line (a few KB; the full record with every
+statistic goes to --detail-json, gpurun_out/bench_detail.json by default).
+`value` is the mean of the two roofline fractions
 (prefill FLOP/s over the bf16 MFMA peak, decode KV bytes/s over the HBM
 peak) in percent; each leg is also reported on its own.  FLOP and byte
 counts are algorithmic (unmasked query-key pairs; Q + O + the K/V rows
@@ -34,6 +36,7 @@ and ragged inputs are drawn on the device from a seeded generator (same
 distributions as the host-generated parity inputs) to keep start-up short.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
+                    [--detail-json PATH]
 """
 
 from __future__ import annotations
@@ -142,6 +145,24 @@ def _decode_one(args):
     return decode_ref(q, k, v, [0, length], sinks, 0, scale)
 
 
+def affinity_cores() -> int:
+    """Host cores this process may run on (its affinity mask)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _stop_process_helpers() -> None:
+    """End the helper process that spawned pools leave behind (the
+    multiprocessing resource tracker), so nothing outlives the benchmark."""
+    try:
+        from multiprocessing import resource_tracker
+        resource_tracker._resource_tracker._stop()
+    except Exception:  # pragma: no cover - private API, best effort
+        pass
+
+
 def cpu_baseline() -> dict:
     import multiprocessing as mp
 
@@ -171,19 +192,26 @@ def cpu_baseline() -> dict:
     tasks = [(qf[b:b + 1], kf[b * DEC_CTX:(b + 1) * DEC_CTX], vf[b * DEC_CTX:(b + 1) * DEC_CTX], d.sinks, DEC_CTX,
               d.scale) for b in range(DEC_BATCH)]
     ctx = mp.get_context("spawn")
-    with ctx.Pool(processes=cores, initializer=_pool_init) as pool:
+    pool = ctx.Pool(processes=cores, initializer=_pool_init)
+    try:
         pool.map(_decode_one, tasks[:cores], chunksize=1)  # start-up outside the timing
         t0 = time.perf_counter()
         pool.map(_decode_one, tasks, chunksize=1)
         t_dec = time.perf_counter() - t0
+    finally:
+        pool.close()
+        pool.join()
     dec_gbs = decode_bytes([DEC_CTX] * DEC_BATCH, 0) / t_dec / 1e9
     value = 100.0 * 0.5 * (pre_tflops / PEAK_BF16_TFLOPS + dec_gbs / PEAK_HBM_GBS)
     others = _cpu_other_configs(cores)
+    _stop_process_helpers()
     return {
-        "value": value, "unit": "% of MI355X peak (same formula as value)", "cores": cores, "kind": "oracle",
+        "value": value, "unit": "% of MI355X peak (same formula as value)", "cores": cores,
+        "affinity_cores": affinity_cores(), "kind": "oracle",
         "sample": "one whole step: prefill 1 x 8192 tokens (causal + 128-window layers) and decode 64 x 8192 "
                   "keys, 64/8 heads, on %d spawned processes with 1 BLAS thread each (pool start-up included "
                   "for prefill, excluded for decode)" % cores,
+        "sample_short": "whole step (prefill 1 x 8192 causal + w128, decode 64 x 8192), %d processes" % cores,
         "prefill_tflops_f64": pre_tflops, "prefill_seconds": t_pre,
         "decode_gbs_f64": dec_gbs, "decode_seconds": t_dec,
         "other_configs": others,
@@ -454,15 +482,20 @@ def gpu_bench(steps: int, warmup: int, extras: bool = True) -> dict:
     all_marks = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
 
     def step(i, record):
+        # The window layer reads another input set than the causal layer of
+        # the same step: set (i + 1) % 3 was last read two steps earlier, and
+        # each step's 1 GiB decode has since streamed through the Infinity
+        # Cache, so both layers start cold.
         s = sets[i % 3]
+        sw = sets[(i + 1) % 3]
         marks = all_marks[i] if record else None
         if record:
             marks[0].record()
         binding.prefill_varlen(s["q"], s["k"], s["v"], s["sinks"], s["cu"], PREFILL_LEN, 0, scale, out=s["o"])
         if record:
             marks[1].record()
-        binding.prefill_varlen(s["q"], s["k"], s["v"], s["sinks"], s["cu"], PREFILL_LEN, WINDOW, scale,
-                               out=s["o"])
+        binding.prefill_varlen(sw["q"], sw["k"], sw["v"], sw["sinks"], sw["cu"], PREFILL_LEN, WINDOW, scale,
+                               out=sw["o"])
         if record:
             marks[2].record()
         binding.decode_splitkv(dq, dk, dv, dcu, DEC_CTX, dsinks, 0, scale, DEC_SPLITS, workspace=ws, out=do)
@@ -869,6 +902,74 @@ def _other_configs(torch, np, binding, inputs, dev, bf16, timed, hbm_entry, mfma
     return {"configs": out, "bandwidth": bw}
 
 
+def _r(x, nd=4):
+    """Round a float for the compact line (None stays None)."""
+    return None if x is None else float("%.*g" % (nd, x))
+
+
+def _leg(st, extra=None):
+    out = {"median_ms": _r(st["median_ms"]), "min_ms": _r(st["min_ms"]), "mean_ms": _r(st["mean_ms"])}
+    if extra:
+        out.update(extra)
+    return out
+
+
+def _pct(entry):
+    """The fraction of the peak an entry reports (MFMA for MFMA-bound
+    workloads, else HBM), in percent."""
+    if entry is None:
+        return None
+    key = "pct_mfma_peak" if entry.get("bound") == "mfma" and "pct_mfma_peak" in entry else "pct_hbm_peak"
+    return _r(entry.get(key), 3)
+
+
+def compact_record(full: dict, detail_path) -> dict:
+    """The benchmark's last stdout line: the headline, each leg of the step,
+    the rooflines, the CPU baseline and one figure per side workload, kept to
+    a few KB so that it survives a short log tail.  Everything else (every
+    statistic of every side workload, the bandwidth reference, the engine
+    clock samples) is in the detail file."""
+    pre, dec = full["prefill"], full["decode"]
+
+    def roof(rf, named=True):
+        if rf is None:
+            return None
+        out = {"kernel": rf.get("kernel")} if named else {}
+        out.update({"bound": rf["bound"], "achieved": _r(rf["achieved"]), "peak": rf["peak"], "unit": rf["unit"],
+                    "frac": _r(rf["frac"]), "traffic": _r(rf.get("traffic")), "ms": _r(rf.get("ms"))})
+        return out
+
+    cpu = full.get("cpu_baseline")
+    cpu_c = None
+    if cpu is not None:
+        cpu_c = {"value": _r(cpu["value"]), "unit": cpu["unit"], "cores": cpu["cores"],
+                 "affinity_cores": cpu.get("affinity_cores"), "kind": cpu["kind"], "sample": cpu.get("sample_short", cpu["sample"]),
+                 "prefill_seconds": _r(cpu["prefill_seconds"]), "prefill_tflops_f64": _r(cpu["prefill_tflops_f64"]),
+                 "decode_seconds": _r(cpu["decode_seconds"]), "decode_gbs_f64": _r(cpu["decode_gbs_f64"])}
+    others = full.get("other_configs") or {}
+    clock = full.get("engine_clock") or {}
+    return {
+        "metric": full["metric"], "value": _r(full["value"], 5), "unit": full["unit"], "n_gpus": full["n_gpus"],
+        "steps": full["steps"], "warmup": full["warmup"], "ms_per_step": _r(full["ms_per_step"], 5),
+        "higher_is_better": full["higher_is_better"], "scaling": full["scaling"], "vs_baseline": full["vs_baseline"],
+        "dtype": full["dtype"], "data": full["data"], "config": {"workload": full["config"]["workload"]},
+        "legs": {
+            "prefill_causal": _leg(pre["causal_timing"], {"tflops": _r(pre["causal_tflops"])}),
+            "prefill_w128": _leg(pre["window_timing"], {"gbs": _r(pre["window_gbs"])}),
+            "decode_s16": _leg(dec["timing"], {"gbs": _r(dec["gbs"])}),
+        },
+        "decode_pct_hbm_by_splits": {k: _r(v["pct_hbm_peak"], 3) for k, v in dec["by_splits"].items()},
+        "fp8_decode_pct_hbm_by_splits": {k: _r(v["pct_hbm_peak"], 3) for k, v in (dec.get("fp8_kv_by_splits") or {}).items()},
+        "roofline": roof(full["roofline"]),
+        # the step's three legs: causal prefill (= roofline), window prefill, decode
+        "rooflines": [roof(r, named=False) for r in full["rooflines"]],
+        "cpu_baseline": cpu_c,
+        "other_pct_of_peak": {k: _pct(v) for k, v in others.items()},
+        "engine_clock_mhz": clock.get("mhz_median"), "clock_samples": clock.get("samples"),
+        "detail": detail_path,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -880,6 +981,8 @@ def main():
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (a reference "
                          "for HBM byte counters)")
+    ap.add_argument("--detail-json", default=os.path.join("gpurun_out", "bench_detail.json"),
+                    help="where the full record goes (the last stdout line is its compact form)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -898,7 +1001,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     g = gpu_bench(args.steps, args.warmup, extras=not args.no_extras)
-    out = {
+    full = {
         "metric": METRIC, "value": g["value"],
         "unit": "% of MI355X peak (mean of prefill bf16-MFMA and decode HBM fractions)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": g["ms_per_step"],
@@ -913,7 +1016,19 @@ def main():
         "cpu_baseline": cpu, "other_configs": g["other_configs"],
         "bandwidth_reference": g["bandwidth_reference"], "engine_clock": g["engine_clock"], "device": g["device"],
     }
-    print(json.dumps(out))
+    detail = None
+    if args.detail_json:
+        try:
+            d = os.path.dirname(args.detail_json)
+            if d:
+                os.makedirs(d, exist_ok=True)
+            with open(args.detail_json, "w") as f:
+                json.dump(full, f, indent=1)
+            detail = args.detail_json
+        except OSError as e:
+            print("could not write %s: %s" % (args.detail_json, e), file=sys.stderr)
+    sys.stdout.flush()
+    print(json.dumps(compact_record(full, detail), separators=(",", ":")), flush=True)
 
 
 if __name__ == "__main__":

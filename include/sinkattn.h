@@ -416,11 +416,15 @@ SINKATTN_API sinkattn_status sinkattn_decode_paged_multi(
  * rotation is the RoFormer one with dimension i pairing with i + head_dim/2:
  *     (x_i, x_{i+32}) -> m * (x_i cos a - x_{i+32} sin a, x_{i+32} cos a + x_i sin a),
  *     a = position * f_i,  f_i = rope_theta^(-2i/64),
- * and for yarn_factor s > 1 YaRN's NTK-by-parts rescaling (Peng et al.): with
- * r_i = yarn_original_max_position * f_i / (2 pi) turns over the original
- * context, gamma_i = clamp((r_i - yarn_beta_slow) / (yarn_beta_fast -
- * yarn_beta_slow), 0, 1), f_i -> (1 - gamma_i) f_i / s + gamma_i f_i, and the
- * temperature m = 0.1 ln s + 1 (m = 1 for s <= 1).
+ * and for yarn_factor s > 1 YaRN's NTK-by-parts rescaling (Peng et al.) in
+ * the form its own code and the GPT-OSS / DeepSeek-V3 models use: with
+ * L = yarn_original_max_position, the pair index at which a frequency turns
+ * beta times over the original context is c(beta) = 32 ln(L / (2 pi beta)) /
+ * ln(rope_theta); low = c(yarn_beta_fast), high = c(yarn_beta_slow) (floor
+ * and ceil when yarn_truncate != 0, as DeepSeek-V3; unrounded when 0, as
+ * GPT-OSS), clamped to [0, 63]; gamma_i = clamp((i - low) / (high - low), 0,
+ * 1) and f_i -> (1 - gamma_i) f_i + gamma_i f_i / s; the temperature
+ * m = 0.1 ln s + 1 (m = 1 for s <= 1).
  *
  *   qkv           bf16 [num_tokens, num_q_heads + 2 num_kv_heads, head_dim]:
  *                 the q heads, then the k heads, then the v heads of a token
@@ -436,7 +440,7 @@ SINKATTN_API sinkattn_status sinkattn_decode_paged_multi(
  * Angles are reduced modulo 2 pi in fp64 before sin / cos in fp32, so the
  * phase of large positions is kept.  Errors: rope_theta must be finite and
  * > 1, yarn_factor finite and > 0, and with yarn_factor > 1 the original
- * context >= 1 and finite yarn_beta_fast > yarn_beta_slow
+ * context >= 1 and finite yarn_beta_fast > yarn_beta_slow > 0
  * (SINKATTN_ERR_INVALID_ARG); head_dim 64 only.  Slots outside
  * [-1, cache_rows) are skipped; slots out of range or repeated are reported
  * under SINKATTN_DEBUG_CHECKS=1.
@@ -445,7 +449,7 @@ SINKATTN_API sinkattn_status sinkattn_rope_qkv_append(
     const void* qkv, const int32_t* positions, const int32_t* slot_mapping, int32_t num_tokens,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
     double rope_theta, double yarn_factor, int32_t yarn_original_max_position,
-    double yarn_beta_fast, double yarn_beta_slow,
+    double yarn_beta_fast, double yarn_beta_slow, int32_t yarn_truncate,
     void* q_out, void* k_cache, void* v_cache, int32_t cache_rows, void* stream);
 
 /*

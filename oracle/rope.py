@@ -18,11 +18,17 @@ parameter.  Readings (all listed in the design notes):
   x_{i+D/2} cos a + x_i sin a), a = position * f_i;
 * frequencies: f_i = theta^(-2i/D), rescaled by YaRN's NTK-by-parts rule
   (Peng et al., "YaRN: Efficient Context Window Extension of Large Language
-  Models", section 3): with r_i = L / (2 pi / f_i) the number of turns of
-  frequency i over the original context L and the ramp
-  gamma(r) = clamp((r - alpha) / (beta - alpha), 0, 1), the frequency
-  becomes (1 - gamma_i) f_i / s + gamma_i f_i for a scale factor s; a factor
-  s <= 1 leaves plain RoPE;
+  Models", section 3) as its own code and the GPT-OSS / DeepSeek-V3 models
+  apply it: frequency i turns r_i = L f_i / (2 pi) times over the original
+  context L; the pair index at which r equals beta is
+  c(beta) = (D/2) ln(L / (2 pi beta)) / ln(theta) (solving r_i = beta for
+  i); with low = c(beta_fast) and high = c(beta_slow) (floored and ceiled
+  when `truncate` is set, as DeepSeek-V3 does; GPT-OSS leaves them
+  unrounded), clamped to [0, D - 1], the ramp
+  gamma_i = clamp((i - low) / (high - low), 0, 1) is linear in the index,
+  i.e. in log r, and the frequency becomes f_i (1 - gamma_i) + gamma_i f_i / s
+  for a scale factor s (kept above beta_fast turns, divided by s below
+  beta_slow); a factor s <= 1 leaves plain RoPE;
 * temperature: YaRN's sqrt(1/t) = 0.1 ln s + 1 multiplies the rotated q and k
   (so the logits scale by its square); 1 for s <= 1;
 * fusion: qkv [T, Hq + 2 Hkv, D] holds the q heads, then the k heads, then
@@ -32,9 +38,12 @@ parameter.  Readings (all listed in the design notes):
 
 Parity status: pinned by CPU tests (tests/test_oracle_rope.py) against the
 complex-number form of the rotation, relative-position invariance, norm
-preservation, position 0, YaRN's limiting cases (r > beta unchanged, r < alpha
-divided by s, factor 1 = plain RoPE), brute force with the math module, and
-the scatter into the cache.
+preservation, position 0, YaRN's limiting cases (more than beta_fast turns
+unchanged, fewer than beta_slow divided by s, factor 1 = plain RoPE),
+constructed parameters whose ramp bounds fall on chosen indices (values of
+the ramp's interior worked out by hand), the library routine transformers
+uses for the GPT-OSS configuration, brute force with the math module, and the
+scatter into the cache.
 """
 
 from __future__ import annotations
@@ -44,20 +53,31 @@ import math
 import numpy as np
 
 
-def yarn_inv_freq_ref(head_dim: int, theta: float, factor: float = 1.0, original_max_position: int = 4096,
-                      beta_fast: float = 32.0, beta_slow: float = 1.0):
+def yarn_inv_freq_ref(head_dim: int, theta: float, factor: float = 1.0, original_max_position: float = 4096,
+                      beta_fast: float = 32.0, beta_slow: float = 1.0, truncate: bool = False):
     """Frequencies f_i (i < head_dim / 2, float64) after YaRN's NTK-by-parts
     rescaling, and the temperature factor 0.1 ln s + 1 (1 when s <= 1).
-    beta_slow and beta_fast are YaRN's alpha and beta (turns over the
-    original context)."""
+    beta_fast / beta_slow are the turn counts over the original context at
+    which the ramp over the pair index starts and ends."""
     half = head_dim // 2
     i = np.arange(half, dtype=np.float64)
     base = theta ** (-2.0 * i / head_dim)
     if factor <= 1.0:
         return base, 1.0
-    turns = original_max_position * base / (2.0 * math.pi)    # r_i = L / lambda_i
-    gamma = np.clip((turns - beta_slow) / (beta_fast - beta_slow), 0.0, 1.0)
-    freq = (1.0 - gamma) * base / factor + gamma * base
+
+    def index_of(turns):
+        # the (fractional) pair index whose frequency turns `turns` times
+        # over the original context
+        return (head_dim / 2.0) * math.log(original_max_position / (2.0 * math.pi * turns)) / math.log(theta)
+
+    low, high = index_of(beta_fast), index_of(beta_slow)
+    if truncate:
+        low, high = math.floor(low), math.ceil(high)
+    low, high = max(low, 0.0), min(high, head_dim - 1.0)
+    if high == low:
+        high += 0.001   # a zero-width ramp becomes a step
+    gamma = np.clip((i - low) / (high - low), 0.0, 1.0)
+    freq = base * (1.0 - gamma) + gamma * base / factor
     return freq, 0.1 * math.log(factor) + 1.0
 
 

@@ -318,8 +318,12 @@ def _run(tasks: Sequence, workers: int):
         return [_prefill_task(t) for t in tasks]
     import multiprocessing as mp
     ctx = mp.get_context("spawn")
-    with ctx.Pool(processes=workers, initializer=_pool_init) as pool:
+    pool = ctx.Pool(processes=workers, initializer=_pool_init)
+    try:
         return pool.map(_prefill_task, tasks, chunksize=1)
+    finally:
+        pool.close()
+        pool.join()
 
 
 def default_workers() -> int:

@@ -379,8 +379,8 @@ def _rope(lib, **kw):
     a.update(kw)
     return lib.sinkattn_rope_qkv_append(a["qkv"], a["pos"], a["slots"], a["t"], a["hq"], a["hkv"], a["d"],
                                         ctypes.c_double(a["theta"]), ctypes.c_double(a["s"]), a["L"],
-                                        ctypes.c_double(a["bf"]), ctypes.c_double(a["bs"]), a["q"], a["kc"], a["vc"],
-                                        a["rows"], None)
+                                        ctypes.c_double(a["bf"]), ctypes.c_double(a["bs"]), a.get("trunc", 0), a["q"],
+                                        a["kc"], a["vc"], a["rows"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -393,6 +393,8 @@ def _rope(lib, **kw):
     (dict(s=float("nan")), 1),
     (dict(L=0), 1),                   # YaRN without an original context
     (dict(bf=1.0, bs=1.0), 1),        # empty ramp
+    (dict(bf=32.0, bs=0.0), 1),       # a turn count of 0 has no pair index
+    (dict(bf=32.0, bs=-1.0, trunc=1), 1),
     (dict(qkv=None), 1),
     (dict(slots=None), 1),
     (dict(kc=ctypes.c_void_p((1 << 20) + 8)), 1),

@@ -76,3 +76,51 @@ def test_append_counts_by_enumeration(q_len, k_len, window):
     rows = {j for p in pos for j in range(p + 1) if window <= 0 or j > p - window}
     expect = 2 * q_len * 64 * 64 * 2 + 2 * len(rows) * 8 * 64 * 2 + 64 * 4 + 2 * 2 * 4
     assert b.append_bytes([q_len], [k_len], window) == expect
+
+
+def _fake_full_record(b, n_others):
+    """A full benchmark record with the structure gpu_bench and main build,
+    filled with placeholder numbers (only the line's length is tested)."""
+    st = {"median_ms": 0.123456789, "min_ms": 0.1111111, "mean_ms": 0.12345678, "max_ms": 0.2, "reps": 20}
+    entry = dict(st, algorithmic_bytes=1.0748e9, gbs_median=6000.123456, gbs_best=6500.98765,
+                 pct_hbm_peak=75.0123456, pct_mfma_peak=40.0123456, bound="hbm", shape="x" * 100)
+    roof = {"kernel": "prefill_kernel (causal, L=8192, 64/8 heads)", "bound": "mfma", "achieved": 1234.56789,
+            "peak": 2516.6, "unit": "TFLOP/s", "frac": 0.49056789, "traffic": 159465195.05569646,
+            "ms": 0.558030778169632, "algorithmic_flop": 549822922752.0}
+    splits = {k: dict(entry) for k in ("1", "4", "16")}
+    return {
+        "metric": b.METRIC, "value": 58.123456789, "unit": "% of MI355X peak (mean of prefill bf16-MFMA and "
+        "decode HBM fractions)", "n_gpus": 1, "steps": 50, "warmup": 1000, "ms_per_step": 0.812345678,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) Q/K/V rounded to bf16, N(0,1) fp32 sinks",
+        "config": {"workload": "w" * 220, "prefill": {}, "decode": {}},
+        "prefill": {"causal_timing": st, "window_timing": st, "causal_tflops": 1234.5678, "window_gbs": 3456.789},
+        "decode": {"timing": st, "gbs": 6000.1234, "by_splits": splits, "fp8_kv_by_splits": splits},
+        "roofline": roof, "rooflines": [roof, roof, roof],
+        "cpu_baseline": {"value": 0.0123456, "unit": "% of MI355X peak (same formula as value)", "cores": 16,
+                         "affinity_cores": 128, "kind": "oracle", "sample": "s" * 300, "sample_short": "s" * 100,
+                         "prefill_seconds": 12.3456, "prefill_tflops_f64": 0.0456789, "decode_seconds": 3.456789,
+                         "decode_gbs_f64": 0.3456789, "other_configs": {"x": {"seconds": 1.0}}},
+        "other_configs": {"workload_name_of_this_length_%02d_causal" % i: dict(entry) for i in range(n_others)},
+        "bandwidth_reference": {"read": dict(st)}, "engine_clock": {"mhz_median": 2100, "samples": 40},
+        "device": {"name": "AMD Instinct MI355X"},
+    }
+
+
+def test_compact_line_fits_a_short_log_tail():
+    """The last stdout line carries the headline, the rooflines and the CPU
+    baseline in a few KB (a long line loses its head in a short log tail),
+    with every side workload named; here 42 side workloads (the benchmark has
+    37) with names of 41 characters (the benchmark's average is 33)."""
+    import json
+    b = _bench()
+    full = _fake_full_record(b, 42)
+    line = json.dumps(b.compact_record(full, "gpurun_out/bench_detail.json"), separators=(",", ":"))
+    assert len(line) < 4096, len(line)
+    rec = json.loads(line)
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "dtype", "config",
+                "roofline", "rooflines", "cpu_baseline", "legs"):
+        assert rec[key] is not None, key
+    assert set(rec["roofline"]) >= {"bound", "achieved", "peak", "unit", "frac", "traffic"}
+    assert rec["cpu_baseline"]["cores"] == 16 and rec["cpu_baseline"]["affinity_cores"] == 128
+    assert len(rec["other_pct_of_peak"]) == 42 and len(rec["rooflines"]) == 3

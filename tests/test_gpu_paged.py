@@ -91,7 +91,7 @@ def test_paged_equals_contiguous_decode_bitwise():
 
 def test_paged_debug_checks(monkeypatch):
     monkeypatch.setenv("SINKATTN_DEBUG_CHECKS", "1")
-    p = inputs.make_paged_decode([40, 70], 16, hq=8, hkv=2, seed=72, fill_bits=0x3F80)  # finite fill: 1.0
+    p = inputs.make_paged_decode([40, 70], 16, hq=8, hkv=2, seed=72)  # NaN in every unowned slot: not inspected
     o, _ = _run(p, 0, 1)
     ro, _ = _ref(p, 0)
     assert_close_out(o, ro, "paged debug valid")
@@ -106,6 +106,13 @@ def test_paged_debug_checks(monkeypatch):
         binding.decode_paged(bf16_to_device(p.q), _pages_to_device(p.k_pages), _pages_to_device(p.v_pages),
                              i32_to_device(p.block_table), short, 70, f32_to_device(p.sinks), 0, p.scale, 1)
     assert err.value.status == 1 and "empty" in str(err.value)
+    nan_k = p.k_pages.copy()
+    nan_k[p.block_table[0, 2], 7, 0, 3] = 0x7FC0  # a bf16 NaN in a slot sequence 0 uses
+    with pytest.raises(binding.SinkAttnError) as err:
+        binding.decode_paged(bf16_to_device(p.q), _pages_to_device(nan_k), _pages_to_device(p.v_pages),
+                             i32_to_device(p.block_table), i32_to_device(p.seq_lens), 70, f32_to_device(p.sinks), 0,
+                             p.scale, 1)
+    assert err.value.status == 1 and "k holds" in str(err.value)
 
 
 def _run_fp8(p, window, splits):
@@ -153,7 +160,7 @@ def test_paged_fp8_equals_contiguous_fp8_bitwise():
 
 def test_paged_fp8_debug_checks(monkeypatch):
     monkeypatch.setenv("SINKATTN_DEBUG_CHECKS", "1")
-    p = inputs.make_paged_decode_fp8([40, 70], 16, hq=8, hkv=2, seed=92, fill_code=0x38)  # finite fill: 1.0
+    p = inputs.make_paged_decode_fp8([40, 70], 16, hq=8, hkv=2, seed=92)  # NaN codes in every unowned slot: not inspected
     o, _ = _run_fp8(p, 0, 1)
     ro, _ = decode_paged_fp8_ref(inputs.bf16_bits_to_f32(p.q), p.k_pages, p.v_pages, p.k_scale, p.v_scale,
                                  p.block_table, p.seq_lens, 16, p.sinks, 0, p.scale)

@@ -96,7 +96,7 @@ def test_paged_append_equals_contiguous_append_bitwise():
 
 def test_paged_append_debug_checks(monkeypatch):
     monkeypatch.setenv("SINKATTN_DEBUG_CHECKS", "1")
-    p = inputs.make_paged_append([30, 2], [40, 70], 16, hq=8, hkv=2, seed=10, fill_bits=0x3F80)  # finite fill: 1.0
+    p = inputs.make_paged_append([30, 2], [40, 70], 16, hq=8, hkv=2, seed=10)  # NaN in every unowned slot: not inspected
     o, _ = _run(p, 0)
     ro, _ = _ref(p, 0)
     assert_close_out(o, ro, "paged append debug valid")

@@ -102,7 +102,7 @@ def test_paged_multi_equals_contiguous_multi_bitwise():
 
 def test_paged_multi_debug_checks(monkeypatch):
     monkeypatch.setenv("SINKATTN_DEBUG_CHECKS", "1")
-    p = inputs.make_paged_append([3, 2], [40, 70], 16, hq=8, hkv=2, seed=82, fill_bits=0x3F80)  # finite fill: 1.0
+    p = inputs.make_paged_append([3, 2], [40, 70], 16, hq=8, hkv=2, seed=82)  # NaN in every unowned slot: not inspected
     o, _ = _run(p, 0, 1)
     ro, _ = _ref(p, 0)
     assert_close_out(o, ro, "paged multi debug valid")

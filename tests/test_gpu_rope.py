@@ -22,6 +22,11 @@ pytestmark = pytest.mark.gpu
 YARN = dict(rope_theta=150000.0, yarn_factor=32.0, yarn_original_max_position=4096, yarn_beta_fast=32.0,
             yarn_beta_slow=1.0)
 PLAIN = dict(rope_theta=10000.0, yarn_factor=1.0)
+# the same YaRN setting with the ramp ends rounded outwards (DeepSeek-V3's
+# form), and a setting whose ramp spans most of the pairs
+YARN_TRUNC = dict(YARN, yarn_truncate=True)
+YARN_WIDE = dict(rope_theta=10000.0, yarn_factor=8.0, yarn_original_max_position=2048, yarn_beta_fast=64.0,
+                 yarn_beta_slow=0.5)
 
 
 def _close(got, ref, what):
@@ -42,7 +47,7 @@ def _run_and_check(r, hq, hkv, params):
     torch.cuda.synchronize()
     f, m = yarn_inv_freq_ref(64, params["rope_theta"], params.get("yarn_factor", 1.0),
                              params.get("yarn_original_max_position", 4096), params.get("yarn_beta_fast", 32.0),
-                             params.get("yarn_beta_slow", 1.0))
+                             params.get("yarn_beta_slow", 1.0), params.get("yarn_truncate", False))
     rq, rk, rv = rope_qkv_append_ref(inputs.bf16_bits_to_f32(r.qkv), r.positions, hq, hkv, f, m, r.slot_mapping,
                                      inputs.bf16_bits_to_f32(r.k_cache), inputs.bf16_bits_to_f32(r.v_cache))
     _close(to_f64(q_out), rq, "q")
@@ -61,7 +66,7 @@ def _run_and_check(r, hq, hkv, params):
 
 
 @pytest.mark.parametrize("hq,hkv", [(64, 8), (8, 1), (16, 16)])
-@pytest.mark.parametrize("params", [YARN, PLAIN], ids=["yarn", "plain"])
+@pytest.mark.parametrize("params", [YARN, PLAIN, YARN_TRUNC, YARN_WIDE], ids=["yarn", "plain", "yarn_trunc", "yarn_wide"])
 def test_rope_qkv_append(hq, hkv, params):
     r = inputs.make_rope(1000, hq, hkv, cache_rows=1500, seed=hq + hkv)
     _run_and_check(r, hq, hkv, params)

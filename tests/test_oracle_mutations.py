@@ -12,8 +12,10 @@ for the append oracle (tests/test_oracle_append.py): top-left causal
 alignment, the window one key too wide, queries one position late; and for
 the paged oracle (tests/test_oracle_paged.py): page and slot swapped, the
 slot off by one; and for the rotary oracle (tests/test_oracle_rope.py): the
-rotation the wrong way, the YaRN ramp reversed, the temperature without its
-0.1, V rotated as well; and for the projection oracle
+rotation the wrong way, the YaRN ramp reversed, the ramp linear in the turn
+count instead of the pair index, the 2 pi of the turn count dropped, the
+truncated ramp ends rounded inwards, the temperature without its 0.1, V
+rotated as well; and for the projection oracle
 (tests/test_oracle_oproj.py): output features reversed, the bias reversed.
 """
 
@@ -68,8 +70,13 @@ PAGED_MUTATIONS = [
 ROPE_MUTATIONS = [
     ("out = np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)",
      "out = np.concatenate([x1 * c + x2 * s, x2 * c - x1 * s], axis=-1)"),      # rotation the wrong way
-    ("freq = (1.0 - gamma) * base / factor + gamma * base",
-     "freq = gamma * base / factor + (1.0 - gamma) * base"),                     # ramp reversed
+    ("freq = base * (1.0 - gamma) + gamma * base / factor",
+     "freq = base * gamma + (1.0 - gamma) * base / factor"),                     # ramp reversed
+    ("gamma = np.clip((i - low) / (high - low), 0.0, 1.0)",                      # ramp linear in turns
+     "gamma = 1.0 - np.clip((original_max_position * base / (2.0 * math.pi) - beta_slow) / (beta_fast - beta_slow), "
+     "0.0, 1.0)"),
+    ("original_max_position / (2.0 * math.pi * turns)", "original_max_position / turns"),   # 2 pi dropped
+    ("low, high = math.floor(low), math.ceil(high)", "low, high = math.ceil(low), math.floor(high)"),
     ("return freq, 0.1 * math.log(factor) + 1.0", "return freq, math.log(factor) + 1.0"),
     ("vc[slot] = v[t]", "vc[slot] = rope_ref(v[t:t + 1], positions[t:t + 1], inv_freq, attention_factor)[0]"),
 ]

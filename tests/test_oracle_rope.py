@@ -3,9 +3,12 @@
 Checked against things other than the functions themselves: the rotation in
 complex-number form, the relative-position property of rotary embeddings,
 norm preservation, position 0, YaRN's limiting cases (frequencies that turn
-more than beta times over the original context are kept, fewer than alpha
-divided by the factor; factor 1 is plain RoPE), a brute-force evaluation with
-the math module, and the scatter into the cache.
+more than beta_fast times over the original context are kept, fewer than
+beta_slow times divided by the factor; factor 1 is plain RoPE), the ramp's
+interior on constructed parameters that put its ends on chosen indices
+(values by hand, with and without truncated ends), transformers' YaRN
+initialiser for the GPT-OSS configuration, a brute-force evaluation of the
+rotation with the math module, and the scatter into the cache.
 
 Sources: the RoFormer rotary embedding and the YaRN method (Peng et al.,
 section 3), named by the pages as RoPE (NVIDIA gpt-oss announcement, model
@@ -65,8 +68,11 @@ def test_yarn_limits_and_temperature():
     assert np.allclose(base, [theta ** (-2 * i / d) for i in range(d // 2)], rtol=1e-15)
     f, m = yarn_inv_freq_ref(d, theta, s, L, 32.0, 1.0)
     assert m == pytest.approx(0.1 * math.log(32.0) + 1.0, rel=1e-15)
-    turns = L * base / (2 * math.pi)
-    fast, slow = turns > 32.0, turns < 1.0
+    # a pair whose frequency turns more than beta_fast = 32 times over the
+    # original 4096 positions (wavelength below 128 positions) is kept, one
+    # turning less than once (wavelength above 4096) is divided by s
+    wavelength = 2 * math.pi / base
+    fast, slow = wavelength < L / 32.0, wavelength > L
     assert fast.any() and slow.any() and (~fast & ~slow).any()
     assert np.array_equal(f[fast], base[fast])               # high frequencies kept
     assert np.allclose(f[slow], base[slow] / s, rtol=1e-15)  # low frequencies interpolated
@@ -76,14 +82,70 @@ def test_yarn_limits_and_temperature():
     assert np.array_equal(f1, base) and m1 == 1.0
 
 
-def test_brute_force_yarn_and_rotation():
+# theta = e^32 at head_dim 64 gives f_i = e^-i, and the pair index whose
+# frequency turns r times over L positions is ln(L / (2 pi r)).  Turn counts
+# L / (2 pi e^a) therefore put a ramp end exactly on index a.
+E32 = math.exp(32.0)
+
+
+def _beta_at(index, L=4096):
+    return L / (2 * math.pi * math.exp(index))
+
+
+def test_yarn_ramp_interior_on_constructed_indices():
+    """Ramp ends on indices 2 (beta_fast) and 6 (beta_slow), factor 8: the
+    ramp is linear in the index, so index 3 is a quarter of the way to the
+    interpolated frequency, 4 half, 5 three quarters (values by hand)."""
+    f, m = yarn_inv_freq_ref(64, E32, 8.0, 4096, _beta_at(2.0), _beta_at(6.0))
+    hand = {0: 1.0, 1: math.exp(-1), 2: math.exp(-2),
+            3: math.exp(-3) * (3 / 4 + 1 / 32), 4: math.exp(-4) * (1 / 2 + 1 / 16), 5: math.exp(-5) * (1 / 4 + 3 / 32),
+            6: math.exp(-6) / 8, 20: math.exp(-20) / 8, 31: math.exp(-31) / 8}
+    for i, want in hand.items():
+        assert f[i] == pytest.approx(want, rel=1e-12), i
+    assert m == pytest.approx(0.1 * math.log(8.0) + 1.0, rel=1e-15)
+
+
+def test_yarn_truncated_ramp_on_constructed_indices():
+    """Ramp ends on 2.5 and 5.5: unrounded (the GPT-OSS setting) index 3 sits
+    a sixth of the way, 4 half, 5 five sixths; with truncation the ends
+    become 2 and 6 (floor, ceil) and the quarters of the previous case."""
+    bf, bs = _beta_at(2.5), _beta_at(5.5)
+    f, _ = yarn_inv_freq_ref(64, E32, 8.0, 4096, bf, bs)
+    hand = {2: math.exp(-2), 3: math.exp(-3) * (5 / 6 + 1 / 48), 4: math.exp(-4) * (1 / 2 + 1 / 16),
+            5: math.exp(-5) * (1 / 6 + 5 / 48), 6: math.exp(-6) / 8}
+    for i, want in hand.items():
+        assert f[i] == pytest.approx(want, rel=1e-12), i
+    ft, _ = yarn_inv_freq_ref(64, E32, 8.0, 4096, bf, bs, truncate=True)
+    hand_t = {2: math.exp(-2), 3: math.exp(-3) * (3 / 4 + 1 / 32), 4: math.exp(-4) * (1 / 2 + 1 / 16),
+              5: math.exp(-5) * (1 / 4 + 3 / 32), 6: math.exp(-6) / 8}
+    for i, want in hand_t.items():
+        assert ft[i] == pytest.approx(want, rel=1e-12), i
+
+
+@pytest.mark.parametrize("truncate", [False, True])
+@pytest.mark.parametrize("params", [dict(), dict(rope_theta=10000.0, factor=8.0, original_max_position_embeddings=2048),
+                                    dict(beta_fast=16.0, beta_slow=2.0, factor=4.0)], ids=["gpt_oss", "p1", "p2"])
+def test_yarn_matches_transformers_library_routine(truncate, params):
+    """transformers' YaRN initialiser (the routine its GPT-OSS model uses;
+    float32) on the GPT-OSS configuration (theta 150000, factor 32, 4096
+    original positions, beta 32 / 1, no truncation) and variations."""
+    transformers = pytest.importorskip("transformers")
+    from transformers.modeling_rope_utils import ROPE_INIT_FUNCTIONS
+    cfg = transformers.GptOssConfig()
+    rp = dict(cfg.rope_parameters)
+    rp.update(params)
+    rp["truncate"] = truncate
+    cfg.rope_parameters = rp
+    lib_f, lib_m = ROPE_INIT_FUNCTIONS["yarn"](cfg, "cpu")
+    f, m = yarn_inv_freq_ref(cfg.head_dim, rp["rope_theta"], rp["factor"], rp["original_max_position_embeddings"],
+                             rp["beta_fast"], rp["beta_slow"], truncate)
+    assert np.allclose(f, lib_f.double().numpy(), rtol=1e-6, atol=0)
+    assert m == pytest.approx(lib_m, rel=1e-12)
+
+
+def test_brute_force_rotation():
     d, theta, s, L, bf, bs = 16, 5000.0, 4.0, 64, 8.0, 2.0
     f, m = yarn_inv_freq_ref(d, theta, s, L, bf, bs)
-    for i in range(d // 2):
-        fi = theta ** (-2 * i / d)
-        r = L / (2 * math.pi / fi)
-        g = 0.0 if r < bs else (1.0 if r > bf else (r - bs) / (bf - bs))
-        assert f[i] == pytest.approx((1 - g) * fi / s + g * fi, rel=1e-14)
     rng = np.random.default_rng(3)
     x = rng.standard_normal((2, 1, d))
     out = rope_ref(x, [5, 77], f, m)

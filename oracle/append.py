@@ -54,6 +54,20 @@ def append_mask_ref(q_len: int, k_len: int, window: int) -> np.ndarray:
     return valid
 
 
+def append_mask_cols_ref(q_len: int, k_len: int, window: int, cols) -> np.ndarray:
+    """Columns `cols` (key positions; positions outside [0, k_len) are never
+    visible) of append_mask_ref(q_len, k_len, window), Boolean
+    [q_len, len(cols)], without forming the whole [q_len, k_len] matrix: for
+    the mask probes of long sequences.  q_len = k_len is the prefill mask."""
+    assert 0 <= q_len <= k_len
+    pos = (k_len - q_len) + np.arange(q_len)[:, None]
+    j = np.asarray(cols, dtype=np.int64)[None, :]
+    valid = (j >= 0) & (j < k_len) & (j <= pos)
+    if window > 0:
+        valid &= j > pos - window
+    return valid
+
+
 def prefill_append_ref(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, window: int, scale: float,
                        rows: Optional[Iterable[int]] = None):
     """Append prefill with sinks, float64.

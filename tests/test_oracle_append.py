@@ -25,7 +25,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import append_mask_ref, decode_ref, prefill_append_ref, prefill_varlen_ref
+from oracle import append_mask_cols_ref, append_mask_ref, decode_ref, prefill_append_ref, prefill_varlen_ref
 
 
 def _cu(lengths):
@@ -151,3 +151,23 @@ def test_rows_subset_and_mask():
                           [False, False, False, True, True, False],
                           [False, False, False, False, True, True]]
     assert append_mask_ref(4, 4, 0).tolist() == np.tril(np.ones((4, 4), dtype=bool)).tolist()
+
+
+@pytest.mark.parametrize("q_len,k_len", [(1, 1), (5, 9), (70, 70), (3, 200), (130, 130)])
+@pytest.mark.parametrize("window", [0, 1, 64, 128, 129, 500])
+def test_mask_columns_equal_columns_of_the_whole_mask(q_len, k_len, window):
+    """The column form used by the long-sequence mask probes equals the
+    columns of the whole mask (brute force below); keys outside the sequence
+    are never visible."""
+    cols = np.array([-3, -1, 0, 1, 31, 32, 63, 64, 65, 127, 128, 129, k_len - 1, k_len, k_len + 40])
+    got = append_mask_cols_ref(q_len, k_len, window, cols)
+    whole = append_mask_ref(q_len, k_len, window)
+    for c_i, c in enumerate(cols):
+        if 0 <= c < k_len:
+            assert np.array_equal(got[:, c_i], whole[:, c]), (c, window)
+        else:
+            assert not got[:, c_i].any()
+    off = k_len - q_len
+    brute = np.array([[0 <= c < k_len and c <= off + i and (window <= 0 or c > off + i - window) for c in cols]
+                      for i in range(q_len)])
+    assert np.array_equal(got, brute)

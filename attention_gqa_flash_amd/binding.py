@@ -48,6 +48,9 @@ def library() -> ctypes.CDLL:
     lib.sinkattn_decode_splitkv.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, f32, i32,
                                             vp, sz, vp, vp, vp]
     lib.sinkattn_decode_splitkv.restype = ctypes.c_int
+    lib.sinkattn_decode_splitkv_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, f32, i32, vp, vp,
+                                                    vp]
+    lib.sinkattn_decode_splitkv_noalloc.restype = ctypes.c_int
     lib.sinkattn_decode_splitkv_fp8.argtypes = [vp, vp, vp, f32, f32, vp, i32, i32, vp, i32, i32, i32, i32, f32,
                                                 i32, vp, sz, vp, vp, vp]
     lib.sinkattn_decode_splitkv_fp8.restype = ctypes.c_int
@@ -228,6 +231,41 @@ def decode_splitkv(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_k), bsz, int(max_seqlen_k), _ptr(sinks),
         hq, hkv, d, int(window), float(softmax_scale), int(num_splits), _ptr(workspace), ws_bytes,
         _ptr(out), _ptr(lse), _stream(q.device)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # the static scratch of decode_splitkv_noalloc
+
+
+def decode_splitkv_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           cu_seqlens_k: torch.Tensor, max_seqlen_k: int, sinks: Optional[torch.Tensor],
+                           window: int = 0, softmax_scale: float = 0.125, num_splits: int = 1,
+                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                           return_lse: bool = False):
+    """decode_splitkv without a workspace: the library's static per-device
+    scratch holds the split partials (at most NOALLOC_SCRATCH_BYTES).  The
+    call allocates nothing when ``out`` (and ``lse``, if wanted) are given."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 3)
+    _need(v_cache, "v_cache", torch.bfloat16, 3)
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    bsz, hq, d = q.shape
+    hkv = k_cache.shape[1]
+    if v_cache.shape != k_cache.shape or k_cache.shape[2] != d:
+        raise ValueError("k_cache and v_cache must be [Tk, Hkv, D] matching q")
+    if cu_seqlens_k.shape[0] != bsz + 1:
+        raise ValueError("cu_seqlens_k must have batch + 1 entries")
+    if sinks is not None:
+        _need(sinks, "sinks", torch.float32, 1)
+        if sinks.shape[0] != hq:
+            raise ValueError("sinks must have num_q_heads entries")
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((bsz, hq), dtype=torch.float32, device=q.device)
+    _check(library().sinkattn_decode_splitkv_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_k), bsz, int(max_seqlen_k), _ptr(sinks),
+        hq, hkv, d, int(window), float(softmax_scale), int(num_splits), _ptr(out), _ptr(lse), _stream(q.device)))
     return (out, lse) if (return_lse or lse is not None) else out
 
 

@@ -226,7 +226,7 @@ static sinkattn_status decode_common(const void* q, const void* k_cache, const v
                                      float k_scale, float v_scale, const int32_t* cu_seqlens_q = nullptr,
                                      int32_t max_seqlen_q = 1, int32_t total_q = 0,
                                      const int32_t* block_table = nullptr, int32_t max_pages = 0,
-                                     int32_t page_size = 0, int32_t num_pages = 0) {
+                                     int32_t page_size = 0, int32_t num_pages = 0, bool static_scratch = false) {
   const bool multi = cu_seqlens_q != nullptr;
   const bool paged = block_table != nullptr;  // cu_seqlens_k then holds the lengths [batch]
   if (batch < 0 || max_seqlen_k < 0) return fail(SINKATTN_ERR_INVALID_ARG, "batch and max_seqlen_k must be >= 0");
@@ -311,6 +311,21 @@ static sinkattn_status decode_common(const void* q, const void* k_cache, const v
   if (num_splits == 1) return hip_status(sinkattn::launch_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
 
   const size_t need = sinkattn_decode_workspace_bytes(rows_out, num_q_heads, head_dim, num_splits);
+  if (static_scratch) {
+    // the allocation-free form: the library's static array on the stream's
+    // device (the current device for the null stream)
+    if (need > sinkattn::kNoAllocScratchBytes)
+      return fail(SINKATTN_ERR_WORKSPACE,
+                  "the split-KV partials need %zu bytes, above the %zu-byte static scratch of the allocation-free "
+                  "decode (use fewer splits, or sinkattn_decode_splitkv with a workspace)",
+                  need, sinkattn::kNoAllocScratchBytes);
+    int device = -1;
+    hipError_t e = stream != nullptr ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &device)
+                                     : hipGetDevice(&device);
+    if (e == hipSuccess) e = sinkattn::noalloc_scratch(device, &workspace);
+    if (e != hipSuccess) return hip_status(e, "static scratch lookup");
+    workspace_bytes = sinkattn::kNoAllocScratchBytes;
+  }
   if (workspace == nullptr || workspace_bytes < need)
     return fail(SINKATTN_ERR_WORKSPACE, "workspace of %zu bytes is too small (need %zu)", workspace_bytes, need);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
@@ -335,6 +350,17 @@ sinkattn_status sinkattn_decode_splitkv(const void* q, const void* k_cache, cons
   return decode_common(q, k_cache, v_cache, cu_seqlens_k, batch, max_seqlen_k, sinks, num_q_heads, num_kv_heads,
                        head_dim, window, softmax_scale, num_splits, workspace, workspace_bytes, o, lse, stream, false,
                        1.0f, 1.0f);
+}
+
+sinkattn_status sinkattn_decode_splitkv_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                                const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_k,
+                                                const float* sinks, int32_t num_q_heads, int32_t num_kv_heads,
+                                                int32_t head_dim, int32_t window, float softmax_scale,
+                                                int32_t num_splits, void* o, float* lse, void* stream) {
+  static_assert(SINKATTN_NOALLOC_SCRATCH_BYTES == sinkattn::kNoAllocScratchBytes, "scratch size mismatch");
+  return decode_common(q, k_cache, v_cache, cu_seqlens_k, batch, max_seqlen_k, sinks, num_q_heads, num_kv_heads,
+                       head_dim, window, softmax_scale, num_splits, nullptr, 0, o, lse, stream, false, 1.0f, 1.0f,
+                       nullptr, 1, 0, nullptr, 0, 0, 0, /*static_scratch=*/true);
 }
 
 sinkattn_status sinkattn_decode_splitkv_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale,

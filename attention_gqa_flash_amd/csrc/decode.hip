@@ -23,6 +23,8 @@
 // wave is in flight while the current one is computed, and each tile passes
 // through a wave-private LDS tile: K is read back in MFMA A-operand order, V
 // with the transposing read that O^T = V^T P^T needs.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -744,5 +746,40 @@ hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream) {
 }
 
 int decode_max_group() { return 32; }
+
+// Split-KV partials of sinkattn_decode_splitkv_noalloc: a fixed device array
+// instead of a caller workspace.  Each device the library runs on holds its
+// own copy for the life of the process.  Nothing in it needs to start at
+// zero (every split writes its partial rows before the merge reads them), and
+// calls that overlap on one device share it, so they race.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// The device address of `scratch` on `device`, looked up once per device
+// (hipGetSymbolAddress with that device current) and kept.  In host code the
+// name `scratch` is only a host-side stand-in: kernels get this address.
+hipError_t noalloc_scratch(int device, void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[device] == nullptr) {
+    int current = -1;
+    hipError_t e = hipGetDevice(&current);
+    if (e != hipSuccess) return e;
+    if (current != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (current != device) {
+      const hipError_t r = hipSetDevice(current);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[device] = p;
+  }
+  *ptr = addr[device];
+  return hipSuccess;
+}
 
 }  // namespace sinkattn

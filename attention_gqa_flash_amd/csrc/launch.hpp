@@ -123,6 +123,12 @@ enum CheckBits : unsigned {
   kCheckW = 1u << 14,            // output projection: NaN / Inf in w
   kCheckAll = (1u << 15) - 1u,
 };
+// Size of the static split-KV scratch of the allocation-free decode (32 MiB:
+// the partials of 64 sequences x 64 query heads at 16 splits need 17 MB).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+// Device address of that scratch on `device` (looked up on first use).
+hipError_t noalloc_scratch(int device, void** ptr);
+
 hipError_t check_clear(hipStream_t stream);
 hipError_t check_offsets(const int32_t* cu, int batch, int max_len, int min_len, int total_limit,
                          hipStream_t stream);

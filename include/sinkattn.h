@@ -205,6 +205,32 @@ SINKATTN_API sinkattn_status sinkattn_decode_splitkv(
     void* o, float* lse, void* stream);
 
 /*
+ * Allocation-free form of sinkattn_decode_splitkv, for callers that cannot
+ * allocate device memory around the call (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * computation, kernels and errors, minus the workspace: the split-KV
+ * partials go to a static device array of SINKATTN_NOALLOC_SCRATCH_BYTES
+ * (32 MiB) that the library holds on each device it runs on until the
+ * process ends.  The call itself allocates and frees nothing; its first call
+ * on a device looks the array's address up (hipGetSymbolAddress).
+ *
+ * Limit: sinkattn_decode_workspace_bytes(batch, num_q_heads, head_dim,
+ * num_splits) must not exceed SINKATTN_NOALLOC_SCRATCH_BYTES
+ * (SINKATTN_ERR_WORKSPACE otherwise, before any launch; e.g. 64 sequences x
+ * 64 query heads fit up to 31 splits).  num_splits = 1 uses no scratch.
+ * Calls that overlap on one device (two streams, two threads) share the
+ * array and race; serialise them.
+ */
+#define SINKATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+SINKATTN_API sinkattn_status sinkattn_decode_splitkv_noalloc(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_k,
+    const float* sinks,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t window, float softmax_scale, int32_t num_splits,
+    void* o, float* lse, void* stream);
+
+/*
  * Split-KV decode against an FP8 KV cache (vLLM, "GPT-OSS performance
  * optimizations on NVIDIA Blackwell", FlashInfer integration: the KV cache
  * is stored in FP8).  The page names neither the 8-bit format nor the

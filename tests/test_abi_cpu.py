@@ -28,7 +28,7 @@ def _lib():
 def test_header_declares_the_entry_points():
     assert _declared() == sorted([
         "sinkattn_decode_paged", "sinkattn_decode_paged_fp8", "sinkattn_decode_paged_multi", "sinkattn_decode_splitkv", "sinkattn_decode_splitkv_fp8",
-        "sinkattn_decode_splitkv_multi",
+        "sinkattn_decode_splitkv_multi", "sinkattn_decode_splitkv_noalloc",
         "sinkattn_decode_workspace_bytes", "sinkattn_oproj_bias", "sinkattn_oproj_workspace_bytes",
         "sinkattn_rope_qkv_append",
         "sinkattn_last_error", "sinkattn_merge_lse", "sinkattn_prefill_append", "sinkattn_prefill_append_paged",
@@ -434,3 +434,40 @@ def test_oproj_workspace_size():
     assert lib.sinkattn_oproj_workspace_bytes(64, 4096, 2880) == 4 * 64 * 2880 * 4
     assert lib.sinkattn_oproj_workspace_bytes(8192, 4096, 2880) == 0
     assert lib.sinkattn_oproj_workspace_bytes(0, 4096, 2880) == 0
+
+
+def _noalloc(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE2, b=64, mk=8192, sinks=None, hq=64, hkv=8, d=64, w=0, scale=0.125, s=16,
+             o=FAKE, lse=None)
+    a.update(kw)
+    return lib.sinkattn_decode_splitkv_noalloc(a["q"], a["k"], a["v"], a["cu"], a["b"], a["mk"], a["sinks"], a["hq"],
+                                               a["hkv"], a["d"], a["w"], ctypes.c_float(a["scale"]), a["s"], a["o"],
+                                               a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(s=32), 3),                  # 64 x 64 heads x 32 splits: 34.1 MB of partials, above the 32 MiB scratch
+    (dict(b=4096, s=2), 3),
+    (dict(d=128), 2),
+    (dict(hq=60), 1),
+    (dict(s=0), 1),
+    (dict(scale=0.0), 1),
+    (dict(q=None), 1),
+])
+def test_noalloc_decode_rejects_before_any_launch(kw, status):
+    """The allocation-free decode validates its arguments and its scratch
+    limit on the host (no device is touched on these paths)."""
+    lib = _lib()
+    assert _noalloc(lib, **kw) == status
+    msg = lib.sinkattn_last_error()
+    assert msg
+    if status == 3:
+        assert b"static scratch" in msg
+
+
+def test_noalloc_scratch_limit_matches_workspace_sizes():
+    """31 splits of the 64 x 64-head decode fit the 32 MiB scratch, 32 do not."""
+    lib = _lib()
+    limit = 32 << 20
+    assert lib.sinkattn_decode_workspace_bytes(64, 64, 64, 31) <= limit < lib.sinkattn_decode_workspace_bytes(64, 64, 64, 32)
+    assert _noalloc(lib, b=0) == 0

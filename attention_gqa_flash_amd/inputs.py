@@ -330,6 +330,70 @@ def make_paged_decode_fp8(lengths, page_size: int, hq: int, hkv: int, d: int = 6
                                 dec.sinks, page_size, scale, list(dec.lengths))
 
 
+@dataclass
+class AppendFp8Inputs:
+    q: np.ndarray             # uint16 bf16 bits [Tq, Hq, D]
+    k: np.ndarray             # uint8 E4M3 codes [Tk, Hkv, D]
+    v: np.ndarray
+    k_scale: float
+    v_scale: float
+    sinks: np.ndarray         # float32 [Hq]
+    cu_seqlens_q: np.ndarray  # int32 [B+1]
+    cu_seqlens_k: np.ndarray  # int32 [B+1]
+    scale: float
+    q_lens: list = field(default_factory=list)
+    k_lens: list = field(default_factory=list)
+
+
+def make_append_fp8(q_lens, k_lens, hq: int, hkv: int, d: int = 64, seed: int = 0, scale: float = 0.125,
+                    k_scale: float = 1.0 / 16, v_scale: float = 1.0 / 16,
+                    rng: Optional[np.random.Generator] = None) -> AppendFp8Inputs:
+    """Queries appended to an E4M3 cache: the layout of make_append with the
+    cache of make_decode_fp8 (N(0,1) / scale rounded to E4M3).  Draw order
+    q -> k -> v -> sinks."""
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    q_lens = [int(x) for x in q_lens]
+    k_lens = [int(x) for x in k_lens]
+    assert len(q_lens) == len(k_lens) and all(0 <= a <= b for a, b in zip(q_lens, k_lens))
+    tk = sum(k_lens)
+    q = _normal_bf16(rng, (sum(q_lens), hq, d))
+    k = to_e4m3_codes(rng.standard_normal(size=(tk, hkv, d), dtype=np.float32) / np.float32(k_scale))
+    v = to_e4m3_codes(rng.standard_normal(size=(tk, hkv, d), dtype=np.float32) / np.float32(v_scale))
+    sinks = rng.standard_normal(size=hq, dtype=np.float32)
+    return AppendFp8Inputs(q, k, v, float(k_scale), float(v_scale), sinks.astype(np.float32), _cu(q_lens),
+                           _cu(k_lens), scale, q_lens, k_lens)
+
+
+@dataclass
+class PagedAppendFp8Inputs:
+    q: np.ndarray             # uint16 bf16 bits [Tq, Hq, D]
+    k_pages: np.ndarray       # uint8 E4M3 codes [P, page_size, Hkv, D]
+    v_pages: np.ndarray
+    k_scale: float
+    v_scale: float
+    block_table: np.ndarray   # int32 [B, max_pages] (-1 past a sequence's pages)
+    seq_lens: np.ndarray      # int32 [B] (key lengths)
+    cu_seqlens_q: np.ndarray  # int32 [B+1]
+    sinks: np.ndarray         # float32 [Hq]
+    page_size: int
+    scale: float
+    q_lens: list = field(default_factory=list)
+    k_lens: list = field(default_factory=list)
+
+
+def make_paged_append_fp8(q_lens, k_lens, page_size: int, hq: int, hkv: int, d: int = 64, seed: int = 0,
+                          scale: float = 0.125, spare_pages: int = 3, fill_code: int = 0x7F,
+                          rng: Optional[np.random.Generator] = None) -> PagedAppendFp8Inputs:
+    """The draws of make_append_fp8 with the cache scattered into pages as
+    make_paged_decode does (permutation drawn after the sinks; unowned slots
+    hold ``fill_code``, an E4M3 NaN by default)."""
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    a = make_append_fp8(q_lens, k_lens, hq, hkv, d, rng=rng, scale=scale)
+    kp, vp, bt = _scatter_pages(a.k, a.v, a.cu_seqlens_k, a.k_lens, page_size, rng, spare_pages, fill_code)
+    return PagedAppendFp8Inputs(a.q, kp, vp, a.k_scale, a.v_scale, bt, np.asarray(a.k_lens, dtype=np.int32),
+                                a.cu_seqlens_q, a.sinks, page_size, scale, list(a.q_lens), list(a.k_lens))
+
+
 def ragged_lengths(rng: np.random.Generator, n: int = 32, lo: int = 128, hi: int = 32768):
     """Log-uniform lengths round(exp(U[ln lo, ln hi]))."""
     u = rng.uniform(math.log(lo), math.log(hi), size=n)

@@ -7,10 +7,11 @@ only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 """
 
 from .append import append_mask_cols_ref, append_mask_ref, prefill_append_ref  # noqa: F401
-from .paged import decode_paged_fp8_ref, decode_paged_multi_ref, decode_paged_ref, gather_pages  # noqa: F401
+from .paged import (decode_paged_fp8_multi_ref, decode_paged_fp8_ref, decode_paged_multi_ref, decode_paged_ref,  # noqa: F401
+                    gather_pages)  # noqa: F401
 from .rope import rope_qkv_append_ref, rope_ref, yarn_inv_freq_ref  # noqa: F401
 from .oproj import oproj_ref  # noqa: F401
-from .fp8 import decode_fp8_ref, e4m3_to_float64  # noqa: F401
+from .fp8 import decode_fp8_multi_ref, decode_fp8_ref, e4m3_to_float64  # noqa: F401
 from .sink_attention import (  # noqa: F401
     LOG2E,
     decode_key_range,

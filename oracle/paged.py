@@ -35,7 +35,7 @@ from __future__ import annotations
 import numpy as np
 
 from .append import prefill_append_ref
-from .fp8 import decode_fp8_ref
+from .fp8 import decode_fp8_multi_ref, decode_fp8_ref
 from .sink_attention import decode_ref
 
 
@@ -85,3 +85,13 @@ def decode_paged_fp8_ref(q, k_pages, v_pages, k_scale: float, v_scale: float, bl
     k, cu = gather_pages(k_pages, block_table, seq_lens, page_size)
     v, _ = gather_pages(v_pages, block_table, seq_lens, page_size)
     return decode_fp8_ref(q, k, v, k_scale, v_scale, cu, sinks, window, scale)
+
+
+def decode_paged_fp8_multi_ref(q, k_pages, v_pages, k_scale: float, v_scale: float, block_table, seq_lens,
+                               cu_seqlens_q, page_size: int, sinks, window: int, scale: float, rows=None):
+    """Several query tokens per sequence against a paged cache of E4M3
+    codes (float64): queries as ``decode_paged_multi_ref``, pages, table and
+    scales as ``decode_paged_fp8_ref``."""
+    k, cu = gather_pages(k_pages, block_table, seq_lens, page_size)
+    v, _ = gather_pages(v_pages, block_table, seq_lens, page_size)
+    return decode_fp8_multi_ref(q, k, v, k_scale, v_scale, cu_seqlens_q, cu, sinks, window, scale, rows=rows)

@@ -77,3 +77,72 @@ def test_generated_cache_is_close_to_its_normal_draw():
     k = d.k_scale * e4m3_to_float64(d.k)
     assert np.isfinite(k).all()
     assert 0.95 < k.std() < 1.05 and abs(k.mean()) < 0.02
+
+
+# --- several query tokens per sequence (draft tokens) against an E4M3 cache ---
+
+from oracle import decode_fp8_multi_ref  # noqa: E402
+
+
+def _e4m3_by_hand(code: int) -> float:
+    """E4M3 from the format definition with the math module (independent of
+    the oracle's vectorised decoding): bias 7, subnormals 2^-6 * m / 8."""
+    s = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 15, code & 7
+    return s * (math.ldexp(m / 8.0, -6) if e == 0 else math.ldexp(1.0 + m / 8.0, e - 7))
+
+
+def test_multi_with_one_query_is_the_single_token_decode():
+    a = inputs.make_append_fp8([1, 1, 1], [1, 37, 300], hq=8, hkv=2, seed=6, k_scale=0.0625, v_scale=0.125)
+    d_cu = a.cu_seqlens_k
+    qf = inputs.bf16_bits_to_f32(a.q)
+    for window in (0, 1, 16):
+        o1, l1 = decode_fp8_multi_ref(qf, a.k, a.v, a.k_scale, a.v_scale, a.cu_seqlens_q, d_cu, a.sinks, window, a.scale)
+        o2, l2 = decode_fp8_ref(qf, a.k, a.v, a.k_scale, a.v_scale, d_cu, a.sinks, window, a.scale)
+        assert np.allclose(o1, o2, rtol=0, atol=1e-14) and np.allclose(l1, l2, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("window", [0, 1, 2, 5, 40])
+def test_multi_brute_force(window):
+    """Python loops over the codes decoded by hand, the bottom-right causal /
+    window mask written out, math.fsum for the sums."""
+    q_lens, k_lens = [3, 1, 4], [5, 9, 12]
+    hq, hkv, d = 4, 2, 8
+    a = inputs.make_append_fp8(q_lens, k_lens, hq=hq, hkv=hkv, d=d, seed=7, k_scale=0.125, v_scale=0.25)
+    qf = inputs.bf16_bits_to_f32(a.q).astype(np.float64)
+    o, lse = decode_fp8_multi_ref(qf, a.k, a.v, a.k_scale, a.v_scale, a.cu_seqlens_q, a.cu_seqlens_k, a.sinks, window,
+                                  a.scale)
+    g = hq // hkv
+    for b in range(len(q_lens)):
+        for r in range(q_lens[b]):
+            row = a.cu_seqlens_q[b] + r
+            pos = k_lens[b] - q_lens[b] + r
+            keys = [j for j in range(k_lens[b]) if j <= pos and (window <= 0 or j > pos - window)]
+            for h in range(hq):
+                kh = h // g
+                logits = []
+                for j in keys:
+                    kr = a.cu_seqlens_k[b] + j
+                    dot = math.fsum(qf[row, h, c] * a.k_scale * _e4m3_by_hand(int(a.k[kr, kh, c])) for c in range(d))
+                    logits.append(a.scale * dot)
+                z = float(a.sinks[h])
+                big = max(logits + [z])
+                w = [math.exp(x - big) for x in logits]
+                den = math.fsum(w) + math.exp(z - big)
+                for c in range(d):
+                    num = math.fsum(wj * a.v_scale * _e4m3_by_hand(int(a.v[a.cu_seqlens_k[b] + j, kh, c]))
+                                    for wj, j in zip(w, keys))
+                    assert abs(o[row, h, c] - num / den) < 1e-12
+                assert abs(lse[row, h] - (big + math.log(den))) < 1e-12
+
+
+def test_multi_scales_act_on_logits_and_outputs():
+    a = inputs.make_append_fp8([2, 3], [20, 33], hq=8, hkv=2, seed=8)
+    qf = inputs.bf16_bits_to_f32(a.q)
+    args = (a.cu_seqlens_q, a.cu_seqlens_k, a.sinks, 7)
+    o1, l1 = decode_fp8_multi_ref(qf, a.k, a.v, 0.0625, 0.0625, *args, a.scale)
+    o2, l2 = decode_fp8_multi_ref(qf, a.k, a.v, 0.0625, 0.5, *args, a.scale)
+    assert np.allclose(o2, 8 * o1, rtol=1e-15, atol=0) and np.array_equal(l1, l2)
+    o3, l3 = decode_fp8_multi_ref(qf, a.k, a.v, 0.125, 0.0625, *args, a.scale)
+    o4, l4 = decode_fp8_multi_ref(qf, a.k, a.v, 0.0625, 0.0625, *args, 2 * a.scale)
+    assert np.allclose(o3, o4, rtol=0, atol=1e-15) and np.allclose(l3, l4, rtol=0, atol=1e-13)

@@ -7,11 +7,13 @@ the softmax scale (in the max or in the denominator), the sink dropped, the
 window one key too wide, the sink in every split, the decode window one key
 too wide, the wrong GQA grouping, a base-2 lse, an unweighted merge; and
 for the FP8 oracle (checked by tests/test_oracle_fp8.py): exponent bias 8
-instead of 7, subnormals scaled like normals, the two scales swapped; and
+instead of 7, subnormals scaled like normals, the two scales swapped, and
+with several query tokens the window dropped or the query offsets read as
+the key offsets; and
 for the append oracle (tests/test_oracle_append.py): top-left causal
 alignment, the window one key too wide, queries one position late; and for
 the paged oracle (tests/test_oracle_paged.py): page and slot swapped, the
-slot off by one; and for the rotary oracle (tests/test_oracle_rope.py): the
+slot off by one, K and V swapped in the E4M3 multi-token form; and for the rotary oracle (tests/test_oracle_rope.py): the
 rotation the wrong way, the YaRN ramp reversed, the ramp linear in the turn
 count instead of the pair index, the 2 pi of the turn count dropped, the
 truncated ramp ends rounded inwards, the temperature without its 0.1, V
@@ -45,6 +47,11 @@ FP8_MUTATIONS = [
     ("np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64))", "np.ldexp(1.0 + m / 8.0, (e - 8).astype(np.int64))"),
     ("subnormal = np.ldexp(m / 8.0, -6)", "subnormal = np.ldexp(1.0 + m / 8.0, -7)"),
     ("k = float(k_scale) * e4m3_to_float64(k_codes)", "k = float(v_scale) * e4m3_to_float64(k_codes)"),
+    # several query tokens: the window dropped, the queries aligned top-left
+    ("return prefill_append_ref(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, window, scale, rows=rows)",
+     "return prefill_append_ref(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, 0, scale, rows=rows)"),
+    ("return prefill_append_ref(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, window, scale, rows=rows)",
+     "return prefill_append_ref(q, k, v, sinks, cu_seqlens_q, cu_seqlens_q, window, scale, rows=rows)"),
 ]
 
 
@@ -64,6 +71,8 @@ PAGED_MUTATIONS = [
      "return prefill_append_ref(q, k, v, sinks, cu_seqlens_q, cu, 0, scale, rows=rows)"),
     ("return decode_fp8_ref(q, k, v, k_scale, v_scale, cu, sinks, window, scale)",
      "return decode_fp8_ref(q, k, v, v_scale, k_scale, cu, sinks, window, scale)"),
+    ("return decode_fp8_multi_ref(q, k, v, k_scale, v_scale, cu_seqlens_q, cu, sinks, window, scale, rows=rows)",
+     "return decode_fp8_multi_ref(q, v, k, k_scale, v_scale, cu_seqlens_q, cu, sinks, window, scale, rows=rows)"),
 ]
 
 

@@ -181,3 +181,38 @@ def test_fp8_equals_contiguous_fp8_decode_and_the_decoded_paged_decode(page_size
         o2, lse2 = decode_paged_ref(q, ks * e4m3_to_float64(kp), vs * e4m3_to_float64(vp), bt, lens, page_size,
                                     sinks, window, 0.3)
         assert np.max(np.abs(o - o2)) < 1e-12 and np.max(np.abs(lse - lse2)) < 1e-12
+
+
+@pytest.mark.parametrize("page_size", [1, 16, 48])
+@pytest.mark.parametrize("window", [0, 5])
+def test_fp8_multi_equals_contiguous_fp8_multi_under_any_page_order(page_size, window):
+    from attention_gqa_flash_amd import inputs
+    from oracle import decode_fp8_multi_ref, decode_paged_fp8_multi_ref
+    q_lens, k_lens = [2, 1, 4, 0], [9, 64, 130, 5]
+    a = inputs.make_append_fp8(q_lens, k_lens, hq=8, hkv=2, d=8, seed=300 + page_size + window)
+    qf = inputs.bf16_bits_to_f32(a.q)
+    ro, rl = decode_fp8_multi_ref(qf, a.k, a.v, a.k_scale, a.v_scale, a.cu_seqlens_q, a.cu_seqlens_k, a.sinks,
+                                  window, a.scale)
+    rng = np.random.default_rng(page_size)
+    for shuffle in (None, rng):
+        kp, vp, bt = _paged_from_contiguous(a.k.astype(np.float64), a.v.astype(np.float64), k_lens, page_size, shuffle)
+        kp = np.nan_to_num(kp, nan=127.0).astype(np.uint8)   # unowned slots: E4M3 NaN codes
+        vp = np.nan_to_num(vp, nan=127.0).astype(np.uint8)
+        o, lse = decode_paged_fp8_multi_ref(qf, kp, vp, a.k_scale, a.v_scale, bt, k_lens, a.cu_seqlens_q, page_size,
+                                            a.sinks, window, a.scale)
+        assert np.max(np.abs(o - ro)) < 1e-13 and np.array_equal(np.isneginf(lse), np.isneginf(rl))
+        fin = np.isfinite(rl)
+        assert np.max(np.abs(lse[fin] - rl[fin])) < 1e-13
+
+
+def test_fp8_multi_with_one_query_is_the_paged_fp8_decode():
+    from attention_gqa_flash_amd import inputs
+    from oracle import decode_paged_fp8_multi_ref
+    p = inputs.make_paged_append_fp8([1, 1, 1], [3, 40, 77], 16, hq=8, hkv=2, seed=301)
+    qf = inputs.bf16_bits_to_f32(p.q)
+    for window in (0, 9):
+        o1, l1 = decode_paged_fp8_multi_ref(qf, p.k_pages, p.v_pages, p.k_scale, p.v_scale, p.block_table, p.seq_lens,
+                                            p.cu_seqlens_q, 16, p.sinks, window, p.scale)
+        o2, l2 = decode_paged_fp8_ref(qf, p.k_pages, p.v_pages, p.k_scale, p.v_scale, p.block_table, p.seq_lens, 16,
+                                      p.sinks, window, p.scale)
+        assert np.allclose(o1, o2, rtol=0, atol=1e-14) and np.allclose(l1, l2, rtol=0, atol=1e-13)

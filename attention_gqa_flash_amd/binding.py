@@ -69,6 +69,12 @@ def library() -> ctypes.CDLL:
     lib.sinkattn_decode_paged_multi.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, i32,
                                                 i32, i32, i32, f32, i32, vp, sz, vp, vp, vp]
     lib.sinkattn_decode_paged_multi.restype = ctypes.c_int
+    lib.sinkattn_decode_splitkv_multi_fp8.argtypes = [vp, vp, vp, f32, f32, vp, vp, i32, i32, i32, i32, vp, i32, i32,
+                                                      i32, i32, f32, i32, vp, sz, vp, vp, vp]
+    lib.sinkattn_decode_splitkv_multi_fp8.restype = ctypes.c_int
+    lib.sinkattn_decode_paged_multi_fp8.argtypes = [vp, vp, vp, f32, f32, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                                    vp, i32, i32, i32, i32, f32, i32, vp, sz, vp, vp, vp]
+    lib.sinkattn_decode_paged_multi_fp8.restype = ctypes.c_int
     f64 = ctypes.c_double
     lib.sinkattn_rope_qkv_append.argtypes = [vp, vp, vp, i32, i32, i32, i32, f64, f64, i32, f64, f64, i32, vp, vp, vp, i32,
                                              vp]
@@ -315,9 +321,28 @@ def decode_splitkv_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
     """Multi-token-query split-KV decode: q [Tq, Hq, 64] bf16 packed by
     cu_seqlens_q, caches [Tk, Hkv, 64] bf16 packed by cu_seqlens_k; each
     sequence's queries are its newest tokens (bottom-right causal)."""
+    return _decode_multi(q, k_cache, v_cache, None, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, sinks,
+                         window, softmax_scale, num_splits, workspace, out, lse, return_lse)
+
+
+def decode_splitkv_multi_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: float,
+                             v_scale: float, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_q: int,
+                             max_seqlen_k: int, sinks: Optional[torch.Tensor], window: int = 0,
+                             softmax_scale: float = 0.125, num_splits: int = 1,
+                             workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                             lse: Optional[torch.Tensor] = None, return_lse: bool = False):
+    """decode_splitkv_multi against an E4M3 cache: k/v uint8 codes
+    [Tk, Hkv, 64], K = k_scale * e4m3(code), V = v_scale * e4m3(code)."""
+    return _decode_multi(q, k_cache, v_cache, (k_scale, v_scale), cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                         max_seqlen_k, sinks, window, softmax_scale, num_splits, workspace, out, lse, return_lse)
+
+
+def _decode_multi(q, k_cache, v_cache, scales, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, sinks, window,
+                  softmax_scale, num_splits, workspace, out, lse, return_lse):
     _need(q, "q", torch.bfloat16, 3)
-    _need(k_cache, "k_cache", torch.bfloat16, 3)
-    _need(v_cache, "v_cache", torch.bfloat16, 3)
+    kv_dtype = torch.bfloat16 if scales is None else torch.uint8
+    _need(k_cache, "k_cache", kv_dtype, 3)
+    _need(v_cache, "v_cache", kv_dtype, 3)
     _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
     _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
     tq, hq, d = q.shape
@@ -338,10 +363,14 @@ def decode_splitkv_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
         out = torch.empty_like(q)
     if return_lse and lse is None:
         lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
-    _check(library().sinkattn_decode_splitkv_multi(
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), cu_seqlens_q.shape[0] - 1,
-        int(max_seqlen_q), int(max_seqlen_k), tq, _ptr(sinks), hq, hkv, d, int(window), float(softmax_scale),
-        int(num_splits), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(q.device)))
+    tail = (_ptr(cu_seqlens_q), _ptr(cu_seqlens_k), cu_seqlens_q.shape[0] - 1, int(max_seqlen_q), int(max_seqlen_k),
+            tq, _ptr(sinks), hq, hkv, d, int(window), float(softmax_scale), int(num_splits), _ptr(workspace),
+            ws_bytes, _ptr(out), _ptr(lse), _stream(q.device))
+    if scales is None:
+        _check(library().sinkattn_decode_splitkv_multi(_ptr(q), _ptr(k_cache), _ptr(v_cache), *tail))
+    else:
+        _check(library().sinkattn_decode_splitkv_multi_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), float(scales[0]),
+                                                           float(scales[1]), *tail))
     return (out, lse) if (return_lse or lse is not None) else out
 
 
@@ -466,9 +495,30 @@ def decode_paged_multi(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Te
     """Multi-token-query decode against a paged cache: q [Tq, Hq, 64] bf16
     packed by cu_seqlens_q; k/v pages [P, page_size, Hkv, 64] bf16;
     block_table [B, max_pages] int32; seq_lens [B] int32 (all device)."""
+    return _decode_paged_multi(q, k_pages, v_pages, None, block_table, seq_lens, cu_seqlens_q, max_seqlen_q,
+                               max_seqlen_k, sinks, window, softmax_scale, num_splits, workspace, out, lse, return_lse)
+
+
+def decode_paged_multi_fp8(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, k_scale: float,
+                           v_scale: float, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                           cu_seqlens_q: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                           sinks: Optional[torch.Tensor], window: int = 0, softmax_scale: float = 0.125,
+                           num_splits: int = 1, workspace: Optional[torch.Tensor] = None,
+                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                           return_lse: bool = False):
+    """decode_paged_multi over pages of E4M3 codes (uint8 [P, page_size,
+    Hkv, 64]) with per-tensor scales."""
+    return _decode_paged_multi(q, k_pages, v_pages, (k_scale, v_scale), block_table, seq_lens, cu_seqlens_q,
+                               max_seqlen_q, max_seqlen_k, sinks, window, softmax_scale, num_splits, workspace, out, lse,
+                               return_lse)
+
+
+def _decode_paged_multi(q, k_pages, v_pages, scales, block_table, seq_lens, cu_seqlens_q, max_seqlen_q, max_seqlen_k,
+                        sinks, window, softmax_scale, num_splits, workspace, out, lse, return_lse):
     _need(q, "q", torch.bfloat16, 3)
-    _need(k_pages, "k_pages", torch.bfloat16, 4)
-    _need(v_pages, "v_pages", torch.bfloat16, 4)
+    kv_dtype = torch.bfloat16 if scales is None else torch.uint8
+    _need(k_pages, "k_pages", kv_dtype, 4)
+    _need(v_pages, "v_pages", kv_dtype, 4)
     _need(block_table, "block_table", torch.int32, 2)
     _need(seq_lens, "seq_lens", torch.int32, 1)
     _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
@@ -491,11 +541,14 @@ def decode_paged_multi(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Te
         out = torch.empty_like(q)
     if return_lse and lse is None:
         lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
-    _check(library().sinkattn_decode_paged_multi(
-        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), _ptr(cu_seqlens_q), bsz,
-        block_table.shape[1], page_size, num_pages, int(max_seqlen_q), int(max_seqlen_k), tq, _ptr(sinks), hq, hkv,
-        d, int(window), float(softmax_scale), int(num_splits), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
-        _stream(q.device)))
+    tail = (_ptr(block_table), _ptr(seq_lens), _ptr(cu_seqlens_q), bsz, block_table.shape[1], page_size, num_pages,
+            int(max_seqlen_q), int(max_seqlen_k), tq, _ptr(sinks), hq, hkv, d, int(window), float(softmax_scale),
+            int(num_splits), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(q.device))
+    if scales is None:
+        _check(library().sinkattn_decode_paged_multi(_ptr(q), _ptr(k_pages), _ptr(v_pages), *tail))
+    else:
+        _check(library().sinkattn_decode_paged_multi_fp8(_ptr(q), _ptr(k_pages), _ptr(v_pages), float(scales[0]),
+                                                         float(scales[1]), *tail))
     return (out, lse) if (return_lse or lse is not None) else out
 
 

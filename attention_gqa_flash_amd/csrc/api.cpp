@@ -243,9 +243,9 @@ static sinkattn_status decode_common(const void* q, const void* k_cache, const v
   if (num_q_heads / num_kv_heads > sinkattn::decode_max_group())
     return fail(SINKATTN_ERR_UNSUPPORTED, "decode supports at most %d query heads per KV head",
                 sinkattn::decode_max_group());
-  if (multi && static_cast<long long>(max_seqlen_q) * (num_q_heads / num_kv_heads) > 32)
-    return fail(SINKATTN_ERR_UNSUPPORTED, "max_seqlen_q * (num_q_heads / num_kv_heads) must be at most 32 (got %d * %d)",
-                max_seqlen_q, num_q_heads / num_kv_heads);
+  if (multi && static_cast<long long>(max_seqlen_q) * (num_q_heads / num_kv_heads) > sinkattn::decode_max_cols())
+    return fail(SINKATTN_ERR_UNSUPPORTED, "max_seqlen_q * (num_q_heads / num_kv_heads) must be at most %d (got %d * %d)",
+                sinkattn::decode_max_cols(), max_seqlen_q, num_q_heads / num_kv_heads);
   if (multi && max_seqlen_q > total_q)
     return fail(SINKATTN_ERR_INVALID_ARG, "max_seqlen_q (%d) exceeds total_q (%d)", max_seqlen_q, total_q);
   if (batch == 0 || (multi && (max_seqlen_q == 0 || total_q == 0))) return ok();
@@ -408,6 +408,21 @@ static sinkattn_status check_pages(const int32_t* block_table, const int32_t* se
   return ok();
 }
 
+sinkattn_status sinkattn_decode_splitkv_multi_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                                  float k_scale, float v_scale, const int32_t* cu_seqlens_q,
+                                                  const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_q,
+                                                  int32_t max_seqlen_k, int32_t total_q, const float* sinks,
+                                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                                  int32_t window, float softmax_scale, int32_t num_splits,
+                                                  void* workspace, size_t workspace_bytes, void* o, float* lse,
+                                                  void* stream) {
+  if (cu_seqlens_q == nullptr && batch > 0)
+    return fail(SINKATTN_ERR_INVALID_ARG, "cu_seqlens_q must not be NULL");
+  return decode_common(q, k_cache, v_cache, cu_seqlens_k, batch, max_seqlen_k, sinks, num_q_heads, num_kv_heads,
+                       head_dim, window, softmax_scale, num_splits, workspace, workspace_bytes, o, lse, stream, true,
+                       k_scale, v_scale, cu_seqlens_q, max_seqlen_q, total_q);
+}
+
 sinkattn_status sinkattn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
                                       const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
                                       int32_t max_pages, int32_t page_size, int32_t num_pages, int32_t max_seqlen_k,
@@ -450,6 +465,24 @@ sinkattn_status sinkattn_decode_paged_multi(const void* q, const void* k_pages, 
   return decode_common(q, k_pages, v_pages, seq_lens, batch, max_seqlen_k, sinks, num_q_heads, num_kv_heads,
                        head_dim, window, softmax_scale, num_splits, workspace, workspace_bytes, o, lse, stream, false,
                        1.0f, 1.0f, cu_seqlens_q, max_seqlen_q, total_q, block_table, max_pages, page_size, num_pages);
+}
+
+sinkattn_status sinkattn_decode_paged_multi_fp8(const void* q, const void* k_pages, const void* v_pages,
+                                                float k_scale, float v_scale, const int32_t* block_table,
+                                                const int32_t* seq_lens, const int32_t* cu_seqlens_q, int32_t batch,
+                                                int32_t max_pages, int32_t page_size, int32_t num_pages,
+                                                int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t total_q,
+                                                const float* sinks, int32_t num_q_heads, int32_t num_kv_heads,
+                                                int32_t head_dim, int32_t window, float softmax_scale,
+                                                int32_t num_splits, void* workspace, size_t workspace_bytes, void* o,
+                                                float* lse, void* stream) {
+  sinkattn_status st = check_pages(block_table, seq_lens, batch, max_pages, page_size, num_pages, max_seqlen_k);
+  if (st != SINKATTN_OK) return st;
+  if (cu_seqlens_q == nullptr && batch > 0) return fail(SINKATTN_ERR_INVALID_ARG, "cu_seqlens_q must not be NULL");
+  return decode_common(q, k_pages, v_pages, seq_lens, batch, max_seqlen_k, sinks, num_q_heads, num_kv_heads,
+                       head_dim, window, softmax_scale, num_splits, workspace, workspace_bytes, o, lse, stream, true,
+                       k_scale, v_scale, cu_seqlens_q, max_seqlen_q, total_q, block_table, max_pages, page_size,
+                       num_pages);
 }
 
 sinkattn_status sinkattn_prefill_append_paged(const void* q, const void* k_pages, const void* v_pages,

@@ -24,6 +24,7 @@
 // through a wave-private LDS tile: K is read back in MFMA A-operand order, V
 // with the transposing read that O^T = V^T P^T needs.
 #include <mutex>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -213,6 +214,55 @@ __device__ __forceinline__ void stage_tile(const TileRegs<kFp8>& cur, uint16_t* 
   }
 }
 
+// MFMA column layouts of a decode wave (the N side of S^T = K Q^T: one
+// column per (query token, query head) pair).
+//   kN = 16: one v_mfma_f32_16x16x32_bf16 block: lane l holds column l % 16;
+//            S^T C registers i of key block kb are key 8 (l / 16) + 4 kb + i
+//            (rows permuted by key16_of_row) and O^T registers i of d block
+//            db are d = 16 db + 4 (l / 16) + i.  Half the matrix-core work
+//            and half the softmax lanes of the 32-column layout: the layout
+//            for GQA groups of at most 16 (G = 8: 8 of 16 columns real
+//            instead of 8 of 32).
+//   kN = 32: one v_mfma_f32_32x32x16_bf16 block (key_of_row, key_of_reg).
+//   kN = 64: two 32-column blocks sharing every K and V operand read: draft
+//            tokens with Lq * G of 33 to 64 columns (5 to 8 tokens at G = 8)
+//            in one pass over the keys.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma_16x16x32(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Key (within a 32-key tile) read by A-operand row m of key block kb, so that
+// C register i of lane group q is key 8 q + 4 kb + i: the 8 keys of a lane
+// group are then exactly the k slots 8 q + 0..7 of the B operand of
+// O^T = V^T P^T.
+__device__ __forceinline__ int key16_of_row(int m, int kb) { return 8 * (m >> 2) + 4 * kb + (m & 3); }
+
+// Max / sum over the four lanes l % 16 of a column (16-column layout).
+__device__ __forceinline__ float quad_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return pair_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return pair_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
+template <int kN>
+struct DecodeCols {
+  static constexpr bool k16 = kN == 16;
+  static constexpr int kBlocks = kN == 64 ? 2 : 1;  // column blocks per wave
+  static constexpr int kBlockCols = k16 ? 16 : 32;
+  static constexpr int kQRegs = k16 ? 2 : 4;        // bf16x8 Q^T operands per block
+  typedef typename std::conditional<k16, f32x4_t, f32x16_t>::type Acc;  // one C block
+  static constexpr int kAccBlocks = k16 ? 4 : 2;    // d blocks of O^T
+  static constexpr int kAccRegs = k16 ? 4 : 16;
+  static constexpr int kSBlocks = k16 ? 2 : 1;      // key blocks of S^T per 32-key tile
+};
+
 // kSplitPerWave: each wave owns one whole split (split = 4 * group of
 // splits + wave) and writes that split's partial itself; kHeadPerWave: the
 // workgroup is one (sequence, split) and wave w takes KV head w of it, so the
@@ -226,14 +276,14 @@ __device__ __forceinline__ void stage_tile(const TileRegs<kFp8>& cur, uint16_t* 
 // queries (rows cu_seqlens_q[b] .. of q, o and the partials), and MFMA
 // column c = t * group + h serves token t and query head h of the group, so
 // one pass over the keys serves every query token (nq_b * group <= ncols <=
-// 32 columns).  Token t sits at position len - nq_b + t and sees the keys at
+// kN columns).  Token t sits at position len - nq_b + t and sees the keys at
 // or before it (and, with a window W, after position - W): the causal mask
 // aligned at the bottom right, applied per column.
 //
 // kPaged: the cache is paged (load_tile_paged); cu_seqlens_k then holds the
 // sequence lengths [batch] instead of offsets.
 template <int kDecWaves, bool kSplitPerWave, bool kHeadPerWave = false, int kHeadsPerWG = 1, bool kFp8 = false,
-          bool kMulti = false, bool kPaged = false>
+          bool kMulti = false, bool kPaged = false, int kN = 32>
 __device__ __forceinline__ void decode_body(
     const uint16_t* __restrict__ q, const void* __restrict__ k,
     const void* __restrict__ v, const float* __restrict__ sinks,
@@ -242,9 +292,11 @@ __device__ __forceinline__ void decode_body(
     float* __restrict__ lse, float* __restrict__ o_part, float* __restrict__ lse_part, int splits_per_wg,
     float v_scale, const int32_t* __restrict__ cu_seqlens_q, int ncols, int out_rows,
     const int32_t* __restrict__ block_table, int max_pages, int page_shift, int num_pages) {
+  typedef DecodeCols<kN> L;
+  constexpr int kCB = L::kBlocks;
   // Wave-private K and V staging tiles (2 x 4 KiB per wave); the whole
-  // buffer is reused for the cross-wave merge of up to 32 heads x 64 d per
-  // wave (index (wave * group + head) * 64 + d).
+  // buffer is reused for the cross-wave merge of up to 32 columns x 64 d per
+  // wave and column block (index (wave * cols + column) * 64 + d).
   __shared__ __attribute__((aligned(16))) float lds_buf[kDecWaves * 32 * kHeadDim];
   __shared__ float red_m[kDecWaves][32];
   __shared__ float red_l[kDecWaves][32];
@@ -252,8 +304,8 @@ __device__ __forceinline__ void decode_body(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int col = lane & 31;   // query head within the group
-  const int half = lane >> 5;
+  const int lc = L::k16 ? (lane & 15) : (lane & 31);  // column within a block
+  const int lq = L::k16 ? (lane >> 4) : (lane >> 5);  // k group of the MFMA operands
 
   constexpr bool kOwnSplit = kSplitPerWave || kHeadPerWave;  // the wave streams its range alone
   // kHeadsPerWG > 1 (interleaved mode): the workgroup serves kHeadsPerWG
@@ -325,18 +377,24 @@ __device__ __forceinline__ void decode_body(
   const int a = split < num_splits ? min(len, lo + split * chunk) : len;
   int e = split_end(split);
 
-  // Column -> (query token, head of the group); single-token: token 0.
-  const int tok = kMulti ? col / group : 0;
-  const bool col_ok = kMulti ? tok < nq : col < group;
-  const int head = g * group + (col_ok ? col - tok * group : 0);
-  const int qrow = kMulti ? q_row0 + (col_ok ? tok : 0) : b;  // row of q / o / partials
-  const int qpos = len - nq + (col_ok ? tok : 0);              // the query's position (kMulti masks)
+  // Column -> (query token, head of the group) per column block;
+  // single-token: token 0.
+  int tok[kCB], head[kCB], qrow[kCB], qpos[kCB];
+  bool col_ok[kCB];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) {
+    const int c = 32 * cb + lc;
+    tok[cb] = kMulti ? c / group : 0;
+    col_ok[cb] = kMulti ? tok[cb] < nq : c < group;
+    head[cb] = g * group + (col_ok[cb] ? c - tok[cb] * group : 0);
+    qrow[cb] = kMulti ? q_row0 + (col_ok[cb] ? tok[cb] : 0) : b;  // row of q / o / partials
+    qpos[cb] = len - nq + (col_ok[cb] ? tok[cb] : 0);              // the query's position (kMulti masks)
+  }
 
   uint16_t* kt = reinterpret_cast<uint16_t*>(lds_buf) + wave * 2 * kKeys * kHeadDim;
   uint16_t* vt = kt + kKeys * kHeadDim;
   const int grp_lane = lane & 15;
   const int dcol0 = 16 * ((lane >> 4) & 1) + 4 * (grp_lane & 3);
-  const int krow = key_of_row(col);
 
   // Register double buffering: the loads of the next tile of this wave are in
   // flight while the current one is computed.  The first tile is requested
@@ -345,51 +403,83 @@ __device__ __forceinline__ void decode_body(
   int k0 = kOwnSplit ? a : a + kKeys * wl;
   if (k0 < e) load(cur, k0, e);
 
-  bf16x8_t qreg[4];
+  // Q^T (B operand): column lc of each block, d = (32 or 16) s + 8 lq + t.
+  // Every lane loads; columns past the group repeat the group's first head
+  // (S columns are independent, and theirs are never written).
+  bf16x8_t qreg[kCB][L::kQRegs];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    // (every lane loads; columns past the group repeat the group's first
-    // head: S columns are independent, and theirs are never written)
-    const u32x4_t val = load16(q + (static_cast<size_t>(qrow) * hq + head) * kHeadDim + 16 * s + 8 * half);
-    qreg[s] = __builtin_bit_cast(bf16x8_t, val);
-  }
+  for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+    for (int s = 0; s < L::kQRegs; ++s) {
+      const int d0 = (L::k16 ? 32 : 16) * s + 8 * lq;
+      const u32x4_t val = load16(q + (static_cast<size_t>(qrow[cb]) * hq + head[cb]) * kHeadDim + d0);
+      qreg[cb][s] = __builtin_bit_cast(bf16x8_t, val);
+    }
   // The sink belongs to split 0 only (its wave 0 when the waves share a
   // split).  It is folded into the state after the keys (the order of the
   // logits does not matter), so nothing waits for it before the loop.
-  float z = kNegInf;
-  if (split == 0 && (kOwnSplit || wl == 0) && sinks != nullptr && col_ok) z = sinks[head];
-  float m2 = kNegInf, lsum = 0.0f;
-  f32x16_t acc[2] = {zero16(), zero16()};
+  float z[kCB];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb)
+    z[cb] = (split == 0 && (kOwnSplit || wl == 0) && sinks != nullptr && col_ok[cb]) ? sinks[head[cb]] : kNegInf;
+  float m2[kCB], lsum[kCB];
+  typename L::Acc acc[kCB][L::kAccBlocks];
+  auto reset_state = [&]() {
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      m2[cb] = kNegInf;
+      lsum[cb] = 0.0f;
+#pragma unroll
+      for (int db = 0; db < L::kAccBlocks; ++db)
+#pragma unroll
+        for (int r = 0; r < L::kAccRegs; ++r) acc[cb][db][r] = 0.0f;
+    }
+  };
+  reset_state();
+  // d of O^T register r of d block db in this lane.
+  auto d_of = [&](int db, int r) {
+    return L::k16 ? 16 * db + 4 * lq + r : 32 * db + 8 * (r >> 2) + 4 * lq + (r & 3);
+  };
+  auto col_sum = [&](float x) { return L::k16 ? quad_sum(x) : pair_sum(x); };
+  auto col_max = [&](float x) { return L::k16 ? quad_max(x) : pair_max(x); };
 
   // The sink: one more logit z (already in natural-log units) with no value.
   auto fold_sink = [&]() {
-    if (z > kNegInf) {
-      const float z2 = z * kLog2e;
-      const float m_new = fmaxf(m2, z2);
-      const float alpha = fast_exp2(m2 - m_new);  // 0 when no key was seen
-      lsum = lsum * alpha + (half == 0 ? fast_exp2(z2 - m_new) : 0.0f);
-  #pragma unroll
-      for (int db = 0; db < 2; ++db)
-  #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-      m2 = m_new;
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      if (z[cb] > kNegInf) {
+        const float z2 = z[cb] * kLog2e;
+        const float m_new = fmaxf(m2[cb], z2);
+        const float alpha = fast_exp2(m2[cb] - m_new);  // 0 when no key was seen
+        lsum[cb] = lsum[cb] * alpha + (lq == 0 ? fast_exp2(z2 - m_new) : 0.0f);
+#pragma unroll
+        for (int db = 0; db < L::kAccBlocks; ++db)
+#pragma unroll
+          for (int r = 0; r < L::kAccRegs; ++r) acc[cb][db][r] *= alpha;
+        m2[cb] = m_new;
+      }
     }
   };
   // This wave's split sp alone: normalise and write its partial.
-  auto write_partial = [&](int sp, float den) {
-    if (sp >= num_splits || !col_ok) return;
-    float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    if constexpr (kFp8) inv *= v_scale;  // V = v_scale * e4m3(code)
-    const size_t prow = (static_cast<size_t>(sp) * out_rows + qrow) * hq + head;
+  auto write_partial = [&](int sp) {
+    if (sp >= num_splits) return;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int cb = 0; cb < kCB; ++cb) {
+      const float den = col_sum(lsum[cb]);
+      if (!col_ok[cb]) continue;
+      float inv = den > 0.0f ? 1.0f / den : 0.0f;
+      if constexpr (kFp8) inv *= v_scale;  // V = v_scale * e4m3(code)
+      const size_t prow = (static_cast<size_t>(sp) * out_rows + qrow[cb]) * hq + head[cb];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int d = 32 * db + 8 * (r >> 2) + 4 * half + (r & 3);
-        o_part[prow * kHeadDim + d] = acc[db][r] * inv;
-      }
-    if (half == 0) lse_part[prow] = den > 0.0f ? (m2 + __log2f(den)) * kLn2 : kNegInf;
+      for (int db = 0; db < L::kAccBlocks; ++db)
+#pragma unroll
+        for (int r = 0; r < L::kAccRegs; ++r) o_part[prow * kHeadDim + d_of(db, r)] = acc[cb][db][r] * inv;
+      if (lq == 0) lse_part[prow] = den > 0.0f ? (m2[cb] + __log2f(den)) * kLn2 : kNegInf;
+    }
   };
+  // Key offset (within the tile) of S register r of key block kb in this lane.
+  auto key_of = [&](int kb, int r) { return L::k16 ? 8 * lq + 4 * kb + r : key_of_reg(r, lq); };
+
   // One 32-key tile (keys k0 .. k0 + 31; those at or past `end` masked) into
   // the wave's online-softmax state.
   auto tile_step = [&](const TileRegs<kFp8>& cur, int k0, int end) {
@@ -397,64 +487,113 @@ __device__ __forceinline__ void decode_body(
     stage_tile<kFp8>(cur, kt, vt, lane);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // K and V tiles written
 
-    // S^T = K Q^T: MFMA row m reads key row key_of_row(m) of the tile.
-    f32x16_t sacc = zero16();
+    // S^T = K Q^T.
+    typename L::Acc sacc[kCB][L::kSBlocks];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + swz(krow, 16 * s + 8 * half));
-      sacc = mfma_32x32x16(a, qreg[s], sacc);
+    for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+      for (int kb = 0; kb < L::kSBlocks; ++kb)
+#pragma unroll
+        for (int r = 0; r < L::kAccRegs; ++r) sacc[cb][kb][r] = 0.0f;
+    if constexpr (L::k16) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8_t ak = *reinterpret_cast<const bf16x8_t*>(kt + swz(key16_of_row(lc, kb), 32 * s + 8 * lq));
+          sacc[0][kb] = mfma_16x16x32(ak, qreg[0][s], sacc[0][kb]);
+        }
+    } else {
+      const int krow = key_of_row(lc);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8_t ak = *reinterpret_cast<const bf16x8_t*>(kt + swz(krow, 16 * s + 8 * lq));
+#pragma unroll
+        for (int cb = 0; cb < kCB; ++cb) sacc[cb][0] = mfma_32x32x16(ak, qreg[cb][s], sacc[cb][0]);
+      }
     }
 
     if (k0 + kKeys > end) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (k0 + key_of_reg(r, half) >= end) sacc[r] = kNegInf;
+      for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+        for (int kb = 0; kb < L::kSBlocks; ++kb)
+#pragma unroll
+          for (int r = 0; r < L::kAccRegs; ++r)
+            if (k0 + key_of(kb, r) >= end) sacc[cb][kb][r] = kNegInf;
     }
     if constexpr (kMulti) {
       // Per-column causal / window mask where the tile reaches past the
       // first query's position or below the last query's window.
       if (k0 + kKeys - 1 > len - nq || (window > 0 && k0 <= len - 1 - window)) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + key_of_reg(r, half);
-          if (key > qpos || (window > 0 && key <= qpos - window)) sacc[r] = kNegInf;
+        for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+          for (int kb = 0; kb < L::kSBlocks; ++kb)
+#pragma unroll
+            for (int r = 0; r < L::kAccRegs; ++r) {
+              const int key = k0 + key_of(kb, r);
+              if (key > qpos[cb] || (window > 0 && key <= qpos[cb] - window)) sacc[cb][kb][r] = kNegInf;
+            }
+      }
+    }
+
+    // P (B operand of O^T = V^T P^T): 32-column layout: pb[cb][u][t] is key
+    // 16 u + 8 lq + t; 16-column layout: pb[0][0][4 kb + i] is key
+    // 8 lq + 4 kb + i.
+    bf16x8_t pb[kCB][L::k16 ? 1 : 2];
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      float mx = sacc[cb][0][0];
+#pragma unroll
+      for (int kb = 0; kb < L::kSBlocks; ++kb)
+#pragma unroll
+        for (int r = 0; r < L::kAccRegs; ++r) mx = fmaxf(mx, sacc[cb][kb][r]);
+      mx = col_max(mx) * scale_log2;
+      const float m_new = fmaxf(m2[cb], mx);
+      const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
+      const float alpha = fast_exp2(m2[cb] - m_use);
+      m2[cb] = m_new;
+      float psum = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < L::kSBlocks; ++kb)
+#pragma unroll
+        for (int r = 0; r < L::kAccRegs; ++r) {
+          const float p = fast_exp2(fmaf(sacc[cb][kb][r], scale_log2, -m_use));
+          psum += p;
+          if constexpr (L::k16)
+            pb[cb][0][4 * kb + r] = static_cast<__bf16>(p);
+          else
+            pb[cb][r >> 3][r & 7] = static_cast<__bf16>(p);
         }
-      }
+      lsum[cb] = lsum[cb] * alpha + psum;
+#pragma unroll
+      for (int db = 0; db < L::kAccBlocks; ++db)
+#pragma unroll
+        for (int r = 0; r < L::kAccRegs; ++r) acc[cb][db][r] *= alpha;
     }
 
-    float mx = sacc[0];
+    if constexpr (L::k16) {
+      // V^T rows d = 16 db + lc, keys 8 lq + 0..7: two transposing reads of
+      // 4 key rows each.
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-    mx = pair_max(mx) * scale_log2;
-    const float m_new = fmaxf(m2, mx);
-    const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-    const float alpha = fast_exp2(m2 - m_use);
-    m2 = m_new;
-    float psum = 0.0f;
-    bf16x8_t pb[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const float p = fast_exp2(fmaf(sacc[8 * u + tt], scale_log2, -m_use));
-        psum += p;
-        pb[u][tt] = static_cast<__bf16>(p);
-      }
-    }
-    lsum = lsum * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-
-#pragma unroll
-    for (int db = 0; db < 2; ++db) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int rbase = 16 * u + 8 * half + (grp_lane >> 2);
-        const int dcol = 32 * db + dcol0;
+      for (int db = 0; db < 4; ++db) {
+        const int rbase = 8 * lq + (lc >> 2);
+        const int dcol = 16 * db + 4 * (lc & 3);
         const bf16x8_t av = cat4(lds_read_tr(vt + swz(rbase, dcol)), lds_read_tr(vt + swz(rbase + 4, dcol)));
-        acc[db] = mfma_32x32x16(av, pb[u], acc[db]);
+        acc[0][db] = mfma_16x16x32(av, pb[0][0], acc[0][db]);
+      }
+    } else {
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int rbase = 16 * u + 8 * lq + (grp_lane >> 2);
+          const int dcol = 32 * db + dcol0;
+          const bf16x8_t av = cat4(lds_read_tr(vt + swz(rbase, dcol)), lds_read_tr(vt + swz(rbase + 4, dcol)));
+#pragma unroll
+          for (int cb = 0; cb < kCB; ++cb) acc[cb][db] = mfma_32x32x16(av, pb[cb][u], acc[cb][db]);
+        }
       }
     }
   };
@@ -475,13 +614,11 @@ __device__ __forceinline__ void decode_body(
         cur = nxt;
       }
       fold_sink();
-      write_partial(sp, pair_sum(lsum));
+      write_partial(sp);
       if (++sp >= split_stop) return;
-      z = kNegInf;  // the sink belongs to split 0 only
-      m2 = kNegInf;
-      lsum = 0.0f;
-      acc[0] = zero16();
-      acc[1] = zero16();
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb) z[cb] = kNegInf;  // the sink belongs to split 0 only
+      reset_state();
       k0 = e;
       e = split_end(sp);
     }
@@ -495,63 +632,66 @@ __device__ __forceinline__ void decode_body(
   }
 
   fold_sink();
-  const float den = pair_sum(lsum);
   if constexpr (kOwnSplit) {
-    write_partial(split, den);
+    write_partial(split);
     return;
   }
 
-  // Cross-wave merge.  Each wave publishes (m, l, unnormalised O) per head.
-  __syncthreads();  // all waves are done with their V tiles
-  float* red_o = lds_buf;  // [wave][group][64 d]
-  if (half == 0) {
-    red_m[wave][col] = m2;
-    red_l[wave][col] = den;
-  }
-  const int cols = kMulti ? ncols : group;  // columns per wave in red_o
-  if (col_ok) {
+  // Cross-wave merge, one column block at a time.  Each wave publishes
+  // (m, l, unnormalised O) per column.
+  const int cols = kMulti ? min(ncols, 32) : group;  // columns per wave and block in red_o
+  float* red_o = lds_buf;  // [wave][column][64 d]
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int d = 32 * db + 8 * (r >> 2) + 4 * half + (r & 3);
-        red_o[(wave * cols + col) * kHeadDim + d] = acc[db][r];
-      }
-  }
-  __syncthreads();
-
-  for (int idx = tid; idx < kHeadsPerWG * cols * kHeadDim; idx += 64 * kDecWaves) {
-    const int hs = idx / (cols * kHeadDim);  // KV head within the workgroup
-    const int hc = (idx / kHeadDim) % cols;  // column
-    const int d = idx % kHeadDim;
-    const int ct = kMulti ? hc / group : 0;  // its query token
-    if (kMulti && ct >= nq) continue;
-    float big_m = kNegInf;
-#pragma unroll
-    for (int i = 0; i < kIl; ++i) big_m = fmaxf(big_m, red_m[hs + kHeadsPerWG * i][hc]);
-    float out = 0.0f, out_lse = kNegInf;
-    if (big_m > kNegInf) {
-      float num = 0.0f, tot = 0.0f;
-#pragma unroll
-      for (int i = 0; i < kIl; ++i) {
-        const int w = hs + kHeadsPerWG * i;
-        const float sc = fast_exp2(red_m[w][hc] - big_m);
-        tot += sc * red_l[w][hc];
-        num += sc * red_o[(w * cols + hc) * kHeadDim + d];
-      }
-      out = num / tot;
-      if constexpr (kFp8) out *= v_scale;  // V = v_scale * e4m3(code)
-      out_lse = (big_m + __log2f(tot)) * kLn2;
+  for (int cb = 0; cb < kCB; ++cb) {
+    const float den = col_sum(lsum[cb]);
+    const int cb_cols = kMulti ? min(ncols - 32 * cb, cols) : cols;  // columns of this block
+    __syncthreads();  // all waves are done with their V tiles (or with the previous block's merge)
+    if (lq == 0 && lc < 32) {
+      red_m[wave][lc] = m2[cb];
+      red_l[wave][lc] = den;
     }
-    const int h = (g - hsub + hs) * group + (hc - ct * group);
-    const int row = kMulti ? q_row0 + ct : b;
-    if (num_splits == 1) {
-      o[(static_cast<size_t>(row) * hq + h) * kHeadDim + d] = to_bf16_bits(out);
-      if (lse != nullptr && d == 0) lse[static_cast<size_t>(row) * hq + h] = out_lse;
-    } else {
-      const size_t prow = (static_cast<size_t>(split) * out_rows + row) * hq + h;
-      o_part[prow * kHeadDim + d] = out;
-      if (d == 0) lse_part[prow] = out_lse;
+    if (col_ok[cb]) {
+#pragma unroll
+      for (int db = 0; db < L::kAccBlocks; ++db)
+#pragma unroll
+        for (int r = 0; r < L::kAccRegs; ++r) red_o[(wave * cols + lc) * kHeadDim + d_of(db, r)] = acc[cb][db][r];
+    }
+    __syncthreads();
+
+    for (int idx = tid; idx < kHeadsPerWG * cb_cols * kHeadDim; idx += 64 * kDecWaves) {
+      const int hs = idx / (cb_cols * kHeadDim);  // KV head within the workgroup
+      const int hc = (idx / kHeadDim) % cb_cols;  // column within the block
+      const int d = idx % kHeadDim;
+      const int c = 32 * cb + hc;                 // column of the wave
+      const int ct = kMulti ? c / group : 0;      // its query token
+      if (kMulti && ct >= nq) continue;
+      float big_m = kNegInf;
+#pragma unroll
+      for (int i = 0; i < kIl; ++i) big_m = fmaxf(big_m, red_m[hs + kHeadsPerWG * i][hc]);
+      float out = 0.0f, out_lse = kNegInf;
+      if (big_m > kNegInf) {
+        float num = 0.0f, tot = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kIl; ++i) {
+          const int w = hs + kHeadsPerWG * i;
+          const float sc = fast_exp2(red_m[w][hc] - big_m);
+          tot += sc * red_l[w][hc];
+          num += sc * red_o[(w * cols + hc) * kHeadDim + d];
+        }
+        out = num / tot;
+        if constexpr (kFp8) out *= v_scale;  // V = v_scale * e4m3(code)
+        out_lse = (big_m + __log2f(tot)) * kLn2;
+      }
+      const int h = (g - hsub + hs) * group + (c - ct * group);
+      const int row = kMulti ? q_row0 + ct : b;
+      if (num_splits == 1) {
+        o[(static_cast<size_t>(row) * hq + h) * kHeadDim + d] = to_bf16_bits(out);
+        if (lse != nullptr && d == 0) lse[static_cast<size_t>(row) * hq + h] = out_lse;
+      } else {
+        const size_t prow = (static_cast<size_t>(split) * out_rows + row) * hq + h;
+        o_part[prow * kHeadDim + d] = out;
+        if (d == 0) lse_part[prow] = out_lse;
+      }
     }
   }
 }
@@ -590,25 +730,26 @@ __device__ __forceinline__ float wave_sum(float x) {
       splits_per_wg, v_scale, cu_seqlens_q, ncols, out_rows, block_table, max_pages, page_shift, num_pages
 
 // Short splits (at most kShortChunk keys): two-wave workgroups at three
-// waves per SIMD, i.e. more workgroups and so more loads in flight.
-template <bool kFp8, bool kMulti, bool kPaged>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3, 3))) void decode_kernel_w2(
+// waves per SIMD, i.e. more workgroups and so more loads in flight (two with
+// 64 columns, whose state needs the registers).
+template <bool kFp8, bool kMulti, bool kPaged, int kN>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(kN == 64 ? 2 : 3, kN == 64 ? 2 : 3))) void decode_kernel_w2(
     SINKATTN_DECODE_PARAMS) {
-  decode_body<2, false, false, 1, kFp8, kMulti, kPaged>(SINKATTN_DECODE_ARGS);
+  decode_body<2, false, false, 1, kFp8, kMulti, kPaged, kN>(SINKATTN_DECODE_ARGS);
 }
 
 // Four or more long splits: four-wave workgroups, one split per wave (each
 // wave writes its split's partial; no cross-wave merge).
-template <bool kFp8, bool kMulti, bool kPaged>
+template <bool kFp8, bool kMulti, bool kPaged, int kN>
 __global__ __launch_bounds__(256) void decode_kernel_ps(SINKATTN_DECODE_PARAMS) {
-  decode_body<4, true, false, 1, kFp8, kMulti, kPaged>(SINKATTN_DECODE_ARGS);
+  decode_body<4, true, false, 1, kFp8, kMulti, kPaged, kN>(SINKATTN_DECODE_ARGS);
 }
 
 // Four or more splits over 4 to 8 KV heads: one workgroup per (sequence,
 // split), one wave per KV head.
-template <bool kFp8, bool kMulti, bool kPaged>
+template <bool kFp8, bool kMulti, bool kPaged, int kN>
 __global__ __launch_bounds__(512) void decode_kernel_hw(SINKATTN_DECODE_PARAMS) {
-  decode_body<8, false, true, 1, kFp8, kMulti, kPaged>(SINKATTN_DECODE_ARGS);
+  decode_body<8, false, true, 1, kFp8, kMulti, kPaged, kN>(SINKATTN_DECODE_ARGS);
 }
 
 // One split of more than kShortChunk keys over an even number of KV heads:
@@ -616,17 +757,17 @@ __global__ __launch_bounds__(512) void decode_kernel_hw(SINKATTN_DECODE_PARAMS) 
 // waves each, so that a workgroup reads 256 contiguous bytes of every token
 // row it touches (a plain-load probe: 6.4-6.6 TB/s against 6.0-6.2 for one
 // head per workgroup; 64 x 8192 at S = 1 from 180 to 165 us).
-template <bool kFp8, bool kMulti, bool kPaged>
+template <bool kFp8, bool kMulti, bool kPaged, int kN>
 __global__ __launch_bounds__(512) void decode_kernel_w8p(SINKATTN_DECODE_PARAMS) {
-  decode_body<8, false, false, 2, kFp8, kMulti, kPaged>(SINKATTN_DECODE_ARGS);
+  decode_body<8, false, false, 2, kFp8, kMulti, kPaged, kN>(SINKATTN_DECODE_ARGS);
 }
 
 // Long splits: four-wave workgroups at the compiler's own register budget
 // (two waves per SIMD; at three, S = 4 on 64 x 8192 would end on a
 // two-thirds-full round of workgroups).
-template <bool kFp8, bool kMulti, bool kPaged>
+template <bool kFp8, bool kMulti, bool kPaged, int kN>
 __global__ __launch_bounds__(256) void decode_kernel_w4(SINKATTN_DECODE_PARAMS) {
-  decode_body<4, false, false, 1, kFp8, kMulti, kPaged>(SINKATTN_DECODE_ARGS);
+  decode_body<4, false, false, 1, kFp8, kMulti, kPaged, kN>(SINKATTN_DECODE_ARGS);
 }
 
 #undef SINKATTN_DECODE_PARAMS
@@ -688,7 +829,19 @@ bool decode_merges_in_kernel(const DecodeLaunch& a) {
          (keys_per_split <= kKeys || max_range(a) <= kDirectWholeKeys);
 }
 
-template <bool kFp8, bool kMulti, bool kPaged>
+// Columns per decode wave: the 16-column layout for E4M3 caches with at most
+// 16 (token, head) columns (G = 8: half the padded matrix-core and softmax
+// work of the 32-column layout, which the E4M3 tile's conversions leave the
+// limit there); 32 otherwise; 64 for 33 to 64 columns of draft tokens.
+static int decode_cols(const DecodeLaunch& a) {
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const int ncols = a.cu_seqlens_q != nullptr ? a.max_q * group : group;
+  if (ncols > 32) return 64;
+  if (ncols <= 16 && a.fp8) return 16;
+  return 32;
+}
+
+template <int kN, bool kFp8, bool kMulti, bool kPaged>
 static hipError_t launch_decode_t(const DecodeLaunch& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
   // Splits of at most 32 keys: the whole range in one workgroup per
@@ -700,25 +853,25 @@ static hipError_t launch_decode_t(const DecodeLaunch& a, hipStream_t stream) {
   unsigned grid = static_cast<unsigned>(a.batch) * a.num_kv_heads * splits;
   unsigned threads = 128;
   int per_wg = 1;
-  decltype(&decode_kernel_w4<kFp8, kMulti, kPaged>) kernel = decode_kernel_w2<kFp8, kMulti, kPaged>;
+  decltype(&decode_kernel_w4<kFp8, kMulti, kPaged, kN>) kernel = decode_kernel_w2<kFp8, kMulti, kPaged, kN>;
   if (splits >= kHeadPerWaveMinSplits && a.num_kv_heads >= 4 && a.num_kv_heads <= 8 &&
       keys_per_split >= kHeadPerWaveMinKeys) {
     const long long units = static_cast<long long>(a.batch) * splits;
     per_wg = static_cast<int>(std::max<long long>(1, std::min<long long>(splits, units / kHeadPerWaveTarget)));
     grid = static_cast<unsigned>(static_cast<long long>(a.batch) * ((splits + per_wg - 1) / per_wg));
     threads = 64 * a.num_kv_heads;
-    kernel = decode_kernel_hw<kFp8, kMulti, kPaged>;
+    kernel = decode_kernel_hw<kFp8, kMulti, kPaged, kN>;
   } else if (splits == 1 && !short_chunks && a.num_kv_heads % 2 == 0) {
     grid = static_cast<unsigned>(a.batch) * (a.num_kv_heads / 2);
     threads = 512;
-    kernel = decode_kernel_w8p<kFp8, kMulti, kPaged>;
+    kernel = decode_kernel_w8p<kFp8, kMulti, kPaged, kN>;
   } else if (splits >= kSplitPerWaveMin && !short_chunks) {
     grid = static_cast<unsigned>(a.batch) * a.num_kv_heads * ((splits + 3) / 4);
     threads = 256;
-    kernel = decode_kernel_ps<kFp8, kMulti, kPaged>;
+    kernel = decode_kernel_ps<kFp8, kMulti, kPaged, kN>;
   } else if (!short_chunks) {
     threads = 256;
-    kernel = decode_kernel_w4<kFp8, kMulti, kPaged>;
+    kernel = decode_kernel_w4<kFp8, kMulti, kPaged, kN>;
   }
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, stream, static_cast<const uint16_t*>(a.q), a.k, a.v,
                      a.sinks, a.cu_seqlens_k, a.batch, a.num_q_heads, a.num_kv_heads, group, a.window, scale_log2,
@@ -728,13 +881,28 @@ static hipError_t launch_decode_t(const DecodeLaunch& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
-  if (a.block_table != nullptr) {
-    if (a.cu_seqlens_q != nullptr) return launch_decode_t<false, true, true>(a, stream);
-    return a.fp8 ? launch_decode_t<true, false, true>(a, stream) : launch_decode_t<false, false, true>(a, stream);
+template <bool kFp8, bool kMulti, bool kPaged>
+static hipError_t launch_decode_cols(const DecodeLaunch& a, hipStream_t stream) {
+  const int cols = decode_cols(a);
+  if constexpr (kMulti) {
+    if (cols == 64) return launch_decode_t<64, kFp8, kMulti, kPaged>(a, stream);
   }
-  if (a.cu_seqlens_q != nullptr) return launch_decode_t<false, true, false>(a, stream);
-  return a.fp8 ? launch_decode_t<true, false, false>(a, stream) : launch_decode_t<false, false, false>(a, stream);
+  if constexpr (kFp8) {
+    if (cols == 16) return launch_decode_t<16, kFp8, kMulti, kPaged>(a, stream);
+  }
+  return launch_decode_t<32, kFp8, kMulti, kPaged>(a, stream);
+}
+
+hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
+  const bool multi = a.cu_seqlens_q != nullptr;
+  if (a.block_table != nullptr) {
+    if (multi)
+      return a.fp8 ? launch_decode_cols<true, true, true>(a, stream) : launch_decode_cols<false, true, true>(a, stream);
+    return a.fp8 ? launch_decode_cols<true, false, true>(a, stream) : launch_decode_cols<false, false, true>(a, stream);
+  }
+  if (multi)
+    return a.fp8 ? launch_decode_cols<true, true, false>(a, stream) : launch_decode_cols<false, true, false>(a, stream);
+  return a.fp8 ? launch_decode_cols<true, false, false>(a, stream) : launch_decode_cols<false, false, false>(a, stream);
 }
 
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream) {
@@ -746,6 +914,8 @@ hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream) {
 }
 
 int decode_max_group() { return 32; }
+
+int decode_max_cols() { return 64; }
 
 // Split-KV partials of sinkattn_decode_splitkv_noalloc: a fixed device array
 // instead of a caller workspace.  Each device the library runs on holds its

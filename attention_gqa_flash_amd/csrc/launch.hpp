@@ -159,5 +159,7 @@ hipError_t check_read(unsigned* flags, int* total, hipStream_t stream);
 long long prefill_blocks(int batch, int total_tokens, int num_kv_heads, int group);
 long long prefill_max_blocks();
 int decode_max_group();
+// Most (query token, query head) columns one multi-token decode wave serves.
+int decode_max_cols();
 
 }  // namespace sinkattn

@@ -320,7 +320,8 @@ SINKATTN_API sinkattn_status sinkattn_decode_paged(
  *   v_cache       bf16 [total_kv, num_kv_heads, head_dim], packed by
  *                 cu_seqlens_k (int32 [batch + 1], device)
  *   max_seqlen_q  host int >= every Lq_b; max_seqlen_q * (num_q_heads /
- *                 num_kv_heads) <= 32 (else SINKATTN_ERR_UNSUPPORTED)
+ *                 num_kv_heads) <= 64 (else SINKATTN_ERR_UNSUPPORTED): up
+ *                 to 8 draft tokens per sequence at 8 query heads per KV head
  *   max_seqlen_k  host int >= every Lk_b (>= 1)
  *   total_q       rows of q / o / lse
  *   num_splits,
@@ -401,6 +402,38 @@ SINKATTN_API sinkattn_status sinkattn_decode_paged_fp8(
     void* o, float* lse, void* stream);
 
 /*
+ * Multi-token-query decode against an FP8 (E4M3) cache: the draft-token
+ * verification of sinkattn_decode_splitkv_multi over the E4M3 cache of
+ * sinkattn_decode_splitkv_fp8 (vLLM, "GPT-OSS performance optimizations on
+ * NVIDIA Blackwell", FlashInfer integration: FP8 KV cache; Perplexity,
+ * "GPT-OSS on day 0", in-house inference engine: speculative and MTP
+ * decoders).  K = k_scale * e4m3(k_cache), V = v_scale * e4m3(v_cache); the
+ * result equals sinkattn_decode_splitkv_multi on those K and V.
+ *
+ *   q, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, total_q,
+ *   num_splits, workspace, o, lse
+ *                  as sinkattn_decode_splitkv_multi
+ *   k_cache,
+ *   v_cache        uint8 E4M3 codes [total_kv, num_kv_heads, head_dim]
+ *   k_scale,
+ *   v_scale        host floats, finite and > 0
+ *
+ * Preconditions and errors: those of sinkattn_decode_splitkv_multi and of
+ * sinkattn_decode_splitkv_fp8 (NaN codes reported under
+ * SINKATTN_DEBUG_CHECKS=1).
+ */
+SINKATTN_API sinkattn_status sinkattn_decode_splitkv_multi_fp8(
+    const void* q, const void* k_cache, const void* v_cache,
+    float k_scale, float v_scale,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+    int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t total_q,
+    const float* sinks,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t window, float softmax_scale, int32_t num_splits,
+    void* workspace, size_t workspace_bytes,
+    void* o, float* lse, void* stream);
+
+/*
  * Multi-token-query decode against a paged cache: the draft-token
  * verification of sinkattn_decode_splitkv_multi, with the keys and values in
  * the pages of sinkattn_decode_paged.  The result equals
@@ -423,6 +456,35 @@ SINKATTN_API sinkattn_status sinkattn_decode_paged_fp8(
  */
 SINKATTN_API sinkattn_status sinkattn_decode_paged_multi(
     const void* q, const void* k_pages, const void* v_pages,
+    const int32_t* block_table, const int32_t* seq_lens, const int32_t* cu_seqlens_q, int32_t batch,
+    int32_t max_pages, int32_t page_size, int32_t num_pages,
+    int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t total_q,
+    const float* sinks,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t window, float softmax_scale, int32_t num_splits,
+    void* workspace, size_t workspace_bytes,
+    void* o, float* lse, void* stream);
+
+/*
+ * Multi-token-query decode against a paged cache of E4M3 codes: the queries
+ * of sinkattn_decode_paged_multi with the pages and per-tensor scales of
+ * sinkattn_decode_paged_fp8 (vLLM, FlashInfer integration: FP8 KV cache;
+ * Perplexity, in-house inference engine: speculative and MTP decoders).  The
+ * result equals sinkattn_decode_splitkv_multi_fp8 on the gathered cache.
+ *
+ *   k_pages,
+ *   v_pages        uint8 E4M3 codes [num_pages, page_size, num_kv_heads,
+ *                  head_dim]
+ *   k_scale,
+ *   v_scale        host floats, finite and > 0
+ *   (the other arguments as sinkattn_decode_paged_multi)
+ *
+ * Preconditions and errors: those of sinkattn_decode_paged_multi and of
+ * sinkattn_decode_paged_fp8.
+ */
+SINKATTN_API sinkattn_status sinkattn_decode_paged_multi_fp8(
+    const void* q, const void* k_pages, const void* v_pages,
+    float k_scale, float v_scale,
     const int32_t* block_table, const int32_t* seq_lens, const int32_t* cu_seqlens_q, int32_t batch,
     int32_t max_pages, int32_t page_size, int32_t num_pages,
     int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t total_q,

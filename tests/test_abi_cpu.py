@@ -28,7 +28,8 @@ def _lib():
 def test_header_declares_the_entry_points():
     assert _declared() == sorted([
         "sinkattn_decode_paged", "sinkattn_decode_paged_fp8", "sinkattn_decode_paged_multi", "sinkattn_decode_splitkv", "sinkattn_decode_splitkv_fp8",
-        "sinkattn_decode_splitkv_multi", "sinkattn_decode_splitkv_noalloc",
+        "sinkattn_decode_splitkv_multi", "sinkattn_decode_splitkv_multi_fp8", "sinkattn_decode_splitkv_noalloc",
+        "sinkattn_decode_paged_multi_fp8",
         "sinkattn_decode_workspace_bytes", "sinkattn_oproj_bias", "sinkattn_oproj_workspace_bytes",
         "sinkattn_rope_qkv_append",
         "sinkattn_last_error", "sinkattn_merge_lse", "sinkattn_prefill_append", "sinkattn_prefill_append_paged",
@@ -218,8 +219,8 @@ def _decode_multi(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(mq=5), 2),                  # 5 tokens x 8 heads > 32 columns
-    (dict(hq=64, hkv=2, mq=2), 2),    # a group of 32 leaves room for one token only
+    (dict(mq=9), 2),                  # 9 tokens x 8 heads > 64 columns
+    (dict(hq=64, hkv=2, mq=3), 2),    # a group of 32 leaves room for two tokens only
     (dict(cuq=None), 1),
     (dict(hq=8, hkv=8, mq=20, tq=16), 1),  # max_seqlen_q above total_q
     (dict(mq=-1), 1),
@@ -322,7 +323,7 @@ def _decode_paged_multi(lib, **kw):
     (dict(mp=6), 1),                  # 6 x 16 < max_seqlen_k
     (dict(bt=None), 1),
     (dict(cuq=None), 1),
-    (dict(mq=5), 2),                  # 5 tokens x 8 heads > 32 columns
+    (dict(mq=9), 2),                  # 9 tokens x 8 heads > 64 columns
     (dict(mq=4, tq=3), 1),            # more than total_q
     (dict(splits=4), 3),              # no workspace
     (dict(splits=4, ws=FAKE, ws_bytes=(1 << 20)), 3),  # workspace sized for batch rows, not total_q

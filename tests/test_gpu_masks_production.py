@@ -12,10 +12,11 @@ benchmark and the named workloads run:
 * the ragged pack of 32 sequences (log-uniform lengths 128..32768, seed 0,
   heads 0, 9, 18, 27 without sink), causal and 128-window, on the first
   rounds and the last round of several sequences;
-* draft tokens against a cache (1 to 8 queries per sequence; Perplexity,
-  "GPT-OSS on day 0", in-house inference engine) through the multi-token
-  decode, contiguous and paged, windows 0 / 1 / 127 / 128 / 129, 1 / 4 / 16
-  splits, on the rounds at the diagonal and around the window edge.
+* draft tokens against a cache (1 to 8 queries per sequence, 8 to 64
+  (token, head) columns; Perplexity, "GPT-OSS on day 0", in-house inference
+  engine) through the multi-token decode, bf16 and E4M3 caches, contiguous
+  and paged, windows 0 / 1 / 127 / 128 / 129, 1 / 4 / 16 splits, on the
+  rounds at the diagonal and around the window edge.
 
 The zero pattern is compared with the oracle's integer mask
 (append_mask_cols_ref; q_len = k_len is the prefill mask) bit for bit.  Every
@@ -111,17 +112,19 @@ def test_prefill_mask_ragged_pack(window):
     torch.cuda.empty_cache()
 
 
-def _pages(v_bits, cu_k, k_lens, page_size, seed):
-    """Scatter packed rows into a shuffled page pool (spare pages hold NaN)."""
+def _pages(v_bits, cu_k, k_lens, page_size, seed, fill):
+    """Scatter packed rows into a shuffled page pool (spare pages and unowned
+    slots hold the NaN pattern `fill`)."""
     rng = np.random.default_rng(seed)
     zeros = np.zeros_like(v_bits)
-    kp, vp, bt = inputs._scatter_pages(zeros, v_bits, cu_k, k_lens, page_size, rng, 3, 0x7FC0)
+    kp, vp, bt = inputs._scatter_pages(zeros, v_bits, cu_k, k_lens, page_size, rng, 3, fill)
     return kp, vp, bt
 
 
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "e4m3"])
 @pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged16"])
-@pytest.mark.parametrize("hq,lq", [(64, 1), (64, 4), (32, 8)])
-def test_draft_token_decode_mask(paged, hq, lq):
+@pytest.mark.parametrize("hq,lq", [(64, 1), (64, 2), (64, 4), (32, 8), (64, 8)])
+def test_draft_token_decode_mask(paged, hq, lq, fp8):
     hkv = 8
     k_lens = [lq, 127 + lq, 128 + lq, 129 + lq, 1000, 8192]
     q_lens = [lq, lq, lq, max(1, lq - 1), lq, lq]
@@ -142,20 +145,30 @@ def test_draft_token_decode_mask(paged, hq, lq):
         rounds = sorted(x for x in rounds if 64 * x < max(k_lens))
         for r in rounds:
             rows, cols = _one_hot_rows(cu_k, k_lens, r)
-            v_bits = np.zeros((tk, hkv, 64), dtype=np.uint16)
-            v_bits[rows, :, cols] = 0x3F80
-            if paged:
-                kp, vp, bt = _pages(v_bits, cu_k, k_lens, 16, seed=r)
-                kp_d = torch.from_numpy(kp.view(np.int16)).view(torch.bfloat16).cuda()
-                vp_d = torch.from_numpy(vp.view(np.int16)).view(torch.bfloat16).cuda()
-                bt_d = i32_to_device(bt)
+            # one-hot V: bf16 1.0 (0x3F80) or the E4M3 code of 1.0 (0x38)
+            v_bits = np.zeros((tk, hkv, 64), dtype=np.uint8 if fp8 else np.uint16)
+            v_bits[rows, :, cols] = 0x38 if fp8 else 0x3F80
+            if fp8:
+                def dev(x):
+                    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
             else:
-                k_d = torch.zeros((tk, hkv, 64), dtype=torch.bfloat16, device="cuda")
-                v_d = torch.from_numpy(v_bits.view(np.int16)).view(torch.bfloat16).cuda()
+                def dev(x):
+                    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+            if paged:
+                kp, vp, bt = _pages(v_bits, cu_k, k_lens, 16, seed=r, fill=0x7F if fp8 else 0x7FC0)
+                kp_d, vp_d, bt_d = dev(kp), dev(vp), i32_to_device(bt)
+            else:
+                k_d, v_d = dev(np.zeros_like(v_bits)), dev(v_bits)
             for splits in (1, 4, 16):
-                if paged:
+                if paged and fp8:
+                    o = binding.decode_paged_multi_fp8(q, kp_d, vp_d, 1.0, 1.0, bt_d, lens_d, cq_d, max(q_lens),
+                                                       max(k_lens), sinks, window, 0.125, splits)
+                elif paged:
                     o = binding.decode_paged_multi(q, kp_d, vp_d, bt_d, lens_d, cq_d, max(q_lens), max(k_lens), sinks,
                                                    window, 0.125, splits)
+                elif fp8:
+                    o = binding.decode_splitkv_multi_fp8(q, k_d, v_d, 1.0, 1.0, cq_d, ck_d, max(q_lens), max(k_lens),
+                                                         sinks, window, 0.125, splits)
                 else:
                     o = binding.decode_splitkv_multi(q, k_d, v_d, cq_d, ck_d, max(q_lens), max(k_lens), sinks, window,
                                                      0.125, splits)

@@ -15,7 +15,7 @@ statistic goes to --detail-json, gpurun_out/bench_detail.json by default).
 peak) in percent; each leg is also reported on its own.  FLOP and byte
 counts are algorithmic (unmasked query-key pairs; Q + O + the K/V rows
 attended + sinks), measured with HIP events on the stream the kernels run
-on.  Inputs are resident in HBM before timing; the prefill leg rotates three
+on; `value` uses each leg's mean interval, the rooflines its median.  Inputs are resident in HBM before timing; the prefill leg rotates three
 input sets so that its 151 MB working set does not stay in the 256 MB
 Infinity Cache between steps.  Each leg reports mean, median and min.
 
@@ -25,12 +25,13 @@ cached tokens, 32 splits, full then 128-window); the ragged 32-sequence
 varlen prefill (causal and 128-window); the append prefill (the last
 2048-token chunk of an 8192-token prompt; 64 x 4 draft tokens verified
 against 8192 cached tokens, also through the multi-token-query decode at 1
-and 4 splits); the 64 x 8192 decode against a paged cache (16- and 64-token
+and 4 splits; 8 draft tokens per sequence, and 4 or 8 against an E4M3
+cache, through the multi-token decode alone); the 64 x 8192 decode against a paged cache (16- and 64-token
 pages, shuffled), also with 4 draft tokens per sequence, over E4M3 pages, and
 as the keys of a 2048-token prompt chunk (append prefill over pages); the fused rotary step (YaRN; Q out, K/V appended) for 8192
 and 64 tokens; the output projection with bias (64 and 8192 rows, 4096 ->
 2880); a streaming-read and a copy
-bandwidth reference; the engine clock (sysfs pp_dpm_sclk) sampled during the step.
+bandwidth reference; the engine clock (sysfs pp_dpm_sclk) sampled during the warm-up and timed steps.
 Small working sets are timed after a 512 MiB cache scrub.  The long-decode
 and ragged inputs are drawn on the device from a seeded generator (same
 distributions as the host-generated parity inputs) to keep start-up short.
@@ -347,10 +348,18 @@ def _cpu_other_configs(cores: int) -> dict:
 # GPU leg
 # ---------------------------------------------------------------------------
 
-def _kernel_source_hash() -> str:
+# The sources each counted kernel is built from (its own file and the shared
+# device helpers).
+_KERNEL_SOURCES = {"prefill": ("prefill.hip", "device_common.hpp"), "decode": ("decode.hip", "device_common.hpp"),
+                   "merge": ("decode.hip", "device_common.hpp")}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the sources of one counted kernel ('prefill_causal',
+    'decode_s16', ...)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "attention_gqa_flash_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in _KERNEL_SOURCES[kernel.split("_")[0]]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -358,7 +367,7 @@ def _kernel_source_hash() -> str:
 
 def _traffic(kernel: str):
     """Measured HBM bytes per launch from the committed counter summary, if it
-    was taken on the current kernel sources; else None."""
+    was taken on the current sources of that kernel; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -366,7 +375,7 @@ def _traffic(kernel: str):
     except (OSError, ValueError):
         return None
     ent = data.get(kernel)
-    if not ent or ent.get("source_hash") != _kernel_source_hash():
+    if not ent or ent.get("source_hash") != kernel_source_hash(kernel):
         return None
     return ent.get("bytes_per_launch")
 
@@ -505,26 +514,31 @@ def gpu_bench(steps: int, warmup: int, extras: bool = True) -> dict:
             ev["window"].append((marks[1], marks[2]))
             ev["decode"].append((marks[2], marks[3]))
 
-    for i in range(warmup):
-        step(i, False)
-    torch.cuda.synchronize()
-    # No garbage-collector pass inside the timed loop: a full collection can
-    # hold the host thread long enough for the GPU to run out of queued work.
-    gc.collect()
-    gc.disable()
+    # The engine clock is sampled over the warm-up steps and the timed steps
+    # together (the timed steps alone last tens of milliseconds).
     clock = _ClockSampler(pci_bus)
-    try:
-        with clock:
+    with clock:
+        for i in range(warmup):
+            step(i, False)
+        torch.cuda.synchronize()
+        # No garbage-collector pass inside the timed loop: a full collection can
+        # hold the host thread long enough for the GPU to run out of queued work.
+        gc.collect()
+        gc.disable()
+        try:
             t0 = time.perf_counter()
             for i in range(steps):
                 step(i, True)
             torch.cuda.synchronize()
             wall = time.perf_counter() - t0
-    finally:
-        gc.enable()
+        finally:
+            gc.enable()
 
     leg = {name: _stats([a.elapsed_time(b) for a, b in ev[name]]) for name in ev}
     t_causal, t_window, t_decode = (leg[n]["mean_ms"] for n in ("causal", "window", "decode"))
+    # The rooflines use the median interval of each kernel (the mean also
+    # carries the occasional long gap between two launches).
+    m_causal, m_window, m_decode = (leg[n]["median_ms"] for n in ("causal", "window", "decode"))
 
     # Infinity-Cache scrub for legs whose working set would otherwise stay
     # cached between repetitions: a 512 MiB write outside the timed region.
@@ -592,18 +606,22 @@ def gpu_bench(steps: int, warmup: int, extras: bool = True) -> dict:
     decode_gbs = b_decode / (t_decode * 1e-3) / 1e9
     value = 100.0 * 0.5 * (prefill_tflops / PEAK_BF16_TFLOPS + decode_gbs / PEAK_HBM_GBS)
 
+    r_causal = f_causal / (m_causal * 1e-3) / 1e12
+    r_window = b_prefill / (m_window * 1e-3) / 1e9
+    r_decode = b_decode / (m_decode * 1e-3) / 1e9
     roof_causal = {"kernel": "prefill_kernel (causal, L=8192, 64/8 heads)", "bound": "mfma",
-                   "achieved": causal_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                   "frac": causal_tflops / PEAK_BF16_TFLOPS, "traffic": _traffic("prefill_causal"),
-                   "ms": t_causal, "algorithmic_flop": f_causal}
+                   "achieved": r_causal, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                   "frac": r_causal / PEAK_BF16_TFLOPS, "traffic": _traffic("prefill_causal"),
+                   "ms": m_causal, "stat": "median", "algorithmic_flop": f_causal}
     roof_window = {"kernel": "prefill_kernel (window 128, L=8192, 64/8 heads)", "bound": "hbm",
-                   "achieved": window_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                   "frac": window_gbs / PEAK_HBM_GBS, "traffic": _traffic("prefill_window"),
-                   "ms": t_window, "algorithmic_bytes": b_prefill, "tflops": window_tflops}
+                   "achieved": r_window, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                   "frac": r_window / PEAK_HBM_GBS, "traffic": _traffic("prefill_window"),
+                   "ms": m_window, "stat": "median", "algorithmic_bytes": b_prefill,
+                   "tflops": f_window / (m_window * 1e-3) / 1e12}
     roof_decode = {"kernel": "decode_kernel + merge_kernel (B=64, ctx 8192, S=16)", "bound": "hbm",
-                   "achieved": decode_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                   "frac": decode_gbs / PEAK_HBM_GBS, "traffic": _traffic("decode_s16"),
-                   "ms": t_decode, "algorithmic_bytes": b_decode}
+                   "achieved": r_decode, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                   "frac": r_decode / PEAK_HBM_GBS, "traffic": _traffic("decode_s16"),
+                   "ms": m_decode, "stat": "median", "algorithmic_bytes": b_decode}
     return {
         "value": value, "ms_per_step": wall * 1e3 / steps,
         "prefill": {"tflops": prefill_tflops, "pct_mfma_peak": 100 * prefill_tflops / PEAK_BF16_TFLOPS,
@@ -884,6 +902,44 @@ def _other_configs(torch, np, binding, inputs, dev, bf16, timed, hbm_entry, mfma
         del aq, ak, av, ao
     torch.cuda.synchronize()
 
+    # draft tokens through the multi-token decode only: 8 per sequence (64
+    # columns per KV head), against the bf16 cache and against E4M3 caches
+    # (4 and 8 per sequence); causal, 1 and 4 splits
+    gen.manual_seed(8)
+    k_lens = [DEC_CTX] * DEC_BATCH
+    ak = _device_normal_bf16(torch, (sum(k_lens), HKV, D), gen, dev)
+    av = _device_normal_bf16(torch, (sum(k_lens), HKV, D), gen, dev)
+    fk = (torch.randn((sum(k_lens), HKV, D), generator=gen, device=dev) * 16.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    fv = (torch.randn((sum(k_lens), HKV, D), generator=gen, device=dev) * 16.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    asinks = torch.randn(HQ, generator=gen, device=dev, dtype=torch.float32)
+    ack = torch.tensor(np.concatenate([[0], np.cumsum(k_lens)]).astype(np.int32), device=dev)
+    for n_tok, fp8 in ((8, False), (4, True), (8, True)):
+        q_lens = [n_tok] * DEC_BATCH
+        aq = _device_normal_bf16(torch, (sum(q_lens), HQ, D), gen, dev)
+        acq = torch.tensor(np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32), device=dev)
+        ao = torch.empty_like(aq)
+        f = append_flops(q_lens, k_lens, 0)
+        b = append_bytes(q_lens, k_lens, 0)
+        if fp8:  # one byte per cached K / V element
+            b -= 2 * DEC_BATCH * DEC_CTX * HKV * D
+        for s_count in (1, 4):
+            aws = torch.empty(binding.decode_workspace_bytes(sum(q_lens), HQ, D, s_count), dtype=torch.uint8, device=dev)
+            if fp8:
+                st = timed(lambda: binding.decode_splitkv_multi_fp8(aq, fk, fv, 1.0 / 16, 1.0 / 16, acq, ack, n_tok,
+                                                                    DEC_CTX, asinks, 0, scale, s_count, workspace=aws,
+                                                                    out=ao))
+            else:
+                st = timed(lambda: binding.decode_splitkv_multi(aq, ak, av, acq, ack, n_tok, DEC_CTX, asinks, 0, scale,
+                                                                s_count, workspace=aws, out=ao))
+            e = hbm_entry(st, b, f)
+            e["bound"] = "hbm"
+            e["shape"] = "64 sequences, %d queries, 8192 keys (%s), 64/8 heads, causal, S=%d" % (
+                n_tok, "E4M3" if fp8 else "bf16", s_count)
+            out["%sdraft_verify_64x%d_multi_decode_s%d" % ("fp8_" if fp8 else "", n_tok, s_count)] = e
+        del aq, ao
+    del ak, av, fk, fv
+    torch.cuda.synchronize()
+
     # achievable bandwidth: a 2 GiB streaming read (torch sum over fp32) and a
     # 2 GiB device-to-device copy (4 GiB moved)
     n = (2 << 30) // 4
@@ -961,8 +1017,9 @@ def compact_record(full: dict, detail_path) -> dict:
         "decode_pct_hbm_by_splits": {k: _r(v["pct_hbm_peak"], 3) for k, v in dec["by_splits"].items()},
         "fp8_decode_pct_hbm_by_splits": {k: _r(v["pct_hbm_peak"], 3) for k, v in (dec.get("fp8_kv_by_splits") or {}).items()},
         "roofline": roof(full["roofline"]),
-        # the step's three legs: causal prefill (= roofline), window prefill, decode
-        "rooflines": [roof(r, named=False) for r in full["rooflines"]],
+        # the step's other two legs: window prefill, decode (the causal
+        # prefill is `roofline`)
+        "rooflines": [roof(r, named=False) for r in full["rooflines"][1:]],
         "cpu_baseline": cpu_c,
         "other_pct_of_peak": {k: _pct(v) for k, v in others.items()},
         "engine_clock_mhz": clock.get("mhz_median"), "clock_samples": clock.get("samples"),

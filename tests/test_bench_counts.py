@@ -101,7 +101,7 @@ def _fake_full_record(b, n_others):
                          "affinity_cores": 128, "kind": "oracle", "sample": "s" * 300, "sample_short": "s" * 100,
                          "prefill_seconds": 12.3456, "prefill_tflops_f64": 0.0456789, "decode_seconds": 3.456789,
                          "decode_gbs_f64": 0.3456789, "other_configs": {"x": {"seconds": 1.0}}},
-        "other_configs": {"workload_name_of_this_length_%02d_causal" % i: dict(entry) for i in range(n_others)},
+        "other_configs": {"workload_name_of_this_lengt_%02d_w128" % i: dict(entry) for i in range(n_others)},
         "bandwidth_reference": {"read": dict(st)}, "engine_clock": {"mhz_median": 2100, "samples": 40},
         "device": {"name": "AMD Instinct MI355X"},
     }
@@ -110,11 +110,11 @@ def _fake_full_record(b, n_others):
 def test_compact_line_fits_a_short_log_tail():
     """The last stdout line carries the headline, the rooflines and the CPU
     baseline in a few KB (a long line loses its head in a short log tail),
-    with every side workload named; here 42 side workloads (the benchmark has
-    37) with names of 41 characters (the benchmark's average is 33)."""
+    with every side workload named; here 46 side workloads (the benchmark has
+    43) with names of 35 characters (the benchmark's average is 33)."""
     import json
     b = _bench()
-    full = _fake_full_record(b, 42)
+    full = _fake_full_record(b, 46)
     line = json.dumps(b.compact_record(full, "gpurun_out/bench_detail.json"), separators=(",", ":"))
     assert len(line) < 4096, len(line)
     rec = json.loads(line)
@@ -123,4 +123,4 @@ def test_compact_line_fits_a_short_log_tail():
         assert rec[key] is not None, key
     assert set(rec["roofline"]) >= {"bound", "achieved", "peak", "unit", "frac", "traffic"}
     assert rec["cpu_baseline"]["cores"] == 16 and rec["cpu_baseline"]["affinity_cores"] == 128
-    assert len(rec["other_pct_of_peak"]) == 42 and len(rec["rooflines"]) == 3
+    assert len(rec["other_pct_of_peak"]) == 46 and len(rec["rooflines"]) == 2

@@ -17,7 +17,10 @@
 // per head (decode_kernel_w8p, one long split); or, with four or more
 // splits, one per (sequence, split) with a wave per KV head
 // (decode_kernel_hw).  The last two read adjacent pieces of the same token
-// rows of the cache from one workgroup, which streams faster.  K and V rows are read with fully
+// rows of the cache from one workgroup, which streams faster.  E4M3 caches
+// with one query token, G <= 8 and an even number of KV heads take
+// decode_kernel_pair: a wave streams both heads of a pair (128 contiguous
+// bytes per token) with its 16 MFMA columns split between them.  K and V rows are read with fully
 // coalesced 16-byte loads (8 lanes per 128-byte row; a key row of one head is
 // 128 contiguous bytes, rows are Hkv * 128 bytes apart), the next tile of a
 // wave is in flight while the current one is computed, and each tile passes
@@ -139,18 +142,21 @@ __device__ __forceinline__ void fetch_page_ids(PageIds& p, const int32_t* __rest
 
 // Lanes take the same keys and 16-byte pieces as load_tile; rows at or beyond
 // `end` repeat row end - 1.  pid covers page k0 >> page_shift.
+// Cache row (token slot in the pool) of key `key` of the tile whose pages
+// pid covers.
+__device__ __forceinline__ size_t paged_token(const PageIds& pid, int page_shift, int key) {
+  const int rel = (key >> page_shift) - pid.p0;  // 0, 1 or 2
+  // (as differences: written as a choice among the three ids, the compiler
+  // builds a per-work-item table in memory to index)
+  const int id = pid.id0 + (rel >= 1 ? pid.id1 - pid.id0 : 0) + (rel >= 2 ? pid.id2 - pid.id1 : 0);
+  return (static_cast<size_t>(id) << page_shift) + (key & ((1 << page_shift) - 1));
+}
+
 template <bool kFp8>
 __device__ __forceinline__ void load_tile_paged(TileRegs<kFp8>& t, const void* __restrict__ k,
                                                 const void* __restrict__ v, const PageIds& pid, int page_shift,
                                                 int hkv, int g, int k0, int end, int lane) {
-  const int slot_mask = (1 << page_shift) - 1;
-  auto token = [&](int key) {
-    const int rel = (key >> page_shift) - pid.p0;  // 0, 1 or 2
-    // (as differences: written as a choice among the three ids, the
-    // compiler builds a per-work-item table in memory to index)
-    const int id = pid.id0 + (rel >= 1 ? pid.id1 - pid.id0 : 0) + (rel >= 2 ? pid.id2 - pid.id1 : 0);
-    return (static_cast<size_t>(id) << page_shift) + (key & slot_mask);
-  };
+  auto token = [&](int key) { return paged_token(pid, page_shift, key); };
   if constexpr (kFp8) {
     const uint8_t* kb = static_cast<const uint8_t*>(k);
     const uint8_t* vb = static_cast<const uint8_t*>(v);
@@ -770,6 +776,291 @@ __global__ __launch_bounds__(256) void decode_kernel_w4(SINKATTN_DECODE_PARAMS) 
   decode_body<4, false, false, 1, kFp8, kMulti, kPaged, kN>(SINKATTN_DECODE_ARGS);
 }
 
+
+// E4M3 decode over pairs of KV heads (one query token, G <= 8, an even
+// number of KV heads).  A head's E4M3 row is 64 bytes, half of the 128-byte
+// line the next head's row completes, and waves that each read 64-byte
+// pieces 512 bytes apart stream at about 5.7 TB/s, against 6.2-7.0 TB/s for
+// waves reading whole 128-byte pieces with nontemporal loads (plain-load
+// probes, 64 x 8192 tokens x 8 KV heads).  So a wave here takes both heads
+// of a pair: lane l loads 16 bytes of token l / 8 + 8 i (i = 0..3), chunk
+// l % 8, of the pair's 128 contiguous bytes, and the 16 MFMA columns carry
+// the two heads' query heads (column c: head 2 p + c / 8, query head c % 8
+// of its group).  K rows of the two heads feed the A operand of two
+// 16x16x32 MFMAs whose B operands are Q^T with the other head's columns
+// zeroed, so each column accumulates only its own head's logits; P^T is
+// split the same way for O^T = V^T P^T.  Per key and head this is the same
+// matrix-core work as the single-head 16-column layout, with every softmax
+// lane used.
+//
+// Workgroup: one (sequence, pair, split) whose kW waves walk interleaved
+// 32-key tiles of the split and merge through LDS at the end.
+struct PairRegs {
+  u32x4_t k[4];
+  u32x4_t v[4];
+};
+
+// Staging tiles of a wave: K of head 0, K of head 1, V of head 0, V of head
+// 1 of the pair, bf16 rows of 64 (the swz layout), each followed by one
+// 128-byte row of padding so that a head-1 row sits in the other half of the
+// LDS banks from the head-0 row of the same token (the two are written by
+// the same 16 lanes).
+constexpr int kPairTileElems = kKeys * kHeadDim + 64;
+constexpr int kPairStageElems = 4 * kPairTileElems;
+
+template <int kW, bool kPaged>
+__device__ __forceinline__ void decode_pair_body(
+    const uint16_t* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ sinks, const int32_t* __restrict__ cu_seqlens_k, int hq, int hkv, int group,
+    int window, float scale_log2, int num_splits, uint16_t* __restrict__ o, float* __restrict__ lse,
+    float* __restrict__ o_part, float* __restrict__ lse_part, float v_scale, int out_rows,
+    const int32_t* __restrict__ block_table, int max_pages, int page_shift, int num_pages) {
+  __shared__ __attribute__((aligned(16))) uint16_t stage_all[kW * kPairStageElems];
+  __shared__ float red_m[kW][16];
+  __shared__ float red_l[kW][16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lc = lane & 15;  // MFMA column
+  const int lq = lane >> 4;  // k group of the MFMA operands
+  const int npairs = hkv >> 1;
+  int x = blockIdx.x;
+  const int split = x % num_splits;
+  x /= num_splits;
+  const int g0 = 2 * (x % npairs);  // first KV head of the pair
+  const int b = x / npairs;
+
+  const int hp = lc >> 3;  // head of the pair this column serves
+  const bool col_ok = (lc & 7) < group;
+  const int head = (g0 + hp) * group + (col_ok ? (lc & 7) : 0);
+
+  const int base = kPaged ? 0 : cu_seqlens_k[b];
+  const int len = kPaged ? cu_seqlens_k[b] : cu_seqlens_k[b + 1] - base;
+  const int32_t* bt_row = kPaged ? block_table + static_cast<size_t>(b) * max_pages : nullptr;
+  const int plast = kPaged ? min(max(len - 1, 0) >> page_shift, max_pages - 1) : 0;
+  const int lo = window > 0 ? max(0, len - window) : 0;
+  const int n = len - lo;
+  const int chunk = n > 0 ? (n + num_splits - 1) / num_splits : 0;
+  const int a = min(len, lo + split * chunk);
+  const int e = min(len, lo + (split + 1) * chunk);
+
+  const uint8_t* kb8 = static_cast<const uint8_t*>(k);
+  const uint8_t* vb8 = static_cast<const uint8_t*>(v);
+  PageIds pids{-1, 0, 0, 0};
+  auto load = [&](PairRegs& t, int k0, int end) {
+    if constexpr (kPaged) fetch_page_ids(pids, bt_row, k0 >> page_shift, plast, num_pages);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = min(k0 + (lane >> 3) + 8 * i, end - 1);
+      const size_t tok = kPaged ? paged_token(pids, page_shift, key) : static_cast<size_t>(base + key);
+      const size_t off = (tok * hkv + g0) * kHeadDim + (lane & 7) * 16;  // bytes
+      t.k[i] = load16_stream(reinterpret_cast<const uint16_t*>(kb8 + off));
+      t.v[i] = load16_stream(reinterpret_cast<const uint16_t*>(vb8 + off));
+    }
+  };
+
+  uint16_t* const stage = stage_all + wave * kPairStageElems;
+  uint16_t* const kt0 = stage;
+  uint16_t* const kt1 = stage + kPairTileElems;
+  uint16_t* const vt0 = stage + 2 * kPairTileElems;
+  uint16_t* const vt1 = stage + 3 * kPairTileElems;
+
+  PairRegs cur, nxt;
+  int k0 = a + kKeys * wave;
+  if (k0 < e) load(cur, k0, e);
+
+  // Q^T (B operand): column lc, d = 32 s + 8 lq + t; qz[h][s] keeps only the
+  // columns of head h of the pair.
+  bf16x8_t qz[2][2];
+  {
+    const bf16x8_t zero = __builtin_bit_cast(bf16x8_t, zero_u32x4());
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const u32x4_t val = load16(q + (static_cast<size_t>(b) * hq + head) * kHeadDim + 32 * s + 8 * lq);
+      const bf16x8_t qv = __builtin_bit_cast(bf16x8_t, val);
+      qz[0][s] = hp == 0 ? qv : zero;
+      qz[1][s] = hp == 1 ? qv : zero;
+    }
+  }
+  // The sink (split 0, wave 0), folded in after the keys.
+  const float z = (split == 0 && wave == 0 && sinks != nullptr && col_ok) ? sinks[head] : kNegInf;
+  float m2 = kNegInf, lsum = 0.0f;
+  f32x4_t acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[db][r] = 0.0f;
+
+  auto tile_step = [&](const PairRegs& t, int k0, int end) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // previous tile's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (lane >> 3) + 8 * i;
+      const int ch = lane & 7;
+      const int d0 = (ch & 3) * 16;
+      uint16_t* kt = (ch >> 2) ? kt1 : kt0;
+      uint16_t* vt = (ch >> 2) ? vt1 : vt0;
+      u32x4_t lo, hi;
+      e4m3x16_to_bf16(t.k[i], lo, hi);
+      *reinterpret_cast<u32x4_t*>(kt + swz(r, d0)) = lo;
+      *reinterpret_cast<u32x4_t*>(kt + swz(r, d0 + 8)) = hi;
+      e4m3x16_to_bf16(t.v[i], lo, hi);
+      *reinterpret_cast<u32x4_t*>(vt + swz(r, d0)) = lo;
+      *reinterpret_cast<u32x4_t*>(vt + swz(r, d0 + 8)) = hi;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // K and V tiles written
+
+    // S^T = K Q^T: C register i of key block kb is key 8 lq + 4 kb + i.
+    f32x4_t sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sacc[kb][r] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int off = swz(key16_of_row(lc, kb), 32 * s + 8 * lq);
+        const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(kt0 + off);
+        const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(kt1 + off);
+        sacc[kb] = mfma_16x16x32(a0, qz[0][s], sacc[kb]);
+        sacc[kb] = mfma_16x16x32(a1, qz[1][s], sacc[kb]);
+      }
+    }
+    if (k0 + kKeys > end) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (k0 + 8 * lq + 4 * kb + r >= end) sacc[kb][r] = kNegInf;
+    }
+
+    // Online softmax (log2 units) and P: pb[4 kb + i] is key 8 lq + 4 kb + i.
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = quad_max(mx) * scale_log2;
+    const float m_new = fmaxf(m2, mx);
+    const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
+    const float alpha = fast_exp2(m2 - m_use);
+    m2 = m_new;
+    float psum = 0.0f;
+    bf16x8_t pb;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pr = fast_exp2(fmaf(sacc[kb][r], scale_log2, -m_use));
+        psum += pr;
+        pb[4 * kb + r] = static_cast<__bf16>(pr);
+      }
+    lsum = lsum * alpha + psum;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[db][r] *= alpha;
+    const bf16x8_t zero = __builtin_bit_cast(bf16x8_t, zero_u32x4());
+    const bf16x8_t p0 = hp == 0 ? pb : zero;
+    const bf16x8_t p1 = hp == 1 ? pb : zero;
+
+    // O^T += V^T P^T: V^T rows d = 16 db + lc, keys 8 lq + 0..7.
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int rbase = 8 * lq + (lc >> 2);
+      const int dcol = 16 * db + 4 * (lc & 3);
+      const bf16x8_t a0 = cat4(lds_read_tr(vt0 + swz(rbase, dcol)), lds_read_tr(vt0 + swz(rbase + 4, dcol)));
+      const bf16x8_t a1 = cat4(lds_read_tr(vt1 + swz(rbase, dcol)), lds_read_tr(vt1 + swz(rbase + 4, dcol)));
+      acc[db] = mfma_16x16x32(a0, p0, acc[db]);
+      acc[db] = mfma_16x16x32(a1, p1, acc[db]);
+    }
+  };
+
+  constexpr int kStride = kKeys * kW;
+  for (; k0 < e; k0 += kStride) {
+    const int k1 = k0 + kStride;
+    if (k1 < e) load(nxt, k1, e);
+    tile_step(cur, k0, e);
+    cur = nxt;
+  }
+
+  // The sink: one more logit with no value.
+  if (z > kNegInf) {
+    const float z2 = z * kLog2e;
+    const float m_new = fmaxf(m2, z2);
+    const float alpha = fast_exp2(m2 - m_new);  // 0 when no key was seen
+    lsum = lsum * alpha + (lq == 0 ? fast_exp2(z2 - m_new) : 0.0f);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[db][r] *= alpha;
+    m2 = m_new;
+  }
+  const float den = quad_sum(lsum);
+
+  auto emit = [&](int col_head, int d, float out, float out_lse) {
+    if (num_splits == 1) {
+      o[(static_cast<size_t>(b) * hq + col_head) * kHeadDim + d] = to_bf16_bits(out);
+      if (lse != nullptr && d == 0) lse[static_cast<size_t>(b) * hq + col_head] = out_lse;
+    } else {
+      const size_t prow = (static_cast<size_t>(split) * out_rows + b) * hq + col_head;
+      o_part[prow * kHeadDim + d] = out;
+      if (d == 0) lse_part[prow] = out_lse;
+    }
+  };
+
+  if constexpr (kW == 1) {
+    if (!col_ok) return;
+    const float inv = den > 0.0f ? v_scale / den : 0.0f;
+    const float out_lse = den > 0.0f ? (m2 + __log2f(den)) * kLn2 : kNegInf;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) emit(head, 16 * db + 4 * lq + r, acc[db][r] * inv, out_lse);
+    return;
+  }
+
+  // Cross-wave merge: each wave publishes (m, l, unnormalised O) per column.
+  float* red_o = reinterpret_cast<float*>(stage_all);  // [wave][16 columns][64 d]
+  __syncthreads();  // every wave is done with its staging tiles
+  if (lq == 0) {
+    red_m[wave][lc] = m2;
+    red_l[wave][lc] = den;
+  }
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red_o[(wave * 16 + lc) * kHeadDim + 16 * db + 4 * lq + r] = acc[db][r];
+  __syncthreads();
+  for (int idx = tid; idx < 16 * kHeadDim; idx += 64 * kW) {
+    const int c = idx / kHeadDim;
+    const int d = idx % kHeadDim;
+    if ((c & 7) >= group) continue;
+    float big_m = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) big_m = fmaxf(big_m, red_m[w][c]);
+    float out = 0.0f, out_lse = kNegInf;
+    if (big_m > kNegInf) {
+      float num = 0.0f, tot = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kW; ++w) {
+        const float sc = fast_exp2(red_m[w][c] - big_m);
+        tot += sc * red_l[w][c];
+        num += sc * red_o[(w * 16 + c) * kHeadDim + d];
+      }
+      out = num / tot * v_scale;
+      out_lse = (big_m + __log2f(tot)) * kLn2;
+    }
+    emit((g0 + (c >> 3)) * group + (c & 7), d, out, out_lse);
+  }
+}
+
+template <int kW, bool kPaged>
+__global__ __launch_bounds__(64 * kW) void decode_kernel_pair(SINKATTN_DECODE_PARAMS) {
+  decode_pair_body<kW, kPaged>(q, k, v, sinks, cu_seqlens_k, hq, hkv, group, window, scale_log2, num_splits, o, lse,
+                               o_part, lse_part, v_scale, out_rows, block_table, max_pages, page_shift, num_pages);
+}
+
 #undef SINKATTN_DECODE_PARAMS
 #undef SINKATTN_DECODE_ARGS
 
@@ -881,8 +1172,46 @@ static hipError_t launch_decode_t(const DecodeLaunch& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The E4M3 pair kernel: waves per workgroup so that about kPairWavesTarget
+// waves are launched (8 per CU), and no wave is left without a tile.
+constexpr long long kPairWavesTarget = 2048;
+
+template <int kW, bool kPaged>
+static hipError_t launch_pair_w(const DecodeLaunch& a, int splits, hipStream_t stream) {
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const unsigned grid = static_cast<unsigned>(static_cast<long long>(a.batch) * (a.num_kv_heads / 2) * splits);
+  hipLaunchKernelGGL((decode_kernel_pair<kW, kPaged>), dim3(grid), dim3(64 * kW), 0, stream,
+                     static_cast<const uint16_t*>(a.q), a.k, a.v, a.sinks, a.cu_seqlens_k, a.batch, a.num_q_heads,
+                     a.num_kv_heads, group, a.window, a.softmax_scale * a.k_scale * kLog2e, splits,
+                     static_cast<uint16_t*>(a.o), a.lse, a.o_part, a.lse_part, 1, a.v_scale, nullptr, group, a.batch,
+                     a.block_table, a.max_pages, a.page_shift, a.num_pages);
+  return hipGetLastError();
+}
+
+template <bool kPaged>
+static hipError_t launch_decode_pair(const DecodeLaunch& a, hipStream_t stream) {
+  const int splits = decode_merges_in_kernel(a) ? 1 : a.num_splits;
+  const long long units = static_cast<long long>(a.batch) * (a.num_kv_heads / 2) * splits;
+  const long long tiles = ((max_range(a) + splits - 1) / splits + kKeys - 1) / kKeys;
+  int w = 1;
+  while (w < 8 && units * w * 2 <= kPairWavesTarget && w * 2 <= tiles) w *= 2;
+  switch (w) {
+    case 8: return launch_pair_w<8, kPaged>(a, splits, stream);
+    case 4: return launch_pair_w<4, kPaged>(a, splits, stream);
+    case 2: return launch_pair_w<2, kPaged>(a, splits, stream);
+    default: return launch_pair_w<1, kPaged>(a, splits, stream);
+  }
+}
+
+static bool decode_pairs(const DecodeLaunch& a) {
+  return a.fp8 && a.cu_seqlens_q == nullptr && a.num_kv_heads % 2 == 0 && a.num_q_heads / a.num_kv_heads <= 8;
+}
+
 template <bool kFp8, bool kMulti, bool kPaged>
 static hipError_t launch_decode_cols(const DecodeLaunch& a, hipStream_t stream) {
+  if constexpr (kFp8 && !kMulti) {
+    if (decode_pairs(a)) return launch_decode_pair<kPaged>(a, stream);
+  }
   const int cols = decode_cols(a);
   if constexpr (kMulti) {
     if (cols == 64) return launch_decode_t<64, kFp8, kMulti, kPaged>(a, stream);

@@ -4,7 +4,9 @@ performance optimizations on NVIDIA Blackwell", FlashInfer integration).
 
 Every decode kernel shape is reached: one short or long split (two-wave,
 head-pair and four-wave workgroups), long splits per wave, a wave per KV
-head, and window layers whose splits are evaluated as one range.  Bar as the
+head, the KV-head-pair kernel (G <= 8 over an even number of KV heads: a
+wave streams both heads of a pair), and window layers whose splits are
+evaluated as one range.  Bar as the
 bf16 path: max |err| <= 2e-2, mean |err| <= 2e-3, lse within 4e-3.
 """
 
@@ -43,6 +45,22 @@ def test_fp8_decode_kernel_shapes(hq, hkv, splits):
         o, lse, ro, rl = _case(d, window, splits)
         assert_close_out(o, ro, "fp8 G=%d S=%d W=%d" % (hq // hkv, splits, window))
         assert_close_lse(lse, rl, "fp8")
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (24, 4), (64, 8), (128, 16), (4, 2)])
+@pytest.mark.parametrize("splits", [1, 3, 16, 64])
+def test_fp8_pair_kernel(hq, hkv, splits):
+    """The KV-head-pair kernel (one query token, G <= 8, an even number of KV
+    heads) at G = 1, 2, 6 and 8, with 1-, 2-, 4- and 8-wave workgroups (the
+    wave count follows sequences x pairs x splits and the tiles per split),
+    ragged lengths with more splits than some sequences have tiles, and
+    window layers (evaluated as one range)."""
+    d = inputs.make_decode_fp8([1, 33, 700, 4100, 32, 2049], hq=hq, hkv=hkv, seed=hq * 11 + hkv + splits)
+    d.sinks[1] = -np.inf
+    for window in (0, 128, 1800):
+        o, lse, ro, rl = _case(d, window, splits)
+        assert_close_out(o, ro, "fp8 pair G=%d Hkv=%d S=%d W=%d" % (hq // hkv, hkv, splits, window))
+        assert_close_lse(lse, rl, "fp8 pair")
 
 
 @pytest.mark.parametrize("k_scale,v_scale", [(1.0 / 16, 1.0 / 8), (0.0371, 0.0213), (1.0, 1.0 / 64)])

@@ -206,7 +206,9 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
   // Ring of LDS tile buffers, each K rows then V rows.  Tile t lives in
   // buffer (t - t_begin) % kBufs; the loop below is unrolled over the ring so
   // every LDS address is a per-lane base plus an immediate offset.
-  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[kBufs][2 * kKTile * kHeadDim];
+  // Window layers get a fifth buffer: a query tile whose keys span at most
+  // three tiles then has all of them and its Q block in flight at once.
+  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[kWindow ? kBufs + 1 : kBufs][2 * kKTile * kHeadDim];
 
   constexpr int kThreads = threads_for<kCols>();
   constexpr int kCopies = copies_per_tile<kThreads>();
@@ -278,11 +280,17 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
   // The first two tiles go out before anything else, then the workgroup's
   // Q block (32 tokens x 8 head slots x 128 B, 1 KB contiguous per token)
   // into buffers 2 and 3, which receive their tiles once Q is in registers.
+  // A window tile whose keys span at most three tiles (the 128-token window)
+  // sends its third tile at once too and puts Q in buffers 3 and 4: one
+  // round trip to memory instead of two.
+  const bool all_at_once = kWindow && t_end - t_begin <= 2;
+  const int q_buf = all_at_once ? 3 : 2;
   if (t_begin <= t_end) issue(t_begin, 0);
   if (t_begin + 1 <= t_end) issue(t_begin + 1, 1);
-  uint16_t* const q_lds = &kv_lds[2][0];
+  if (all_at_once && t_begin + 2 <= t_end) issue(t_begin + 2, 2);
+  uint16_t* const q_lds = &kv_lds[q_buf][0];
   {
-    const uint32_t q_dst = ring + 2 * (2 * kKTile * kHeadDim * 2);
+    const uint32_t q_dst = ring + q_buf * (2 * kKTile * kHeadDim * 2);
     const int slot = lane >> 3;
     const int head_q = g * group + min(hchunk * kHeadsPerBlock + slot, group - 1);
 #pragma unroll
@@ -489,8 +497,10 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
                                                      (((2 * s + half) ^ (col & 7)) << 3));
   }
   lds_barrier();
-  if (t_begin + 2 <= t_end) issue(t_begin + 2, 2);
-  if (t_begin + 3 <= t_end) issue(t_begin + 3, 3);
+  if (!all_at_once) {
+    if (t_begin + 2 <= t_end) issue(t_begin + 2, 2);
+    if (t_begin + 3 <= t_end) issue(t_begin + 3, 3);
+  }
 
   if (wave_active) {
     // Prologue: S of step h_begin, K of step h_begin + 1, empty P of step

@@ -1160,7 +1160,11 @@ static hipError_t launch_decode_t(const DecodeLaunch& a, hipStream_t stream) {
     grid = static_cast<unsigned>(a.batch) * a.num_kv_heads * ((splits + 3) / 4);
     threads = 256;
     kernel = decode_kernel_ps<kFp8, kMulti, kPaged, kN>;
-  } else if (!short_chunks) {
+  } else if (!short_chunks || (splits == 1 && max_range(a) <= kDirectWholeKeys && kN <= 32)) {
+    // (a whole range of at most kDirectWholeKeys keys, a 128-token window
+    // layer: four waves take its 4-5 tiles one or two each, a shorter chain
+    // than two waves' 2-3; 16 x 32768 8.4 -> 7.8 us, 64 x 4 draft tokens
+    // 19.4 -> 17.4 us, eight waves slower again at 64 sequences)
     threads = 256;
     kernel = decode_kernel_w4<kFp8, kMulti, kPaged, kN>;
   }

@@ -15,10 +15,11 @@
 // kOprojTiles weight tiles); the 8 waves split K into 8 slices, so W is read
 // once per 64 rows (from HBM for the first block) while o stays in L2, and
 // the slices are summed through LDS, where the bias is added and the result
-// rounded to bf16.  The
-// split-KV merge is not fused in: every 32-feature tile would re-read all of
-// the split partials, so the merge writes o once (bf16) and this kernel reads
-// it from L2.
+// rounded to bf16.  The split-KV merge is not fused in: every feature tile
+// would re-read all of the split partials of its rows (a probe that forms o
+// from 16 partials inside the K loop ran 172-181 us at 64 rows x 4096 ->
+// 2880, against 29-36 us for the merge followed by this kernel), so the
+// merge writes o once (bf16) and this kernel reads it from L2.
 #include "device_common.hpp"
 #include "launch.hpp"
 

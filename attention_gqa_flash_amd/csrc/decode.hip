@@ -847,9 +847,14 @@ __device__ __forceinline__ void decode_pair_body(
 
   const uint8_t* kb8 = static_cast<const uint8_t*>(k);
   const uint8_t* vb8 = static_cast<const uint8_t*>(v);
+  // Paged: the ids of the pages a tile needs are read one tile ahead (a
+  // wave's next tile starts kKeys * kW keys on), so that no row address of a
+  // tile waits for a table read.
   PageIds pids{-1, 0, 0, 0};
   auto load = [&](PairRegs& t, int k0, int end) {
-    if constexpr (kPaged) fetch_page_ids(pids, bt_row, k0 >> page_shift, plast, num_pages);
+    if constexpr (kPaged) {
+      if ((k0 >> page_shift) != pids.p0) fetch_page_ids(pids, bt_row, k0 >> page_shift, plast, num_pages);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key = min(k0 + (lane >> 3) + 8 * i, end - 1);
@@ -858,6 +863,7 @@ __device__ __forceinline__ void decode_pair_body(
       t.k[i] = load16_stream(reinterpret_cast<const uint16_t*>(kb8 + off));
       t.v[i] = load16_stream(reinterpret_cast<const uint16_t*>(vb8 + off));
     }
+    if constexpr (kPaged) fetch_page_ids(pids, bt_row, (k0 + kKeys * kW) >> page_shift, plast, num_pages);
   };
 
   uint16_t* const stage = stage_all + wave * kPairStageElems;

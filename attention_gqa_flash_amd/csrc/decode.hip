@@ -776,7 +776,6 @@ __global__ __launch_bounds__(256) void decode_kernel_w4(SINKATTN_DECODE_PARAMS) 
   decode_body<4, false, false, 1, kFp8, kMulti, kPaged, kN>(SINKATTN_DECODE_ARGS);
 }
 
-
 // E4M3 decode over pairs of KV heads (one query token, G <= 8, an even
 // number of KV heads).  A head's E4M3 row is 64 bytes, half of the 128-byte
 // line the next head's row completes, and waves that each read 64-byte

@@ -1015,13 +1015,32 @@ __device__ __forceinline__ void decode_pair_body(
   };
 
   if constexpr (kW == 1) {
+    // A lane holds d = 16 db + 4 lq + 0..3 of its column: one 8- or 16-byte
+    // store per db.
     if (!col_ok) return;
     const float inv = den > 0.0f ? v_scale / den : 0.0f;
     const float out_lse = den > 0.0f ? (m2 + __log2f(den)) * kLn2 : kNegInf;
+    if (num_splits == 1) {
+      uint16_t* orow = o + (static_cast<size_t>(b) * hq + head) * kHeadDim + 4 * lq;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db) {
+        u16x4_t w;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) emit(head, 16 * db + 4 * lq + r, acc[db][r] * inv, out_lse);
+        for (int r = 0; r < 4; ++r) w[r] = to_bf16_bits(acc[db][r] * inv);
+        *reinterpret_cast<u16x4_t*>(orow + 16 * db) = w;
+      }
+      if (lse != nullptr && lq == 0) lse[static_cast<size_t>(b) * hq + head] = out_lse;
+    } else {
+      const size_t prow = (static_cast<size_t>(split) * out_rows + b) * hq + head;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        f32x4_t w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = acc[db][r] * inv;
+        *reinterpret_cast<f32x4_t*>(o_part + prow * kHeadDim + 16 * db + 4 * lq) = w;
+      }
+      if (lq == 0) lse_part[prow] = out_lse;
+    }
     return;
   }
 

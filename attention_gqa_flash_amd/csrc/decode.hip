@@ -428,6 +428,17 @@ __device__ __forceinline__ void decode_body(
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb)
     z[cb] = (split == 0 && (kOwnSplit || wl == 0) && sinks != nullptr && col_ok[cb]) ? sinks[head[cb]] : kNegInf;
+  // Q and the sink are taken into registers before the loop (the first
+  // tile, requested before them, has then landed too).  Without this use the
+  // compiler's wait counters treat their loads as possibly still in flight
+  // inside the loop and wait for every outstanding load there, the next
+  // tile's included, which leaves no tile in flight during the computation.
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) {
+#pragma unroll
+    for (int s = 0; s < L::kQRegs; ++s) asm volatile("" ::"v"(qreg[cb][s]));
+    asm volatile("" ::"v"(z[cb]));
+  }
   float m2[kCB], lsum[kCB];
   typename L::Acc acc[kCB][L::kAccBlocks];
   auto reset_state = [&]() {
@@ -890,6 +901,10 @@ __device__ __forceinline__ void decode_pair_body(
   }
   // The sink (split 0, wave 0), folded in after the keys.
   const float z = (split == 0 && wave == 0 && sinks != nullptr && col_ok) ? sinks[head] : kNegInf;
+  // Q and the sink in registers before the loop (see decode_body).
+#pragma unroll
+  for (int s = 0; s < 2; ++s) asm volatile("" ::"v"(qz[0][s]), "v"(qz[1][s]));
+  asm volatile("" ::"v"(z));
   float m2 = kNegInf, lsum = 0.0f;
   f32x4_t acc[4];
 #pragma unroll

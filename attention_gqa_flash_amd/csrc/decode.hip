@@ -48,6 +48,10 @@ constexpr int kShortChunk = 1024;
 // against 5.5 with the waves interleaved; at S = 16, 512-key splits, the
 // two-wave interleaved kernel is 12% faster).
 constexpr int kSplitPerWaveMin = 4;
+// ... when that still launches at least this many workgroups; fewer (few KV
+// heads: 64 x 8192 with 16 / 2 heads at S = 4 has 128) leave most CUs idle,
+// and the four-wave interleaved kernel takes the splits one workgroup each.
+constexpr long long kSplitPerWaveMinGroups = 256;
 // With at least kHeadPerWaveMinSplits splits of at least kHeadPerWaveMinKeys
 // keys over 4 to 8 KV heads, a workgroup is one (sequence, split) and its
 // waves are the KV heads (decode_kernel_hw): 64 x 8192 at S = 4 from 182 to
@@ -1195,7 +1199,8 @@ static hipError_t launch_decode_t(const DecodeLaunch& a, hipStream_t stream) {
     grid = static_cast<unsigned>(a.batch) * (a.num_kv_heads / 2);
     threads = 512;
     kernel = decode_kernel_w8p<kFp8, kMulti, kPaged, kN>;
-  } else if (splits >= kSplitPerWaveMin && !short_chunks) {
+  } else if (splits >= kSplitPerWaveMin && !short_chunks &&
+             static_cast<long long>(a.batch) * a.num_kv_heads * ((splits + 3) / 4) >= kSplitPerWaveMinGroups) {
     grid = static_cast<unsigned>(a.batch) * a.num_kv_heads * ((splits + 3) / 4);
     threads = 256;
     kernel = decode_kernel_ps<kFp8, kMulti, kPaged, kN>;

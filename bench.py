@@ -940,6 +940,40 @@ def _other_configs(torch, np, binding, inputs, dev, bf16, timed, hbm_entry, mfma
     del ak, av, fk, fv
     torch.cuda.synchronize()
 
+    # one GPU's share of the heads under 4-way tensor parallelism (16 query /
+    # 2 KV heads, the decode layout of the cost section), same batch, context
+    # and sequence length: decode at 1, 4 and 16 splits and the causal
+    # prefill; the quarter-size cache is read after a scrub
+    gen.manual_seed(8)
+    thq, thkv = HQ // 4, HKV // 4
+    tq = _device_normal_bf16(torch, (DEC_BATCH, thq, D), gen, dev)
+    tk = _device_normal_bf16(torch, (DEC_BATCH * DEC_CTX, thkv, D), gen, dev)
+    tv = _device_normal_bf16(torch, (DEC_BATCH * DEC_CTX, thkv, D), gen, dev)
+    tsinks = torch.randn(thq, generator=gen, device=dev, dtype=torch.float32)
+    tcu = torch.arange(0, (DEC_BATCH + 1) * DEC_CTX, DEC_CTX, dtype=torch.int32, device=dev)
+    to_ = torch.empty_like(tq)
+    tws = torch.empty(binding.decode_workspace_bytes(DEC_BATCH, thq, D, 16), dtype=torch.uint8, device=dev)
+    for s_count in (1, 4, 16):
+        st = timed(lambda: binding.decode_splitkv(tq, tk, tv, tcu, DEC_CTX, tsinks, 0, scale, s_count,
+                                                  workspace=tws, out=to_), scrub_each=True)
+        e = hbm_entry(st, decode_bytes([DEC_CTX] * DEC_BATCH, 0, thq, thkv))
+        e["shape"] = "B=64, ctx 8192, 16/2 heads (the 4-way tensor-parallel share), S=%d" % s_count
+        out["tp4_share_decode_s%d" % s_count] = e
+    del tq, tk, tv, to_, tws
+    pq4 = _device_normal_bf16(torch, (PREFILL_LEN, thq, D), gen, dev)
+    pk4 = _device_normal_bf16(torch, (PREFILL_LEN, thkv, D), gen, dev)
+    pv4 = _device_normal_bf16(torch, (PREFILL_LEN, thkv, D), gen, dev)
+    pcu4 = torch.tensor([0, PREFILL_LEN], dtype=torch.int32, device=dev)
+    po4 = torch.empty_like(pq4)
+    st = timed(lambda: binding.prefill_varlen(pq4, pk4, pv4, tsinks, pcu4, PREFILL_LEN, 0, scale, out=po4),
+               scrub_each=True)
+    e = mfma_entry(st, prefill_flops([PREFILL_LEN], 0, hq=thq), prefill_bytes([PREFILL_LEN], 0, thq, thkv))
+    e["bound"] = "mfma"
+    e["shape"] = "B=1, L=8192, 16/2 heads (the 4-way tensor-parallel share), causal"
+    out["tp4_share_prefill_causal"] = e
+    del pq4, pk4, pv4, po4
+    torch.cuda.synchronize()
+
     # achievable bandwidth: a 2 GiB streaming read (torch sum over fp32) and a
     # 2 GiB device-to-device copy (4 GiB moved)
     n = (2 << 30) // 4

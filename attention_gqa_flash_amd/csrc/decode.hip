@@ -52,6 +52,10 @@ constexpr int kSplitPerWaveMin = 4;
 // heads: 64 x 8192 with 16 / 2 heads at S = 4 has 128) leave most CUs idle,
 // and the four-wave interleaved kernel takes the splits one workgroup each.
 constexpr long long kSplitPerWaveMinGroups = 256;
+// A single long split serves pairs of KV heads per workgroup (w8p) when
+// that gives at least this many workgroups; fewer (64 x 8192 with 16 / 2
+// heads: 64) take one KV head per workgroup (w8) for twice as many.
+constexpr long long kPairMinGroups = 128;
 // With at least kHeadPerWaveMinSplits splits of at least kHeadPerWaveMinKeys
 // keys over 4 to 8 KV heads, a workgroup is one (sequence, split) and its
 // waves are the KV heads (decode_kernel_hw): 64 x 8192 at S = 4 from 182 to
@@ -783,6 +787,13 @@ __global__ __launch_bounds__(512) void decode_kernel_w8p(SINKATTN_DECODE_PARAMS)
   decode_body<8, false, false, 2, kFp8, kMulti, kPaged, kN>(SINKATTN_DECODE_ARGS);
 }
 
+// One long split when the pairs of KV heads give too few workgroups (few KV
+// heads): eight interleaved waves on one KV head, twice the workgroups.
+template <bool kFp8, bool kMulti, bool kPaged, int kN>
+__global__ __launch_bounds__(512) void decode_kernel_w8(SINKATTN_DECODE_PARAMS) {
+  decode_body<8, false, false, 1, kFp8, kMulti, kPaged, kN>(SINKATTN_DECODE_ARGS);
+}
+
 // Long splits: four-wave workgroups at the compiler's own register budget
 // (two waves per SIMD; at three, S = 4 on 64 x 8192 would end on a
 // two-thirds-full round of workgroups).
@@ -1195,6 +1206,11 @@ static hipError_t launch_decode_t(const DecodeLaunch& a, hipStream_t stream) {
     grid = static_cast<unsigned>(static_cast<long long>(a.batch) * ((splits + per_wg - 1) / per_wg));
     threads = 64 * a.num_kv_heads;
     kernel = decode_kernel_hw<kFp8, kMulti, kPaged, kN>;
+  } else if (splits == 1 && !short_chunks &&
+             static_cast<long long>(a.batch) * (a.num_kv_heads / 2) < kPairMinGroups) {
+    grid = static_cast<unsigned>(a.batch) * a.num_kv_heads;
+    threads = 512;
+    kernel = decode_kernel_w8<kFp8, kMulti, kPaged, kN>;
   } else if (splits == 1 && !short_chunks && a.num_kv_heads % 2 == 0) {
     grid = static_cast<unsigned>(a.batch) * (a.num_kv_heads / 2);
     threads = 512;
@@ -1252,7 +1268,11 @@ static hipError_t launch_decode_pair(const DecodeLaunch& a, hipStream_t stream) 
 }
 
 static bool decode_pairs(const DecodeLaunch& a) {
-  return a.fp8 && a.cu_seqlens_q == nullptr && a.num_kv_heads % 2 == 0 && a.num_q_heads / a.num_kv_heads <= 8;
+  // (a single split over too few pairs of KV heads takes the one-head
+  // eight-wave kernel instead, for twice the workgroups)
+  const bool few_pairs = a.num_splits == 1 && static_cast<long long>(a.batch) * (a.num_kv_heads / 2) < kPairMinGroups;
+  return a.fp8 && a.cu_seqlens_q == nullptr && a.num_kv_heads % 2 == 0 && a.num_q_heads / a.num_kv_heads <= 8 &&
+         !few_pairs;
 }
 
 template <bool kFp8, bool kMulti, bool kPaged>

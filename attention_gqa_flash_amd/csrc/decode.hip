@@ -14,7 +14,8 @@
 // softmax states, merged through LDS at the end (decode_kernel_w2/_w4); one
 // per (sequence, KV head, 4 splits) with a split per wave (decode_kernel_ps);
 // one per (sequence, pair of KV heads, split) with four interleaved waves
-// per head (decode_kernel_w8p, one long split); or, with four or more
+// per head (decode_kernel_w8p, one long split), or per (sequence, KV head)
+// with eight (decode_kernel_w8, one long split over few KV heads); or, with four or more
 // splits, one per (sequence, split) with a wave per KV head
 // (decode_kernel_hw).  The last two read adjacent pieces of the same token
 // rows of the cache from one workgroup, which streams faster.  E4M3 caches

@@ -354,14 +354,28 @@ _KERNEL_SOURCES = {"prefill": ("prefill.hip", "device_common.hpp"), "decode": ("
                    "merge": ("decode.hip", "device_common.hpp")}
 
 
+def _code_only(text: str) -> str:
+    """Source text without its // comments, trailing blanks and empty lines:
+    what a comment-only edit leaves unchanged."""
+    lines = []
+    for line in text.splitlines():
+        cut = line.find("//")
+        if cut >= 0 and line.count('"', 0, cut) % 2 == 0:  # not inside a string literal
+            line = line[:cut]
+        line = line.rstrip()
+        if line:
+            lines.append(line)
+    return "\n".join(lines)
+
+
 def kernel_source_hash(kernel: str) -> str:
-    """Hash of the sources of one counted kernel ('prefill_causal',
-    'decode_s16', ...)."""
+    """Hash of the code (comments aside) of the sources of one counted kernel
+    ('prefill_causal', 'decode_s16', ...)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "attention_gqa_flash_amd", "csrc")
     for name in _KERNEL_SOURCES[kernel.split("_")[0]]:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -834,14 +834,18 @@ struct PairRegs {
 constexpr int kPairTileElems = kKeys * kHeadDim + 64;
 constexpr int kPairStageElems = 4 * kPairTileElems;
 
-template <int kW, bool kPaged>
+// kPW > 1 (with kW = 1): the workgroup is one (sequence, split) and its kPW
+// waves take its kPW pairs of KV heads, so that together they read whole
+// token rows (8 heads: 512 contiguous bytes).
+template <int kW, bool kPaged, int kPW = 1>
 __device__ __forceinline__ void decode_pair_body(
     const uint16_t* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ sinks, const int32_t* __restrict__ cu_seqlens_k, int hq, int hkv, int group,
     int window, float scale_log2, int num_splits, uint16_t* __restrict__ o, float* __restrict__ lse,
     float* __restrict__ o_part, float* __restrict__ lse_part, float v_scale, int out_rows,
     const int32_t* __restrict__ block_table, int max_pages, int page_shift, int num_pages) {
-  __shared__ __attribute__((aligned(16))) uint16_t stage_all[kW * kPairStageElems];
+  static_assert(kPW == 1 || kW == 1, "pair waves take whole splits");
+  __shared__ __attribute__((aligned(16))) uint16_t stage_all[(kW > kPW ? kW : kPW) * kPairStageElems];
   __shared__ float red_m[kW][16];
   __shared__ float red_l[kW][16];
 
@@ -854,8 +858,8 @@ __device__ __forceinline__ void decode_pair_body(
   int x = blockIdx.x;
   const int split = x % num_splits;
   x /= num_splits;
-  const int g0 = 2 * (x % npairs);  // first KV head of the pair
-  const int b = x / npairs;
+  const int g0 = kPW > 1 ? 2 * wave : 2 * (x % npairs);  // first KV head of the pair
+  const int b = kPW > 1 ? x : x / npairs;
 
   const int hp = lc >> 3;  // head of the pair this column serves
   const bool col_ok = (lc & 7) < group;
@@ -899,7 +903,7 @@ __device__ __forceinline__ void decode_pair_body(
   uint16_t* const vt1 = stage + 3 * kPairTileElems;
 
   PairRegs cur, nxt;
-  int k0 = a + kKeys * wave;
+  int k0 = kPW > 1 ? a : a + kKeys * wave;
   if (k0 < e) load(cur, k0, e);
 
   // Q^T (B operand): column lc, d = 32 s + 8 lq + t; qz[h][s] keeps only the
@@ -916,7 +920,7 @@ __device__ __forceinline__ void decode_pair_body(
     }
   }
   // The sink (split 0, wave 0), folded in after the keys.
-  const float z = (split == 0 && wave == 0 && sinks != nullptr && col_ok) ? sinks[head] : kNegInf;
+  const float z = (split == 0 && (kPW > 1 || wave == 0) && sinks != nullptr && col_ok) ? sinks[head] : kNegInf;
   // Q and the sink in registers before the loop (see decode_body).
 #pragma unroll
   for (int s = 0; s < 2; ++s) asm volatile("" ::"v"(qz[0][s]), "v"(qz[1][s]));
@@ -1116,6 +1120,15 @@ __global__ __launch_bounds__(64 * kW) void decode_kernel_pair(SINKATTN_DECODE_PA
                                o_part, lse_part, v_scale, out_rows, block_table, max_pages, page_shift, num_pages);
 }
 
+// Four or more splits over 4 or 8 KV heads: one workgroup per (sequence,
+// split), one wave per pair of KV heads.
+template <int kPW, bool kPaged>
+__global__ __launch_bounds__(64 * kPW) void decode_kernel_pair_hw(SINKATTN_DECODE_PARAMS) {
+  decode_pair_body<1, kPaged, kPW>(q, k, v, sinks, cu_seqlens_k, hq, hkv, group, window, scale_log2, num_splits, o,
+                                   lse, o_part, lse_part, v_scale, out_rows, block_table, max_pages, page_shift,
+                                   num_pages);
+}
+
 #undef SINKATTN_DECODE_PARAMS
 #undef SINKATTN_DECODE_ARGS
 
@@ -1253,9 +1266,25 @@ static hipError_t launch_pair_w(const DecodeLaunch& a, int splits, hipStream_t s
   return hipGetLastError();
 }
 
+template <int kPW, bool kPaged>
+static hipError_t launch_pair_hw(const DecodeLaunch& a, int splits, hipStream_t stream) {
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const unsigned grid = static_cast<unsigned>(static_cast<long long>(a.batch) * splits);
+  hipLaunchKernelGGL((decode_kernel_pair_hw<kPW, kPaged>), dim3(grid), dim3(64 * kPW), 0, stream,
+                     static_cast<const uint16_t*>(a.q), a.k, a.v, a.sinks, a.cu_seqlens_k, a.batch, a.num_q_heads,
+                     a.num_kv_heads, group, a.window, a.softmax_scale * a.k_scale * kLog2e, splits,
+                     static_cast<uint16_t*>(a.o), a.lse, a.o_part, a.lse_part, 1, a.v_scale, nullptr, group, a.batch,
+                     a.block_table, a.max_pages, a.page_shift, a.num_pages);
+  return hipGetLastError();
+}
+
 template <bool kPaged>
 static hipError_t launch_decode_pair(const DecodeLaunch& a, hipStream_t stream) {
   const int splits = decode_merges_in_kernel(a) ? 1 : a.num_splits;
+  if (splits >= kHeadPerWaveMinSplits) {
+    if (a.num_kv_heads == 8) return launch_pair_hw<4, kPaged>(a, splits, stream);
+    if (a.num_kv_heads == 4) return launch_pair_hw<2, kPaged>(a, splits, stream);
+  }
   const long long units = static_cast<long long>(a.batch) * (a.num_kv_heads / 2) * splits;
   const long long tiles = ((max_range(a) + splits - 1) / splits + kKeys - 1) / kKeys;
   int w = 1;

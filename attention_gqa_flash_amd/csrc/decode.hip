@@ -57,6 +57,10 @@ constexpr long long kSplitPerWaveMinGroups = 256;
 // that gives at least this many workgroups; fewer (64 x 8192 with 16 / 2
 // heads: 64) take one KV head per workgroup (w8) for twice as many.
 constexpr long long kPairMinGroups = 128;
+// Online softmax: the reference maximum (log2 units) is raised only when a
+// logit passes it by more than this, so most tiles skip the rescale of the
+// output accumulators; the unnormalised weights stay below 2^kLazyLog2.
+constexpr float kLazyLog2 = 8.0f;
 // With at least kHeadPerWaveMinSplits splits of at least kHeadPerWaveMinKeys
 // keys over 4 to 8 KV heads, a workgroup is one (sequence, split) and its
 // waves are the KV heads (decode_kernel_hw): 64 x 8192 at S = 4 from 182 to
@@ -576,10 +580,22 @@ __device__ __forceinline__ void decode_body(
 #pragma unroll
         for (int r = 0; r < L::kAccRegs; ++r) mx = fmaxf(mx, sacc[cb][kb][r]);
       mx = col_max(mx) * scale_log2;
-      const float m_new = fmaxf(m2[cb], mx);
-      const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-      const float alpha = fast_exp2(m2[cb] - m_use);
-      m2[cb] = m_new;
+      // The reference m2 moves lazily (the wave's columns together): only
+      // when a column's tile maximum passes its reference by more than
+      // kLazyLog2 are the references raised to the running maxima and the
+      // state rescaled; otherwise the weights stay below 2^kLazyLog2 and the
+      // rescale of the accumulators is skipped.
+      if (__builtin_amdgcn_ballot_w64(mx > m2[cb] + kLazyLog2) != 0) {
+        const float m_new = fmaxf(m2[cb], mx);
+        const float alpha = fast_exp2(m2[cb] - ((m_new == kNegInf) ? 0.0f : m_new));
+        m2[cb] = m_new;
+        lsum[cb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < L::kAccBlocks; ++db)
+#pragma unroll
+          for (int r = 0; r < L::kAccRegs; ++r) acc[cb][db][r] *= alpha;
+      }
+      const float m_use = (m2[cb] == kNegInf) ? 0.0f : m2[cb];
       float psum = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < L::kSBlocks; ++kb)
@@ -592,11 +608,7 @@ __device__ __forceinline__ void decode_body(
           else
             pb[cb][r >> 3][r & 7] = static_cast<__bf16>(p);
         }
-      lsum[cb] = lsum[cb] * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < L::kAccBlocks; ++db)
-#pragma unroll
-        for (int r = 0; r < L::kAccRegs; ++r) acc[cb][db][r] *= alpha;
+      lsum[cb] += psum;
     }
 
     if constexpr (L::k16) {
@@ -981,10 +993,18 @@ __device__ __forceinline__ void decode_pair_body(
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kb][r]);
     mx = quad_max(mx) * scale_log2;
-    const float m_new = fmaxf(m2, mx);
-    const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-    const float alpha = fast_exp2(m2 - m_use);
-    m2 = m_new;
+    // Lazy reference, as in decode_body.
+    if (__builtin_amdgcn_ballot_w64(mx > m2 + kLazyLog2) != 0) {
+      const float m_new = fmaxf(m2, mx);
+      const float alpha = fast_exp2(m2 - ((m_new == kNegInf) ? 0.0f : m_new));
+      m2 = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[db][r] *= alpha;
+    }
+    const float m_use = (m2 == kNegInf) ? 0.0f : m2;
     float psum = 0.0f;
     bf16x8_t pb;
 #pragma unroll
@@ -995,11 +1015,7 @@ __device__ __forceinline__ void decode_pair_body(
         psum += pr;
         pb[4 * kb + r] = static_cast<__bf16>(pr);
       }
-    lsum = lsum * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[db][r] *= alpha;
+    lsum += psum;
     const bf16x8_t zero = __builtin_bit_cast(bf16x8_t, zero_u32x4());
     const bf16x8_t p0 = hp == 0 ? pb : zero;
     const bf16x8_t p1 = hp == 1 ? pb : zero;

@@ -351,7 +351,8 @@ def _cpu_other_configs(cores: int) -> dict:
 # The sources each counted kernel is built from (its own file and the shared
 # device helpers).
 _KERNEL_SOURCES = {"prefill": ("prefill.hip", "device_common.hpp"), "decode": ("decode.hip", "device_common.hpp"),
-                   "merge": ("decode.hip", "device_common.hpp")}
+                   "merge": ("decode.hip", "device_common.hpp"), "oproj": ("oproj.hip", "device_common.hpp"),
+                   "rope": ("rope.hip", "device_common.hpp")}
 
 
 def _code_only(text: str) -> str:

@@ -68,6 +68,13 @@ constexpr float kLazyLog2 = 8.0f;
 // SIMD spills and runs 20-40% slower.)
 constexpr int kHeadPerWaveMinSplits = 4;
 constexpr int kHeadPerWaveMinKeys = 128;
+// ... and only when sequences x splits give at least this many workgroups:
+// below it (one or a few long sequences split a few ways) the layouts with a
+// workgroup per (sequence, KV head, split) keep more CUs busy.  1 x 131072
+// at S = 16: 0.304 -> 0.077 ms; 4 x 32768 at S = 8: 0.160 -> 0.056 ms;
+// 8 x 8192 at S = 4: 0.084 -> 0.033 ms.  At 128 (4 x 32768 at S = 32,
+// 8 x 8192 at S = 16) the head-per-wave layout is still the faster one.
+constexpr long long kHeadPerWaveMinUnits = 128;
 // Consecutive splits of a sequence share a decode_kernel_hw workgroup when
 // the launch would otherwise exceed about kHeadPerWaveTarget workgroups (two
 // per CU): 64 x 8192 at S = 16, 184 to 180 us.
@@ -740,6 +747,9 @@ __device__ __forceinline__ void decode_body(
 // sum, weighted sum) is updated per batch with the same rescaling as the
 // online softmax.
 constexpr int kMergeBatch = 32;
+// Rows below which a merge of more than kMergeBatch parts gives each row a
+// workgroup of several waves (fewer rows than the chip has wave slots).
+constexpr int kMergeWideMaxRows = 2048;
 
 // Max / sum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_max(float x) {
@@ -1148,14 +1158,13 @@ __global__ __launch_bounds__(64 * kPW) void decode_kernel_pair_hw(SINKATTN_DECOD
 #undef SINKATTN_DECODE_PARAMS
 #undef SINKATTN_DECODE_ARGS
 
-__global__ __launch_bounds__(kThreads) void merge_kernel(
-    const float* __restrict__ o_parts, const float* __restrict__ lse_parts, int num_parts,
-    int rows, uint16_t* __restrict__ o, float* __restrict__ lse) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  float big_m = kNegInf, tot = 0.0f, num = 0.0f;
-  for (int s0 = 0; s0 < num_parts; s0 += kMergeBatch) {
+// The parts s_first, s_first + stride, ... (batches of kMergeBatch from
+// s_first on, every stride parts) of one row folded into a running (max,
+// weight sum, weighted sum); lane = d.
+__device__ __forceinline__ void merge_batches(const float* __restrict__ o_parts, const float* __restrict__ lse_parts,
+                                              int num_parts, int rows, int row, int lane, int s_first, int stride,
+                                              float& big_m, float& tot, float& num) {
+  for (int s0 = s_first; s0 < num_parts; s0 += stride) {
     const int cnt = min(kMergeBatch, num_parts - s0);
     // The batch's lse values (lane j holds part s0 + j) and O values (register
     // j holds part s0 + j at d = lane) are all requested before any is used.
@@ -1179,6 +1188,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
       num += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j)) * ov[j];
     big_m = bm;
   }
+}
+
+__device__ __forceinline__ void merge_store(uint16_t* __restrict__ o, float* __restrict__ lse, int row, int lane,
+                                            float big_m, float tot, float num) {
   float out = 0.0f, out_lse = kNegInf;
   if (big_m > kNegInf) {
     out = num / tot;
@@ -1186,6 +1199,55 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
   }
   o[static_cast<size_t>(row) * kHeadDim + lane] = to_bf16_bits(out);
   if (lse != nullptr && lane == 0) lse[row] = out_lse;
+}
+
+__global__ __launch_bounds__(kThreads) void merge_kernel(
+    const float* __restrict__ o_parts, const float* __restrict__ lse_parts, int num_parts,
+    int rows, uint16_t* __restrict__ o, float* __restrict__ lse) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  float big_m = kNegInf, tot = 0.0f, num = 0.0f;
+  merge_batches(o_parts, lse_parts, num_parts, rows, row, lane, 0, kMergeBatch, big_m, tot, num);
+  merge_store(o, lse, row, lane, big_m, tot, num);
+}
+
+// Few rows over many parts (one long sequence split many ways): a workgroup
+// per row whose kMergeWideWaves waves take every kMergeWideWaves-th batch of
+// its parts, so the batches' memory latencies overlap instead of following
+// one another; wave 0 combines the waves' (max, weight sum, weighted sum).
+constexpr int kMergeWideWaves = 8;
+
+__global__ __launch_bounds__(64 * kMergeWideWaves) void merge_kernel_wide(
+    const float* __restrict__ o_parts, const float* __restrict__ lse_parts, int num_parts,
+    int rows, uint16_t* __restrict__ o, float* __restrict__ lse) {
+  __shared__ float red_m[kMergeWideWaves], red_t[kMergeWideWaves], red_n[kMergeWideWaves][kHeadDim];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row = blockIdx.x;
+  float big_m = kNegInf, tot = 0.0f, num = 0.0f;
+  merge_batches(o_parts, lse_parts, num_parts, rows, row, lane, wave * kMergeBatch, kMergeWideWaves * kMergeBatch,
+                big_m, tot, num);
+  if (lane == 0) {
+    red_m[wave] = big_m;
+    red_t[wave] = tot;
+  }
+  red_n[wave][lane] = num;
+  __syncthreads();
+  if (wave != 0) return;
+  float m = kNegInf;
+#pragma unroll
+  for (int w = 0; w < kMergeWideWaves; ++w) m = fmaxf(m, red_m[w]);
+  float t = 0.0f, n = 0.0f;
+  if (m > kNegInf) {
+#pragma unroll
+    for (int w = 0; w < kMergeWideWaves; ++w) {
+      const float sc = fast_exp2((red_m[w] - m) * kLog2e);  // 0 for a wave that saw no part
+      t += sc * red_t[w];
+      n += sc * red_n[w][lane];
+    }
+  }
+  merge_store(o, lse, row, lane, m, t, n);
 }
 
 }  // namespace
@@ -1230,7 +1292,7 @@ static hipError_t launch_decode_t(const DecodeLaunch& a, hipStream_t stream) {
   int per_wg = 1;
   decltype(&decode_kernel_w4<kFp8, kMulti, kPaged, kN>) kernel = decode_kernel_w2<kFp8, kMulti, kPaged, kN>;
   if (splits >= kHeadPerWaveMinSplits && a.num_kv_heads >= 4 && a.num_kv_heads <= 8 &&
-      keys_per_split >= kHeadPerWaveMinKeys) {
+      keys_per_split >= kHeadPerWaveMinKeys && static_cast<long long>(a.batch) * splits >= kHeadPerWaveMinUnits) {
     const long long units = static_cast<long long>(a.batch) * splits;
     per_wg = static_cast<int>(std::max<long long>(1, std::min<long long>(splits, units / kHeadPerWaveTarget)));
     grid = static_cast<unsigned>(static_cast<long long>(a.batch) * ((splits + per_wg - 1) / per_wg));
@@ -1297,7 +1359,10 @@ static hipError_t launch_pair_hw(const DecodeLaunch& a, int splits, hipStream_t 
 template <bool kPaged>
 static hipError_t launch_decode_pair(const DecodeLaunch& a, hipStream_t stream) {
   const int splits = decode_merges_in_kernel(a) ? 1 : a.num_splits;
-  if (splits >= kHeadPerWaveMinSplits) {
+  // (its workgroups hold half the waves of decode_kernel_hw's, so it needs
+  // twice the workgroups: 1 x 131072 at S = 128 0.045 -> 0.033 ms, 4 x 32768
+  // at S = 32 0.045 -> 0.035 ms on the interleaved pair kernel)
+  if (splits >= kHeadPerWaveMinSplits && static_cast<long long>(a.batch) * splits >= 2 * kHeadPerWaveMinUnits) {
     if (a.num_kv_heads == 8) return launch_pair_hw<4, kPaged>(a, splits, stream);
     if (a.num_kv_heads == 4) return launch_pair_hw<2, kPaged>(a, splits, stream);
   }
@@ -1350,6 +1415,11 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
 
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream) {
   const int rows = a.n * a.num_heads;
+  if (a.num_parts > kMergeBatch && rows < kMergeWideMaxRows) {
+    hipLaunchKernelGGL(merge_kernel_wide, dim3(static_cast<unsigned>(rows)), dim3(64 * kMergeWideWaves), 0, stream,
+                       a.o_parts, a.lse_parts, a.num_parts, rows, static_cast<uint16_t*>(a.o), a.lse);
+    return hipGetLastError();
+  }
   const unsigned blocks = static_cast<unsigned>((rows + kWaves - 1) / kWaves);
   hipLaunchKernelGGL(merge_kernel, dim3(blocks), dim3(kThreads), 0, stream, a.o_parts, a.lse_parts,
                      a.num_parts, rows, static_cast<uint16_t*>(a.o), a.lse);

@@ -68,12 +68,16 @@ constexpr float kLazyLog2 = 8.0f;
 // SIMD spills and runs 20-40% slower.)
 constexpr int kHeadPerWaveMinSplits = 4;
 constexpr int kHeadPerWaveMinKeys = 128;
-// ... and only when sequences x splits give at least this many workgroups:
-// below it (one or a few long sequences split a few ways) the layouts with a
-// workgroup per (sequence, KV head, split) keep more CUs busy.  1 x 131072
-// at S = 16: 0.304 -> 0.077 ms; 4 x 32768 at S = 8: 0.160 -> 0.056 ms;
-// 8 x 8192 at S = 4: 0.084 -> 0.033 ms.  At 128 (4 x 32768 at S = 32,
-// 8 x 8192 at S = 16) the head-per-wave layout is still the faster one.
+// ... and only when sequences x splits give enough workgroups: at least
+// twice this many, or at least this many when the split-per-wave kernel
+// (long splits) is not the alternative.  Below that (one or a few long
+// sequences split a few ways) the layouts with a workgroup per (sequence,
+// KV head, split) keep more CUs busy: 1 x 131072 at S = 16 0.304 -> 0.077
+// ms, 4 x 32768 at S = 8 0.160 -> 0.056 ms, 8 x 8192 at S = 4 0.084 ->
+// 0.033 ms.  Between the two bounds the split-per-wave kernel is faster
+// (16 x 32768 at S = 8 0.188 -> 0.178 ms, 32 x 8192 at S = 4 0.103 ->
+// 0.095 ms) and the short-split two-wave kernel slower (4 x 32768 at S = 32,
+// 8 x 8192 at S = 16 keep this layout).
 constexpr long long kHeadPerWaveMinUnits = 128;
 // Consecutive splits of a sequence share a decode_kernel_hw workgroup when
 // the launch would otherwise exceed about kHeadPerWaveTarget workgroups (two
@@ -1291,8 +1295,12 @@ static hipError_t launch_decode_t(const DecodeLaunch& a, hipStream_t stream) {
   unsigned threads = 128;
   int per_wg = 1;
   decltype(&decode_kernel_w4<kFp8, kMulti, kPaged, kN>) kernel = decode_kernel_w2<kFp8, kMulti, kPaged, kN>;
+  // (the split-per-wave kernel's condition below)
+  const bool ps_ok = splits >= kSplitPerWaveMin && !short_chunks &&
+                     static_cast<long long>(a.batch) * a.num_kv_heads * ((splits + 3) / 4) >= kSplitPerWaveMinGroups;
+  const long long hw_units = static_cast<long long>(a.batch) * splits;
   if (splits >= kHeadPerWaveMinSplits && a.num_kv_heads >= 4 && a.num_kv_heads <= 8 &&
-      keys_per_split >= kHeadPerWaveMinKeys && static_cast<long long>(a.batch) * splits >= kHeadPerWaveMinUnits) {
+      keys_per_split >= kHeadPerWaveMinKeys && (hw_units >= 2 * kHeadPerWaveMinUnits || (hw_units >= kHeadPerWaveMinUnits && !ps_ok))) {
     const long long units = static_cast<long long>(a.batch) * splits;
     per_wg = static_cast<int>(std::max<long long>(1, std::min<long long>(splits, units / kHeadPerWaveTarget)));
     grid = static_cast<unsigned>(static_cast<long long>(a.batch) * ((splits + per_wg - 1) / per_wg));

@@ -43,6 +43,9 @@ def library() -> ctypes.CDLL:
     lib.sinkattn_prefill_append.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                             f32, vp, vp, vp]
     lib.sinkattn_prefill_append.restype = ctypes.c_int
+    lib.sinkattn_prefill_append_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                                    i32, f32, i32, vp, sz, vp, vp, vp]
+    lib.sinkattn_prefill_append_splitkv.restype = ctypes.c_int
     lib.sinkattn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.sinkattn_decode_workspace_bytes.restype = sz
     lib.sinkattn_decode_splitkv.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, f32, i32,
@@ -160,11 +163,14 @@ def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: Opt
 def prefill_append(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: Optional[torch.Tensor],
                    cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
                    window: int = 0, softmax_scale: float = 0.125, out: Optional[torch.Tensor] = None,
-                   lse: Optional[torch.Tensor] = None, return_lse: bool = False):
+                   lse: Optional[torch.Tensor] = None, return_lse: bool = False, num_splits: int = 1,
+                   workspace: Optional[torch.Tensor] = None):
     """Append prefill / multi-token-query decode: q [Tq, Hq, 64] bf16 packed
     by cu_seqlens_q, k/v [Tk, Hkv, 64] bf16 packed by cu_seqlens_k (both
     [B+1] int32, device); each sequence's queries are its last tokens
-    (bottom-right causal).  Returns o (and lse)."""
+    (bottom-right causal).  num_splits > 1 splits each query tile's keys
+    (sinkattn_prefill_append_splitkv); ``workspace`` (uint8, device) is then
+    allocated here when not given.  Returns o (and lse)."""
     _need(q, "q", torch.bfloat16, 3)
     _need(k, "k", torch.bfloat16, 3)
     _need(v, "v", torch.bfloat16, 3)
@@ -192,10 +198,21 @@ def prefill_append(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: Opt
         _need(lse, "lse", torch.float32, 2)
         if lse.shape != (tq, hq):
             raise ValueError("lse must be [Tq, Hq]")
-    _check(library().sinkattn_prefill_append(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), cu_seqlens_q.shape[0] - 1,
-        int(max_seqlen_q), int(max_seqlen_k), tq, tk, hq, hkv, d, int(window), float(softmax_scale), _ptr(out),
-        _ptr(lse), _stream(q.device)))
+    if int(num_splits) > 1:
+        need = decode_workspace_bytes(tq, hq, d, int(num_splits))
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+        _check(library().sinkattn_prefill_append_splitkv(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+            cu_seqlens_q.shape[0] - 1, int(max_seqlen_q), int(max_seqlen_k), tq, tk, hq, hkv, d, int(window),
+            float(softmax_scale), int(num_splits), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
+            _stream(q.device)))
+    else:
+        _check(library().sinkattn_prefill_append(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+            cu_seqlens_q.shape[0] - 1, int(max_seqlen_q), int(max_seqlen_k), tq, tk, hq, hkv, d, int(window),
+            float(softmax_scale), _ptr(out), _ptr(lse), _stream(q.device)))
     return (out, lse) if (return_lse or lse is not None) else out
 
 

@@ -113,12 +113,17 @@ const char* sinkattn_last_error(void) { return g_last_error.c_str(); }
 const char* sinkattn_version(void) { return "sinkattn 0.1.0 (gfx950)"; }
 
 // Self-attention prefill (cu_q == cu_k) and append prefill share one kernel.
+// Splits of the split-KV append prefill: gridDim.y of its launch.
+constexpr int32_t kMaxPrefillSplits = 1024;
+
 static sinkattn_status prefill_common(const void* q, const void* k, const void* v, const float* sinks,
                                       const int32_t* cu_q, const int32_t* cu_k, int32_t batch, int32_t max_q,
                                       int32_t max_k, int32_t total_q, int32_t total_k, int32_t num_q_heads,
                                       int32_t num_kv_heads, int32_t head_dim, int32_t window, float softmax_scale,
                                       void* o, float* lse, void* stream, const int32_t* block_table = nullptr,
-                                      int32_t max_pages = 0, int32_t page_size = 0, int32_t num_pages = 0) {
+                                      int32_t max_pages = 0, int32_t page_size = 0, int32_t num_pages = 0,
+                                      int32_t num_splits = 1, void* workspace = nullptr,
+                                      size_t workspace_bytes = 0) {
   const bool append = cu_k != cu_q;
   const bool paged = block_table != nullptr;  // k / v are page pools, cu_k the key lengths [batch]
   sinkattn_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
@@ -179,6 +184,18 @@ static sinkattn_status prefill_common(const void* q, const void* k, const void* 
     a.num_pages = num_pages;
     while ((1 << a.page_shift) < page_size) ++a.page_shift;
   }
+  if (num_splits > 1) {
+    const size_t need = sinkattn_decode_workspace_bytes(total_q, num_q_heads, head_dim, num_splits);
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(SINKATTN_ERR_WORKSPACE, "workspace of %zu bytes is too small (need %zu)", workspace_bytes, need);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(SINKATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    const size_t rows = static_cast<size_t>(num_splits) * total_q * num_q_heads;
+    char* ws = static_cast<char*>(workspace);
+    a.num_splits = num_splits;
+    a.o_part = reinterpret_cast<float*>(ws);
+    a.lse_part = reinterpret_cast<float*>(ws + round_up(rows * head_dim * sizeof(float), 256));
+  }
   return hip_status(sinkattn::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
 }
 
@@ -209,6 +226,26 @@ sinkattn_status sinkattn_prefill_append(const void* q, const void* k, const void
     return fail(SINKATTN_ERR_INVALID_ARG, "one offsets array for queries and keys needs equal maxima and totals");
   return prefill_common(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k, total_q,
                         total_k, num_q_heads, num_kv_heads, head_dim, window, softmax_scale, o, lse, stream);
+}
+
+sinkattn_status sinkattn_prefill_append_splitkv(const void* q, const void* k, const void* v, const float* sinks,
+                                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                                int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                                int32_t total_q, int32_t total_k, int32_t num_q_heads,
+                                                int32_t num_kv_heads, int32_t head_dim, int32_t window,
+                                                float softmax_scale, int32_t num_splits, void* workspace,
+                                                size_t workspace_bytes, void* o, float* lse, void* stream) {
+  if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
+    return fail(SINKATTN_ERR_INVALID_ARG, "batch, lengths and totals must be >= 0");
+  if (num_splits < 1) return fail(SINKATTN_ERR_INVALID_ARG, "num_splits must be >= 1 (got %d)", num_splits);
+  if (num_splits > kMaxPrefillSplits)
+    return fail(SINKATTN_ERR_UNSUPPORTED, "num_splits must be <= %d (got %d)", kMaxPrefillSplits, num_splits);
+  if (cu_seqlens_q != nullptr && cu_seqlens_q == cu_seqlens_k &&
+      !(max_seqlen_q == max_seqlen_k && total_q == total_k))
+    return fail(SINKATTN_ERR_INVALID_ARG, "one offsets array for queries and keys needs equal maxima and totals");
+  return prefill_common(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k, total_q,
+                        total_k, num_q_heads, num_kv_heads, head_dim, window, softmax_scale, o, lse, stream, nullptr,
+                        0, 0, 0, num_splits, workspace, workspace_bytes);
 }
 
 size_t sinkattn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim, int32_t num_splits) {

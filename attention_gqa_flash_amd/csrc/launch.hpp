@@ -25,6 +25,12 @@ struct PrefillLaunch {
   // cu_seqlens_k holds the key lengths [batch].
   const int32_t* block_table = nullptr;
   int max_pages = 0, page_shift = 0, num_pages = 0;
+  // num_splits > 1: each query tile's keys are cut into that many shares
+  // whose fp32 partials [num_splits, total_tokens, num_q_heads, (head_dim)]
+  // go to o_part / lse_part, then merged into o and lse.
+  int num_splits = 1;
+  float* o_part = nullptr;
+  float* lse_part = nullptr;
 };
 
 struct DecodeLaunch {

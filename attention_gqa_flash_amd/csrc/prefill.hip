@@ -195,14 +195,22 @@ __device__ __forceinline__ int find_sequence(const int32_t* __restrict__ cu, int
   }
 }
 
-template <bool kWindow, int kCols, bool kPaged>
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// kSplit: the key tiles of every query tile are cut into gridDim.y
+// contiguous shares (blockIdx.y = split); each workgroup writes its share's
+// normalised fp32 output and lse as a partial ([split][out_rows][hq] rows of
+// o_part / lse_part), the sink counted in split 0 only, and the log-sum-exp
+// merge combines them (Perplexity, "GPT-OSS on day 0", Sink attention: with
+// the KV length split into chunks, the sink initialises only the first).
+template <bool kWindow, int kCols, bool kPaged, bool kSplit = false>
 __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_per_eu(4 / kCols, 4 / kCols))) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ sinks,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ cu_seqlens_k, int hq, int hkv, int group,
     int n_hchunk, int batch, int max_seqlen, int max_seqlen_k, int window, float scale_log2,
     uint16_t* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ block_table, int max_pages,
-    int page_shift, int num_pages) {
+    int page_shift, int num_pages, float* __restrict__ o_part, float* __restrict__ lse_part, int out_rows) {
   // Ring of LDS tile buffers, each K rows then V rows.  Tile t lives in
   // buffer (t - t_begin) % kBufs; the loop below is unrolled over the ring so
   // every LDS address is a per-lane base plus an immediate offset.
@@ -252,12 +260,25 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
   const int last_q = min(len - 1, q0 + kQTile - 1);
   const int last_pos = last_q + off;  // the last key any query of the tile sees
   const int first_key = kWindow ? max(0, q0 + off - window + 1) : 0;
-  const int t_begin = first_key / kKTile;
-  const int t_end = last_pos / kKTile;
+  int t_begin = first_key / kKTile;
+  int t_end = last_pos / kKTile;
   // 32-key steps h_begin..h_end: every one holds a key some query of the
   // tile sees.
-  const int h_begin = first_key >> 5;
-  const int h_end = last_pos >> 5;
+  int h_begin = first_key >> 5;
+  int h_end = last_pos >> 5;
+  const int split = kSplit ? static_cast<int>(blockIdx.y) : 0;
+  if constexpr (kSplit) {
+    // This split's share of the tiles: ceil(n / S) consecutive tiles, the
+    // trailing shares possibly empty (t_begin > t_end: no step runs and the
+    // partial is empty).
+    const int n_t = t_end - t_begin + 1;
+    const int per = (n_t + static_cast<int>(gridDim.y) - 1) / static_cast<int>(gridDim.y);
+    const int tb = t_begin + split * per;
+    t_end = min(t_end, tb + per - 1);
+    t_begin = tb;
+    h_begin = max(h_begin, 2 * t_begin);
+    h_end = min(h_end, 2 * t_end + 1);
+  }
 
   // K / V rows of this sequence and KV head; a key's row is hkv * 64
   // elements further on.
@@ -326,7 +347,7 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
   f32x16_t acc[kCols][2];
 #pragma unroll
   for (int c = 0; c < kCols; ++c) {
-    const float z = (sinks != nullptr && head_ok[c]) ? sinks[head[c]] : kNegInf;
+    const float z = (sinks != nullptr && head_ok[c] && split == 0) ? sinks[head[c]] : kNegInf;
     if (z > kNegInf) {
       m2[c] = z * kLog2e;
       lsum[c] = half == 0 ? 1.0f : 0.0f;
@@ -552,6 +573,35 @@ __global__ __launch_bounds__(threads_for<kCols>()) __attribute__((amdgpu_waves_p
   // Epilogue.  Every K/V read is done once all waves pass this barrier;
   // buffers 0 and 1 then stage the O block (same layout as the Q block) so
   // that it is stored as whole 1 KB token rows.
+  if constexpr (kSplit) {
+    // This split's partial straight from the registers: a lane holds
+    // d = 32 db + 8 j + 4 half + 0..3 of query column col, one 16-byte store
+    // each; rows past the sequence and columns past the group are skipped.
+    if (!wave_active) return;
+    pv_chains(p_buf);  // O^T of the last step
+    const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int colr = lane_e & 31;
+    const int halfr = lane_e >> 5;
+    if (q0 + colr >= len) return;
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) {
+      const float den = pair_sum(lsum[c]);
+      if (!head_ok[c]) continue;
+      const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+      const size_t prow = (static_cast<size_t>(split) * out_rows + seq0 + q0 + colr) * hq + head[c];
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4_t w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[i] = acc[c][db][4 * j + i] * inv;
+          *reinterpret_cast<f32x4_t*>(o_part + prow * kHeadDim + 32 * db + 8 * j + 4 * halfr) = w;
+        }
+      if (halfr == 0) lse_part[prow] = den > 0.0f ? (m2[c] + __log2f(den)) * kLn2 : kNegInf;
+    }
+    return;
+  }
   lds_barrier();
   uint16_t* const o_lds = &kv_lds[0][0];
   if (wave_active) {
@@ -617,15 +667,27 @@ hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream) {
   dim3 grid(static_cast<unsigned>(blocks), 1, 1);
   const bool windowed = a.window > 0 && a.window < a.max_seqlen_k;
   const bool paged = a.block_table != nullptr;
+  const bool split = a.num_splits > 1;
   auto kernel = paged ? (windowed ? prefill_kernel<true, kColsPerWave, true> : prefill_kernel<false, kColsPerWave, true>)
                       : (windowed ? prefill_kernel<true, kColsPerWave, false> : prefill_kernel<false, kColsPerWave, false>);
+  if (split) {
+    kernel = paged ? (windowed ? prefill_kernel<true, kColsPerWave, true, true>
+                               : prefill_kernel<false, kColsPerWave, true, true>)
+                   : (windowed ? prefill_kernel<true, kColsPerWave, false, true>
+                               : prefill_kernel<false, kColsPerWave, false, true>);
+    grid.y = static_cast<unsigned>(a.num_splits);
+  }
   hipLaunchKernelGGL(kernel, grid, dim3(threads_for<kColsPerWave>()), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.sinks, a.cu_seqlens, a.cu_seqlens_k, a.num_q_heads,
                      a.num_kv_heads, group, n_hchunk, a.batch, a.max_seqlen, a.max_seqlen_k, a.window,
                      a.softmax_scale * kLog2e, static_cast<uint16_t*>(a.o), a.lse, a.block_table, a.max_pages,
-                     a.page_shift, a.num_pages);
-  return hipGetLastError();
+                     a.page_shift, a.num_pages, a.o_part, a.lse_part, a.total_tokens);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || !split) return err;
+  // The partials of every (query row, head) combined into o and lse.
+  MergeLaunch m{a.o_part, a.lse_part, a.num_splits, a.total_tokens, a.num_q_heads, a.o, a.lse};
+  return launch_merge(m, stream);
 }
 
 long long prefill_blocks(int batch, int total_tokens, int num_kv_heads, int group) {

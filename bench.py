@@ -917,6 +917,29 @@ def _other_configs(torch, np, binding, inputs, dev, bf16, timed, hbm_entry, mfma
         del aq, ak, av, ao
     torch.cuda.synchronize()
 
+    # a short chunk over a long cache: 256 new tokens after 32512 cached
+    # (32768 keys), causal, unsplit and with each query tile's keys split 8
+    # ways (sinkattn_prefill_append_splitkv)
+    gen.manual_seed(9)
+    q_lens, k_lens = [256], [32768]
+    aq = _device_normal_bf16(torch, (256, HQ, D), gen, dev)
+    ak = _device_normal_bf16(torch, (32768, HKV, D), gen, dev)
+    av = _device_normal_bf16(torch, (32768, HKV, D), gen, dev)
+    asinks = torch.randn(HQ, generator=gen, device=dev, dtype=torch.float32)
+    acq = torch.tensor([0, 256], dtype=torch.int32, device=dev)
+    ack = torch.tensor([0, 32768], dtype=torch.int32, device=dev)
+    ao = torch.empty_like(aq)
+    aws = torch.empty(binding.decode_workspace_bytes(256, HQ, D, 8), dtype=torch.uint8, device=dev)
+    for s_count in (1, 8):
+        st = timed(lambda: binding.prefill_append(aq, ak, av, asinks, acq, ack, 256, 32768, 0, scale, out=ao,
+                                                  num_splits=s_count, workspace=aws), scrub_each=True)
+        e = mfma_entry(st, append_flops(q_lens, k_lens, 0), append_bytes(q_lens, k_lens, 0))
+        e["bound"] = "mfma"
+        e["shape"] = "1 sequence, 256 queries, 32768 keys, 64/8 heads, causal, S=%d" % s_count
+        out["chunked_prefill_256_of_32768_s%d" % s_count] = e
+    del aq, ak, av, ao, aws
+    torch.cuda.synchronize()
+
     # draft tokens through the multi-token decode only: 8 per sequence (64
     # columns per KV head), against the bf16 cache and against E4M3 caches
     # (4 and 8 per sequence); causal, 1 and 4 splits

@@ -152,6 +152,48 @@ SINKATTN_API sinkattn_status sinkattn_prefill_append(
     void* o, float* lse, void* stream);
 
 /*
+ * sinkattn_prefill_append with each query tile's keys split across
+ * workgroups, for chunks of few queries over long caches (a 256-token chunk
+ * has only 8 query tiles per KV head): the keys a 32-query tile sees are cut
+ * into num_splits contiguous shares of 64-key tiles (trailing shares may be
+ * empty), each share's output is normalised on its own and written to the
+ * workspace in fp32 with its lse, the sink counted in the first share only,
+ * and the shares are combined with the log-sum-exp merge of
+ * sinkattn_merge_lse before returning (Perplexity, "GPT-OSS on day 0", Sink
+ * attention: attention parallelised over heads and KV length, the sink
+ * initialising only the first chunk).  The merge is exact, so the result
+ * equals sinkattn_prefill_append's up to fp32 rounding.
+ *
+ *   (arguments as sinkattn_prefill_append, plus)
+ *   num_splits     1 to 1024; 1 runs sinkattn_prefill_append's path
+ *   workspace      device buffer, 256-byte aligned, of at least
+ *                  sinkattn_decode_workspace_bytes(total_q, num_q_heads,
+ *                  head_dim, num_splits) bytes when num_splits > 1
+ *                  (SINKATTN_ERR_WORKSPACE otherwise): fp32 partial outputs
+ *                  [num_splits, total_q, num_q_heads, head_dim], then fp32
+ *                  partial lse [num_splits, total_q, num_q_heads]; owned by
+ *                  the caller, overwritten; may be NULL when num_splits == 1
+ *   workspace_bytes  its size
+ *
+ * num_splits < 1 is SINKATTN_ERR_INVALID_ARG, above 1024
+ * SINKATTN_ERR_UNSUPPORTED.  Calls that share one workspace on overlapping
+ * streams race.  With num_splits > 1 the merge writes every one of the
+ * total_q rows of o (and lse): rows that belong to no sequence (past
+ * cu_seqlens_q[batch], or of a sequence that breaks Lq_b <= Lk_b) hold
+ * unspecified values afterwards, where sinkattn_prefill_append leaves them
+ * untouched.
+ */
+SINKATTN_API sinkattn_status sinkattn_prefill_append_splitkv(
+    const void* q, const void* k, const void* v,
+    const float* sinks,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+    int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t total_q, int32_t total_k,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t window, float softmax_scale, int32_t num_splits,
+    void* workspace, size_t workspace_bytes,
+    void* o, float* lse, void* stream);
+
+/*
  * Bytes of workspace sinkattn_decode_splitkv needs for num_splits > 1:
  * fp32 partial outputs [num_splits, batch, num_q_heads, head_dim] and fp32
  * partial lse [num_splits, batch, num_q_heads], each 256-byte aligned.

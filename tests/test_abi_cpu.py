@@ -33,6 +33,7 @@ def test_header_declares_the_entry_points():
         "sinkattn_decode_workspace_bytes", "sinkattn_oproj_bias", "sinkattn_oproj_workspace_bytes",
         "sinkattn_rope_qkv_append",
         "sinkattn_last_error", "sinkattn_merge_lse", "sinkattn_prefill_append", "sinkattn_prefill_append_paged",
+        "sinkattn_prefill_append_splitkv",
         "sinkattn_prefill_varlen",
         "sinkattn_version"])
 
@@ -133,6 +134,46 @@ def test_append_empty_is_ok_without_launch():
     lib = _lib()
     assert _append(lib, batch=0) == 0
     assert _append(lib, tq=0, mq=0) == 0
+
+
+def _append_split(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, sinks=None, cuq=FAKE, cuk=FAKE2, batch=2, mq=16, mk=64, tq=20, tk=100,
+             hq=8, hkv=2, d=64, window=0, scale=0.125, splits=4, ws=None, ws_bytes=0, o=FAKE, lse=None)
+    a.update(kw)
+    return lib.sinkattn_prefill_append_splitkv(a["q"], a["k"], a["v"], a["sinks"], a["cuq"], a["cuk"], a["batch"],
+                                               a["mq"], a["mk"], a["tq"], a["tk"], a["hq"], a["hkv"], a["d"],
+                                               a["window"], a["scale"], a["splits"], a["ws"], a["ws_bytes"], a["o"],
+                                               a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(splits=0), 1),
+    (dict(splits=1025), 2),
+    (dict(), 3),                                  # no workspace
+    (dict(ws=FAKE, ws_bytes=100), 3),
+    (dict(ws=ctypes.c_void_p((1 << 20) + 16), ws_bytes=1 << 30), 1),  # misaligned workspace
+    (dict(d=128), 2),
+    (dict(mk=0, tk=0), 1),
+    (dict(cuk=FAKE, mk=16, tk=100), 1),          # one offsets array, different maxima or totals
+    (dict(batch=-1), 1),
+])
+def test_append_split_rejects(kw, status):
+    lib = _lib()
+    assert _append_split(lib, **kw) == status
+    assert lib.sinkattn_last_error()
+
+
+def test_append_split_empty_is_ok_without_launch():
+    lib = _lib()
+    assert _append_split(lib, batch=0) == 0
+    assert _append_split(lib, tq=0, mq=0) == 0
+
+
+def test_append_split_workspace_size():
+    lib = _lib()
+    need = lib.sinkattn_decode_workspace_bytes(20, 8, 64, 4)
+    rows = 4 * 20 * 8
+    assert need == -(-rows * 64 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
 
 
 def _decode(lib, **kw):

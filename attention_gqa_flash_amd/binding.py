@@ -69,6 +69,9 @@ def library() -> ctypes.CDLL:
     lib.sinkattn_prefill_append_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp,
                                                   i32, i32, i32, i32, f32, vp, vp, vp]
     lib.sinkattn_prefill_append_paged.restype = ctypes.c_int
+    lib.sinkattn_prefill_append_paged_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                                          vp, i32, i32, i32, i32, f32, i32, vp, sz, vp, vp, vp]
+    lib.sinkattn_prefill_append_paged_splitkv.restype = ctypes.c_int
     lib.sinkattn_decode_paged_multi.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, i32,
                                                 i32, i32, i32, f32, i32, vp, sz, vp, vp, vp]
     lib.sinkattn_decode_paged_multi.restype = ctypes.c_int
@@ -471,10 +474,13 @@ def prefill_append_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.
                          seq_lens_k: torch.Tensor, cu_seqlens_q: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
                          sinks: Optional[torch.Tensor], window: int = 0, softmax_scale: float = 0.125,
                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                         return_lse: bool = False):
+                         return_lse: bool = False, num_splits: int = 1, workspace: Optional[torch.Tensor] = None):
     """Append (chunked) prefill against a paged cache: q [Tq, Hq, 64] bf16
     packed by cu_seqlens_q; k/v pages [P, page_size, Hkv, 64] bf16;
-    block_table [B, max_pages] int32; seq_lens_k [B] int32 (all device)."""
+    block_table [B, max_pages] int32; seq_lens_k [B] int32 (all device).
+    num_splits > 1 splits each query tile's keys
+    (sinkattn_prefill_append_paged_splitkv; ``workspace`` allocated here when
+    not given)."""
     _need(q, "q", torch.bfloat16, 3)
     _need(k_pages, "k_pages", torch.bfloat16, 4)
     _need(v_pages, "v_pages", torch.bfloat16, 4)
@@ -496,10 +502,20 @@ def prefill_append_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.
         out = torch.empty_like(q)
     if return_lse and lse is None:
         lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
-    _check(library().sinkattn_prefill_append_paged(
-        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens_k), _ptr(cu_seqlens_q), bsz,
-        block_table.shape[1], page_size, num_pages, int(max_seqlen_q), int(max_seqlen_k), tq, _ptr(sinks), hq, hkv, d,
-        int(window), float(softmax_scale), _ptr(out), _ptr(lse), _stream(q.device)))
+    if int(num_splits) > 1:
+        if workspace is None:
+            workspace = torch.empty(decode_workspace_bytes(tq, hq, d, int(num_splits)), dtype=torch.uint8,
+                                    device=q.device)
+        _check(library().sinkattn_prefill_append_paged_splitkv(
+            _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens_k), _ptr(cu_seqlens_q), bsz,
+            block_table.shape[1], page_size, num_pages, int(max_seqlen_q), int(max_seqlen_k), tq, _ptr(sinks), hq,
+            hkv, d, int(window), float(softmax_scale), int(num_splits), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(q.device)))
+    else:
+        _check(library().sinkattn_prefill_append_paged(
+            _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens_k), _ptr(cu_seqlens_q), bsz,
+            block_table.shape[1], page_size, num_pages, int(max_seqlen_q), int(max_seqlen_k), tq, _ptr(sinks), hq,
+            hkv, d, int(window), float(softmax_scale), _ptr(out), _ptr(lse), _stream(q.device)))
     return (out, lse) if (return_lse or lse is not None) else out
 
 

@@ -541,6 +541,26 @@ sinkattn_status sinkattn_prefill_append_paged(const void* q, const void* k_pages
                         lse, stream, block_table, max_pages, page_size, num_pages);
 }
 
+sinkattn_status sinkattn_prefill_append_paged_splitkv(
+    const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table, const int32_t* seq_lens_k,
+    const int32_t* cu_seqlens_q, int32_t batch, int32_t max_pages, int32_t page_size, int32_t num_pages,
+    int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t total_q, const float* sinks, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t window, float softmax_scale, int32_t num_splits, void* workspace,
+    size_t workspace_bytes, void* o, float* lse, void* stream) {
+  if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0)
+    return fail(SINKATTN_ERR_INVALID_ARG, "batch, lengths and totals must be >= 0");
+  if (num_splits < 1) return fail(SINKATTN_ERR_INVALID_ARG, "num_splits must be >= 1 (got %d)", num_splits);
+  if (num_splits > kMaxPrefillSplits)
+    return fail(SINKATTN_ERR_UNSUPPORTED, "num_splits must be <= %d (got %d)", kMaxPrefillSplits, num_splits);
+  sinkattn_status st = check_pages(block_table, seq_lens_k, batch, max_pages, page_size, num_pages, max_seqlen_k);
+  if (st != SINKATTN_OK) return st;
+  if (cu_seqlens_q == nullptr && batch > 0) return fail(SINKATTN_ERR_INVALID_ARG, "cu_seqlens_q must not be NULL");
+  return prefill_common(q, k_pages, v_pages, sinks, cu_seqlens_q, seq_lens_k, batch, max_seqlen_q, max_seqlen_k,
+                        total_q, num_pages * page_size, num_q_heads, num_kv_heads, head_dim, window, softmax_scale, o,
+                        lse, stream, block_table, max_pages, page_size, num_pages, num_splits, workspace,
+                        workspace_bytes);
+}
+
 // Rotary frequencies of the pairs (i, i + 32): theta^(-2i/64), rescaled by
 // YaRN's NTK-by-parts rule when factor > 1, with the ramp over the pair index
 // that YaRN's own code and the GPT-OSS / DeepSeek-V3 models use: the index at

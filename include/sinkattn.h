@@ -415,6 +415,28 @@ SINKATTN_API sinkattn_status sinkattn_prefill_append_paged(
     void* o, float* lse, void* stream);
 
 /*
+ * sinkattn_prefill_append_paged with each query tile's keys split across
+ * workgroups: short chunks of a prompt appended to a long paged cache (vLLM
+ * and FlashInfer page their KV caches; "GPT-OSS on day 0", Perplexity, Sink
+ * attention, for the split with the sink in the first chunk).  The split,
+ * the workspace (sinkattn_decode_workspace_bytes(total_q, num_q_heads,
+ * head_dim, num_splits) bytes, 256-byte aligned, when num_splits > 1), the
+ * limits and the unspecified rows outside every sequence are those of
+ * sinkattn_prefill_append_splitkv; the other arguments and checks those of
+ * sinkattn_prefill_append_paged.
+ */
+SINKATTN_API sinkattn_status sinkattn_prefill_append_paged_splitkv(
+    const void* q, const void* k_pages, const void* v_pages,
+    const int32_t* block_table, const int32_t* seq_lens_k, const int32_t* cu_seqlens_q, int32_t batch,
+    int32_t max_pages, int32_t page_size, int32_t num_pages,
+    int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t total_q,
+    const float* sinks,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t window, float softmax_scale, int32_t num_splits,
+    void* workspace, size_t workspace_bytes,
+    void* o, float* lse, void* stream);
+
+/*
  * Split-KV decode against a paged FP8 cache: the pages and block table of
  * sinkattn_decode_paged holding the E4M3 codes and per-tensor scales of
  * sinkattn_decode_splitkv_fp8.  The result equals sinkattn_decode_splitkv_fp8's

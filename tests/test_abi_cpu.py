@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
         "sinkattn_decode_workspace_bytes", "sinkattn_oproj_bias", "sinkattn_oproj_workspace_bytes",
         "sinkattn_rope_qkv_append",
         "sinkattn_last_error", "sinkattn_merge_lse", "sinkattn_prefill_append", "sinkattn_prefill_append_paged",
-        "sinkattn_prefill_append_splitkv",
+        "sinkattn_prefill_append_splitkv", "sinkattn_prefill_append_paged_splitkv",
         "sinkattn_prefill_varlen",
         "sinkattn_version"])
 

@@ -99,3 +99,46 @@ def test_split_chunk_256_over_32768(window):
     what = "chunk 256 of 32768 S=16 W=%d" % window
     assert_close_out(o[rows], ro[rows], what)
     assert_close_lse(lse[rows], rl[rows], what)
+
+
+# ---------------------------------------------------------------------------
+# Over a paged cache (sinkattn_prefill_append_paged_splitkv)
+# ---------------------------------------------------------------------------
+
+P_Q_LENS = [5, 1, 40, 33, 64, 300, 7, 0, 129]
+P_K_LENS = [5, 2, 71, 65, 97, 3364, 107, 3, 4129]
+
+
+def _paged_run(p, window, splits, with_sinks=True):
+    o, lse = binding.prefill_append_paged(bf16_to_device(p.q), bf16_to_device(p.k_pages), bf16_to_device(p.v_pages),
+                                          i32_to_device(p.block_table), i32_to_device(p.seq_lens),
+                                          i32_to_device(p.cu_seqlens_q), max(p.q_lens), max(p.k_lens),
+                                          f32_to_device(p.sinks) if with_sinks else None, window, p.scale,
+                                          return_lse=True, num_splits=splits)
+    torch.cuda.synchronize()
+    return to_f64(o), lse.cpu().numpy()
+
+
+def _paged_ref(p, window, with_sinks=True):
+    from oracle import decode_paged_multi_ref
+    return decode_paged_multi_ref(inputs.bf16_bits_to_f32(p.q), inputs.bf16_bits_to_f32(p.k_pages),
+                                  inputs.bf16_bits_to_f32(p.v_pages), p.block_table, p.seq_lens, p.cu_seqlens_q,
+                                  p.page_size, p.sinks if with_sinks else None, window, p.scale)
+
+
+@pytest.mark.parametrize("page_size", [16, 64, 256])
+@pytest.mark.parametrize("splits", [2, 7, 32])
+def test_split_paged_append_prefill(page_size, splits):
+    p = inputs.make_paged_append(P_Q_LENS, P_K_LENS, page_size, hq=64, hkv=8, seed=980 + page_size + splits)
+    cu = p.cu_seqlens_q
+    rows = np.concatenate([np.arange(cu[b], cu[b + 1]) for b in range(len(cu) - 1)]).astype(np.int64)
+    for window in (0, 128):
+        o, lse = _paged_run(p, window, splits)
+        ro, rl = _paged_ref(p, window)
+        what = "split paged append ps=%d S=%d W=%d" % (page_size, splits, window)
+        assert_close_out(o[rows], ro[rows], what)
+        assert_close_lse(lse[rows], rl[rows], what)
+    o, lse = _paged_run(p, 0, splits, with_sinks=False)
+    ro, rl = _paged_ref(p, 0, with_sinks=False)
+    assert_close_out(o[rows], ro[rows], "split paged append, no sinks")
+    assert_close_lse(lse[rows], rl[rows], "split paged append, no sinks")

@@ -142,3 +142,22 @@ def test_split_paged_append_prefill(page_size, splits):
     ro, rl = _paged_ref(p, 0, with_sinks=False)
     assert_close_out(o[rows], ro[rows], "split paged append, no sinks")
     assert_close_lse(lse[rows], rl[rows], "split paged append, no sinks")
+
+
+def test_split_debug_checks(monkeypatch):
+    """SINKATTN_DEBUG_CHECKS=1 applies to the split entry point as to the
+    unsplit one: valid inputs pass with the same result, a sequence with
+    fewer keys than queries is reported before anything is launched."""
+    a = inputs.make_append([4, 6], [10, 600], hq=8, hkv=2, seed=990)
+    q, k, v = (bf16_to_device(x) for x in (a.q, a.k, a.v))
+    sinks, cq, ck = f32_to_device(a.sinks), i32_to_device(a.cu_seqlens_q), i32_to_device(a.cu_seqlens_k)
+    plain = binding.prefill_append(q, k, v, sinks, cq, ck, 6, 600, 0, a.scale, num_splits=3)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("SINKATTN_DEBUG_CHECKS", "1")
+    checked = binding.prefill_append(q, k, v, sinks, cq, ck, 6, 600, 0, a.scale, num_splits=3)
+    torch.cuda.synchronize()
+    assert torch.equal(checked, plain)
+    bad_k = i32_to_device(np.array([0, 10, 13], np.int32))  # sequence 1: 3 keys for 6 queries
+    with pytest.raises(binding.SinkAttnError) as err:
+        binding.prefill_append(q, k[:13], v[:13], sinks, cq, bad_k, 6, 10, 0, a.scale, num_splits=3)
+    assert err.value.status == 1 and "fewer keys" in str(err.value)

@@ -92,3 +92,21 @@ def test_merge_many_parts(parts, rows):
     assert_close_out(to_f64(o), ro, what)
     assert_close_lse(lse.cpu().numpy(), rl, what)
     assert np.all(to_f64(o)[0] == 0.0)
+
+
+@pytest.mark.parametrize("page_size,splits", [(16, 16), (64, 64), (64, 256)])
+def test_long_context_paged_decode(page_size, splits):
+    """The same few-sequence launch choices over a paged cache (pages in a
+    shuffled physical order, NaN in every slot no sequence owns)."""
+    from oracle import decode_paged_ref
+    p = inputs.make_paged_decode([131072], page_size, hq=64, hkv=8, seed=70 + page_size)
+    o, lse = binding.decode_paged(bf16_to_device(p.q), bf16_to_device(p.k_pages), bf16_to_device(p.v_pages),
+                                  i32_to_device(p.block_table), i32_to_device(p.seq_lens), 131072,
+                                  f32_to_device(p.sinks), 0, p.scale, splits, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = decode_paged_ref(inputs.bf16_bits_to_f32(p.q), inputs.bf16_bits_to_f32(p.k_pages),
+                              inputs.bf16_bits_to_f32(p.v_pages), p.block_table, p.seq_lens, page_size, p.sinks, 0,
+                              p.scale)
+    what = "long paged decode ps=%d S=%d" % (page_size, splits)
+    assert_close_out(to_f64(o), ro, what)
+    assert_close_lse(lse.cpu().numpy(), rl, what)

@@ -161,3 +161,17 @@ def test_split_debug_checks(monkeypatch):
     with pytest.raises(binding.SinkAttnError) as err:
         binding.prefill_append(q, k[:13], v[:13], sinks, cq, bad_k, 6, 10, 0, a.scale, num_splits=3)
     assert err.value.status == 1 and "fewer keys" in str(err.value)
+
+
+def test_split_append_prefill_is_deterministic():
+    """Repeated calls give bit-identical outputs (no atomics: every partial
+    has one writer and the merge a fixed order)."""
+    a = inputs.make_append([256, 40], [32768, 900], hq=64, hkv=8, seed=995)
+    q, k, v = (bf16_to_device(x) for x in (a.q, a.k, a.v))
+    args = (q, k, v, f32_to_device(a.sinks), i32_to_device(a.cu_seqlens_q), i32_to_device(a.cu_seqlens_k), 256, 32768,
+            0, a.scale)
+    first = binding.prefill_append(*args, num_splits=8)
+    for _ in range(3):
+        again = binding.prefill_append(*args, num_splits=8)
+        torch.cuda.synchronize()
+        assert torch.equal(first, again)
